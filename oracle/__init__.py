@@ -1,0 +1,10 @@
+"""fp64 CPU oracle of the sparse MoE layer -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library and is never a fallback
+for it.
+"""
+from .moe_oracle import (to_f64, router_logits, softmax_rows, top_k_desc, route, selection_gap,
+                         dispatch, Dispatch, silu, gelu, ffn_swiglu, ffn_gelu, expert_apply,
+                         aux_loss, bias_step, oracle_route, oracle_layer, RouteResult,
+                         GATE_TOPK_SOFTMAX, GATE_SOFTMAX_RENORM, GATE_SWITCH_TOP1)

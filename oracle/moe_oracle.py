@@ -1,0 +1,342 @@
+"""fp64 CPU oracle of one sparse Mixture-of-Experts FFN layer (forward pass).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module.  It is the slow, obviously correct statement
+of what the layer computes, and it shares no code with the HIP library.
+
+Every value is computed in float64 from the exact values of the stored inputs
+(fp32, or bfloat16 bit patterns).  A numpy matmul (BLAS dgemm), a stable sort
+and ``scipy.special.erfc`` are the only library steps.
+
+Sources (the pages describing the method; cited by title and section):
+
+[L] "Mixture of Experts (MoE)", AI Engineering from Scratch, Phase 07 lesson 11
+    (aiengineeringfromscratch.com): sections "Concept / FFN swap", "The load
+    balance problem", "Shared experts", "Build it / Step 1: the router",
+    "Step 2: run 100 tokens through the router", "Key terms".
+[N] "MoE architecture: load balancing and gating implementation" (nextadmin.net):
+    the same lesson, cleaner text: "Load balancing" items 1-3, "Shared experts".
+[G] "Mixture of Experts (MoE)" glossary (ultralytics.com): "How an MoE layer
+    works", "Load balancing and expert capacity" (seeded top-2 example and its
+    printed output).
+[X] "Expert Parallelism for MoE Serving" (aiunderstanding.org): "Deep dive",
+    "Technical insight" (dispatch groups tokens by expert; capacity).
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes):
+
+* top-k order: descending key, exact ties to the lower expert index ([L] Step 1
+  sorts the experts with a stable sort on the negated key);
+* softmax subtracts the row maximum before exponentiating ([L] Step 1);
+* SwiGLU expert: ``(SiLU(X W1^T) * (X W3^T)) W2^T``, SiLU on W1, no biases;
+* GELU expert: ``GELU(X W1^T + b1) W2^T + b2`` with the exact erf GELU;
+* capacity ``C = floor(cf * N / E)``; each expert keeps its first C slots in
+  ascending slot id ``s = t*k + j``; a dropped slot contributes nothing and the
+  kept gates of that token are not renormalised;
+* dropped tokens still receive the residual (and the shared expert, if any);
+* auxiliary loss ``E * sum_e f_e * P_e`` with ``f_e = counts_e / (N k)`` from
+  the pre-drop counts and ``P_e`` the full-softmax probability averaged over
+  all N tokens;
+* bias step ``b_e <- b_e - gamma * sign(counts_e * E - N k)``, sign(0) = 0,
+  applied after the forward pass (it feeds the next call only).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+from scipy.special import erfc
+
+GATE_TOPK_SOFTMAX = "topk_softmax"
+GATE_SOFTMAX_RENORM = "softmax_renorm"
+GATE_SWITCH_TOP1 = "switch_top1"
+
+
+# --------------------------------------------------------------------------- inputs
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored fp32 values or bfloat16 bit patterns."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------- router
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, logit_bias=None) -> np.ndarray:
+    """z[t, e] = x[t] . W_r[e] (+ a fixed per-expert logit offset).
+
+    [L] "Build it / Step 1: the router": each expert's score is the dot product
+    of the hidden vector with that expert's router row; [G] "How an MoE layer
+    works": the router is one linear layer scoring every expert for every token.
+    """
+    z = x @ w_router.T
+    if logit_bias is not None:
+        z = z + np.asarray(logit_bias, dtype=np.float64)[None, :]
+    return z
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first ([L] Step 1)."""
+    m = z.max(axis=1, keepdims=True)
+    ez = np.exp(z - m)
+    return ez / ez.sum(axis=1, keepdims=True)
+
+
+def top_k_desc(key: np.ndarray, k: int) -> np.ndarray:
+    """Per row, the k column indices with the largest key, largest first,
+    exact ties to the lower index: a full stable sort on the negated key
+    ([L] Step 1 sorts all experts this way and keeps the first k)."""
+    order = np.argsort(-key, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def route(z: np.ndarray, k: int, rule: str, sel_bias=None):
+    """Selection and gate weights for every token.
+
+    Returns ``(idx [N,k], gates [N,k], p [N,E])`` where ``p`` is the softmax
+    over all E raw logits (used by the auxiliary loss).
+
+    * ``topk_softmax`` ([L] Step 1; [G] example): key = z + selection bias;
+      gate = softmax over the *raw* logits of the k selected experts.
+    * ``softmax_renorm`` ([L] "The load balance problem", DeepSeek-V3 approach;
+      [N] Load balancing item 3): p = softmax(z); key = p + bias; gate = p of
+      the selected experts renormalised to sum 1.  The bias moves selection
+      only; gates use the raw scores.
+    * ``switch_top1`` ([G] "Load balancing and expert capacity": Switch sends
+      each token to one expert): the argmax of z (ties to the lower index);
+      gate = its full-softmax probability, not renormalised.
+    """
+    N, E = z.shape
+    b = np.zeros(E) if sel_bias is None else np.asarray(sel_bias, dtype=np.float32).astype(np.float64)
+    p = softmax_rows(z)
+    if rule == GATE_TOPK_SOFTMAX:
+        idx = top_k_desc(z + b[None, :], k)
+        chosen = np.take_along_axis(z, idx, axis=1)
+        m = chosen.max(axis=1, keepdims=True)
+        ex = np.exp(chosen - m)
+        gates = ex / ex.sum(axis=1, keepdims=True)
+    elif rule == GATE_SOFTMAX_RENORM:
+        idx = top_k_desc(p + b[None, :], k)
+        ps = np.take_along_axis(p, idx, axis=1)
+        gates = ps / ps.sum(axis=1, keepdims=True)
+    elif rule == GATE_SWITCH_TOP1:
+        if k != 1:
+            raise ValueError("switch_top1 routes each token to exactly one expert")
+        idx = top_k_desc(z, 1)
+        gates = np.take_along_axis(p, idx, axis=1)
+    else:
+        raise ValueError(rule)
+    return idx, gates, p
+
+
+def selection_gap(z: np.ndarray, k: int, rule: str, sel_bias=None) -> np.ndarray:
+    """Per token, key[k-th chosen] - key[(k+1)-th]: how far the selection is
+    from a tie (inf when k == E).  Used to report near-ties."""
+    N, E = z.shape
+    if k >= E:
+        return np.full(N, np.inf)
+    b = np.zeros(E) if sel_bias is None else np.asarray(sel_bias, dtype=np.float32).astype(np.float64)
+    if rule == GATE_TOPK_SOFTMAX:
+        key = z + b[None, :]
+    elif rule == GATE_SOFTMAX_RENORM:
+        key = softmax_rows(z) + b[None, :]
+    else:
+        key = z
+    s = -np.sort(-key, axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+# --------------------------------------------------------------------------- dispatch
+
+@dataclass
+class Dispatch:
+    counts: np.ndarray      # [E] pre-drop tokens per expert (sum = N k)
+    offsets: np.ndarray     # [E+1] exclusive scan of kept counts
+    perm: np.ndarray        # [sum kept] slot id s = t*k + j, grouped by expert, ascending within
+    slot_pos: np.ndarray    # [N k] position of slot s in perm, -1 if dropped
+    drop_count: int
+
+
+def dispatch(idx: np.ndarray, n_experts: int, capacity: int | None) -> Dispatch:
+    """Group the N*k slots by expert ([G] example: per expert, the tokens that
+    chose it; [X] "Deep dive": tokens are sent to the holder of their expert).
+
+    Within an expert, slots keep ascending slot id.  With a capacity C
+    ([N] Load balancing item 2: each expert takes at most C * N / E tokens;
+    the overflow skips the experts), only the first C slots of each expert
+    are kept.
+    """
+    expert_of_slot = idx.reshape(-1)
+    n_slots = expert_of_slot.size
+    counts = np.zeros(n_experts, dtype=np.int64)
+    kept_lists = []
+    drop = 0
+    for e in range(n_experts):
+        slots = np.nonzero(expert_of_slot == e)[0]          # ascending slot id
+        counts[e] = slots.size
+        if capacity is not None and slots.size > capacity:
+            drop += slots.size - capacity
+            slots = slots[:capacity]
+        kept_lists.append(slots)
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum([len(s) for s in kept_lists])
+    perm = np.concatenate(kept_lists) if kept_lists else np.zeros(0, np.int64)
+    slot_pos = np.full(n_slots, -1, dtype=np.int64)
+    slot_pos[perm] = np.arange(perm.size)
+    return Dispatch(counts=counts, offsets=offsets, perm=perm.astype(np.int64),
+                    slot_pos=slot_pos, drop_count=int(drop))
+
+
+# --------------------------------------------------------------------------- experts
+
+def silu(u: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return u / (1.0 + np.exp(-u))
+
+
+def gelu(u: np.ndarray) -> np.ndarray:
+    """Exact (erf) GELU, the form torch.nn.GELU() uses by default ([G] example):
+    u * Phi(u) with Phi(u) = (1 + erf(u/sqrt 2))/2, written as erfc(-u/sqrt 2)/2
+    so the negative tail keeps its relative precision."""
+    return u * 0.5 * erfc(-u / math.sqrt(2.0))
+
+
+def ffn_swiglu(X: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """SwiGLU feed-forward ([L] "FFN swap": each expert is usually a SwiGLU FFN)."""
+    return (silu(X @ w1.T) * (X @ w3.T)) @ w2.T
+
+
+def ffn_gelu(X: np.ndarray, w1: np.ndarray, b1, w2: np.ndarray, b2) -> np.ndarray:
+    """Linear -> GELU -> Linear expert ([G] example's expert form)."""
+    h = X @ w1.T
+    if b1 is not None:
+        h = h + b1[None, :]
+    y = gelu(h) @ w2.T
+    if b2 is not None:
+        y = y + b2[None, :]
+    return y
+
+
+def expert_apply(act: str, X: np.ndarray, w: dict) -> np.ndarray:
+    if act == "swiglu":
+        return ffn_swiglu(X, w["w1"], w["w3"], w["w2"])
+    if act == "gelu":
+        return ffn_gelu(X, w["w1"], w.get("b1"), w["w2"], w.get("b2"))
+    raise ValueError(act)
+
+
+# --------------------------------------------------------------------------- balancing
+
+def aux_loss(counts: np.ndarray, p: np.ndarray, k: int) -> float:
+    """E * sum_e f_e * P_e: f_e = counts_e / (N k) (pre-drop), P_e = mean_t p[t,e].
+
+    [G] "Load balancing and expert capacity": Switch adds a loss term that is
+    smallest when tokens and router probabilities are spread evenly; [N] item 1.
+    """
+    N, E = p.shape
+    f = counts.astype(np.float64) / float(N * k)
+    P = p.sum(axis=0) / float(N)
+    return float(E * np.sum(f * P))
+
+
+def bias_step(counts: np.ndarray, sel_bias: np.ndarray, gamma: float, n_tokens: int, k: int):
+    """Aux-loss-free balancing ([L] "The load balance problem", DeepSeek-V3
+    approach; [L] Step 2): after a step, each expert whose load is above the
+    target N k / E moves its selection bias down by gamma, one below it moves
+    it up.  Returns (signs [E] int, updated bias [E] float64)."""
+    E = counts.size
+    diff = counts.astype(np.int64) * E - int(n_tokens) * int(k)   # load - target, times E
+    signs = np.sign(diff).astype(np.int64)
+    b = np.asarray(sel_bias, dtype=np.float32).astype(np.float64)
+    g = float(np.float32(gamma))
+    return signs, b - g * signs
+
+
+# --------------------------------------------------------------------------- layer
+
+@dataclass
+class RouteResult:
+    logits: np.ndarray
+    topk_idx: np.ndarray
+    gates: np.ndarray
+    probs: np.ndarray
+    disp: Dispatch
+    aux: float | None
+    signs: np.ndarray | None
+    new_bias: np.ndarray | None
+    min_gap: float
+
+
+def oracle_route(cfg, logits: np.ndarray, sel_bias=None) -> RouteResult:
+    """Everything the layer decides from the logits: selection, gates,
+    counts, permutation, capacity, aux loss and the bias step."""
+    z = np.asarray(logits, dtype=np.float64)
+    idx, gates, p = route(z, cfg.top_k, cfg.gate_rule, sel_bias)
+    d = dispatch(idx, cfg.n_experts, cfg.capacity)
+    aux = aux_loss(d.counts, p, cfg.top_k) if cfg.aux_loss else None
+    signs = new_bias = None
+    if cfg.gamma > 0:
+        b = sel_bias if sel_bias is not None else np.zeros(cfg.n_experts, np.float32)
+        signs, new_bias = bias_step(d.counts, b, cfg.gamma, cfg.n_tokens, cfg.top_k)
+    gap = selection_gap(z, cfg.top_k, cfg.gate_rule, sel_bias)
+    return RouteResult(logits=z, topk_idx=idx, gates=gates, probs=p, disp=d, aux=aux,
+                       signs=signs, new_bias=new_bias, min_gap=float(gap.min()) if gap.size else math.inf)
+
+
+def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"):
+    """The whole forward pass in fp64.
+
+    ``inputs`` is a :class:`workloads.LayerInputs`.  ``logits_override`` replaces
+    the router product (parity hook: the GPU's fp32 logits decide routing on
+    both sides).  ``rows`` restricts the expert work and the output to those
+    tokens (routing, counts and capacity still cover all N).
+
+    [L] "Concept / FFN swap": h + sum over the chosen experts of gate * expert(h);
+    [G] example: out[tokens of e] += weight * expert_e(tokens of e) for each e;
+    [L] "Shared experts": every token also passes through the shared expert.
+    """
+    dt = cfg.dtype
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    x = to_f64(inputs.x, dt)
+    if logits_override is None:
+        z = router_logits(x, to_f64(inputs.w_router, dt), inputs.logit_bias)
+    else:
+        z = np.asarray(logits_override, dtype=np.float32).astype(np.float64)
+    sb = inputs.sel_bias if isinstance(sel_bias, str) else sel_bias
+    r = oracle_route(cfg, z, sb)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    want = np.zeros(N, dtype=bool)
+    want[rows] = True
+
+    d_model = cfg.d_model
+    y_slot = {}
+    expert_of_slot = r.topk_idx.reshape(-1)
+    for e in range(E):
+        lo, hi = r.disp.offsets[e], r.disp.offsets[e + 1]
+        slots = r.disp.perm[lo:hi]
+        slots = slots[want[slots // k]]
+        if slots.size == 0:
+            continue
+        assert np.all(expert_of_slot[slots] == e)
+        w = {n: to_f64(v, dt) for n, v in inputs.expert(e).items()}
+        Y = expert_apply(cfg.act, x[slots // k], w)
+        for s, yrow in zip(slots, Y):
+            y_slot[int(s)] = yrow
+
+    out = np.zeros((rows.size, d_model))
+    if cfg.residual:
+        out += x[rows]
+    if cfg.d_ff_shared > 0:
+        sw = {"w1": to_f64(inputs.sh_w1, dt), "w3": to_f64(inputs.sh_w3, dt), "w2": to_f64(inputs.sh_w2, dt)}
+        out += ffn_swiglu(x[rows], sw["w1"], sw["w3"], sw["w2"])
+    for i, t in enumerate(rows):
+        for j in range(k):
+            s = int(t) * k + j
+            if r.disp.slot_pos[s] >= 0:
+                out[i] += r.gates[t, j] * y_slot[s]
+    return r, out

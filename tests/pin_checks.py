@@ -1,0 +1,387 @@
+"""Checks that pin the fp64 oracle to facts outside itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with what the
+pages print, with a closed form, with brute force on tiny inputs, or with an
+independent library routine.  ``test_oracle_pins.py`` runs them as they are;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle and shows
+that some check catches each one.
+"""
+from __future__ import annotations
+
+import ast
+import os
+
+import numpy as np
+import scipy.special
+import torch
+import torch.nn.functional as TF
+
+import oracle.moe_oracle as mo
+from workloads import (TINY_TOP2_FP32, MoEConfig, make_inputs, GATE_TOPK_SOFTMAX,
+                       GATE_SOFTMAX_RENORM, GATE_SWITCH_TOP1)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split("=", 1)
+            vals[k.strip()] = ast.literal_eval(v.strip())
+    return vals
+
+
+# ----------------------------------------------------------------- printed example
+
+def check_printed_example():
+    """Glossary page, "Load balancing and expert capacity": the seeded top-2
+    example prints the chosen expert pairs and the tokens per expert."""
+    g = _golden("glossary_top2_example.txt")
+    inp = make_inputs(TINY_TOP2_FP32)
+    r, _ = mo.oracle_layer(TINY_TOP2_FP32, inp)
+    assert r.topk_idx.tolist() == g["experts_per_token"], r.topk_idx.tolist()
+    assert r.disp.counts.tolist() == g["tokens_per_expert"], r.disp.counts.tolist()
+
+
+def check_printed_example_output():
+    """The same example's layer output, computed here with torch's own fp32
+    modules (every expert run densely on every token, then masked), agrees
+    with the oracle to fp32 accuracy."""
+    cfg = TINY_TOP2_FP32
+    inp = make_inputs(cfg)
+    _, out = mo.oracle_layer(cfg, inp)
+    x = torch.from_numpy(inp.x)
+    router = torch.nn.Linear(cfg.d_model, cfg.n_experts, bias=False)
+    with torch.no_grad():
+        router.weight.copy_(torch.from_numpy(inp.w_router))
+        logits = router(x)
+        top_val, top_idx = torch.topk(logits, cfg.top_k, dim=-1)
+        w = torch.softmax(top_val, dim=-1)
+        ref = torch.zeros_like(x)
+        for e in range(cfg.n_experts):
+            l1 = torch.nn.Linear(cfg.d_model, cfg.d_ff)
+            l2 = torch.nn.Linear(cfg.d_ff, cfg.d_model)
+            l1.weight.copy_(torch.from_numpy(inp.w1[e])); l1.bias.copy_(torch.from_numpy(inp.b1[e]))
+            l2.weight.copy_(torch.from_numpy(inp.w2[e])); l2.bias.copy_(torch.from_numpy(inp.b2[e]))
+            ye = l2(torch.nn.GELU()(l1(x)))                      # all tokens, dense
+            mask = (top_idx == e).to(torch.float32)              # [N, k]
+            ref += (mask * w).sum(dim=1, keepdim=True) * ye
+    ref = ref.double().numpy()
+    err = np.abs(out - ref).max() / np.abs(ref).max()
+    assert err <= 1e-5, err
+
+
+# ----------------------------------------------------------------- selection
+
+def _brute_rank(key_row):
+    """rank[e] = #{e' : key[e'] > key[e] or (key[e'] == key[e] and e' < e)}."""
+    E = key_row.size
+    return np.array([sum(1 for f in range(E) if key_row[f] > key_row[e] or (key_row[f] == key_row[e] and f < e))
+                     for e in range(E)])
+
+
+def _brute_topk(key, k):
+    out = np.zeros((key.shape[0], k), np.int64)
+    for t in range(key.shape[0]):
+        rank = _brute_rank(key[t])
+        for e in range(key.shape[1]):
+            if rank[e] < k:
+                out[t, rank[e]] = e
+    return out
+
+
+def _tiny_keys(seed, N=40, E=8, tie_heavy=True):
+    rng = np.random.default_rng(seed)
+    if tie_heavy:
+        return rng.choice(np.array([-1.0, 0.25, 0.5]), size=(N, E))
+    return rng.standard_normal((N, E))
+
+
+def check_topk_brute_force():
+    """Top-k with ties to the lower index equals an O(E^2) brute-force rank."""
+    for seed in range(6):
+        for E in (1, 3, 8):
+            for k in range(1, E + 1):
+                key = _tiny_keys(seed, E=E, tie_heavy=seed % 2 == 0)
+                assert np.array_equal(mo.top_k_desc(key, k), _brute_topk(key, k)), (seed, E, k)
+
+
+def check_route_selection_brute_force():
+    """Each gate rule selects by its own key: A on z + b, B on softmax(z) + b,
+    C on z alone; compared against the brute-force rank."""
+    rng = np.random.default_rng(7)
+    for E, k in ((8, 2), (6, 3), (5, 1)):
+        z = rng.choice(np.array([-0.5, 0.0, 0.75, 1.0]), size=(30, E))
+        b = rng.choice(np.array([0.0, 0.25]), size=E).astype(np.float32)
+        idx, _, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, b)
+        assert np.array_equal(idx, _brute_topk(z + b.astype(np.float64), k))
+        idx, _, _ = mo.route(z, k, GATE_SOFTMAX_RENORM, b)
+        p = scipy.special.softmax(z, axis=1)
+        assert np.array_equal(idx, _brute_topk(p + b.astype(np.float64), k))
+        idx, _, _ = mo.route(z, 1, GATE_SWITCH_TOP1, None)
+        assert np.array_equal(idx, _brute_topk(z, 1))
+
+
+# ----------------------------------------------------------------- gates
+
+def check_softmax_library():
+    """Row softmax equals scipy's, including rows whose logits would overflow exp."""
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((20, 9)) * 4
+    z[0] = 1000.0 + np.arange(9)
+    z[1] = -1000.0 - np.arange(9)
+    ref = scipy.special.softmax(z, axis=1)
+    got = mo.softmax_rows(z)
+    assert np.all(np.isfinite(got))
+    assert np.allclose(got, ref, rtol=1e-13, atol=0)
+
+
+def check_gate_closed_forms():
+    rng = np.random.default_rng(11)
+    N, E, k = 64, 8, 3
+    z = rng.standard_normal((N, E)) * 2
+    # rule A: softmax over the selected raw logits (scipy on the selected values)
+    idx, g, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, None)
+    ref = scipy.special.softmax(np.take_along_axis(z, idx, 1), axis=1)
+    assert np.allclose(g, ref, rtol=1e-13, atol=1e-15)
+    assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-14)
+    # rule A == rule B without bias: softmax over S equals p_S / sum p_S
+    idxb, gb, _ = mo.route(z, k, GATE_SOFTMAX_RENORM, None)
+    assert np.array_equal(idx, idxb)
+    assert np.allclose(g, gb, rtol=1e-12, atol=1e-15)
+    # rule C: gate is the full-softmax probability of the argmax, at least 1/E
+    idxc, gc, _ = mo.route(z, 1, GATE_SWITCH_TOP1, None)
+    p = scipy.special.softmax(z, axis=1)
+    assert np.array_equal(idxc[:, 0], np.argmax(z, axis=1))
+    assert np.allclose(gc[:, 0], p[np.arange(N), idxc[:, 0]], rtol=1e-13)
+    assert np.all(gc >= 1.0 / E - 1e-15)
+
+
+def check_bias_moves_selection_not_gates():
+    """[L] Step 1: the bias changes which experts are picked, never the gate
+    values computed from the raw scores."""
+    rng = np.random.default_rng(5)
+    N, E, k = 200, 8, 2
+    z = rng.standard_normal((N, E))
+    b = (rng.random(E).astype(np.float32) - np.float32(0.5)) * np.float32(0.6)
+    for rule in (GATE_TOPK_SOFTMAX, GATE_SOFTMAX_RENORM):
+        i0, g0, _ = mo.route(z, k, rule, None)
+        i1, g1, _ = mo.route(z, k, rule, b)
+        same = np.array([set(i0[t]) == set(i1[t]) for t in range(N)])
+        changed = ~same
+        assert same.sum() > 0 and changed.sum() > 0
+        for t in np.nonzero(same)[0]:
+            m0 = dict(zip(i0[t], g0[t]))
+            m1 = dict(zip(i1[t], g1[t]))
+            assert all(abs(m0[e] - m1[e]) < 1e-14 for e in m0)
+    # a bias large enough to force expert 5 in: its gate is the raw-logit softmax over the forced set
+    bf = np.zeros(E, np.float32)
+    bf[5] = 100.0
+    i2, g2, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, bf)
+    assert np.all(i2[:, 0] == 5)
+    ref = scipy.special.softmax(np.take_along_axis(z, i2, 1), axis=1)
+    assert np.allclose(g2, ref, rtol=1e-13)
+
+
+# ----------------------------------------------------------------- dispatch / capacity
+
+def check_dispatch_invariants():
+    rng = np.random.default_rng(9)
+    for E, k, N in ((8, 2, 50), (16, 4, 33), (5, 1, 17)):
+        z = rng.standard_normal((N, E))
+        idx, _, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, None)
+        d = mo.dispatch(idx, E, None)
+        assert int(d.counts.sum()) == N * k                              # exactly k experts per token
+        assert np.array_equal(d.counts, np.bincount(idx.reshape(-1), minlength=E))
+        assert sorted(d.perm.tolist()) == list(range(N * k))            # a permutation of all slots
+        assert d.offsets[0] == 0 and d.offsets[-1] == N * k
+        for e in range(E):
+            seg = d.perm[d.offsets[e]:d.offsets[e + 1]]
+            assert np.all(np.diff(seg) > 0)                              # ascending slot id
+            assert np.all(idx.reshape(-1)[seg] == e)
+        assert np.array_equal(d.perm[d.slot_pos], np.arange(N * k))
+        assert d.drop_count == 0
+
+
+def check_capacity_brute_force():
+    """Each expert keeps the first C of its slots in slot order; drop = sum max(0, count - C)."""
+    rng = np.random.default_rng(21)
+    for E, k, N, C in ((4, 1, 40, 6), (8, 2, 30, 5), (6, 3, 20, 0)):
+        z = rng.standard_normal((N, E))
+        z[:, 1] += 1.0                                                   # skew towards expert 1
+        idx, _, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, None)
+        d = mo.dispatch(idx, E, C)
+        es = idx.reshape(-1)
+        for s in range(N * k):
+            rank = int(np.sum(es[:s] == es[s]))                          # earlier slots on the same expert
+            assert (d.slot_pos[s] >= 0) == (rank < C), (s, rank, C)
+        assert np.array_equal(np.diff(d.offsets), np.minimum(d.counts, C))
+        assert d.drop_count == int(np.maximum(d.counts - C, 0).sum())
+
+
+# ----------------------------------------------------------------- layer reductions
+
+def _small_inputs(cfg, w_override=None, seed=0):
+    """fp32 inputs drawn directly (independent of the workload presets)."""
+    rng = np.random.default_rng(seed)
+    N, d, E, F = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.d_ff
+
+    class Inp:
+        pass
+    inp = Inp()
+    inp.cfg = cfg
+    inp.x = rng.standard_normal((N, d)).astype(np.float32)
+    inp.w_router = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    inp.logit_bias = None
+    inp.sel_bias = None
+    ws = []
+    for e in range(E):
+        w = {"w1": (rng.standard_normal((F, d)) / np.sqrt(d)).astype(np.float32),
+             "w2": (rng.standard_normal((d, F)) / np.sqrt(F)).astype(np.float32)}
+        if cfg.act == "swiglu":
+            w["w3"] = (rng.standard_normal((F, d)) / np.sqrt(d)).astype(np.float32)
+        if cfg.ffn_bias:
+            w["b1"] = rng.standard_normal(F).astype(np.float32) * np.float32(0.1)
+            w["b2"] = rng.standard_normal(d).astype(np.float32) * np.float32(0.1)
+        ws.append(w)
+    if w_override == "identical":
+        ws = [ws[0]] * E
+    inp.expert = lambda e: ws[e]
+    inp.sh_w1 = inp.sh_w3 = inp.sh_w2 = None
+    return inp, ws
+
+
+def _torch_dense_ffn(act, x, w):
+    """Dense FFN in torch float64 (library ops, independent of the oracle)."""
+    X = torch.from_numpy(x.astype(np.float64))
+    t = {k: torch.from_numpy(v.astype(np.float64)) for k, v in w.items()}
+    if act == "swiglu":
+        h = TF.silu(TF.linear(X, t["w1"])) * TF.linear(X, t["w3"])
+        return TF.linear(h, t["w2"]).numpy()
+    h = TF.gelu(TF.linear(X, t["w1"], t.get("b1")), approximate="none")
+    return TF.linear(h, t["w2"], t.get("b2")).numpy()
+
+
+def check_single_expert_is_dense():
+    """E = 1, k = 1: the layer is x + FFN(x) (the dense block of [L] "FFN swap")."""
+    for act, bias in (("swiglu", False), ("gelu", True)):
+        cfg = MoEConfig(name="dense", n_tokens=13, d_model=24, n_experts=1, top_k=1, d_ff=40,
+                        act=act, ffn_bias=bias, dtype="f32", residual=True)
+        inp, ws = _small_inputs(cfg, seed=1)
+        _, out = mo.oracle_layer(cfg, inp)
+        ref = inp.x.astype(np.float64) + _torch_dense_ffn(act, inp.x, ws[0])
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12), np.abs(out - ref).max()
+
+
+def check_identical_experts_are_dense():
+    """With every expert identical, gates summing to 1 make any top-k layer dense
+    (rules A and B); rule C scales the dense FFN by the chosen probability."""
+    for rule, k in ((GATE_TOPK_SOFTMAX, 3), (GATE_SOFTMAX_RENORM, 2), (GATE_SWITCH_TOP1, 1)):
+        for act, bias in (("swiglu", False), ("gelu", True)):
+            cfg = MoEConfig(name="ident", n_tokens=11, d_model=16, n_experts=5, top_k=k, d_ff=20,
+                            act=act, ffn_bias=bias, dtype="f32", residual=True, gate_rule=rule)
+            inp, ws = _small_inputs(cfg, w_override="identical", seed=2)
+            r, out = mo.oracle_layer(cfg, inp)
+            dense = _torch_dense_ffn(act, inp.x, ws[0])
+            scale = np.ones((cfg.n_tokens, 1))
+            if rule == GATE_SWITCH_TOP1:
+                z = inp.x.astype(np.float64) @ inp.w_router.astype(np.float64).T
+                scale = scipy.special.softmax(z, axis=1).max(axis=1, keepdims=True)
+            ref = inp.x.astype(np.float64) + scale * dense
+            assert np.allclose(out, ref, rtol=1e-12, atol=1e-12), (rule, act, np.abs(out - ref).max())
+
+
+def check_dropped_tokens_pass_residual():
+    """[N] item 2 / [G]: overflow tokens skip the experts and keep the residual."""
+    cfg = MoEConfig(name="cap", n_tokens=40, d_model=16, n_experts=4, top_k=1, d_ff=12, act="gelu",
+                    ffn_bias=True, dtype="f32", residual=True, gate_rule=GATE_SWITCH_TOP1,
+                    capacity_factor=0.5)
+    inp, _ = _small_inputs(cfg, seed=4)
+    inp.logit_bias = np.array([0, 3.0, 0, 0], np.float32)              # most tokens want expert 1
+    r, out = mo.oracle_layer(cfg, inp)
+    dropped = np.nonzero(r.disp.slot_pos < 0)[0]
+    assert dropped.size > 0 and cfg.capacity == 5
+    x64 = inp.x.astype(np.float64)
+    assert np.array_equal(out[dropped], x64[dropped])
+    kept = np.nonzero(r.disp.slot_pos >= 0)[0]
+    assert not np.array_equal(out[kept], x64[kept])
+
+
+# ----------------------------------------------------------------- balancing
+
+def check_aux_uniform_is_one():
+    """[G]: the Switch term is smallest (here: exactly 1) when the router
+    probabilities are uniform, whatever the counts; and it reaches E when all
+    tokens and all probability mass sit on one expert."""
+    for E, k, N in ((8, 2, 30), (64, 1, 100), (5, 1, 7)):
+        z = np.zeros((N, E))
+        idx, _, p = mo.route(z, k, GATE_TOPK_SOFTMAX if k > 1 else GATE_SWITCH_TOP1, None)
+        d = mo.dispatch(idx, E, max(1, N // (4 * E)))                  # heavy dropping on purpose
+        assert abs(mo.aux_loss(d.counts, p, k) - 1.0) < 1e-12
+    E, N = 16, 50
+    z = np.full((N, E), -60.0)
+    z[:, 3] = 60.0
+    idx, _, p = mo.route(z, 1, GATE_SWITCH_TOP1, None)
+    d = mo.dispatch(idx, E, None)
+    assert abs(mo.aux_loss(d.counts, p, 1) - E) < 1e-9
+
+
+def check_bias_step_signs():
+    """[L] DeepSeek-V3 approach: over-target experts move down by gamma,
+    under-target up by gamma, on-target stay."""
+    E, N, k = 8, 12, 2                                                  # target N k / E = 3
+    counts = np.array([3, 4, 2, 0, 9, 3, 1, 2])
+    b = np.array([0.01, -0.02, 0, 0.5, -0.5, 0.25, 1.0, -1.0], np.float32)
+    gamma = 1e-3
+    signs, nb = mo.bias_step(counts, b, gamma, N, k)
+    assert signs.tolist() == [0, 1, -1, -1, 1, 0, -1, -1]
+    g32 = float(np.float32(gamma))
+    for e in range(E):
+        want = float(b[e]) - g32 * (1 if counts[e] > 3 else -1 if counts[e] < 3 else 0)
+        assert abs(nb[e] - want) < 1e-15
+
+
+def check_bias_loop_equalises():
+    """[L] Step 2 / Exercises: repeated bias steps even out expert usage on a
+    DeepSeek-V3-shaped batch (256 experts, top-8, bias ~ U(+-0.05), gamma 1e-3).
+    The pages give no number; the bar here is a 10x drop of the load spread."""
+    rng = np.random.default_rng(1234)
+    N, E, k, gamma = 4096, 256, 8, 1e-3
+    z = rng.standard_normal((N, E))
+    b = ((rng.random(E) * 2 - 1) * 0.05).astype(np.float32)
+    std0 = None
+    for _ in range(50):
+        idx, _, _ = mo.route(z, k, GATE_SOFTMAX_RENORM, b)
+        counts = np.bincount(idx.reshape(-1), minlength=E)
+        if std0 is None:
+            std0 = counts.std()
+        _, nb = mo.bias_step(counts, b, gamma, N, k)
+        b = nb.astype(np.float32)
+    idx, _, _ = mo.route(z, k, GATE_SOFTMAX_RENORM, b)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    assert counts.min() > 0
+    assert counts.std() * 10 <= std0, (std0, counts.std())
+
+
+def check_activation_library():
+    """SiLU and exact GELU against 40-digit mpmath evaluations over [-30, 30]
+    (relative error), and against torch's float64 ops where those are accurate."""
+    import mpmath
+    mpmath.mp.dps = 40
+    u = np.linspace(-30, 30, 601)
+    s_ref = np.array([float(mpmath.mpf(v) / (1 + mpmath.exp(-mpmath.mpf(v)))) for v in u])
+    g_ref = np.array([float(mpmath.mpf(v) * mpmath.erfc(-mpmath.mpf(v) / mpmath.sqrt(2)) / 2) for v in u])
+    nz = (g_ref != 0) & (s_ref != 0)
+    assert np.max(np.abs(mo.silu(u)[nz] - s_ref[nz]) / np.abs(s_ref[nz])) < 1e-14
+    assert np.max(np.abs(mo.gelu(u)[nz] - g_ref[nz]) / np.abs(g_ref[nz])) < 1e-12
+    v = np.linspace(-6, 6, 1201)
+    V = torch.from_numpy(v)
+    assert np.allclose(mo.silu(v), TF.silu(V).numpy(), rtol=1e-14, atol=1e-16)
+    assert np.allclose(mo.gelu(v), TF.gelu(V, approximate="none").numpy(), rtol=1e-12, atol=1e-14)
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

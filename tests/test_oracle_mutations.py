@@ -1,0 +1,119 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show a pin catches each.
+
+Every mutation replaces one oracle function with a subtly wrong variant; the
+named checks must then fail.  This guards the pins themselves: a pin set that
+still passed with a dropped term, a wrong sign or a swapped operand would not
+be pinning anything.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as mo
+import pin_checks as pc
+
+_orig = {n: getattr(mo, n) for n in ("top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
+                                       "aux_loss", "bias_step", "softmax_rows", "oracle_layer")}
+
+
+def _ties_to_higher(key, k):
+    E = key.shape[1]
+    order = np.argsort(-key[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int64)
+
+
+def _gates_from_biased_key(z, k, rule, sel_bias=None):
+    if sel_bias is None or rule != mo.GATE_TOPK_SOFTMAX:
+        return _orig["route"](z, k, rule, sel_bias)
+    zb = z + np.asarray(sel_bias, np.float64)[None, :]
+    idx, _, p = _orig["route"](z, k, rule, sel_bias)
+    ch = np.take_along_axis(zb, idx, 1)
+    ex = np.exp(ch - ch.max(1, keepdims=True))
+    return idx, ex / ex.sum(1, keepdims=True), p
+
+
+def _silu_on_w3(X, w1, w3, w2):
+    return (mo.silu(X @ w3.T) * (X @ w1.T)) @ w2.T
+
+
+def _gelu_tanh(u):
+    return 0.5 * u * (1 + np.tanh(np.sqrt(2 / np.pi) * (u + 0.044715 * u ** 3)))
+
+
+def _gelu_no_b2(X, w1, b1, w2, b2):
+    return _orig["ffn_gelu"](X, w1, b1, w2, None)
+
+
+def _keep_last(idx, E, C):
+    d = _orig["dispatch"](idx, E, None)
+    if C is None:
+        return d
+    es = idx.reshape(-1)
+    lists, drop = [], 0
+    for e in range(E):
+        s = np.nonzero(es == e)[0]
+        if s.size > C:
+            drop += s.size - C
+            s = s[-C:] if C > 0 else s[:0]
+        lists.append(s)
+    perm = np.concatenate(lists)
+    offs = np.zeros(E + 1, np.int64)
+    offs[1:] = np.cumsum([len(s) for s in lists])
+    sp = np.full(es.size, -1, np.int64)
+    sp[perm] = np.arange(perm.size)
+    return mo.Dispatch(d.counts, offs, perm, sp, drop)
+
+
+def _descending_segments(idx, E, C):
+    d = _orig["dispatch"](idx, E, C)
+    perm = d.perm.copy()
+    for e in range(E):
+        perm[d.offsets[e]:d.offsets[e + 1]] = perm[d.offsets[e]:d.offsets[e + 1]][::-1]
+    sp = np.full(d.slot_pos.size, -1, np.int64)
+    sp[perm] = np.arange(perm.size)
+    return mo.Dispatch(d.counts, d.offsets, perm, sp, d.drop_count)
+
+
+def _aux_post_drop(counts, p, k):
+    N, E = p.shape
+    C = max(1, N // (4 * E))
+    return _orig["aux_loss"](np.minimum(counts, C), p, k)
+
+
+def _bias_sign_flipped(counts, b, gamma, N, k):
+    s, nb = _orig["bias_step"](counts, b, gamma, N, k)
+    return s, np.asarray(b, np.float32).astype(np.float64) + float(np.float32(gamma)) * s
+
+
+def _softmax_no_max(z):
+    ez = np.exp(z)
+    return ez / ez.sum(1, keepdims=True)
+
+
+def _layer_no_residual(cfg, inputs, *a, **kw):
+    import dataclasses
+    return _orig["oracle_layer"](dataclasses.replace(cfg, residual=False), inputs, *a, **kw)
+
+
+MUTATIONS = [
+    ("top_k_desc", _ties_to_higher, [pc.check_topk_brute_force]),
+    ("route", _gates_from_biased_key, [pc.check_bias_moves_selection_not_gates]),
+    ("ffn_swiglu", _silu_on_w3, [pc.check_single_expert_is_dense, pc.check_identical_experts_are_dense]),
+    ("gelu", _gelu_tanh, [pc.check_activation_library, pc.check_single_expert_is_dense]),
+    ("ffn_gelu", _gelu_no_b2, [pc.check_single_expert_is_dense, pc.check_printed_example_output]),
+    ("dispatch", _keep_last, [pc.check_capacity_brute_force]),
+    ("dispatch", _descending_segments, [pc.check_dispatch_invariants]),
+    ("aux_loss", _aux_post_drop, [pc.check_aux_uniform_is_one]),
+    ("bias_step", _bias_sign_flipped, [pc.check_bias_step_signs, pc.check_bias_loop_equalises]),
+    ("softmax_rows", _softmax_no_max, [pc.check_softmax_library]),
+    ("oracle_layer", _layer_no_residual, [pc.check_single_expert_is_dense, pc.check_dropped_tokens_pass_residual]),
+]
+
+
+@pytest.mark.parametrize("name,fn,checks", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, fn, checks):
+    monkeypatch.setattr(mo, name, fn)
+    if name == "oracle_layer":
+        monkeypatch.setattr(pc.mo, name, fn)
+    for check in checks:
+        with pytest.raises((AssertionError, FloatingPointError, ValueError)):
+            check()
