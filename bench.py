@@ -1,0 +1,223 @@
+"""Benchmark of the single-GPU MoE layer (forward pass) on MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic input:
+router GEMM + top-k -> histogram/scan/permute/gather -> grouped expert GEMMs
+(up with fused activation, down) -> [shared expert] -> combine -> [aux loss]
+-> [bias step], each a C-ABI call into libmoe_hip.so on one HIP stream.
+Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  `value` is layer tokens/s; `roofline` describes the
+dominant kernel (the grouped up-projection GEMM with the fused activation),
+timed with HIP events around its launches inside the timed region;
+`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec @DeepSeek-V3 & Mixtral shapes; % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", "grouped_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--oracle-tokens", type=int, default=None,
+                    help="tokens in the CPU-baseline sample (default: whole batch for prefill shapes)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from rocprofv3 counters, if
+    they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        ent = t.get(workload)
+        if ent and ent.get("kernel_src_sha256_16") == src_hash(GEMM_SRC):
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's layer; --gpus {args.gpus} is not supported "
+              "(this build uses a single GPU and no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import BY_NAME, make_inputs
+
+    cfg = BY_NAME[args.config]
+    dev_name = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg)
+    dev = M.upload_inputs(inp, dev_name)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+
+    c = M.config_from(cfg)
+    N, E, k, d, F, Fs = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    st = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    i32, f32 = torch.int32, torch.float32
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device=dev_name)
+    z = torch.empty((N, E), dtype=f32, device=dev_name)
+    idx = torch.empty((N, k), dtype=i32, device=dev_name)
+    gates = torch.empty((N, k), dtype=f32, device=dev_name)
+    probsum = torch.empty(E, dtype=f32, device=dev_name) if cfg.aux_loss else None
+    counts = torch.empty(E, dtype=i32, device=dev_name)
+    offs = torch.empty(E + 1, dtype=i32, device=dev_name)
+    perm = torch.empty(N * k, dtype=i32, device=dev_name)
+    slot_pos = torch.empty(N * k, dtype=i32, device=dev_name)
+    drop = torch.empty(1, dtype=torch.int64, device=dev_name)
+    x_perm = torch.empty((N * k, d), dtype=st, device=dev_name)
+    h = torch.empty((N * k, F), dtype=st, device=dev_name)
+    y = torch.empty((N * k, d), dtype=st, device=dev_name)
+    h_sh = torch.empty((N, Fs), dtype=st, device=dev_name) if Fs else None
+    y_sh = torch.empty((N, d), dtype=st, device=dev_name) if Fs else None
+    out = torch.empty((N, d), dtype=st, device=dev_name)
+    aux = torch.empty(1, dtype=f32, device=dev_name) if cfg.aux_loss else None
+    signs = torch.empty(E, dtype=torch.int8, device=dev_name)
+    # the bias step writes a copy, so every timed step routes with the same selection bias
+    sel_next = dev["sel_bias"].clone() if dev["sel_bias"] is not None else None
+    residual = dev["x"] if cfg.residual else None
+
+    names = ["route", "permute", "expert_up", "expert_down", "shared", "combine", "aux_bias"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        M.route(c, dev["x"], dev["w_router"], idx, gates, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"],
+                logits=z, probsum=probsum, ws=ws)
+        mark(1)
+        M.permute(c, idx, dev["x"], counts, offs, perm, slot_pos, x_perm, drop_count=drop, ws=ws)
+        mark(2)
+        M.expert_up(c, x_perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+        mark(3)
+        M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
+        mark(4)
+        if Fs:
+            M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], h_sh, y_sh, ws=ws)
+        mark(5)
+        M.combine(c, y, slot_pos, gates, out, residual=residual, shared_y=y_sh)
+        mark(6)
+        if cfg.aux_loss:
+            M.aux_loss(c, counts, probsum, aux)
+        if cfg.gamma > 0:
+            M.bias_update(c, counts, cfg.gamma, sel_next, signs)
+        mark(7)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K
+    parts = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+             for j, n in enumerate(names)}
+
+    kept = int(offs[-1].item())
+    n_up = 2 if cfg.act == "swiglu" else 1
+    up_flop = 2.0 * n_up * d * F * kept
+    down_flop = 2.0 * F * d * kept
+    up_tflops = up_flop / (parts["expert_up"] * 1e-3) / 1e12
+    expert_tflops = (up_flop + down_flop) / ((parts["expert_up"] + parts["expert_down"]) * 1e-3) / 1e12
+    traffic = measured_traffic(cfg.name)
+
+    result = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random weights of the named shapes)",
+        "config": {"workload": cfg.name, "n_tokens": N, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
+                   "d_ff_shared": Fs, "act": cfg.act, "gate_rule": cfg.gate_rule,
+                   "capacity_factor": cfg.capacity_factor, "kept_slots": kept},
+        "roofline": {"kernel": "grouped_gemm_bf16_kernel (expert up-projection, fused activation)",
+                     "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "expert_gemm_tflops": expert_tflops,
+        "breakdown_ms": parts,
+        "wall_s_timed": wall_s,
+        "input_gen_s": gen_s,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, inp, n_tok):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    N = cfg.n_tokens
+    if n_tok is None:
+        n_tok = N if N * cfg.d_model * cfg.d_ff <= 4096 * 4096 * 14336 else min(N, 256)
+    n_tok = max(1, min(N, n_tok))
+    sub = cfg.scaled(n_tokens=n_tok)
+    sub_inp = type(inp)(cfg=sub, x=inp.x[:n_tok], w_router=inp.w_router, logit_bias=inp.logit_bias,
+                        sel_bias=inp.sel_bias, w1=inp.w1, w3=inp.w3, w2=inp.w2, b1=inp.b1, b2=inp.b2,
+                        sh_w1=inp.sh_w1, sh_w3=inp.sh_w3, sh_w2=inp.sh_w2)
+    t0 = time.perf_counter()
+    oracle.oracle_layer(sub, sub_inp)
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {n_tok} of {N} tokens of {cfg.name}, whole layer in fp64 "
+                      f"(routing, capacity and aux computed over the sample)"}
+
+
+if __name__ == "__main__":
+    main()

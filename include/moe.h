@@ -1,0 +1,236 @@
+/*
+ * moe.h -- C ABI of a single-GPU sparse Mixture-of-Experts FFN layer (forward
+ * pass) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages describing it define it:
+ *   [L] "Mixture of Experts (MoE)", AI Engineering from Scratch, Phase 07
+ *       lesson 11: "Concept / FFN swap" (h + sum over the k chosen experts of
+ *       gate * expert(h)), "The load balance problem" (aux loss, capacity,
+ *       DeepSeek-V3 bias on selection only, +-gamma after each step),
+ *       "Shared experts", "Build it / Step 1: the router".
+ *   [N] "MoE architecture: load balancing and gating implementation"
+ *       (nextadmin.net): "Load balancing" items 1-3 (C * N / E capacity).
+ *   [G] "Mixture of Experts (MoE)" glossary (ultralytics.com): "How an MoE
+ *       layer works", "Load balancing and expert capacity".
+ *   [X] "Expert Parallelism for MoE Serving" (aiunderstanding.org):
+ *       "Deep dive", "Technical insight" (dispatch by expert, capacity).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `cfg` (and the struct pointers of
+ *     moe_forward) is a DEVICE pointer on the current HIP device, allocated by
+ *     the caller.  The library allocates, frees and synchronises nothing; all
+ *     work is enqueued on `stream` and the call returns at once.
+ *   - Device scalars (drop_count, aux) stay on the device.
+ *   - Host-side validation runs before any launch.  On any non-MOE_OK status
+ *     nothing has been enqueued, except MOE_ERR_HIP, which reports a failed
+ *     launch (hipGetLastError) and may leave earlier kernels of the call queued.
+ *   - Integer outputs are deterministic; floating-point outputs are
+ *     bit-reproducible run to run (no floating-point atomics).
+ *   - Storage types: MOE_BF16 stores x, weights, biases, intermediates and
+ *     `out` as bfloat16 (bit patterns, uint16); MOE_F32 stores them as fp32.
+ *     Router logits, gates and probability sums are always fp32;
+ *     accumulation is always fp32.
+ *   - Layouts are row-major.  Weights follow the [out, in] layout of a linear
+ *     layer, so both GEMM operands are contiguous along the reduction axis:
+ *       x [N, d]; w_router [E, d]; w1, w3 [E, F, d]; w2 [E, d, F];
+ *       b1 [E, F]; b2 [E, d]; sh_w1, sh_w3 [Fs, d]; sh_w2 [d, Fs].
+ *   - A slot is one (token, choice) pair; slot id s = t * k + j, where j
+ *     orders the token's k experts by descending selection key.
+ *   - Limits: 1 <= E <= 256; 1 <= k <= min(E, 16); for MOE_BF16, d and F (and
+ *     Fs) must be multiples of 64 and device pointers 16-byte aligned.
+ *     Anything else returns MOE_ERR_ARG or MOE_ERR_UNSUPPORTED.
+ *   - The library is stateless; calls on different streams may run
+ *     concurrently if their buffers are distinct.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* invalid size, NULL required pointer, NaN factor */
+  MOE_ERR_UNSUPPORTED = -2,  /* dtype/activation combination or alignment not supported */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -4,          /* a kernel launch failed */
+  MOE_ERR_INTERNAL = -5
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  /* [L] Step 1, [G]: key = z + sel_bias; gate = softmax over the k selected raw logits. */
+  MOE_GATE_TOPK_SOFTMAX = 0,
+  /* [L] DeepSeek-V3 approach, [N] item 3: p = softmax(z) over all E; key = p + sel_bias;
+     gate = p of the selected experts renormalised to sum 1. */
+  MOE_GATE_SOFTMAX_RENORM = 1,
+  /* [G] Switch: argmax z (ties to the lower index); gate = p[argmax], not renormalised. */
+  MOE_GATE_SWITCH_TOP1 = 2
+} moe_gate_rule;
+
+typedef enum {
+  MOE_ACT_SWIGLU = 0,  /* [L] "FFN swap": (SiLU(x W1^T) * (x W3^T)) W2^T, no biases */
+  MOE_ACT_GELU = 1     /* [G] example: GELU(x W1^T + b1) W2^T + b2, exact erf GELU */
+} moe_act;
+
+typedef struct moe_config {
+  int64_t n_tokens;        /* N >= 0 */
+  int32_t d_model;         /* d > 0 */
+  int32_t n_experts;       /* E */
+  int32_t top_k;           /* k */
+  int32_t d_ff;            /* F: routed expert width */
+  int32_t d_ff_shared;     /* Fs: always-on shared SwiGLU expert width; 0 = none ([L] "Shared experts") */
+  int32_t act;             /* moe_act */
+  int32_t ffn_bias;        /* 1: expert linears carry biases (MOE_ACT_GELU only) */
+  int32_t gate_rule;       /* moe_gate_rule */
+  float   capacity_factor; /* <= 0: unlimited; else C = floor(cf * N / E) ([N] item 2) */
+  int32_t dtype;           /* moe_dtype */
+  int32_t add_residual;    /* 1: out = x + MoE(x) ([L] "FFN swap": h + ...) */
+} moe_config;
+
+/* Bytes of scratch that moe_forward needs for `cfg` (the step entry points
+ * need at most this much too).  Host only, launches nothing. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Router: logits, top-k selection and gates ([L] Step 1; [G] "How an MoE layer works").
+ *   x          [N, d]     layer input (normalised hidden state)
+ *   w_router   [E, d]     router weight (bias-free linear layer)
+ *   logit_bias [E] fp32 | NULL   fixed offset added to every token's logits
+ *   sel_bias   [E] fp32 | NULL   selection-only bias ([L] DeepSeek-V3 approach); never enters a gate
+ *   logits_in  [N, E] fp32 | NULL  if given, used as the logits (the GEMM is skipped)
+ *   logits     [N, E] fp32 | NULL  out: z = x W_r^T + logit_bias (copied from logits_in if given)
+ *   topk_idx   [N, k] int32  out: chosen experts, descending key, exact ties to the lower index
+ *   gates      [N, k] fp32   out: gate weights by `gate_rule`
+ *   probsum    [E] fp32 | NULL   out: sum over tokens of softmax(z)[t, e] (for moe_aux_loss)
+ *   ws/ws_bytes scratch, at least moe_workspace_size(cfg) bytes
+ * Selection keys are formed and compared in fp64 from the fp32 logits and bias. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias, const float* logits_in,
+                     float* logits, int32_t* topk_idx, float* gates, float* probsum,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch: expert histogram, prefix scan, stable permutation, capacity and
+ * the gather of token rows into expert order ([G] example's per-expert token
+ * lists; [X] "Technical insight"; [N] item 2).
+ *   topk_idx  [N, k] int32     from moe_route
+ *   x         [N, d]           rows to gather
+ *   counts    [E] int32        out: slots per expert before dropping (sum = N k)
+ *   offsets   [E+1] int32      out: exclusive scan of kept counts min(counts, C)
+ *   perm      [N k] int32      out: perm[p] = slot id at expert-sorted position p
+ *                              (p < offsets[E]); ascending slot id within an expert
+ *   slot_pos  [N k] int32      out: position of slot s in perm, -1 if dropped
+ *   drop_count int64 | NULL    out: sum_e max(0, counts_e - C)
+ *   x_perm    [N k, d]         out: x_perm[p] = x[perm[p] / k] for p < offsets[E]
+ * Each expert keeps its first C slots in ascending slot id. */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                       int64_t* drop_count, void* x_perm, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Grouped expert FFN over the ragged expert segments of x_perm ([L] "FFN swap";
+ * [X] "Future": grouped GEMMs that batch many experts).  Rows
+ * [offsets[e], offsets[e+1]) of x_perm go through expert e.
+ *   w3 must be NULL for MOE_ACT_GELU; b1, b2 are NULL unless cfg->ffn_bias.
+ *   h_tmp  [N k, F]  scratch/out: activated hidden rows (storage dtype)
+ *   y_perm [N k, d]  out: expert outputs in x_perm's row order (storage dtype)
+ * Equivalent to moe_expert_up followed by moe_expert_down. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const void* w3, const void* w2,
+                          const void* b1, const void* b2, void* h_tmp, void* y_perm,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* First half of moe_expert_ffn: h = act(x_perm W1_e^T [, x_perm W3_e^T] [+ b1_e]). */
+moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
+                         const void* w1, const void* w3, const void* b1, void* h_tmp,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Second half of moe_expert_ffn: y = h W2_e^T [+ b2_e]. */
+moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
+                           const void* w2, const void* b2, void* y_perm,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Shared expert ([L] "Shared experts": every token passes through it, weight 1):
+ * y_sh[N, d] = (SiLU(x sh_w1^T) * (x sh_w3^T)) sh_w2^T.  h_tmp is [N, Fs]. */
+moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* sh_w1,
+                          const void* sh_w3, const void* sh_w2, void* h_tmp, void* y_sh,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gate-weighted combine into token order ([L] "FFN swap"; [G] example):
+ *   out[t] = [residual[t]] + [shared_y[t]] + sum_{j < k, slot_pos[t k + j] >= 0}
+ *            gates[t, j] * y_perm[slot_pos[t k + j]],
+ * summed in ascending j with fp32 accumulation.  A token whose slots were all
+ * dropped receives exactly residual[t] (+ shared_y[t]) ([N] item 2; [G]).
+ *   residual, shared_y: [N, d] or NULL; out [N, d] (storage dtype). */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
+                       const float* gates, const void* residual, const void* shared_y,
+                       void* out, hipStream_t stream);
+
+/* Aux-loss-free balancing step ([L] "The load balance problem", DeepSeek-V3
+ * approach; [L] Step 2): signs[e] = sign(counts[e] * E - N k) (int8: +1 over
+ * target, -1 under, 0 on target; signs may be NULL); sel_bias[e] -= gamma *
+ * signs[e] in fp32, in place.  Intended to run after the forward pass whose
+ * counts it uses. */
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float gamma,
+                           float* sel_bias, int8_t* signs, hipStream_t stream);
+
+/* Auxiliary load-balance loss value ([G] "Load balancing and expert capacity";
+ * [N] item 1): aux = E * sum_e (counts[e] / (N k)) * (probsum[e] / N), one
+ * fp32 device scalar.  counts are pre-drop. */
+moe_status moe_aux_loss(const moe_config* cfg, const int32_t* counts, const float* probsum,
+                        float* aux, hipStream_t stream);
+
+/* Device pointers of one layer's weights (NULL where the config has none). */
+typedef struct moe_weights {
+  const void*  w_router;     /* [E, d] */
+  const float* logit_bias;   /* [E] fp32 | NULL */
+  const void*  w1;           /* [E, F, d] */
+  const void*  w3;           /* [E, F, d] (SwiGLU) */
+  const void*  w2;           /* [E, d, F] */
+  const void*  b1;           /* [E, F] (ffn_bias) */
+  const void*  b2;           /* [E, d] (ffn_bias) */
+  const void*  sh_w1;        /* [Fs, d] (d_ff_shared > 0) */
+  const void*  sh_w3;        /* [Fs, d] */
+  const void*  sh_w2;        /* [d, Fs] */
+} moe_weights;
+
+/* Device pointers of one layer's outputs.  `out` is required; every other
+ * pointer may be NULL (the value is then kept in the workspace only). */
+typedef struct moe_outputs {
+  void*    out;              /* [N, d] storage dtype */
+  float*   logits;           /* [N, E] */
+  int32_t* topk_idx;         /* [N, k] */
+  float*   gates;            /* [N, k] */
+  int32_t* counts;           /* [E] pre-drop */
+  int32_t* offsets;          /* [E+1] */
+  int32_t* perm;             /* [N k] */
+  int32_t* slot_pos;         /* [N k] */
+  int64_t* drop_count;       /* scalar */
+  float*   probsum;          /* [E] */
+  float*   aux;              /* scalar; computed when non-NULL */
+  int8_t*  signs;            /* [E]; bias step runs when bias_gamma > 0 */
+  float*   sel_bias_next;    /* [E] sel_bias - gamma * signs; may alias the sel_bias input */
+  float    bias_gamma;       /* > 0: run the bias step after the forward pass (needs sel_bias
+                                and sel_bias_next); 0 with signs != NULL: signs only */
+} moe_outputs;
+
+/* The whole layer: route -> permute -> grouped expert FFN -> [shared expert]
+ * -> combine -> [aux loss] -> [bias step], all enqueued on `stream`.
+ *   x        [N, d]; residual [N, d] | NULL (NULL with add_residual = 1 uses x)
+ *   sel_bias [E] fp32 | NULL (selection bias used by this pass) */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       const void* residual, const float* sel_bias, const moe_outputs* o,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,141 @@
+// Gate-weighted combine into token order, the auxiliary load-balance loss and
+// the aux-loss-free bias step.
+//
+// [L] "Concept / FFN swap": h + sum over the chosen experts of gate * expert(h);
+// [G] "How an MoE layer works": the chosen experts' outputs are weighted by the
+// normalised router scores and summed; [G] "Load balancing and expert
+// capacity": tokens over capacity skip the layer's experts and continue along
+// the residual connection.
+#include "moe_internal.h"
+
+namespace moe {
+
+template <typename T>
+union Vec16 {
+  uint4 u;
+  T e[16 / sizeof(T)];
+};
+
+// One wavefront per token.  out = (residual + shared) + sum_j g_j * y[slot_pos_j],
+// j ascending, fp32 accumulation, one rounding to the storage type at the end.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_pos,
+                                                      const float* __restrict__ gates, const T* __restrict__ res,
+                                                      const T* __restrict__ sh, T* __restrict__ out, int N,
+                                                      int d, int k) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= N) return;
+  int pos[kMaxTopK];
+  float g[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
+    g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
+  }
+  const size_t trow = (size_t)t * d;
+  if (d % VEC == 0) {
+    for (int c = lane * VEC; c < d; c += 64 * VEC) {
+      float acc[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+      if (res) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = Store<T>::load(res, trow + c + v);
+      }
+      if (sh) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] += Store<T>::load(sh, trow + c + v);
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (pos[j] < 0) continue;
+        const size_t yr = (size_t)pos[j] * d + c;
+        Vec16<T> buf;
+        buf.u = *reinterpret_cast<const uint4*>(y + yr);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g[j], Store<T>::load(buf.e, v), acc[v]);
+      }
+      Vec16<T> ob;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) Store<T>::store(ob.e, v, acc[v]);
+      *reinterpret_cast<uint4*>(out + trow + c) = ob.u;
+    }
+  } else {
+    for (int c = lane; c < d; c += 64) {
+      float acc = res ? Store<T>::load(res, trow + c) : 0.f;
+      if (sh) acc += Store<T>::load(sh, trow + c);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (pos[j] >= 0) acc = fmaf(g[j], Store<T>::load(y, (size_t)pos[j] * d + c), acc);
+      Store<T>::store(out, trow + c, acc);
+    }
+  }
+}
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
+                          const float* gates, const void* residual, const void* shared_y,
+                          void* out, hipStream_t s) {
+  const int N = (int)c.n_tokens;
+  if (N == 0) return hipSuccess;
+  const dim3 grid((N + 3) / 4);
+  if (c.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)y_perm, slot_pos,
+                       gates, (const uint16_t*)residual, (const uint16_t*)shared_y, (uint16_t*)out, N,
+                       c.d_model, c.top_k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float*)y_perm, slot_pos, gates,
+                       (const float*)residual, (const float*)shared_y, (float*)out, N, c.d_model, c.top_k);
+  return hipGetLastError();
+}
+
+// [L] "The load balance problem", DeepSeek-V3 approach: after a step, an
+// expert above its target load moves its bias down by gamma, one below moves
+// it up.  load - target is compared as counts * E against N * k in integers.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, int E,
+                                                          long long nk, float gamma,
+                                                          const float* sel_bias_in, float* sel_bias_out,
+                                                          int8_t* __restrict__ signs) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const long long diff = (long long)counts[e] * E - nk;
+    const int sgn = (diff > 0) - (diff < 0);
+    if (signs) signs[e] = (int8_t)sgn;
+    if (sel_bias_out) sel_bias_out[e] = sel_bias_in[e] - gamma * (float)sgn;
+  }
+}
+
+hipError_t launch_bias_update(const moe_config& c, const int32_t* counts, float gamma,
+                              const float* sel_bias_in, float* sel_bias_out, int8_t* signs,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(256), 0, s, counts, c.n_experts,
+                     (long long)c.n_tokens * c.top_k, gamma, sel_bias_in, sel_bias_out, signs);
+  return hipGetLastError();
+}
+
+// [G] "Load balancing and expert capacity" (Switch's extra loss term, smallest
+// when tokens and probabilities spread evenly): aux = E * sum_e f_e * P_e with
+// f_e = counts_e / (N k), P_e = probsum_e / N.  Fixed-order reduction.
+__global__ __launch_bounds__(256) void aux_loss_kernel(const int32_t* __restrict__ counts,
+                                                       const float* __restrict__ probsum, int E,
+                                                       long long N, int k, float* __restrict__ aux) {
+  __shared__ double wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double term = 0.0;
+  if (N > 0 && tid < E)
+    term = ((double)counts[tid] / (double)(N * k)) * ((double)probsum[tid] / (double)N);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) term += __shfl_xor(term, off);
+  if (lane == 0) wsum[wave] = term;
+  __syncthreads();
+  if (tid == 0) *aux = (float)((double)E * (((wsum[0] + wsum[1]) + wsum[2]) + wsum[3]));
+}
+
+hipError_t launch_aux_loss(const moe_config& c, const int32_t* counts, const float* probsum,
+                           float* aux, hipStream_t s) {
+  hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, s, counts, probsum, c.n_experts,
+                     (long long)c.n_tokens, c.top_k, aux);
+  return hipGetLastError();
+}
+
+}  // namespace moe

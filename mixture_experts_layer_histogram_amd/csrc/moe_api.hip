@@ -1,0 +1,446 @@
+// C-ABI entry points: argument validation, workspace carving and the order of
+// kernel launches.  Nothing here allocates, frees or synchronises.
+#include "moe_internal.h"
+
+#include <math.h>
+
+namespace moe {
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static int pow2ceil(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+Workspace workspace_layout(const moe_config& c) {
+  Workspace W{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t N = (size_t)c.n_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
+  const size_t d = (size_t)c.d_model, F = (size_t)c.d_ff, Fs = (size_t)(c.d_ff_shared > 0 ? c.d_ff_shared : 0);
+  const size_t slots = N * k;
+  const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+
+  // top-k blocking: L lanes per token, 4 waves, iters rounds per block
+  int L = pow2ceil(c.n_experts);
+  if (L < 8) L = 8;
+  if (L > 64) L = 64;
+  const int per_iter = 4 * (64 / L);
+  long long iters = ((long long)N + (long long)per_iter * 256 - 1) / ((long long)per_iter * 256);
+  if (iters < 1) iters = 1;
+  if (iters > 64) iters = 64;
+  W.topk_iters = (int)iters;
+  W.topk_tokens_per_block = per_iter * W.topk_iters;
+  W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
+  W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
+  const int bm = gemm_block_m(c);
+  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E, bm);
+  W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1, bm) : 0;
+
+  W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
+  W.hist_rank = take(slots * 4);
+  W.hist_blocks = take(E * (size_t)(W.hist_blocks_n > 0 ? W.hist_blocks_n : 1) * 4);
+  W.tiles = take((4 + 4 * (size_t)W.max_tiles) * 4);
+  W.tiles_sh = take((4 + 4 * (size_t)W.max_tiles_sh) * 4);
+  W.logits = take(N * E * 4);
+  W.topk_idx = take(slots * 4);
+  W.gates = take(slots * 4);
+  W.probsum = take(E * 4);
+  W.counts = take(E * 4);
+  W.offsets = take((E + 1) * 4);
+  W.perm = take(slots * 4);
+  W.slot_pos = take(slots * 4);
+  W.drop_count = take(8);
+  W.aux = take(4);
+  W.signs = take(E);
+  W.x_perm = take(slots * d * esz);
+  W.h = take(slots * F * esz);
+  W.y = take(slots * d * esz);
+  W.h_sh = take(N * Fs * esz);
+  W.y_sh = take(Fs ? N * d * esz : 0);
+  W.total = off;
+  return W;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_ARG;
+  if (c->n_tokens < 0 || c->n_tokens > (1ll << 24)) return MOE_ERR_ARG;
+  if (c->d_model <= 0 || c->d_ff <= 0 || c->d_ff_shared < 0) return MOE_ERR_ARG;
+  if (c->n_experts < 1 || c->n_experts > kMaxExperts) return MOE_ERR_ARG;
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK) return MOE_ERR_ARG;
+  if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_GELU) return MOE_ERR_ARG;
+  if (c->gate_rule < MOE_GATE_TOPK_SOFTMAX || c->gate_rule > MOE_GATE_SWITCH_TOP1) return MOE_ERR_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_ARG;
+  if (isnan(c->capacity_factor)) return MOE_ERR_ARG;
+  if (c->gate_rule == MOE_GATE_SWITCH_TOP1 && c->top_k != 1) return MOE_ERR_ARG;
+  if (c->ffn_bias && c->act != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16) {
+    if (c->d_model % 64 || c->d_ff % 64 || c->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
+  }
+  const long long slots = c->n_tokens * (long long)c->top_k;
+  if (slots * (long long)c->d_model >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                       \
+  do {                                      \
+    moe_status _st = (expr);                \
+    if (_st != MOE_OK) return _st;          \
+  } while (0)
+
+#define MOE_HIP(expr)                       \
+  do {                                      \
+    hipError_t _e = (expr);                 \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Internal step bodies (validated arguments).
+moe_status do_route(const moe_config& c, const Workspace& W, const void* x, const void* w_router,
+                    const float* logit_bias, const float* sel_bias, const float* logits_in, float* logits,
+                    int32_t* topk_idx, float* gates, float* probsum, void* ws, hipStream_t s) {
+  const float* zin = logits_in;
+  float* zout = nullptr;
+  if (!zin) {
+    MOE_HIP(launch_router_gemm(c, x, w_router, logit_bias, logits, s));
+    zin = logits;
+  } else if (logits && logits != logits_in) {
+    zout = logits;
+  }
+  MOE_HIP(launch_topk(c, W, zin, zout, sel_bias, topk_idx, gates,
+                      reinterpret_cast<float*>(wsp(ws, W.probsum_part)), probsum, s));
+  return MOE_OK;
+}
+
+moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx, const void* x,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                      int64_t* drop_count, void* x_perm, void* ws, hipStream_t s) {
+  MOE_HIP(launch_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm,
+                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_rank)),
+                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_blocks)), s));
+  return MOE_OK;
+}
+
+GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, bool shared) {
+  GroupedGemmArgs g{};
+  g.dtype = c.dtype;
+  g.block_m = gemm_block_m(c);
+  if (shared) {
+    g.n_seg = 1;
+    g.max_rows = (int)c.n_tokens;
+    g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_sh));
+    g.max_tiles = W.max_tiles_sh;
+  } else {
+    g.n_seg = c.n_experts;
+    g.max_rows = (int)(c.n_tokens * c.top_k);
+    g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles));
+    g.max_tiles = W.max_tiles;
+  }
+  return g;
+}
+
+moe_status do_up(const moe_config& c, const Workspace& W, const void* a, const int32_t* offsets,
+                 const void* w1, const void* w3, const void* b1, void* h, void* ws, hipStream_t s,
+                 bool shared) {
+  GroupedGemmArgs g = gemm_args(c, W, ws, shared);
+  const bool swiglu = shared || c.act == MOE_ACT_SWIGLU;
+  g.mode = swiglu ? MODE_SWIGLU_UP : MODE_GELU_UP;
+  g.K = c.d_model;
+  g.Nn = shared ? c.d_ff_shared : c.d_ff;
+  g.a = a;
+  g.offsets = offsets;
+  g.w = w1;
+  g.w3 = swiglu ? w3 : nullptr;
+  g.bias = (!shared && c.ffn_bias) ? b1 : nullptr;
+  g.out = h;
+  MOE_HIP(launch_grouped_gemm(g, s));
+  return MOE_OK;
+}
+
+moe_status do_down(const moe_config& c, const Workspace& W, const void* h, const int32_t* offsets,
+                   const void* w2, const void* b2, void* y, void* ws, hipStream_t s, bool shared) {
+  GroupedGemmArgs g = gemm_args(c, W, ws, shared);
+  g.mode = MODE_DOWN;
+  g.K = shared ? c.d_ff_shared : c.d_ff;
+  g.Nn = c.d_model;
+  g.a = h;
+  g.offsets = offsets;
+  g.w = w2;
+  g.w3 = nullptr;
+  g.bias = (!shared && c.ffn_bias) ? b2 : nullptr;
+  g.out = y;
+  MOE_HIP(launch_grouped_gemm(g, s));
+  return MOE_OK;
+}
+
+moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t scratch_end(const Workspace& W) { return W.logits; }   // the step entry points use [0, logits)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported configuration or alignment";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    case MOE_ERR_INTERNAL: return "MOE_ERR_INTERNAL";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  try {
+    MOE_TRY(check_config(cfg));
+    if (!bytes) return MOE_ERR_ARG;
+    *bytes = workspace_layout(*cfg).total;
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* logit_bias,
+                     const float* sel_bias, const float* logits_in, float* logits, int32_t* topk_idx,
+                     float* gates, float* probsum, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (any && (!topk_idx || !gates)) return MOE_ERR_ARG;
+    if (!logits_in && (!w_router || (any && (!x || !logits)))) return MOE_ERR_ARG;
+    if (!logits_in && (!aligned16(x) || !aligned16(w_router))) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, probsum ? scratch_end(W) : 0));
+    return do_route(c, W, x, w_router, logit_bias, sel_bias, logits_in, logits, topk_idx, gates, probsum,
+                    ws, stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* slot_pos, int64_t* drop_count,
+                       void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (!counts || !offsets) return MOE_ERR_ARG;
+    if (any && (!topk_idx || !x || !perm || !slot_pos || !x_perm)) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    return do_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm, ws, stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* offsets, const void* w1,
+                         const void* w3, const void* b1, void* h_tmp, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (!offsets || !w1 || (any && (!x_perm || !h_tmp))) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_GELU && w3) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b1) return MOE_ERR_ARG;
+    if (!aligned16(x_perm) || !aligned16(w1) || (w3 && !aligned16(w3)) || !aligned16(h_tmp))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    return do_up(c, W, x_perm, offsets, w1, w3, b1, h_tmp, ws, stream, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32_t* offsets, const void* w2,
+                           const void* b2, void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (!offsets || !w2 || (any && (!h_tmp || !y_perm))) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b2) return MOE_ERR_ARG;
+    if (!aligned16(h_tmp) || !aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    return do_down(c, W, h_tmp, offsets, w2, b2, y_perm, ws, stream, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w3, const void* w2, const void* b1, const void* b2, void* h_tmp,
+                          void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (!w2 || (c.n_tokens > 0 && !y_perm)) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b2) return MOE_ERR_ARG;
+    if (!aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(moe_expert_up(cfg, x_perm, offsets, w1, w3, b1, h_tmp, ws, ws_bytes, stream));
+    const Workspace W = workspace_layout(c);
+    return do_down(c, W, h_tmp, offsets, w2, b2, y_perm, ws, stream, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* sh_w1, const void* sh_w3,
+                          const void* sh_w2, void* h_tmp, void* y_sh, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (c.d_ff_shared <= 0) return MOE_ERR_ARG;
+    if (!sh_w1 || !sh_w3 || !sh_w2) return MOE_ERR_ARG;
+    if (c.n_tokens > 0 && (!x || !h_tmp || !y_sh)) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(sh_w1) || !aligned16(sh_w3) || !aligned16(sh_w2) || !aligned16(h_tmp) ||
+        !aligned16(y_sh))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    MOE_TRY(do_up(c, W, x, nullptr, sh_w1, sh_w3, nullptr, h_tmp, ws, stream, true));
+    return do_down(c, W, h_tmp, nullptr, sh_w2, nullptr, y_sh, ws, stream, true);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos, const float* gates,
+                       const void* residual, const void* shared_y, void* out, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (c.n_tokens > 0 && (!y_perm || !slot_pos || !gates || !out)) return MOE_ERR_ARG;
+    if (!aligned16(y_perm) || !aligned16(out) || (residual && !aligned16(residual)) ||
+        (shared_y && !aligned16(shared_y)))
+      return MOE_ERR_UNSUPPORTED;
+    MOE_HIP(launch_combine(c, y_perm, slot_pos, gates, residual, shared_y, out, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float gamma, float* sel_bias,
+                           int8_t* signs, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    if (!counts || !sel_bias) return MOE_ERR_ARG;
+    if (isnan(gamma) || gamma < 0.f) return MOE_ERR_ARG;
+    MOE_HIP(launch_bias_update(*cfg, counts, gamma, sel_bias, sel_bias, signs, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_aux_loss(const moe_config* cfg, const int32_t* counts, const float* probsum, float* aux,
+                        hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    if (!counts || !probsum || !aux) return MOE_ERR_ARG;
+    MOE_HIP(launch_aux_loss(*cfg, counts, probsum, aux, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, const void* residual,
+                       const float* sel_bias, const moe_outputs* o, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (!w || !o) return MOE_ERR_ARG;
+    if (c.n_tokens > 0 && (!x || !o->out)) return MOE_ERR_ARG;
+    if (!w->w_router || !w->w1 || !w->w2) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_ARG;
+    if (c.ffn_bias && (!w->b1 || !w->b2)) return MOE_ERR_ARG;
+    if (c.d_ff_shared > 0 && (!w->sh_w1 || !w->sh_w3 || !w->sh_w2)) return MOE_ERR_ARG;
+    if (o->bias_gamma > 0.f && (!sel_bias || !o->sel_bias_next)) return MOE_ERR_ARG;
+    if (isnan(o->bias_gamma)) return MOE_ERR_ARG;
+    const void* ptrs[] = {x, o->out, w->w_router, w->w1, w->w2, w->w3, w->sh_w1, w->sh_w3, w->sh_w2, residual};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, W.total));
+
+    float* logits = o->logits ? o->logits : reinterpret_cast<float*>(wsp(ws, W.logits));
+    int32_t* topk_idx = o->topk_idx ? o->topk_idx : reinterpret_cast<int32_t*>(wsp(ws, W.topk_idx));
+    float* gates = o->gates ? o->gates : reinterpret_cast<float*>(wsp(ws, W.gates));
+    int32_t* counts = o->counts ? o->counts : reinterpret_cast<int32_t*>(wsp(ws, W.counts));
+    int32_t* offsets = o->offsets ? o->offsets : reinterpret_cast<int32_t*>(wsp(ws, W.offsets));
+    int32_t* perm = o->perm ? o->perm : reinterpret_cast<int32_t*>(wsp(ws, W.perm));
+    int32_t* slot_pos = o->slot_pos ? o->slot_pos : reinterpret_cast<int32_t*>(wsp(ws, W.slot_pos));
+    int64_t* drop = o->drop_count ? o->drop_count : reinterpret_cast<int64_t*>(wsp(ws, W.drop_count));
+    const bool want_aux = o->aux != nullptr;
+    float* probsum = o->probsum ? o->probsum : (want_aux ? reinterpret_cast<float*>(wsp(ws, W.probsum)) : nullptr);
+    void* x_perm = wsp(ws, W.x_perm);
+    void* h = wsp(ws, W.h);
+    void* y = wsp(ws, W.y);
+    const void* res = c.add_residual ? (residual ? residual : x) : nullptr;
+
+    MOE_TRY(do_route(c, W, x, w->w_router, w->logit_bias, sel_bias, nullptr, logits, topk_idx, gates, probsum,
+                     ws, stream));
+    MOE_TRY(do_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop, x_perm, ws, stream));
+    MOE_TRY(do_up(c, W, x_perm, offsets, w->w1, w->w3, w->b1, h, ws, stream, false));
+    MOE_TRY(do_down(c, W, h, offsets, w->w2, w->b2, y, ws, stream, false));
+    const void* shared_y = nullptr;
+    if (c.d_ff_shared > 0) {
+      void* h_sh = wsp(ws, W.h_sh);
+      void* y_sh = wsp(ws, W.y_sh);
+      MOE_TRY(do_up(c, W, x, nullptr, w->sh_w1, w->sh_w3, nullptr, h_sh, ws, stream, true));
+      MOE_TRY(do_down(c, W, h_sh, nullptr, w->sh_w2, nullptr, y_sh, ws, stream, true));
+      shared_y = y_sh;
+    }
+    MOE_HIP(launch_combine(c, y, slot_pos, gates, res, shared_y, o->out, stream));
+    if (want_aux) MOE_HIP(launch_aux_loss(c, counts, probsum, o->aux, stream));
+    if (o->bias_gamma > 0.f) {
+      int8_t* signs = o->signs ? o->signs : reinterpret_cast<int8_t*>(wsp(ws, W.signs));
+      MOE_HIP(launch_bias_update(c, counts, o->bias_gamma, sel_bias, o->sel_bias_next, signs, stream));
+    } else if (o->signs) {
+      MOE_HIP(launch_bias_update(c, counts, 0.f, nullptr, nullptr, o->signs, stream));
+    }
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

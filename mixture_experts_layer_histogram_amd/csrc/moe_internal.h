@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP translation units of libmoe_hip.
+// Device helpers (bf16 conversion, wave reductions) and the host-side launch
+// functions each kernel file exports to the C-ABI layer in moe_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kHistSlotsPerBlock = 1024;   // slots per workgroup in the histogram pass
+
+// ----------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Store<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 0.70710678118654752f); }
+
+// ----------------------------------------------------------------- workspace
+
+struct Workspace {
+  // scratch used by the step entry points (placed first)
+  size_t probsum_part, hist_rank, hist_blocks, tiles, tiles_sh;
+  // buffers moe_forward keeps when the caller passes no output pointer
+  size_t logits, topk_idx, gates, probsum, counts, offsets, perm, slot_pos, drop_count,
+         aux, signs, x_perm, h, y, h_sh, y_sh;
+  size_t total;
+  int topk_blocks, topk_tokens_per_block, topk_iters, hist_blocks_n, max_tiles, max_tiles_sh;
+};
+
+// Layout of the workspace for one config (host).
+Workspace workspace_layout(const moe_config& c);
+int gemm_block_m(const moe_config& c);   // rows per GEMM tile for the routed experts
+
+// ----------------------------------------------------------------- launches (host)
+
+hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w,
+                              const float* logit_bias, float* logits, hipStream_t s);
+hipError_t launch_topk(const moe_config& c, const Workspace& L, const float* z_in, float* z_out,
+                       const float* sel_bias, int32_t* idx, float* gates, float* probsum_part,
+                       float* probsum, hipStream_t s);
+
+hipError_t launch_permute(const moe_config& c, const Workspace& L, const int32_t* topk_idx,
+                          const void* x, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* slot_pos, int64_t* drop_count, void* x_perm,
+                          int32_t* hist_rank, int32_t* hist_blocks, hipStream_t s);
+
+// GEMM modes
+enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2 };
+
+// Grouped GEMM over ragged segments [offsets[e], offsets[e+1]) of `a`.
+//   up   : h[r, :F]  = act(a[r, :K] W1_e^T [, a W3_e^T] [+ b1_e])
+//   down : y[r, :Nn] = a[r, :K] W2_e^T [+ b2_e]
+// `offsets` has n_seg+1 entries; `tiles` is scratch for the device-built tile list.
+struct GroupedGemmArgs {
+  int mode;
+  int dtype;
+  int n_seg;
+  int max_rows;          // upper bound on offsets[n_seg] (host-known)
+  int K;                 // reduction length (d for up, F for down)
+  int Nn;                // output columns (F for up, d for down)
+  const void* a;
+  const int32_t* offsets;
+  const void* w;         // W1 (up) or W2 (down): [n_seg, Nn, K]
+  const void* w3;        // SwiGLU up only
+  const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
+  void* out;             // [rows, Nn]
+  int32_t* tiles;        // scratch: 4 ints per tile + 4 header ints
+  int max_tiles;
+  int block_m;
+};
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
+int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m);
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
+                          const float* gates, const void* residual, const void* shared_y,
+                          void* out, hipStream_t s);
+hipError_t launch_bias_update(const moe_config& c, const int32_t* counts, float gamma,
+                              const float* sel_bias_in, float* sel_bias_out, int8_t* signs,
+                              hipStream_t s);
+hipError_t launch_aux_loss(const moe_config& c, const int32_t* counts, const float* probsum,
+                           float* aux, hipStream_t s);
+
+}  // namespace moe

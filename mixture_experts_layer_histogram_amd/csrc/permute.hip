@@ -1,0 +1,196 @@
+// Dispatch: expert histogram -> prefix scan -> stable permutation -> capacity
+// -> gather of token rows into expert order.
+//
+// [G] "Load balancing and expert capacity": the example counts the tokens per
+// expert (a histogram over the chosen experts) and hands each expert the
+// tokens that chose it.  [X] "Deep dive" / "Technical insight": dispatch sends
+// every token to the holder of its expert; capacity bounds the tokens an
+// expert takes.  [N] "Load balancing" item 2: at most C * N / E tokens per
+// expert, the overflow skips the experts.
+//
+// Three passes, no atomics on values that decide positions:
+//   1. hist_rank   : per block of 1024 slots, the stable rank of every slot
+//                    among the block's slots of the same expert, and the
+//                    block's per-expert counts [E][blocks].
+//   2. scan        : per expert, the exclusive prefix of the block counts (the
+//                    rank base of each block), the total count, the kept
+//                    count min(count, C), offsets (exclusive scan over
+//                    experts) and the drop count.
+//   3. scatter     : global rank = base + local rank; kept slots get their
+//                    position offsets[e] + rank, write perm/slot_pos and copy
+//                    their token row into x_perm with 16-byte loads/stores.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kHistWaves = 4;
+constexpr int kHistChunks = kHistSlotsPerBlock / (64 * kHistWaves);   // 64-slot chunks per wave
+
+// Pass 1.  Wave w of block b owns slots [b*1024 + w*256, +256) and walks them
+// in four chunks of 64.  Lanes holding the same expert are found with eight
+// ballots (one per bit of the expert id); a lane's rank in the chunk is the
+// number of lower lanes in its match set.  The running per-wave count of each
+// expert lives in LDS.
+__global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                        int n_slots, int E, int nblk,
+                                                        int32_t* __restrict__ local_rank,
+                                                        int32_t* __restrict__ block_counts) {
+  __shared__ int cnt[kHistWaves][kMaxExperts];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < kHistWaves * kMaxExperts; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  const int base = blockIdx.x * kHistSlotsPerBlock + wave * 64 * kHistChunks;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank[kHistChunks], eid[kHistChunks];
+#pragma unroll
+  for (int ch = 0; ch < kHistChunks; ++ch) {
+    const int s = base + ch * 64 + lane;
+    const int e = s < n_slots ? topk_idx[s] : -1;
+    uint64_t match = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const int on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(on);
+      match &= on ? bb : ~bb;
+    }
+    const int r = __popcll(match & lower);
+    const int before = e >= 0 ? cnt[wave][e] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && r == 0) cnt[wave][e] = before + __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+    rank[ch] = before + r;
+    eid[ch] = e;
+  }
+  __syncthreads();
+  // exclusive prefix over waves (in wave order) and block totals
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int a = 0;
+#pragma unroll
+    for (int w = 0; w < kHistWaves; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = a;
+      a += c;
+    }
+    block_counts[(size_t)e * nblk + blockIdx.x] = a;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ch = 0; ch < kHistChunks; ++ch) {
+    const int s = base + ch * 64 + lane;
+    if (s < n_slots) local_rank[s] = cnt[wave][eid[ch]] + rank[ch];
+  }
+}
+
+// Pass 2 (one workgroup).  Thread e walks expert e's block counts in block
+// order; then a workgroup scan over experts gives the offsets.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ block_counts,
+                                                            int nblk, int E, int capacity,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int64_t* __restrict__ drop_count) {
+  __shared__ int wave_tot[4];
+  __shared__ long long wave_drop[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int kept = 0;
+  long long drop = 0;
+  if (tid < E) {
+    int a = 0;
+    int32_t* row = block_counts + (size_t)tid * nblk;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = row[b];
+      row[b] = a;
+      a += c;
+    }
+    counts[tid] = a;
+    kept = a < capacity ? a : capacity;
+    drop = (long long)(a - kept);
+  }
+  // inclusive scan of `kept` within the wave
+  int incl = kept;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  long long dsum = drop;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+  if (lane == 63) wave_tot[wave] = incl;
+  if (lane == 0) wave_drop[wave] = dsum;
+  __syncthreads();
+  int prefix = 0;
+  for (int w = 0; w < wave; ++w) prefix += wave_tot[w];
+  if (tid < E) offsets[tid] = prefix + incl - kept;
+  if (tid == 0) {
+    int tot = 0;
+    long long dt = 0;
+    for (int w = 0; w < 4; ++w) { tot += wave_tot[w]; dt += wave_drop[w]; }
+    offsets[E] = tot;
+    if (drop_count) *drop_count = dt;
+  }
+}
+
+// Pass 3.  One wavefront per slot; row copies use 16-byte accesses when the
+// row size allows it.
+__global__ __launch_bounds__(256) void scatter_gather_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
+    const int32_t* __restrict__ rank_base, const int32_t* __restrict__ offsets, int n_slots, int k,
+    int nblk, int capacity, const char* __restrict__ x, size_t row_bytes, int32_t* __restrict__ perm,
+    int32_t* __restrict__ slot_pos, char* __restrict__ x_perm) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = blockIdx.x * 4 + wave;
+  if (s >= n_slots) return;
+  const int e = topk_idx[s];
+  const int r = rank_base[(size_t)e * nblk + s / kHistSlotsPerBlock] + local_rank[s];
+  if (r >= capacity) {
+    if (lane == 0) slot_pos[s] = -1;
+    return;
+  }
+  const int pos = offsets[e] + r;
+  if (lane == 0) {
+    perm[pos] = s;
+    slot_pos[s] = pos;
+  }
+  const char* src = x + (size_t)(s / k) * row_bytes;
+  char* dst = x_perm + (size_t)pos * row_bytes;
+  if ((row_bytes & 15) == 0) {
+    for (size_t i = (size_t)lane * 16; i < row_bytes; i += 64 * 16)
+      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+  } else {
+    for (size_t i = (size_t)lane * 2; i < row_bytes; i += 64 * 2)
+      *reinterpret_cast<uint16_t*>(dst + i) = *reinterpret_cast<const uint16_t*>(src + i);
+  }
+}
+
+hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx,
+                          const void* x, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* slot_pos, int64_t* drop_count, void* x_perm,
+                          int32_t* hist_rank, int32_t* hist_blocks, hipStream_t s) {
+  const long long n_slots_ll = c.n_tokens * (long long)c.top_k;
+  const int n_slots = (int)n_slots_ll;
+  const int nblk = W.hist_blocks_n;
+  const int E = c.n_experts;
+  int capacity = 0x7fffffff;
+  if (c.capacity_factor > 0.f) {
+    const double cap = (double)c.capacity_factor * (double)c.n_tokens / (double)E;
+    capacity = cap >= 2147483647.0 ? 0x7fffffff : (int)cap;   // floor (cap >= 0)
+  }
+  if (n_slots > 0) {
+    hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, n_slots, E, nblk,
+                       hist_rank, hist_blocks);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, hist_blocks, n_slots > 0 ? nblk : 0,
+                     E, capacity, counts, offsets, drop_count);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n_slots == 0) return err;
+  const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  hipLaunchKernelGGL(scatter_gather_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s, topk_idx,
+                     hist_rank, hist_blocks, offsets, n_slots, c.top_k, nblk, capacity,
+                     (const char*)x, (size_t)c.d_model * esz, perm, slot_pos, (char*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP layer (through the C ABI) against the fp64 oracle.
+
+Integer outputs (selected experts, counts, offsets, permutation, slot
+positions / drop mask, drop count, bias signs) must be bit-exact given the
+GPU's fp32 router logits; floating-point outputs must be within
+max|gpu - ref| / max|ref| <= 2e-2 (bf16 storage) or 1e-5 (fp32 storage).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import SMALL, TOL, host, rel_err, run_layer, say
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_route(cfg, inp, o):
+    """Routing, dispatch, aux and bias step against the oracle run on the GPU logits."""
+    tol = TOL[cfg.dtype]
+    dt = cfg.dtype
+    z_ref = oracle.router_logits(oracle.to_f64(inp.x, dt), oracle.to_f64(inp.w_router, dt), inp.logit_bias)
+    assert rel_err(o["logits"], z_ref) <= tol, rel_err(o["logits"], z_ref)
+    r = oracle.oracle_route(cfg, o["logits"], inp.sel_bias)
+    say(f"{cfg.name}: min selection gap {r.min_gap:.3e}")
+    assert np.array_equal(o["topk_idx"], r.topk_idx), "topk_idx differs"
+    assert rel_err(o["gates"], r.gates) <= tol
+    assert np.array_equal(o["counts"], r.disp.counts), (o["counts"], r.disp.counts)
+    assert np.array_equal(o["offsets"], r.disp.offsets)
+    kept = int(r.disp.offsets[-1])
+    assert np.array_equal(o["perm"][:kept], r.disp.perm)
+    assert np.array_equal(o["slot_pos"], r.disp.slot_pos)
+    assert int(o["drop_count"][0]) == r.disp.drop_count
+    if cfg.aux_loss:
+        assert abs(float(o["aux"][0]) - r.aux) <= tol * abs(r.aux), (o["aux"], r.aux)
+        assert rel_err(o["probsum"], r.probs.sum(axis=0)) <= tol
+    if cfg.gamma > 0:
+        assert np.array_equal(o["signs"].astype(np.int64), r.signs)
+        assert rel_err(o["sel_bias_next"], r.new_bias) <= 1e-6
+    return r
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_parity_small(name):
+    cfg = SMALL[name]
+    say(f"case {name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} F={cfg.d_ff}")
+    inp, o, _ = run_layer(cfg)
+    _check_route(cfg, inp, o)
+    _, ref = oracle.oracle_layer(cfg, inp, logits_override=o["logits"])
+    err = rel_err(o["out"], ref)
+    say(f"{name}: out rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_deterministic(name):
+    """Two runs, and a run with the workspace at another address, give identical bits."""
+    import torch
+    cfg = SMALL[name]
+    inp, o1, layer = run_layer(cfg, runs=2)
+    layer.ws = torch.empty(layer.ws.numel() + 4096, dtype=torch.uint8, device="cuda")[4096:]
+    o2 = {k: host(v) for k, v in layer.forward().items()}
+    torch.cuda.synchronize()
+    for k in o1:
+        assert np.array_equal(o1[k], o2[k]), k
+
+
+def test_steps_match_forward():
+    """moe_route -> moe_permute -> moe_expert_ffn / moe_shared_ffn -> moe_combine ->
+    moe_aux_loss / moe_bias_update give the bits moe_forward gives."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    for name in ("deepseek_v3_small", "switch_skewed_small", "mixtral_prefill_small"):
+        cfg = SMALL[name]
+        inp, o, layer = run_layer(cfg)
+        dev, c, ws = layer.dev, layer.cfg, layer.ws
+        N, E, k, d, F = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff
+        st = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        z = torch.empty((N, E), dtype=torch.float32, device="cuda")
+        idx = torch.empty((N, k), dtype=torch.int32, device="cuda")
+        g = torch.empty((N, k), dtype=torch.float32, device="cuda")
+        ps = torch.empty(E, dtype=torch.float32, device="cuda")
+        M.route(c, dev["x"], dev["w_router"], idx, g, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"],
+                logits=z, probsum=ps, ws=ws)
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(N * k, dtype=torch.int32, device="cuda")
+        sp = torch.empty(N * k, dtype=torch.int32, device="cuda")
+        drop = torch.empty(1, dtype=torch.int64, device="cuda")
+        xp = torch.empty((N * k, d), dtype=st, device="cuda")
+        M.permute(c, idx, dev["x"], counts, offs, perm, sp, xp, drop_count=drop, ws=ws)
+        h = torch.empty((N * k, F), dtype=st, device="cuda")
+        y = torch.empty((N * k, d), dtype=st, device="cuda")
+        M.expert_ffn(c, xp, offs, dev["w1"], dev["w3"], dev["w2"], h, y, b1=dev["b1"], b2=dev["b2"], ws=ws)
+        ysh = None
+        if cfg.d_ff_shared:
+            hsh = torch.empty((N, cfg.d_ff_shared), dtype=st, device="cuda")
+            ysh = torch.empty((N, d), dtype=st, device="cuda")
+            M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], hsh, ysh, ws=ws)
+        out = torch.empty((N, d), dtype=st, device="cuda")
+        M.combine(c, y, sp, g, out, residual=dev["x"] if cfg.residual else None, shared_y=ysh)
+        torch.cuda.synchronize()
+        kept = int(host(offs)[-1])
+        # x_perm rows are exact copies of the token rows
+        xp_h, x_h, perm_h = host(xp)[:kept], host(dev["x"]), host(perm)[:kept]
+        assert np.array_equal(xp_h, x_h[perm_h // k])
+        for key, t in (("logits", z), ("topk_idx", idx), ("gates", g), ("counts", counts), ("offsets", offs),
+                       ("slot_pos", sp), ("drop_count", drop), ("out", out)):
+            assert np.array_equal(host(t), o[key]), (name, key)
+        assert np.array_equal(host(perm)[:kept], o["perm"][:kept])
+        if cfg.aux_loss:
+            aux = torch.empty(1, dtype=torch.float32, device="cuda")
+            M.aux_loss(c, counts, ps, aux)
+            torch.cuda.synchronize()
+            assert host(aux)[0] == o["aux"][0]
+        if cfg.gamma > 0:
+            b = dev["sel_bias"].clone()
+            signs = torch.empty(E, dtype=torch.int8, device="cuda")
+            M.bias_update(c, counts, cfg.gamma, b, signs)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(signs), o["signs"])
+            assert np.array_equal(host(b), o["sel_bias_next"])
+
+
+def test_expert_ffn_parity_per_segment():
+    """y_perm rows against the oracle's expert FFN on the same gathered rows."""
+    for name in ("mixtral_prefill_small", "switch_skewed_small", "deepseek_v3_small"):
+        cfg = SMALL[name]
+        inp, o, layer = run_layer(cfg)
+        import torch
+        import mixture_experts_layer_histogram_amd as M
+        N, k, d, F = cfg.n_tokens, cfg.top_k, cfg.d_model, cfg.d_ff
+        st = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        dev = layer.dev
+        offs = torch.from_numpy(o["offsets"]).cuda()
+        perm = o["perm"]
+        kept = int(o["offsets"][-1])
+        xp = dev["x"][torch.from_numpy(perm[:kept] // k).long().cuda()].contiguous()
+        xpad = torch.zeros((N * k, d), dtype=st, device="cuda")
+        xpad[:kept] = xp
+        h = torch.empty((N * k, F), dtype=st, device="cuda")
+        yp = torch.empty((N * k, d), dtype=st, device="cuda")
+        M.expert_ffn(layer.cfg, xpad, offs, dev["w1"], dev["w3"], dev["w2"], h, yp, b1=dev["b1"], b2=dev["b2"],
+                     ws=layer.ws)
+        torch.cuda.synchronize()
+        yp_h = host(yp)
+        x64 = oracle.to_f64(inp.x, cfg.dtype)
+        for e in range(cfg.n_experts):
+            lo, hi = int(o["offsets"][e]), int(o["offsets"][e + 1])
+            if hi == lo:
+                continue
+            w = {n: oracle.to_f64(v, cfg.dtype) for n, v in inp.expert(e).items()}
+            ref = oracle.expert_apply(cfg.act, x64[perm[lo:hi] // k], w)
+            err = rel_err(yp_h[lo:hi], ref)
+            assert err <= TOL[cfg.dtype], (name, e, err)
