@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--oracle-tokens", type=int, default=None,
                     help="tokens in the CPU-baseline sample (default: whole batch for prefill shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (a known-size reference for the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -82,6 +85,15 @@ def main():
     dev = M.upload_inputs(inp, dev_name)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev_name)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     c = M.config_from(cfg)
     N, E, k, d, F, Fs = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff, cfg.d_ff_shared

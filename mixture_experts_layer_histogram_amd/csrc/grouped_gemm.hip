@@ -204,6 +204,229 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tile, persistent, XCD-aware (the routed-expert and shared-expert
+// GEMMs of prefill-sized batches).
+//
+// 256 threads = 4 wavefronts in a 2x2 layout; each wavefront owns a 128 x 128
+// block = 4 x 4 MFMA 32x32x16 blocks whose 256 fp32 accumulators per lane
+// live in AGPRs (one workgroup per CU).
+//
+// Operand pipeline.  BK = 32; a ring of kStages LDS stages (32 KB each: A and
+// B tiles of 256 rows x 64 bytes) is filled by direct-to-LDS buffer loads
+// (each wavefront instruction moves 16 rows x 64 bytes straight into 1 KB of
+// LDS, no staging registers), kStages - 1 K steps ahead of the MFMAs.  A
+// step waits only for its own stage (s_waitcnt vmcnt with the number of
+// younger loads still allowed in flight) and one barrier; the workgroup
+// barrier carries no memory fence, so younger prefetches stay in flight.
+// Buffer loads whose rows fall past the segment (or past the weight matrix)
+// read as zero, so ragged tails need no clamping.
+//
+// LDS layout: row r of a stage occupies 64 bytes = four 16-byte chunks; chunk
+// c is stored in slot c ^ g(r), g(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps
+// the 16-byte fragment reads of 16 consecutive rows on distinct banks.
+//
+// Tile order.  Logical tile L enumerates groups of four M tiles (usually one
+// expert's rows) x all N tiles, N-major inside a group.  Workgroup h runs on
+// XCD h % 8; each XCD walks its own contiguous range of L, so the 32
+// workgroups resident on one XCD share A rows and weight tiles in that XCD's
+// L2.
+constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 32, kStages = 4, kGroupM = 4;
+constexpr int kXcds = 8;
+constexpr int kStageElems = 256 * kBK2;          // one operand tile of one stage (bf16 elements)
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+union Vec8 {
+  uint4 u;
+  uint16_t e[8];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// 16 bytes per lane from `voff + soff` of the buffer straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt alone (gfx9 encoding).
+#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+template <int MODE, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ tiles, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+    int K, int Nn, int n_ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * 2 * kStageElems];
+
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int T_m = tiles[0];
+  const long long T = (long long)T_m * n_ntiles;
+  const int G = gridDim.x;
+  const int per_xcd = G / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  const long long span = (T + kXcds - 1) / kXcds;
+  const long long L_end = min(T, (xcd + 1) * span);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const size_t wstride = (size_t)Nn * K;
+  const int rowbytes = K * 2;
+  const int KT = K / kBK2;
+
+  // DMA source offsets: wavefront w fills 1 KB chunks 4w..4w+3 (rows 64w..64w+63)
+  // of both operands; lane -> row 16 ch + lane/4, slot lane%4 holding chunk slot ^ g(row).
+  int voff[4], voffb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 64 * wave + 16 * u + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(row);
+    voff[u] = row * rowbytes + chunk * 16;
+    // SwiGLU: wavefronts 2 and 3 fill B rows 128..255 from W3, whose rows restart at 0
+    voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * rowbytes + chunk * 16;
+  }
+  // fragment read offsets (elements) inside a stage: row r, chunk c -> r*32 + (c ^ g(r))*8
+  int aoff[4][2], boff[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ar = wm * 128 + i * 32 + l32;
+    const int br = MODE == MODE_SWIGLU_UP ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + l32)
+                                          : (wn * 128 + i * 32 + l32);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 2 * kk + kh;
+      aoff[i][kk] = ar * kBK2 + ((c ^ swz(ar)) << 3);
+      boff[i][kk] = kStageElems + br * kBK2 + ((c ^ swz(br)) << 3);
+    }
+  }
+
+  for (long long L = xcd * span + q; L < L_end; L += per_xcd) {
+    // logical tile -> (M tile i, N tile j)
+    const long long gsz = (long long)kGroupM * n_ntiles;
+    const int g = (int)(L / gsz);
+    const int rem = (int)(L % gsz);
+    const int gm = min(kGroupM, T_m - g * kGroupM);
+    const int j = rem / gm;
+    const int i = g * kGroupM + rem % gm;
+
+    const int4 td = reinterpret_cast<const int4*>(tiles + 4)[i];
+    const int seg = td.x, r0 = td.y, r1 = td.z;
+    const int n0 = j * cols_per_tile;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)r0 * K, (uint32_t)(r1 - r0) * rowbytes);
+    const int nb_rows = min(cols_per_tile, Nn - n0);
+    const uint16_t* wsrc = (MODE == MODE_SWIGLU_UP && wave >= 2) ? W3 : W;   // W3 fills B rows 128..255
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(wsrc + (size_t)seg * wstride + (size_t)n0 * K, (uint32_t)nb_rows * rowbytes);
+
+    auto issue = [&](int kt) {
+      uint16_t* st = lds + (kt % kStages) * (2 * kStageElems);
+      const int so = kt * kBK2 * 2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dma16(ra, st + (64 * wave + 16 * u) * kBK2, voff[u], so);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dma16(rb, st + kStageElems + (64 * wave + 16 * u) * kBK2, voffb[u], so);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+      if (p < KT) issue(p);
+
+    for (int kt = 0; kt < KT; ++kt) {
+      // stage kt has landed once at most (kStages - 2) younger steps' loads remain
+      const int younger = min(kStages - 2, KT - 1 - kt);
+      if (younger >= 2) MOE_WAIT_VM(16);
+      else if (younger == 1) MOE_WAIT_VM(8);
+      else MOE_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);   // refills the stage read at kt - 1
+      const uint16_t* st = lds + (kt % kStages) * (2 * kStageElems);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          fa[x] = *reinterpret_cast<const bf16x8*>(st + aoff[x][kk]);
+          fb[x] = *reinterpret_cast<const bf16x8*>(st + boff[x][kk]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every wavefront is done with the ring before the epilogue reuses it
+
+    // Epilogue, one 32-row block of the wavefront's 128 x 128 at a time: the
+    // fp32 accumulators go to this wavefront's own 16 KB of LDS, are read back
+    // row-wise, activated, rounded to bf16 and written with 16-byte stores.
+    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
+      __builtin_amdgcn_wave_barrier();
+      const int rbase = r0 + wm * 128 + mi * 32;
+      if (MODE == MODE_SWIGLU_UP) {
+        // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
+#pragma unroll 1
+        for (int pass = 0; pass < 4; ++pass) {
+          const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+          const int row = rbase + rr, col = n0 + wn * 64 + c8;
+          if (row < r1 && col < Nn) {
+            const float* src = ep + rr * 128 + c8;
+            Vec8 o;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
+            *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          }
+        }
+      } else {
+#pragma unroll 1
+        for (int pass = 0; pass < 8; ++pass) {
+          const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
+          const int row = rbase + rr, col = n0 + wn * 128 + c8;
+          if (row < r1 && col < Nn) {
+            const float* src = ep + rr * 128 + c8;
+            Vec8 b;
+            if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
+            Vec8 o;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              float x = src[v];
+              if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+              if (MODE == MODE_GELU_UP) x = gelu_f(x);
+              o.e[v] = f32_to_bf16(x);
+            }
+            *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();   // the next tile's first DMA must not overtake this epilogue
+  }
+}
+
 // fp32 storage: one thread per output element, sequential fp32 FMA over K.
 template <int MODE, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
@@ -245,8 +468,34 @@ int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m) {
   return (max_rows + block_m - 1) / block_m + n_seg;
 }
 
+// Rows per M tile: 256-row tiles once the average segment fills half a tile.
+int gemm_block_m(int max_rows, int n_seg) {
+  return (n_seg > 0 && max_rows / n_seg >= kBM2 / 2) ? kBM2 : kBM;
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 template <int MODE, bool HAS_BIAS>
 static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
+  if (g.block_m == kBM2) {
+    const int cols = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+    const int n_ntiles = (g.Nn + cols - 1) / cols;
+    const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
+    hipLaunchKernelGGL((grouped_gemm_256_kernel<MODE, HAS_BIAS>), dim3(grid), dim3(256), 0, s,
+                       (const uint16_t*)g.a, g.tiles, (const uint16_t*)g.w, (const uint16_t*)g.w3,
+                       (const uint16_t*)g.bias, (uint16_t*)g.out, g.K, g.Nn, n_ntiles);
+    return;
+  }
   const int cols = MODE == MODE_SWIGLU_UP ? kBN / 2 : kBN;
   dim3 grid(g.max_tiles, (g.Nn + cols - 1) / cols);
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<MODE, HAS_BIAS>), grid, dim3(256), 0, s,
@@ -280,7 +529,5 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   else hb ? launch_bf16<MODE_DOWN, true>(g, s) : launch_bf16<MODE_DOWN, false>(g, s);
   return hipGetLastError();
 }
-
-int gemm_block_m(const moe_config&) { return kBM; }
 
 }  // namespace moe

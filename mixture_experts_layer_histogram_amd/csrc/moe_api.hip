@@ -39,9 +39,8 @@ Workspace workspace_layout(const moe_config& c) {
   W.topk_tokens_per_block = per_iter * W.topk_iters;
   W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
   W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
-  const int bm = gemm_block_m(c);
-  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E, bm);
-  W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1, bm) : 0;
+  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E, gemm_block_m((int)slots, (int)E));
+  W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1, gemm_block_m((int)N, 1)) : 0;
 
   W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
   W.hist_rank = take(slots * 4);
@@ -141,17 +140,18 @@ moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* to
 GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, bool shared) {
   GroupedGemmArgs g{};
   g.dtype = c.dtype;
-  g.block_m = gemm_block_m(c);
   if (shared) {
     g.n_seg = 1;
     g.max_rows = (int)c.n_tokens;
     g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_sh));
     g.max_tiles = W.max_tiles_sh;
+    g.block_m = gemm_block_m(g.max_rows, 1);
   } else {
     g.n_seg = c.n_experts;
     g.max_rows = (int)(c.n_tokens * c.top_k);
     g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles));
     g.max_tiles = W.max_tiles;
+    g.block_m = gemm_block_m(g.max_rows, c.n_experts);
   }
   return g;
 }
@@ -275,7 +275,8 @@ moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_
     if (c.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
     if (c.act == MOE_ACT_GELU && w3) return MOE_ERR_ARG;
     if (c.ffn_bias && !b1) return MOE_ERR_ARG;
-    if (!aligned16(x_perm) || !aligned16(w1) || (w3 && !aligned16(w3)) || !aligned16(h_tmp))
+    if (!aligned16(x_perm) || !aligned16(w1) || (w3 && !aligned16(w3)) || !aligned16(h_tmp) ||
+        (b1 && !aligned16(b1)))
       return MOE_ERR_UNSUPPORTED;
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
@@ -293,7 +294,8 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32
     const bool any = c.n_tokens > 0;
     if (!offsets || !w2 || (any && (!h_tmp || !y_perm))) return MOE_ERR_ARG;
     if (c.ffn_bias && !b2) return MOE_ERR_ARG;
-    if (!aligned16(h_tmp) || !aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(h_tmp) || !aligned16(w2) || !aligned16(y_perm) || (b2 && !aligned16(b2)))
+      return MOE_ERR_UNSUPPORTED;
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
     return do_down(c, W, h_tmp, offsets, w2, b2, y_perm, ws, stream, false);
@@ -310,7 +312,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
     const moe_config& c = *cfg;
     if (!w2 || (c.n_tokens > 0 && !y_perm)) return MOE_ERR_ARG;
     if (c.ffn_bias && !b2) return MOE_ERR_ARG;
-    if (!aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(w2) || !aligned16(y_perm) || (b2 && !aligned16(b2))) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(moe_expert_up(cfg, x_perm, offsets, w1, w3, b1, h_tmp, ws, ws_bytes, stream));
     const Workspace W = workspace_layout(c);
     return do_down(c, W, h_tmp, offsets, w2, b2, y_perm, ws, stream, false);
@@ -395,7 +397,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     if (c.d_ff_shared > 0 && (!w->sh_w1 || !w->sh_w3 || !w->sh_w2)) return MOE_ERR_ARG;
     if (o->bias_gamma > 0.f && (!sel_bias || !o->sel_bias_next)) return MOE_ERR_ARG;
     if (isnan(o->bias_gamma)) return MOE_ERR_ARG;
-    const void* ptrs[] = {x, o->out, w->w_router, w->w1, w->w2, w->w3, w->sh_w1, w->sh_w3, w->sh_w2, residual};
+    const void* ptrs[] = {x, o->out, w->w_router, w->w1, w->w2, w->w3, w->b1, w->b2, w->sh_w1, w->sh_w3,
+                          w->sh_w2, residual};
     for (const void* p : ptrs)
       if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
     const Workspace W = workspace_layout(c);

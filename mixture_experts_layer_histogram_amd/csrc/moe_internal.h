@@ -60,7 +60,7 @@ struct Workspace {
 
 // Layout of the workspace for one config (host).
 Workspace workspace_layout(const moe_config& c);
-int gemm_block_m(const moe_config& c);   // rows per GEMM tile for the routed experts
+int gemm_block_m(int max_rows, int n_seg);   // rows per GEMM M tile
 
 // ----------------------------------------------------------------- launches (host)
 

@@ -24,6 +24,11 @@ EDGE = {
     "f32_switch_capacity": SWITCH_SKEWED.scaled(name="f32_switch_capacity", n_tokens=129, d_model=36, d_ff=20,
                                                 n_experts=8, dtype="f32", init="normal"),
     "decode_e256": DEEPSEEK_V3.scaled(name="decode_e256", n_tokens=3, d_model=256, d_ff=64, d_ff_shared=64),
+    # large segments: the 256-row GEMM tiles with the GELU + bias epilogues and a ragged tail
+    "gelu_big_segments": SWITCH_SKEWED.scaled(name="gelu_big_segments", n_tokens=2100, n_experts=8, d_model=320,
+                                              d_ff=576, capacity_factor=0.0, logit_offset=None, aux_loss=True),
+    "swiglu_big_segments": BASE.scaled(name="swiglu_big_segments", n_tokens=1500, n_experts=4, d_model=192,
+                                       d_ff=320),
 }
 
 
