@@ -30,7 +30,8 @@ namespace moe {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
 
-// tiles[0] = tile count; tile i at tiles[4 + 4 i] = (segment, row_begin, row_end, 0).
+// tiles[0] = tile count; tile i at tiles[4 + 8 i] = (segment, row_begin, row_end,
+// first tile of the segment, tiles of the segment, 0, 0, 0).
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int n_seg,
                                                           int dense_rows, int block_m,
                                                           int32_t* __restrict__ tiles, int max_tiles) {
@@ -55,12 +56,9 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   for (int i = 0; i < nt; ++i) {
     const int id = base + i;
     if (id >= max_tiles) break;
-    int4 t;
-    t.x = tid;
-    t.y = lo + i * block_m;
-    t.z = min(hi, lo + (i + 1) * block_m);
-    t.w = 0;
-    reinterpret_cast<int4*>(tiles + 4)[id] = t;
+    int4* e = reinterpret_cast<int4*>(tiles + 4 + 8 * id);
+    e[0] = int4{tid, lo + i * block_m, min(hi, lo + (i + 1) * block_m), base};
+    e[1] = int4{nt, 0, 0, 0};
   }
   if (tid == 0) {
     const int tot = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
@@ -78,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
 
   const int tile = blockIdx.x;
   if (tile >= tiles[0]) return;
-  const int4 td = reinterpret_cast<const int4*>(tiles + 4)[tile];
+  const int4 td = *reinterpret_cast<const int4*>(tiles + 4 + 8 * tile);
   const int seg = td.x, r0 = td.y, r1 = td.z;
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN / 2 : kBN;
   const int n0 = blockIdx.y * cols_per_tile;
@@ -212,28 +210,32 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
 // block = 4 x 4 MFMA 32x32x16 blocks whose 256 fp32 accumulators per lane
 // live in AGPRs (one workgroup per CU).
 //
-// Operand pipeline.  BK = 32; a ring of kStages LDS stages (32 KB each: A and
-// B tiles of 256 rows x 64 bytes) is filled by direct-to-LDS buffer loads
-// (each wavefront instruction moves 16 rows x 64 bytes straight into 1 KB of
-// LDS, no staging registers), kStages - 1 K steps ahead of the MFMAs.  A
-// step waits only for its own stage (s_waitcnt vmcnt with the number of
-// younger loads still allowed in flight) and one barrier; the workgroup
-// barrier carries no memory fence, so younger prefetches stay in flight.
-// Buffer loads whose rows fall past the segment (or past the weight matrix)
-// read as zero, so ragged tails need no clamping.
+// Operand pipeline.  BK = 64 (one 128-byte cache line per operand row and K
+// step); two 64 KB LDS stages are filled by direct-to-LDS buffer loads (each
+// wavefront instruction moves 8 rows x 128 bytes straight into 1 KB of LDS,
+// no staging registers).  The loads for step k+1 are issued in slices
+// between the MFMAs of step k, and the fragments of each 16-wide sub-step
+// are read from LDS while the previous sub-step's 16 MFMAs issue.  One
+// fence-free barrier per step.  Rows past the segment (or past the weight
+// matrix) read as zero, so ragged tails need no clamping.
 //
-// LDS layout: row r of a stage occupies 64 bytes = four 16-byte chunks; chunk
-// c is stored in slot c ^ g(r), g(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps
-// the 16-byte fragment reads of 16 consecutive rows on distinct banks.
+// LDS layout: row r of a stage occupies 128 bytes = eight 16-byte chunks;
+// chunk c sits in slot c ^ g(r), g(r) = (r ^ (r >> 3)) & 7, which keeps the
+// 16-byte fragment reads of 16 consecutive rows on distinct banks.
 //
-// Tile order.  Logical tile L enumerates groups of four M tiles (usually one
-// expert's rows) x all N tiles, N-major inside a group.  Workgroup h runs on
-// XCD h % 8; each XCD walks its own contiguous range of L, so the 32
-// workgroups resident on one XCD share A rows and weight tiles in that XCD's
-// L2.
-constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 32, kStages = 4, kGroupM = 4;
+// Work order.  Units enumerate the tiles expert by expert and, inside one
+// expert, N-tile by N-tile over all of its M tiles, so the workgroups running
+// together on one XCD (XCD = workgroup id % 8; each XCD walks a contiguous
+// range of units) share that expert's weight tile and A rows in their L2.
+// When the tile count leaves a last, partly filled round, those last tiles
+// are split along K into s parts (s = floor(grid / leftover)); the parts
+// write fp32 partial tiles and a fix-up kernel adds them in part order, so
+// results do not depend on timing.
+constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 64;
 constexpr int kXcds = 8;
 constexpr int kStageElems = 256 * kBK2;          // one operand tile of one stage (bf16 elements)
+constexpr int kMaxSplitUnits = 256;              // partial tiles the workspace holds
+constexpr int kTileInts = 8;                     // tile entry: seg, r0, r1, first tile of seg, tiles of seg
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -246,31 +248,108 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 // 16 bytes per lane from `voff + soff` of the buffer straight into LDS at lds + 16 * lane.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt alone (gfx9 encoding).
-#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+// s_waitcnt vmcnt(0) leaving lgkmcnt / expcnt alone (gfx9 encoding).
+#define MOE_WAIT_VM0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+
+// How the units of a grouped GEMM are laid out: T tiles of KT steps; the
+// first `full` tiles run whole, the remaining `rem` tiles run in s K-parts.
+struct UnitPlan {
+  int full, rem, s;
+  __device__ __host__ int units() const { return full + rem * s; }
+};
+
+__device__ __forceinline__ UnitPlan plan_units(int T, int G) {
+  UnitPlan p;
+  const int rounds = T / G;
+  p.rem = T - rounds * G;
+  p.s = 1;
+  if (rounds > 0 && p.rem > 0) {
+    p.s = G / p.rem;
+    if (p.s * p.rem > kMaxSplitUnits) p.s = kMaxSplitUnits / p.rem;
+    if (p.s < 1) p.s = 1;
+  }
+  if (p.s == 1) p.rem = 0;
+  p.full = T - p.rem;
+  return p;
+}
+
+// Epilogue of one 128 x 128 wavefront block (rows r0 + wm*128 .., columns of
+// the output n0 ..): activation, bias, bf16 rounding, 16-byte stores.
+// `ep` is this wavefront's 16 KB of LDS; `src_acc` the accumulators.
+template <int MODE, bool HAS_BIAS>
+__device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
+                                            int wn, int r0, int r1, int n0, int Nn, int seg,
+                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
+    __builtin_amdgcn_wave_barrier();
+    const int rbase = r0 + wm * 128 + mi * 32;
+    if (MODE == MODE_SWIGLU_UP) {
+      // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
+#pragma unroll 1
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int row = rbase + rr, col = n0 + wn * 64 + c8;
+        if (row < r1 && col < Nn) {
+          const float* src = ep + rr * 128 + c8;
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
+          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int pass = 0; pass < 8; ++pass) {
+        const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
+        const int row = rbase + rr, col = n0 + wn * 128 + c8;
+        if (row < r1 && col < Nn) {
+          const float* src = ep + rr * 128 + c8;
+          Vec8 b;
+          if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            float x = src[v];
+            if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+            if (MODE == MODE_GELU_UP) x = gelu_f(x);
+            o.e[v] = f32_to_bf16(x);
+          }
+          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
 
 template <int MODE, bool HAS_BIAS>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ tiles, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ W3, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-    int K, int Nn, int n_ntiles) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * 2 * kStageElems];
+    float* __restrict__ partials, int K, int Nn, int n_ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
 
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int T_m = tiles[0];
-  const long long T = (long long)T_m * n_ntiles;
   const int G = gridDim.x;
+  const UnitPlan plan = plan_units(T_m * n_ntiles, G);
+  const int U = plan.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  const long long span = (T + kXcds - 1) / kXcds;
-  const long long L_end = min(T, (xcd + 1) * span);
+  const int span = (U + kXcds - 1) / kXcds;
+  const int u_end = min(U, (xcd + 1) * span);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
@@ -281,59 +360,50 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
   const int rowbytes = K * 2;
   const int KT = K / kBK2;
 
-  // DMA source offsets: wavefront w fills 1 KB chunks 4w..4w+3 (rows 64w..64w+63)
-  // of both operands; lane -> row 16 ch + lane/4, slot lane%4 holding chunk slot ^ g(row).
-  int voff[4], voffb[4];
+  // DMA: wavefront w fills rows 64w..64w+63 of both operands, 8 rows per
+  // instruction; lane -> row (lane >> 3), slot lane & 7 holding chunk slot ^ g(row).
+  int voff[8], voffb[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 64 * wave + 16 * u + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(row);
+  for (int u = 0; u < 8; ++u) {
+    const int row = 64 * wave + 8 * u + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(row);
     voff[u] = row * rowbytes + chunk * 16;
     // SwiGLU: wavefronts 2 and 3 fill B rows 128..255 from W3, whose rows restart at 0
     voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * rowbytes + chunk * 16;
   }
-  // fragment read offsets (elements) inside a stage: row r, chunk c -> r*32 + (c ^ g(r))*8
-  int aoff[4][2], boff[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ar = wm * 128 + i * 32 + l32;
-    const int br = MODE == MODE_SWIGLU_UP ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + l32)
-                                          : (wn * 128 + i * 32 + l32);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = 2 * kk + kh;
-      aoff[i][kk] = ar * kBK2 + ((c ^ swz(ar)) << 3);
-      boff[i][kk] = kStageElems + br * kBK2 + ((c ^ swz(br)) << 3);
+  // Fragment reads: row r = base + 32 x + l32 (base a multiple of 128), chunk
+  // c = 2 kk + kh; g(r) = g(l32) ^ 4 (x & 1), so slot = (2 kk) ^ h ^ 4 (x & 1).
+  const int h = kh ^ swz8(l32);
+  const int abase = (wm * 128 + l32) * kBK2;
+  const int bbase = kStageElems + (MODE == MODE_SWIGLU_UP ? (wn * 64 + l32) : (wn * 128 + l32)) * kBK2;
+
+  for (int u = xcd * span + q; u < u_end; u += per_xcd) {
+    // unit -> (M tile i, N tile j, K range)
+    int tile_lin, kt0 = 0, kt1 = KT, part = -1;
+    if (u < plan.full) {
+      tile_lin = u;
+    } else {
+      const int v = u - plan.full;
+      tile_lin = plan.full + v / plan.s;
+      part = v % plan.s;
+      kt0 = (int)((long long)KT * part / plan.s);
+      kt1 = (int)((long long)KT * (part + 1) / plan.s);
     }
-  }
-
-  for (long long L = xcd * span + q; L < L_end; L += per_xcd) {
-    // logical tile -> (M tile i, N tile j)
-    const long long gsz = (long long)kGroupM * n_ntiles;
-    const int g = (int)(L / gsz);
-    const int rem = (int)(L % gsz);
-    const int gm = min(kGroupM, T_m - g * kGroupM);
-    const int j = rem / gm;
-    const int i = g * kGroupM + rem % gm;
-
-    const int4 td = reinterpret_cast<const int4*>(tiles + 4)[i];
-    const int seg = td.x, r0 = td.y, r1 = td.z;
+    const int ti = tile_lin / n_ntiles;          // the expert's tiles occupy [first, first + cnt) * n_ntiles
+    const int* te = tiles + 4 + kTileInts * ti;
+    const int first = te[3], cnt = te[4];
+    const int o = tile_lin - first * n_ntiles;
+    const int j = o / cnt;
+    const int i = first + o % cnt;
+    const int* td = tiles + 4 + kTileInts * i;
+    const int seg = td[0], r0 = td[1], r1 = td[2];
     const int n0 = j * cols_per_tile;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)r0 * K, (uint32_t)(r1 - r0) * rowbytes);
     const int nb_rows = min(cols_per_tile, Nn - n0);
-    const uint16_t* wsrc = (MODE == MODE_SWIGLU_UP && wave >= 2) ? W3 : W;   // W3 fills B rows 128..255
+    const uint16_t* wsrc = (MODE == MODE_SWIGLU_UP && wave >= 2) ? W3 : W;
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(wsrc + (size_t)seg * wstride + (size_t)n0 * K, (uint32_t)nb_rows * rowbytes);
-
-    auto issue = [&](int kt) {
-      uint16_t* st = lds + (kt % kStages) * (2 * kStageElems);
-      const int so = kt * kBK2 * 2;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(ra, st + (64 * wave + 16 * u) * kBK2, voff[u], so);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dma16(rb, st + kStageElems + (64 * wave + 16 * u) * kBK2, voffb[u], so);
-    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -343,88 +413,119 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
+    {  // prologue: step kt0 into stage kt0 & 1
+      uint16_t* st = lds + (kt0 & 1) * (2 * kStageElems);
+      const int so = kt0 * kBK2 * 2;
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-      if (p < KT) issue(p);
-
-    for (int kt = 0; kt < KT; ++kt) {
-      // stage kt has landed once at most (kStages - 2) younger steps' loads remain
-      const int younger = min(kStages - 2, KT - 1 - kt);
-      if (younger >= 2) MOE_WAIT_VM(16);
-      else if (younger == 1) MOE_WAIT_VM(8);
-      else MOE_WAIT_VM(0);
-      __builtin_amdgcn_s_barrier();
-      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);   // refills the stage read at kt - 1
-      const uint16_t* st = lds + (kt % kStages) * (2 * kStageElems);
+      for (int uu = 0; uu < 8; ++uu) {
+        dma16(ra, st + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
+        dma16(rb, st + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
+      }
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
+      MOE_WAIT_VM0();                      // this wavefront's loads of step kt have landed
+      __builtin_amdgcn_s_barrier();        // ... and everyone's; stage kt+1 is free again
+      const uint16_t* st = lds + (kt & 1) * (2 * kStageElems);
+      uint16_t* nx = lds + ((kt + 1) & 1) * (2 * kStageElems);
+      const bool more = kt + 1 < kt1;
+      const int so = (kt + 1) * kBK2 * 2;
+      bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 fa[4], fb[4];
+      for (int x = 0; x < 4; ++x) {
+        const int sw = (h ^ (4 * (x & 1))) << 3;
+        fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + sw);
+        fb[0][x] = *reinterpret_cast<const bf16x8*>(
+            st + bbase + (MODE == MODE_SWIGLU_UP ? (x >> 1) * 8192 + (x & 1) * 2048 : 2048 * x) + sw);
+      }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          fa[x] = *reinterpret_cast<const bf16x8*>(st + aoff[x][kk]);
-          fb[x] = *reinterpret_cast<const bf16x8*>(st + boff[x][kk]);
+      for (int kk = 0; kk < kBK2 / 16; ++kk) {
+        const int c = kk & 1;
+        if (more) {
+#pragma unroll
+          for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
+            dma16(ra, nx + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
+            dma16(rb, nx + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
+          }
+        }
+        if (kk + 1 < kBK2 / 16) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int sw = (h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3;
+            fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + sw);
+            fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(
+                st + bbase + (MODE == MODE_SWIGLU_UP ? (x >> 1) * 8192 + (x & 1) * 2048 : 2048 * x) + sw);
+          }
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 MFMA
+        }
       }
     }
-    __syncthreads();   // every wavefront is done with the ring before the epilogue reuses it
+    __syncthreads();   // every wavefront is done with the stages before the epilogue reuses them
 
-    // Epilogue, one 32-row block of the wavefront's 128 x 128 at a time: the
-    // fp32 accumulators go to this wavefront's own 16 KB of LDS, are read back
-    // row-wise, activated, rounded to bf16 and written with 16-byte stores.
-    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
+    if (part < 0) {
+      float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
+      store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, r0, r1, n0, Nn, seg, bias, out);
+    } else {
+      // fp32 partial tile, layout [part unit][256 rows][256 accumulator columns] in MFMA order
+      float* dst = partials + (size_t)(u - plan.full) * (kBM2 * kBN2) + (size_t)wave * (128 * 128 * 4 / 4);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
-      __builtin_amdgcn_wave_barrier();
-      const int rbase = r0 + wm * 128 + mi * 32;
-      if (MODE == MODE_SWIGLU_UP) {
-        // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
-#pragma unroll 1
-        for (int pass = 0; pass < 4; ++pass) {
-          const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-          const int row = rbase + rr, col = n0 + wn * 64 + c8;
-          if (row < r1 && col < Nn) {
-            const float* src = ep + rr * 128 + c8;
-            Vec8 o;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
-            *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-          }
-        }
-      } else {
-#pragma unroll 1
-        for (int pass = 0; pass < 8; ++pass) {
-          const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
-          const int row = rbase + rr, col = n0 + wn * 128 + c8;
-          if (row < r1 && col < Nn) {
-            const float* src = ep + rr * 128 + c8;
-            Vec8 b;
-            if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-            Vec8 o;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              float x = src[v];
-              if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
-              if (MODE == MODE_GELU_UP) x = gelu_f(x);
-              o.e[v] = f32_to_bf16(x);
-            }
-            *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+        for (int ni = 0; ni < 4; ++ni)
+          *reinterpret_cast<f32x16*>(dst + ((mi * 4 + ni) * 64 + lane) * 16) = acc[mi][ni];
     }
-    __syncthreads();   // the next tile's first DMA must not overtake this epilogue
+    __syncthreads();   // the next unit's first loads must not overtake this epilogue
   }
+}
+
+// Adds the K-parts of each split tile in part order and runs the epilogue.
+// One workgroup per split tile (grid = kMaxSplitUnits; extra workgroups exit).
+template <int MODE, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void split_fixup_kernel(const int32_t* __restrict__ tiles,
+                                                             const float* __restrict__ partials,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ out, int Nn, int n_ntiles,
+                                                             int G) {
+  __shared__ __attribute__((aligned(1024))) float lds[4 * 32 * 128];
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int T_m = tiles[0];
+  const UnitPlan plan = plan_units(T_m * n_ntiles, G);
+  const int t = blockIdx.x;
+  if (t >= plan.rem) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, kh = lane >> 5;
+  const int tile_lin = plan.full + t;
+  const int ti = tile_lin / n_ntiles;
+  const int* te = tiles + 4 + kTileInts * ti;
+  const int first = te[3], cnt = te[4];
+  const int o = tile_lin - first * n_ntiles;
+  const int j = o / cnt;
+  const int i = first + o % cnt;
+  const int* td = tiles + 4 + kTileInts * i;
+  const int seg = td[0], r0 = td[1], r1 = td[2];
+  const int n0 = j * cols_per_tile;
+  f32x16 acc[4][4];
+  for (int p = 0; p < plan.s; ++p) {
+    const float* src = partials + (size_t)(t * plan.s + p) * (kBM2 * kBN2) + (size_t)wave * (128 * 128);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const f32x16 v = *reinterpret_cast<const f32x16*>(src + ((mi * 4 + ni) * 64 + lane) * 16);
+        acc[mi][ni] = p == 0 ? v : acc[mi][ni] + v;
+      }
+  }
+  store_block<MODE, HAS_BIAS>(acc, lds + wave * (32 * 128), lane, kh, l32, wm, wn, r0, r1, n0, Nn, seg, bias, out);
 }
 
 // fp32 storage: one thread per output element, sequential fp32 FMA over K.
@@ -468,6 +569,8 @@ int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m) {
   return (max_rows + block_m - 1) / block_m + n_seg;
 }
 
+size_t grouped_gemm_partials_bytes() { return (size_t)kMaxSplitUnits * kBM2 * kBN2 * sizeof(float); }
+
 // Rows per M tile: 256-row tiles once the average segment fills half a tile.
 int gemm_block_m(int max_rows, int n_seg) {
   return (n_seg > 0 && max_rows / n_seg >= kBM2 / 2) ? kBM2 : kBM;
@@ -493,7 +596,9 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
     const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL((grouped_gemm_256_kernel<MODE, HAS_BIAS>), dim3(grid), dim3(256), 0, s,
                        (const uint16_t*)g.a, g.tiles, (const uint16_t*)g.w, (const uint16_t*)g.w3,
-                       (const uint16_t*)g.bias, (uint16_t*)g.out, g.K, g.Nn, n_ntiles);
+                       (const uint16_t*)g.bias, (uint16_t*)g.out, g.partials, g.K, g.Nn, n_ntiles);
+    hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(kMaxSplitUnits), dim3(256), 0, s, g.tiles,
+                       (const float*)g.partials, (const uint16_t*)g.bias, (uint16_t*)g.out, g.Nn, n_ntiles, grid);
     return;
   }
   const int cols = MODE == MODE_SWIGLU_UP ? kBN / 2 : kBN;

@@ -45,8 +45,9 @@ Workspace workspace_layout(const moe_config& c) {
   W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
   W.hist_rank = take(slots * 4);
   W.hist_blocks = take(E * (size_t)(W.hist_blocks_n > 0 ? W.hist_blocks_n : 1) * 4);
-  W.tiles = take((4 + 4 * (size_t)W.max_tiles) * 4);
-  W.tiles_sh = take((4 + 4 * (size_t)W.max_tiles_sh) * 4);
+  W.tiles = take((4 + 8 * (size_t)W.max_tiles) * 4);
+  W.tiles_sh = take((4 + 8 * (size_t)W.max_tiles_sh) * 4);
+  W.gemm_partials = take(c.dtype == MOE_BF16 ? grouped_gemm_partials_bytes() : 0);
   W.logits = take(N * E * 4);
   W.topk_idx = take(slots * 4);
   W.gates = take(slots * 4);
@@ -140,6 +141,7 @@ moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* to
 GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, bool shared) {
   GroupedGemmArgs g{};
   g.dtype = c.dtype;
+  g.partials = reinterpret_cast<float*>(wsp(ws, W.gemm_partials));
   if (shared) {
     g.n_seg = 1;
     g.max_rows = (int)c.n_tokens;

@@ -50,7 +50,7 @@ __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 
 
 struct Workspace {
   // scratch used by the step entry points (placed first)
-  size_t probsum_part, hist_rank, hist_blocks, tiles, tiles_sh;
+  size_t probsum_part, hist_rank, hist_blocks, tiles, tiles_sh, gemm_partials;
   // buffers moe_forward keeps when the caller passes no output pointer
   size_t logits, topk_idx, gates, probsum, counts, offsets, perm, slot_pos, drop_count,
          aux, signs, x_perm, h, y, h_sh, y_sh;
@@ -95,12 +95,14 @@ struct GroupedGemmArgs {
   const void* w3;        // SwiGLU up only
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
-  int32_t* tiles;        // scratch: 4 ints per tile + 4 header ints
+  int32_t* tiles;        // scratch: 8 ints per tile + 4 header ints
   int max_tiles;
   int block_m;
+  float* partials;       // scratch for K-split partial tiles (grouped_gemm_partials_bytes())
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
 int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m);
+size_t grouped_gemm_partials_bytes();
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,

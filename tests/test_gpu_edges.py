@@ -29,6 +29,10 @@ EDGE = {
                                               d_ff=576, capacity_factor=0.0, logit_offset=None, aux_loss=True),
     "swiglu_big_segments": BASE.scaled(name="swiglu_big_segments", n_tokens=1500, n_experts=4, d_model=192,
                                        d_ff=320),
+    # more tiles than one round of workgroups with a partial last round: the K-split tail path
+    "split_k_up": BASE.scaled(name="split_k_up", n_tokens=2048, n_experts=4, d_model=256, d_ff=2240),
+    "split_k_down_gelu": SWITCH_SKEWED.scaled(name="split_k_down_gelu", n_tokens=2048, n_experts=4, d_model=8448,
+                                              d_ff=256, capacity_factor=0.0, logit_offset=None),
 }
 
 
