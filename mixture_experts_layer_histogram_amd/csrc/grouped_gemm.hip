@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
 // step); two 64 KB LDS stages are filled by direct-to-LDS buffer loads (each
 // wavefront instruction moves 8 rows x 128 bytes straight into 1 KB of LDS,
 // no staging registers).  The loads for step k+1 are issued in slices
-// between the MFMAs of step k, and the fragments of each 16-wide sub-step
+// between the MFMAs of the first three sub-steps of step k, and the fragments of each 16-wide sub-step
 // are read from LDS while the previous sub-step's 16 MFMAs issue.  One
 // fence-free barrier per step.  Rows past the segment (or past the weight
 // matrix) read as zero, so ragged tails need no clamping.
@@ -440,11 +440,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
 #pragma unroll
       for (int kk = 0; kk < kBK2 / 16; ++kk) {
         const int c = kk & 1;
-        if (more) {
+        if (more && kk < 3) {
+          // slices 3 / 3 / 2 over the first three sub-steps: the last slice still has a
+          // quarter step of MFMAs to land before the wait at the top of the next step
 #pragma unroll
-          for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
-            dma16(ra, nx + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
-            dma16(rb, nx + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
+          for (int uu = 3 * kk; uu < 3 * kk + 3; ++uu) {
+            if (uu < 8) {
+              dma16(ra, nx + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
+              dma16(rb, nx + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
+            }
           }
         }
         if (kk + 1 < kBK2 / 16) {
