@@ -28,177 +28,58 @@
 
 namespace moe {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
 
-// tiles[0] = tile count; tile i at tiles[4 + 8 i] = (segment, row_begin, row_end,
-// first tile of the segment, tiles of the segment, 0, 0, 0).
+// Splits every segment into 256-row tiles and 64-row tiles: floor(rows / 256)
+// full tiles, one more 256-row tile when at least kBigTailMin rows remain,
+// otherwise ceil(rest / 64) 64-row tiles.  Each list: [0] = tile count; tile i
+// at [4 + 8 i] = (segment, row_begin, row_end, first tile of the segment in
+// this list, tiles of the segment in this list, 0, 0, 0).
+constexpr int kBigTailMin = 128;
+
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int n_seg,
-                                                          int dense_rows, int block_m,
-                                                          int32_t* __restrict__ tiles, int max_tiles) {
-  __shared__ int wave_tot[4];
+                                                          int dense_rows, int32_t* __restrict__ big,
+                                                          int max_big, int32_t* __restrict__ small,
+                                                          int max_small) {
+  __shared__ int tot_b[4], tot_s[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int lo = 0, hi = 0, nt = 0;
+  int lo = 0, hi = 0, nb = 0, ns = 0, split = 0;
   if (tid < n_seg) {
     lo = offsets ? offsets[tid] : 0;
     hi = offsets ? offsets[tid + 1] : dense_rows;
-    nt = (hi - lo + block_m - 1) / block_m;
+    const int rows = hi - lo;
+    nb = rows / 256;
+    const int rest = rows - nb * 256;
+    if (rest >= kBigTailMin) { nb += 1; }
+    else { ns = (rest + 63) / 64; }
+    split = min(hi, lo + nb * 256);
   }
-  int incl = nt;
+  int ib = nb, is = ns;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
+    const int vb = __shfl_up(ib, off), vs = __shfl_up(is, off);
+    if (lane >= off) { ib += vb; is += vs; }
   }
-  if (lane == 63) wave_tot[wave] = incl;
+  if (lane == 63) { tot_b[wave] = ib; tot_s[wave] = is; }
   __syncthreads();
-  int base = incl - nt;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  for (int i = 0; i < nt; ++i) {
-    const int id = base + i;
-    if (id >= max_tiles) break;
-    int4* e = reinterpret_cast<int4*>(tiles + 4 + 8 * id);
-    e[0] = int4{tid, lo + i * block_m, min(hi, lo + (i + 1) * block_m), base};
-    e[1] = int4{nt, 0, 0, 0};
+  int base_b = ib - nb, base_s = is - ns;
+  for (int w = 0; w < wave; ++w) { base_b += tot_b[w]; base_s += tot_s[w]; }
+  for (int i = 0; i < nb; ++i) {
+    const int id = base_b + i;
+    if (id >= max_big) break;
+    int4* e = reinterpret_cast<int4*>(big + 4 + 8 * id);
+    e[0] = int4{tid, lo + i * 256, min(hi, lo + (i + 1) * 256), base_b};
+    e[1] = int4{nb, 0, 0, 0};
+  }
+  for (int i = 0; i < ns; ++i) {
+    const int id = base_s + i;
+    if (id >= max_small) break;
+    int4* e = reinterpret_cast<int4*>(small + 4 + 8 * id);
+    e[0] = int4{tid, split + i * 64, min(hi, split + (i + 1) * 64), base_s};
+    e[1] = int4{ns, 0, 0, 0};
   }
   if (tid == 0) {
-    const int tot = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    tiles[0] = min(tot, max_tiles);
-  }
-}
-
-template <int MODE, bool HAS_BIAS>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ tiles, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-    int K, int Nn) {
-  __shared__ uint16_t As[2][kBM * kLDK];
-  __shared__ uint16_t Bs[2][kBN * kLDK];
-
-  const int tile = blockIdx.x;
-  if (tile >= tiles[0]) return;
-  const int4 td = *reinterpret_cast<const int4*>(tiles + 4 + 8 * tile);
-  const int seg = td.x, r0 = td.y, r1 = td.z;
-  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN / 2 : kBN;
-  const int n0 = blockIdx.y * cols_per_tile;
-
-  const int tid = threadIdx.x;
-  const int lr = tid >> 3, lc = tid & 7;      // global->LDS copy: row lr + 32 i, 16-byte chunk lc
-  const size_t wstride = (size_t)Nn * K;      // elements per expert weight matrix
-  const uint16_t* a_ptr0;
-  const uint16_t* a_ptr1;
-  const uint16_t* a_ptr2;
-  const uint16_t* a_ptr3;
-  const uint16_t* b_ptr0;
-  const uint16_t* b_ptr1;
-  const uint16_t* b_ptr2;
-  const uint16_t* b_ptr3;
-#define MOE_ROW_PTRS(i)                                                               \
-  {                                                                                   \
-    const int row = lr + 32 * i;                                                      \
-    int ar = r0 + row;                                                                \
-    if (ar > r1 - 1) ar = r1 - 1;                                                     \
-    a_ptr##i = A + (size_t)ar * K + lc * 8;                                           \
-    const uint16_t* wb = W;                                                           \
-    int n = n0 + row;                                                                 \
-    if (MODE == MODE_SWIGLU_UP && row >= 64) { n = n0 + row - 64; wb = W3; }          \
-    if (n > Nn - 1) n = Nn - 1;                                                       \
-    b_ptr##i = wb + (size_t)seg * wstride + (size_t)n * K + lc * 8;                   \
-  }
-  MOE_ROW_PTRS(0) MOE_ROW_PTRS(1) MOE_ROW_PTRS(2) MOE_ROW_PTRS(3)
-#undef MOE_ROW_PTRS
-
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, kh = lane >> 5;
-  const int brow0 = MODE == MODE_SWIGLU_UP ? wn * 32 + l32 : wn * 64 + l32;
-  const int brow1 = MODE == MODE_SWIGLU_UP ? 64 + wn * 32 + l32 : wn * 64 + 32 + l32;
-
-  f32x16 acc00, acc01, acc10, acc11;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { acc00[r] = 0.f; acc01[r] = 0.f; acc10[r] = 0.f; acc11[r] = 0.f; }
-
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define MOE_GLOAD(kt)                                                                 \
-  {                                                                                   \
-    const size_t ko = (size_t)(kt) * kBK;                                             \
-    ra0 = *reinterpret_cast<const uint4*>(a_ptr0 + ko);                               \
-    ra1 = *reinterpret_cast<const uint4*>(a_ptr1 + ko);                               \
-    ra2 = *reinterpret_cast<const uint4*>(a_ptr2 + ko);                               \
-    ra3 = *reinterpret_cast<const uint4*>(a_ptr3 + ko);                               \
-    rb0 = *reinterpret_cast<const uint4*>(b_ptr0 + ko);                               \
-    rb1 = *reinterpret_cast<const uint4*>(b_ptr1 + ko);                               \
-    rb2 = *reinterpret_cast<const uint4*>(b_ptr2 + ko);                               \
-    rb3 = *reinterpret_cast<const uint4*>(b_ptr3 + ko);                               \
-  }
-#define MOE_LSTORE(buf)                                                               \
-  {                                                                                   \
-    uint16_t* as = &As[buf][lr * kLDK + lc * 8];                                      \
-    uint16_t* bs = &Bs[buf][lr * kLDK + lc * 8];                                      \
-    *reinterpret_cast<uint4*>(as) = ra0;                                              \
-    *reinterpret_cast<uint4*>(as + 32 * kLDK) = ra1;                                  \
-    *reinterpret_cast<uint4*>(as + 64 * kLDK) = ra2;                                  \
-    *reinterpret_cast<uint4*>(as + 96 * kLDK) = ra3;                                  \
-    *reinterpret_cast<uint4*>(bs) = rb0;                                              \
-    *reinterpret_cast<uint4*>(bs + 32 * kLDK) = rb1;                                  \
-    *reinterpret_cast<uint4*>(bs + 64 * kLDK) = rb2;                                  \
-    *reinterpret_cast<uint4*>(bs + 96 * kLDK) = rb3;                                  \
-  }
-
-  const int KT = K / kBK;
-  MOE_GLOAD(0)
-  MOE_LSTORE(0)
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) MOE_GLOAD(kt + 1)
-    const uint16_t* as = &As[cur][(wm * 64 + l32) * kLDK + kh * 8];
-    const uint16_t* bs0 = &Bs[cur][brow0 * kLDK + kh * 8];
-    const uint16_t* bs1 = &Bs[cur][brow1 * kLDK + kh * 8];
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + kk * 16);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(as + 32 * kLDK + kk * 16);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bs0 + kk * 16);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bs1 + kk * 16);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
-      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
-    }
-    if (more) MOE_LSTORE(cur ^ 1)
-    __syncthreads();
-  }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-
-  // epilogue
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const f32x16& c0 = mi == 0 ? acc00 : acc10;
-    const f32x16& c1 = mi == 0 ? acc01 : acc11;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + wm * 64 + mi * 32 + (r >> 2) * 8 + kh * 4 + (r & 3);
-      if (row >= r1) continue;
-      if (MODE == MODE_SWIGLU_UP) {
-        const int col = n0 + wn * 32 + l32;
-        if (col < Nn) {
-          const float h = silu_f(c0[r]) * c1[r];
-          out[(size_t)row * Nn + col] = f32_to_bf16(h);
-        }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = n0 + wn * 64 + ni * 32 + l32;
-          if (col >= Nn) continue;
-          float v = ni == 0 ? c0[r] : c1[r];
-          if (HAS_BIAS) v += bf16_to_f32(bias[(size_t)seg * Nn + col]);
-          if (MODE == MODE_GELU_UP) v = gelu_f(v);
-          out[(size_t)row * Nn + col] = f32_to_bf16(v);
-        }
-      }
-    }
+    big[0] = min(tot_b[0] + tot_b[1] + tot_b[2] + tot_b[3], max_big);
+    small[0] = min(tot_s[0] + tot_s[1] + tot_s[2] + tot_s[3], max_small);
   }
 }
 
@@ -270,7 +151,7 @@ __device__ __forceinline__ UnitPlan plan_units(int T, int G) {
   const int rounds = T / G;
   p.rem = T - rounds * G;
   p.s = 1;
-  if (rounds > 0 && p.rem > 0) {
+  if (p.rem > 0) {
     p.s = G / p.rem;
     if (p.s * p.rem > kMaxSplitUnits) p.s = kMaxSplitUnits / p.rem;
     if (p.s < 1) p.s = 1;
@@ -413,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_256_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    {  // prologue: step kt0 into stage kt0 & 1
+    if (kt0 < kt1) {  // prologue: step kt0 into stage kt0 & 1 (a K-part can be empty)
       uint16_t* st = lds + (kt0 & 1) * (2 * kStageElems);
       const int so = kt0 * kBK2 * 2;
 #pragma unroll
@@ -532,6 +413,266 @@ __global__ __launch_bounds__(256, 1) void split_fixup_kernel(const int32_t* __re
   store_block<MODE, HAS_BIAS>(acc, lds + wave * (32 * 128), lane, kh, l32, wm, wn, r0, r1, n0, Nn, seg, bias, out);
 }
 
+// ---------------------------------------------------------------------------
+// 64 x 256 tile for short segments (decode batches, experts with few routed
+// rows, the tails of long segments): there the GEMM streams the expert's
+// weights for a handful of rows, so the design goal is many bytes in flight
+// per CU rather than MFMA reuse.  4 wavefronts in a 1 x 4 layout, each 64 x 64
+// (2 x 2 MFMA 32x32x16 blocks); a 3-stage LDS ring of 40 KB stages (A: 64 rows,
+// B: 256 rows, 128 bytes each) keeps two K steps of loads in flight.  Same
+// direct-to-LDS loads, swizzle, work order and K-split tail as the 256-row
+// kernel.
+constexpr int kBM3 = 64, kStages3 = 3;
+constexpr int kStage3Elems = (kBM3 + kBN2) * kBK2;
+
+template <int MODE, bool HAS_BIAS>
+__device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, int lane, int kh, int l32, int wn,
+                                              int r0, int r1, int n0, int Nn, int seg,
+                                              const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+    __builtin_amdgcn_wave_barrier();
+    const int rbase = r0 + mi * 32;
+    if (MODE == MODE_SWIGLU_UP) {
+      // cols 0..31 hold x W1^T, cols 32..63 the matching x W3^T
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) {
+        const int rr = pass * 16 + (lane >> 2), c8 = (lane & 3) * 8;
+        const int row = rbase + rr, col = n0 + wn * 32 + c8;
+        if (row < r1 && col < Nn) {
+          const float* src = ep + rr * 64 + c8;
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[32 + v]);
+          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int row = rbase + rr, col = n0 + wn * 64 + c8;
+        if (row < r1 && col < Nn) {
+          const float* src = ep + rr * 64 + c8;
+          Vec8 b;
+          if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            float x = src[v];
+            if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+            if (MODE == MODE_GELU_UP) x = gelu_f(x);
+            o.e[v] = f32_to_bf16(x);
+          }
+          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int MODE, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_64_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ tiles, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+    float* __restrict__ partials, int K, int Nn, int n_ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages3 * kStage3Elems];
+
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int T_m = tiles[0];
+  const int G = gridDim.x;
+  const UnitPlan plan = plan_units(T_m * n_ntiles, G);
+  const int U = plan.units();
+  const int per_xcd = G / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  const int span = (U + kXcds - 1) / kXcds;
+  const int u_end = min(U, (xcd + 1) * span);
+
+  const int tid = threadIdx.x;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);     // wavefront = column block
+  const int lane = tid & 63;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const size_t wstride = (size_t)Nn * K;
+  const int rowbytes = K * 2;
+  const int KT = K / kBK2;
+
+  // DMA: wavefront w fills A rows 16w..16w+15 (2 instructions) and B rows 64w..64w+63 (8).
+  int voffa[2], voffb[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * wn + 8 * u + (lane >> 3);
+    voffa[u] = row * rowbytes + (((lane & 7) ^ swz8(row)) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 64 * wn + 8 * u + (lane >> 3);
+    voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * rowbytes + (((lane & 7) ^ swz8(row)) * 16);
+  }
+  // Fragment reads: A row 32 mi + l32 -> g = swz8(l32) ^ 4 mi; B rows: SwiGLU W1 / W3 rows
+  // (128 ni) + 32 wn + l32 -> g = swz8(l32) ^ 4 (wn & 1); otherwise 64 wn + 32 ni + l32 -> ^ 4 ni.
+  const int h = kh ^ swz8(l32);
+  const int brow0 = MODE == MODE_SWIGLU_UP ? (32 * wn + l32) : (64 * wn + l32);
+  const int bstep = MODE == MODE_SWIGLU_UP ? 128 : 32;
+  const int hb0 = MODE == MODE_SWIGLU_UP ? (h ^ (4 * (wn & 1))) : h;
+  const int hb1 = MODE == MODE_SWIGLU_UP ? hb0 : (h ^ 4);
+
+  for (int u = xcd * span + q; u < u_end; u += per_xcd) {
+    int tile_lin, kt0 = 0, kt1 = KT, part = -1;
+    if (u < plan.full) {
+      tile_lin = u;
+    } else {
+      const int v = u - plan.full;
+      tile_lin = plan.full + v / plan.s;
+      part = v % plan.s;
+      kt0 = (int)((long long)KT * part / plan.s);
+      kt1 = (int)((long long)KT * (part + 1) / plan.s);
+    }
+    const int ti = tile_lin / n_ntiles;
+    const int* te = tiles + 4 + kTileInts * ti;
+    const int first = te[3], cnt = te[4];
+    const int o = tile_lin - first * n_ntiles;
+    const int j = o / cnt;
+    const int i = first + o % cnt;
+    const int* td = tiles + 4 + kTileInts * i;
+    const int seg = td[0], r0 = td[1], r1 = td[2];
+    const int n0 = j * cols_per_tile;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)r0 * K, (uint32_t)(r1 - r0) * rowbytes);
+    const int nb_rows = min(cols_per_tile, Nn - n0);
+    const uint16_t* wsrc = (MODE == MODE_SWIGLU_UP && wn >= 2) ? W3 : W;
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(wsrc + (size_t)seg * wstride + (size_t)n0 * K, (uint32_t)nb_rows * rowbytes);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+    // prologue: steps kt0 and kt0 + 1
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kt = kt0 + p;
+      if (kt < kt1) {
+        uint16_t* st = lds + (kt % kStages3) * kStage3Elems;
+        const int so = kt * kBK2 * 2;
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) dma16(ra, st + (16 * wn + 8 * uu) * kBK2, voffa[uu], so);
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu) dma16(rb, st + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+      }
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
+      // outstanding in issue order: step kt, then step kt + 1 (10 loads) if it exists
+      if (kt + 1 < kt1) __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8));
+      else MOE_WAIT_VM0();
+      __builtin_amdgcn_s_barrier();          // step kt landed everywhere; the slot of kt - 1 is free
+      const uint16_t* st = lds + (kt % kStages3) * kStage3Elems;
+      uint16_t* nx = lds + ((kt + 2) % kStages3) * kStage3Elems;
+      const bool more = kt + 2 < kt1;
+      const int so = (kt + 2) * kBK2 * 2;
+      bf16x8 fa[2][2], fb[2][2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        fa[0][x] = *reinterpret_cast<const bf16x8*>(st + (32 * x + l32) * kBK2 + ((h ^ (4 * x)) << 3));
+        fb[0][x] = *reinterpret_cast<const bf16x8*>(st + (kBM3 + brow0 + bstep * x) * kBK2 + ((x ? hb1 : hb0) << 3));
+      }
+#pragma unroll
+      for (int kk = 0; kk < kBK2 / 16; ++kk) {
+        const int c = kk & 1;
+        if (more && kk < 3) {
+          // 10 loads over the first three sub-steps: 4 / 3 / 3
+          if (kk == 0) {
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) dma16(ra, nx + (16 * wn + 8 * uu) * kBK2, voffa[uu], so);
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) dma16(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+          } else {
+#pragma unroll
+            for (int uu = 3 * kk - 1; uu < 3 * kk + 2; ++uu)
+              dma16(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+          }
+        }
+        if (kk + 1 < kBK2 / 16) {
+          const int k2 = 2 * (kk + 1);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + (32 * x + l32) * kBK2 + ((h ^ (4 * x) ^ k2) << 3));
+            fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(
+                st + (kBM3 + brow0 + bstep * x) * kBK2 + (((x ? hb1 : hb0) ^ k2) << 3));
+          }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every wavefront is done with the ring before the epilogue reuses it
+
+    if (part < 0) {
+      float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
+      store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, r0, r1, n0, Nn, seg, bias, out);
+    } else {
+      float* dst = partials + (size_t)(u - plan.full) * (kBM3 * kBN2) + (size_t)wn * (64 * 64);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          *reinterpret_cast<f32x16*>(dst + ((mi * 2 + ni) * 64 + lane) * 16) = acc[mi][ni];
+    }
+    __syncthreads();   // the next unit's first loads must not overtake this epilogue
+  }
+}
+
+template <int MODE, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void split_fixup64_kernel(const int32_t* __restrict__ tiles,
+                                                               const float* __restrict__ partials,
+                                                               const uint16_t* __restrict__ bias,
+                                                               uint16_t* __restrict__ out, int Nn, int n_ntiles,
+                                                               int G) {
+  __shared__ __attribute__((aligned(1024))) float lds[4 * 32 * 64];
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int T_m = tiles[0];
+  const UnitPlan plan = plan_units(T_m * n_ntiles, G);
+  const int t = blockIdx.x;
+  if (t >= plan.rem) return;
+  const int tid = threadIdx.x;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int tile_lin = plan.full + t;
+  const int ti = tile_lin / n_ntiles;
+  const int* te = tiles + 4 + kTileInts * ti;
+  const int first = te[3], cnt = te[4];
+  const int o = tile_lin - first * n_ntiles;
+  const int j = o / cnt;
+  const int i = first + o % cnt;
+  const int* td = tiles + 4 + kTileInts * i;
+  const int seg = td[0], r0 = td[1], r1 = td[2];
+  const int n0 = j * cols_per_tile;
+  f32x16 acc[2][2];
+  for (int p = 0; p < plan.s; ++p) {
+    const float* src = partials + (size_t)(t * plan.s + p) * (kBM3 * kBN2) + (size_t)wn * (64 * 64);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const f32x16 v = *reinterpret_cast<const f32x16*>(src + ((mi * 2 + ni) * 64 + lane) * 16);
+        acc[mi][ni] = p == 0 ? v : acc[mi][ni] + v;
+      }
+  }
+  store_block64<MODE, HAS_BIAS>(acc, lds + wn * (32 * 64), lane, kh, l32, wn, r0, r1, n0, Nn, seg, bias, out);
+}
+
 // fp32 storage: one thread per output element, sequential fp32 FMA over K.
 template <int MODE, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
@@ -569,16 +710,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   out[i] = v;
 }
 
-int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m) {
-  return (max_rows + block_m - 1) / block_m + n_seg;
-}
-
+int grouped_gemm_max_tiles(int max_rows, int n_seg) { return max_rows / 256 + n_seg; }
+int grouped_gemm_max_small_tiles(int n_seg) { return 2 * n_seg; }
 size_t grouped_gemm_partials_bytes() { return (size_t)kMaxSplitUnits * kBM2 * kBN2 * sizeof(float); }
-
-// Rows per M tile: 256-row tiles once the average segment fills half a tile.
-int gemm_block_m(int max_rows, int n_seg) {
-  return (n_seg > 0 && max_rows / n_seg >= kBM2 / 2) ? kBM2 : kBM;
-}
 
 static int device_cus() {
   static int cus[64] = {0};
@@ -594,22 +728,24 @@ static int device_cus() {
 
 template <int MODE, bool HAS_BIAS>
 static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
-  if (g.block_m == kBM2) {
-    const int cols = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
-    const int n_ntiles = (g.Nn + cols - 1) / cols;
-    const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((grouped_gemm_256_kernel<MODE, HAS_BIAS>), dim3(grid), dim3(256), 0, s,
-                       (const uint16_t*)g.a, g.tiles, (const uint16_t*)g.w, (const uint16_t*)g.w3,
-                       (const uint16_t*)g.bias, (uint16_t*)g.out, g.partials, g.K, g.Nn, n_ntiles);
+  const int cols = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int n_ntiles = (g.Nn + cols - 1) / cols;
+  const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
+  const uint16_t* a = (const uint16_t*)g.a;
+  const uint16_t* w = (const uint16_t*)g.w;
+  const uint16_t* w3 = (const uint16_t*)g.w3;
+  const uint16_t* b = (const uint16_t*)g.bias;
+  uint16_t* out = (uint16_t*)g.out;
+  if (g.max_rows >= kBigTailMin) {   // otherwise no segment can hold a 256-row tile
+    hipLaunchKernelGGL((grouped_gemm_256_kernel<MODE, HAS_BIAS>), dim3(grid), dim3(256), 0, s, a, g.tiles, w, w3,
+                       b, out, g.partials, g.K, g.Nn, n_ntiles);
     hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(kMaxSplitUnits), dim3(256), 0, s, g.tiles,
-                       (const float*)g.partials, (const uint16_t*)g.bias, (uint16_t*)g.out, g.Nn, n_ntiles, grid);
-    return;
+                       (const float*)g.partials, b, out, g.Nn, n_ntiles, grid);
   }
-  const int cols = MODE == MODE_SWIGLU_UP ? kBN / 2 : kBN;
-  dim3 grid(g.max_tiles, (g.Nn + cols - 1) / cols);
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<MODE, HAS_BIAS>), grid, dim3(256), 0, s,
-                     (const uint16_t*)g.a, g.tiles, (const uint16_t*)g.w, (const uint16_t*)g.w3,
-                     (const uint16_t*)g.bias, (uint16_t*)g.out, g.K, g.Nn);
+  hipLaunchKernelGGL((grouped_gemm_64_kernel<MODE, HAS_BIAS>), dim3(grid), dim3(256), 0, s, a, g.tiles_small, w,
+                     w3, b, out, g.partials, g.K, g.Nn, n_ntiles);
+  hipLaunchKernelGGL((split_fixup64_kernel<MODE, HAS_BIAS>), dim3(kMaxSplitUnits), dim3(256), 0, s, g.tiles_small,
+                     (const float*)g.partials, b, out, g.Nn, n_ntiles, grid);
 }
 
 template <int MODE, bool HAS_BIAS>
@@ -629,8 +765,8 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
     else hb ? launch_f32<MODE_DOWN, true>(g, s) : launch_f32<MODE_DOWN, false>(g, s);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, g.offsets, g.n_seg, g.max_rows,
-                     g.block_m, g.tiles, g.max_tiles);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, g.offsets, g.n_seg, g.max_rows, g.tiles,
+                     g.max_tiles, g.tiles_small, g.max_tiles_small);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (g.mode == MODE_SWIGLU_UP) launch_bf16<MODE_SWIGLU_UP, false>(g, s);

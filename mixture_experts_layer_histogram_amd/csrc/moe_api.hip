@@ -39,14 +39,18 @@ Workspace workspace_layout(const moe_config& c) {
   W.topk_tokens_per_block = per_iter * W.topk_iters;
   W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
   W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
-  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E, gemm_block_m((int)slots, (int)E));
-  W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1, gemm_block_m((int)N, 1)) : 0;
+  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E);
+  W.max_tiles_small = grouped_gemm_max_small_tiles((int)E);
+  W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1) : 0;
+  W.max_tiles_sh_small = Fs ? grouped_gemm_max_small_tiles(1) : 0;
 
   W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
   W.hist_rank = take(slots * 4);
   W.hist_blocks = take(E * (size_t)(W.hist_blocks_n > 0 ? W.hist_blocks_n : 1) * 4);
   W.tiles = take((4 + 8 * (size_t)W.max_tiles) * 4);
+  W.tiles_small = take((4 + 8 * (size_t)W.max_tiles_small) * 4);
   W.tiles_sh = take((4 + 8 * (size_t)W.max_tiles_sh) * 4);
+  W.tiles_sh_small = take((4 + 8 * (size_t)W.max_tiles_sh_small) * 4);
   W.gemm_partials = take(c.dtype == MOE_BF16 ? grouped_gemm_partials_bytes() : 0);
   W.logits = take(N * E * 4);
   W.topk_idx = take(slots * 4);
@@ -147,13 +151,15 @@ GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, boo
     g.max_rows = (int)c.n_tokens;
     g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_sh));
     g.max_tiles = W.max_tiles_sh;
-    g.block_m = gemm_block_m(g.max_rows, 1);
+    g.tiles_small = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_sh_small));
+    g.max_tiles_small = W.max_tiles_sh_small;
   } else {
     g.n_seg = c.n_experts;
     g.max_rows = (int)(c.n_tokens * c.top_k);
     g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles));
     g.max_tiles = W.max_tiles;
-    g.block_m = gemm_block_m(g.max_rows, c.n_experts);
+    g.tiles_small = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_small));
+    g.max_tiles_small = W.max_tiles_small;
   }
   return g;
 }

@@ -50,17 +50,17 @@ __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 
 
 struct Workspace {
   // scratch used by the step entry points (placed first)
-  size_t probsum_part, hist_rank, hist_blocks, tiles, tiles_sh, gemm_partials;
+  size_t probsum_part, hist_rank, hist_blocks, tiles, tiles_small, tiles_sh, tiles_sh_small, gemm_partials;
   // buffers moe_forward keeps when the caller passes no output pointer
   size_t logits, topk_idx, gates, probsum, counts, offsets, perm, slot_pos, drop_count,
          aux, signs, x_perm, h, y, h_sh, y_sh;
   size_t total;
-  int topk_blocks, topk_tokens_per_block, topk_iters, hist_blocks_n, max_tiles, max_tiles_sh;
+  int topk_blocks, topk_tokens_per_block, topk_iters, hist_blocks_n, max_tiles, max_tiles_small, max_tiles_sh,
+      max_tiles_sh_small;
 };
 
 // Layout of the workspace for one config (host).
 Workspace workspace_layout(const moe_config& c);
-int gemm_block_m(int max_rows, int n_seg);   // rows per GEMM M tile
 
 // ----------------------------------------------------------------- launches (host)
 
@@ -95,13 +95,15 @@ struct GroupedGemmArgs {
   const void* w3;        // SwiGLU up only
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
-  int32_t* tiles;        // scratch: 8 ints per tile + 4 header ints
+  int32_t* tiles;        // scratch: 256-row tile list (4 header ints + 8 ints per tile)
   int max_tiles;
-  int block_m;
+  int32_t* tiles_small;  // scratch: 64-row tile list
+  int max_tiles_small;
   float* partials;       // scratch for K-split partial tiles (grouped_gemm_partials_bytes())
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
-int grouped_gemm_max_tiles(int max_rows, int n_seg, int block_m);
+int grouped_gemm_max_tiles(int max_rows, int n_seg);
+int grouped_gemm_max_small_tiles(int n_seg);
 size_t grouped_gemm_partials_bytes();
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
