@@ -7,8 +7,10 @@ router GEMM + top-k -> histogram/scan/permute/gather -> grouped expert GEMMs
 Inputs are resident in HBM before the timed region starts.
 
 Prints ONE JSON line.  `value` is layer tokens/s; `roofline` describes the
-dominant kernel (the grouped up-projection GEMM with the fused activation),
-timed with HIP events around its launches inside the timed region;
+dominant kernel (the grouped up-projection GEMM with the fused activation:
+algorithmic FLOPs over kept rows / its HIP-event time on the launch stream
+inside the timed region; `traffic` = rocprofv3 FETCH_SIZE + WRITE_SIZE bytes
+per call, scaled by a copy kernel, when taken on the current source);
 `cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
@@ -192,7 +194,9 @@ def main():
         "config": {"workload": cfg.name, "n_tokens": N, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
                    "d_ff_shared": Fs, "act": cfg.act, "gate_rule": cfg.gate_rule,
                    "capacity_factor": cfg.capacity_factor, "kept_slots": kept},
-        "roofline": {"kernel": "grouped_gemm_bf16_kernel (expert up-projection, fused activation)",
+        "roofline": {"kernel": "expert up-projection grouped GEMM with fused activation (build_tiles_kernel, "
+                               "grouped_gemm_256_kernel, split_fixup_kernel, grouped_gemm_64_kernel, "
+                               "split_fixup64_kernel; one moe_expert_up call)",
                      "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
         "expert_gemm_tflops": expert_tflops,
