@@ -1,9 +1,10 @@
 """Benchmark of the single-GPU MoE layer (forward pass) on MI355X.
 
 One step = one pass of the whole layer over one batch of synthetic input:
-router GEMM + top-k -> histogram/scan/permute/gather -> grouped expert GEMMs
-(up with fused activation, down) -> [shared expert] -> combine -> [aux loss]
--> [bias step], each a C-ABI call into libmoe_hip.so on one HIP stream.
+router GEMM + top-k -> histogram/scan/permute -> grouped expert GEMMs (up with
+the token-row gather and the activation fused, down) -> [shared expert] ->
+combine -> [aux loss] -> [bias step], each a C-ABI call into libmoe_hip.so on
+one HIP stream.
 Inputs are resident in HBM before the timed region starts.
 
 Prints ONE JSON line.  `value` is layer tokens/s; `roofline` describes the
@@ -111,7 +112,6 @@ def main():
     perm = torch.empty(N * k, dtype=i32, device=dev_name)
     slot_pos = torch.empty(N * k, dtype=i32, device=dev_name)
     drop = torch.empty(1, dtype=torch.int64, device=dev_name)
-    x_perm = torch.empty((N * k, d), dtype=st, device=dev_name)
     h = torch.empty((N * k, F), dtype=st, device=dev_name)
     y = torch.empty((N * k, d), dtype=st, device=dev_name)
     h_sh = torch.empty((N, Fs), dtype=st, device=dev_name) if Fs else None
@@ -133,9 +133,9 @@ def main():
         M.route(c, dev["x"], dev["w_router"], idx, gates, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"],
                 logits=z, probsum=probsum, ws=ws)
         mark(1)
-        M.permute(c, idx, dev["x"], counts, offs, perm, slot_pos, x_perm, drop_count=drop, ws=ws)
+        M.permute(c, idx, None, counts, offs, perm, slot_pos, None, drop_count=drop, ws=ws)
         mark(2)
-        M.expert_up(c, x_perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+        M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
         mark(3)
         M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
         mark(4)
@@ -194,9 +194,9 @@ def main():
         "config": {"workload": cfg.name, "n_tokens": N, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
                    "d_ff_shared": Fs, "act": cfg.act, "gate_rule": cfg.gate_rule,
                    "capacity_factor": cfg.capacity_factor, "kept_slots": kept},
-        "roofline": {"kernel": "expert up-projection grouped GEMM with fused activation (build_tiles_kernel, "
-                               "grouped_gemm_256_kernel, split_fixup_kernel, grouped_gemm_64_kernel, "
-                               "split_fixup64_kernel; one moe_expert_up call)",
+        "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
+                               "(build_tiles_kernel, grouped_gemm_kernel, split_fixup_kernel; one "
+                               "moe_expert_up_gather call)",
                      "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
         "expert_gemm_tflops": expert_tflops,

@@ -119,14 +119,16 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  * the gather of token rows into expert order ([G] example's per-expert token
  * lists; [X] "Technical insight"; [N] item 2).
  *   topk_idx  [N, k] int32     from moe_route
- *   x         [N, d]           rows to gather
+ *   x         [N, d] | NULL    rows to gather (may be NULL when x_perm is NULL)
  *   counts    [E] int32        out: slots per expert before dropping (sum = N k)
  *   offsets   [E+1] int32      out: exclusive scan of kept counts min(counts, C)
  *   perm      [N k] int32      out: perm[p] = slot id at expert-sorted position p
  *                              (p < offsets[E]); ascending slot id within an expert
  *   slot_pos  [N k] int32      out: position of slot s in perm, -1 if dropped
  *   drop_count int64 | NULL    out: sum_e max(0, counts_e - C)
- *   x_perm    [N k, d]         out: x_perm[p] = x[perm[p] / k] for p < offsets[E]
+ *   x_perm    [N k, d] | NULL  out: x_perm[p] = x[perm[p] / k] for p < offsets[E];
+ *                              NULL skips the row copy (moe_expert_up_gather then
+ *                              reads the token rows through perm)
  * Each expert keeps its first C slots in ascending slot id. */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
@@ -149,6 +151,19 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
 moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
                          const void* w1, const void* w3, const void* b1, void* h_tmp,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_expert_up with the dispatch gather fused into the GEMM's operand loads
+ * ([X] "Future": fused dispatch and compute kernels): row p of the expert order
+ * is token row x[perm[p] / k], so no x_perm copy is made.
+ *   x     [N, d]     token rows
+ *   perm  [N k] int32  from moe_permute
+ * Results are bit-identical to moe_expert_up on the gathered x_perm.
+ * MOE_ERR_UNSUPPORTED when a bf16 x exceeds 2 GiB - 1 MiB (the kernel's 32-bit
+ * buffer offsets); moe_forward then falls back to the copy. */
+moe_status moe_expert_up_gather(const moe_config* cfg, const void* x, const int32_t* perm,
+                                const int32_t* offsets, const void* w1, const void* w3,
+                                const void* b1, void* h_tmp, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* Second half of moe_expert_ffn: y = h W2_e^T [+ b2_e]. */
 moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,

@@ -54,6 +54,7 @@ _SIGS = {
     "moe_permute": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_expert_up_gather": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_shared_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_combine": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P],
@@ -131,7 +132,8 @@ def route(cfg, x, w_router, topk_idx, gates, logit_bias=None, sel_bias=None, log
           _ptr(logits_in), _ptr(logits), _ptr(topk_idx), _ptr(gates), _ptr(probsum), wp, wb, _stream(stream))
 
 
-def permute(cfg, topk_idx, x, counts, offsets, perm, slot_pos, x_perm, drop_count=None, ws=None, stream=None):
+def permute(cfg, topk_idx, x, counts, offsets, perm, slot_pos, x_perm=None, drop_count=None, ws=None,
+            stream=None):
     wp, wb = _ws(ws)
     _call("moe_permute", ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(perm),
           _ptr(slot_pos), _ptr(drop_count), _ptr(x_perm), wp, wb, _stream(stream))
@@ -147,6 +149,12 @@ def expert_up(cfg, x_perm, offsets, w1, w3, h_tmp, b1=None, ws=None, stream=None
     wp, wb = _ws(ws)
     _call("moe_expert_up", ctypes.byref(cfg), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(b1),
           _ptr(h_tmp), wp, wb, _stream(stream))
+
+
+def expert_up_gather(cfg, x, perm, offsets, w1, w3, h_tmp, b1=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _call("moe_expert_up_gather", ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(w1), _ptr(w3),
+          _ptr(b1), _ptr(h_tmp), wp, wb, _stream(stream))
 
 
 def expert_down(cfg, h_tmp, offsets, w2, y_perm, b2=None, ws=None, stream=None):

@@ -164,10 +164,15 @@ GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, boo
   return g;
 }
 
+// `perm` != NULL: `a` is the token matrix and row r of the expert order is
+// token perm[r] / top_k (the gather of the dispatch done inside the GEMM).
 moe_status do_up(const moe_config& c, const Workspace& W, const void* a, const int32_t* offsets,
                  const void* w1, const void* w3, const void* b1, void* h, void* ws, hipStream_t s,
-                 bool shared) {
+                 bool shared, const int32_t* perm = nullptr) {
   GroupedGemmArgs g = gemm_args(c, W, ws, shared);
+  g.perm = perm;
+  g.gather_k = c.top_k;
+  g.a_rows = (int)c.n_tokens;
   const bool swiglu = shared || c.act == MOE_ACT_SWIGLU;
   g.mode = swiglu ? MODE_SWIGLU_UP : MODE_GELU_UP;
   g.K = c.d_model;
@@ -207,6 +212,13 @@ moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 size_t scratch_end(const Workspace& W) { return W.logits; }   // the step entry points use [0, logits)
+
+// The up GEMM reads token rows through perm when the bf16 token matrix fits
+// its 32-bit buffer offsets (the fp32 path has no such limit).
+bool gather_ok(const moe_config& c) {
+  if (c.dtype != MOE_BF16) return true;
+  return (size_t)c.n_tokens * (size_t)c.d_model * 2 <= grouped_gemm_gather_max_bytes();
+}
 
 }  // namespace
 
@@ -262,7 +274,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const voi
     const moe_config& c = *cfg;
     const bool any = c.n_tokens > 0;
     if (!counts || !offsets) return MOE_ERR_ARG;
-    if (any && (!topk_idx || !x || !perm || !slot_pos || !x_perm)) return MOE_ERR_ARG;
+    if (any && (!topk_idx || !perm || !slot_pos || (x_perm && !x))) return MOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
@@ -289,6 +301,29 @@ moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
     return do_up(c, W, x_perm, offsets, w1, w3, b1, h_tmp, ws, stream, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_up_gather(const moe_config* cfg, const void* x, const int32_t* perm,
+                                const int32_t* offsets, const void* w1, const void* w3, const void* b1,
+                                void* h_tmp, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (!offsets || !w1 || (any && (!x || !perm || !h_tmp))) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_GELU && w3) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b1) return MOE_ERR_ARG;
+    if (!gather_ok(c)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w1) || (w3 && !aligned16(w3)) || !aligned16(h_tmp) || (b1 && !aligned16(b1)))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    if (!any) return MOE_OK;
+    return do_up(c, W, x, offsets, w1, w3, b1, h_tmp, ws, stream, false, perm);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -422,7 +457,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     int64_t* drop = o->drop_count ? o->drop_count : reinterpret_cast<int64_t*>(wsp(ws, W.drop_count));
     const bool want_aux = o->aux != nullptr;
     float* probsum = o->probsum ? o->probsum : (want_aux ? reinterpret_cast<float*>(wsp(ws, W.probsum)) : nullptr);
-    void* x_perm = wsp(ws, W.x_perm);
+    const bool fused = gather_ok(c);   // the up GEMM gathers token rows itself
+    void* x_perm = fused ? nullptr : wsp(ws, W.x_perm);
     void* h = wsp(ws, W.h);
     void* y = wsp(ws, W.y);
     const void* res = c.add_residual ? (residual ? residual : x) : nullptr;
@@ -430,7 +466,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     MOE_TRY(do_route(c, W, x, w->w_router, w->logit_bias, sel_bias, nullptr, logits, topk_idx, gates, probsum,
                      ws, stream));
     MOE_TRY(do_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop, x_perm, ws, stream));
-    MOE_TRY(do_up(c, W, x_perm, offsets, w->w1, w->w3, w->b1, h, ws, stream, false));
+    if (fused) MOE_TRY(do_up(c, W, x, offsets, w->w1, w->w3, w->b1, h, ws, stream, false, perm));
+    else MOE_TRY(do_up(c, W, x_perm, offsets, w->w1, w->w3, w->b1, h, ws, stream, false));
     MOE_TRY(do_down(c, W, h, offsets, w->w2, w->b2, y, ws, stream, false));
     const void* shared_y = nullptr;
     if (c.d_ff_shared > 0) {

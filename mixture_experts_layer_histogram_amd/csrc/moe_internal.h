@@ -82,6 +82,8 @@ enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2 };
 //   up   : h[r, :F]  = act(a[r, :K] W1_e^T [, a W3_e^T] [+ b1_e])
 //   down : y[r, :Nn] = a[r, :K] W2_e^T [+ b2_e]
 // `offsets` has n_seg+1 entries; `tiles` is scratch for the device-built tile list.
+// With `perm` (up only), row r of the expert order is row perm[r] / gather_k
+// of `a`, which then holds a_rows token rows.
 struct GroupedGemmArgs {
   int mode;
   int dtype;
@@ -90,6 +92,9 @@ struct GroupedGemmArgs {
   int K;                 // reduction length (d for up, F for down)
   int Nn;                // output columns (F for up, d for down)
   const void* a;
+  const int32_t* perm;   // gather (up only): expert-order row -> slot id, or NULL
+  int gather_k;          // gather: slots per token
+  int a_rows;            // gather: rows of `a`
   const int32_t* offsets;
   const void* w;         // W1 (up) or W2 (down): [n_seg, Nn, K]
   const void* w3;        // SwiGLU up only
@@ -105,6 +110,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
 int grouped_gemm_max_tiles(int max_rows, int n_seg);
 int grouped_gemm_max_small_tiles(int n_seg);
 size_t grouped_gemm_partials_bytes();
+size_t grouped_gemm_gather_max_bytes();   // largest token matrix (bytes) the bf16 gather path addresses
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,

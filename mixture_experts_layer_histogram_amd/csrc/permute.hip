@@ -19,6 +19,8 @@
 //   3. scatter     : global rank = base + local rank; kept slots get their
 //                    position offsets[e] + rank, write perm/slot_pos and copy
 //                    their token row into x_perm with 16-byte loads/stores.
+//                    Without x_perm (the expert GEMM then reads the token
+//                    rows through perm) only the indices are written.
 #include "moe_internal.h"
 
 namespace moe {
@@ -163,6 +165,26 @@ __global__ __launch_bounds__(256) void scatter_gather_kernel(
   }
 }
 
+// Pass 3 without the row copy: one thread per slot.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                      const int32_t* __restrict__ local_rank,
+                                                      const int32_t* __restrict__ rank_base,
+                                                      const int32_t* __restrict__ offsets, int n_slots,
+                                                      int nblk, int capacity, int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ slot_pos) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n_slots) return;
+  const int e = topk_idx[s];
+  const int r = rank_base[(size_t)e * nblk + s / kHistSlotsPerBlock] + local_rank[s];
+  if (r >= capacity) {
+    slot_pos[s] = -1;
+    return;
+  }
+  const int pos = offsets[e] + r;
+  perm[pos] = s;
+  slot_pos[s] = pos;
+}
+
 hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx,
                           const void* x, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* slot_pos, int64_t* drop_count, void* x_perm,
@@ -187,6 +209,11 @@ hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_slots == 0) return err;
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  if (x_perm == nullptr) {
+    hipLaunchKernelGGL(scatter_kernel, dim3((n_slots + 255) / 256), dim3(256), 0, s, topk_idx, hist_rank,
+                       hist_blocks, offsets, n_slots, nblk, capacity, perm, slot_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(scatter_gather_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s, topk_idx,
                      hist_rank, hist_blocks, offsets, n_slots, c.top_k, nblk, capacity,
                      (const char*)x, (size_t)c.d_model * esz, perm, slot_pos, (char*)x_perm);

@@ -84,6 +84,14 @@ def test_null_and_workspace_errors_before_launch():
     cg = _cfg(act="gelu")
     assert L.moe_expert_up(ctypes.byref(cg), P, P, P, P, None, P, P, 1 << 40, None) == _lib.MOE_ERR_ARG
     assert L.moe_expert_up(ctypes.byref(c), P, P, P, None, None, P, P, 1 << 40, None) == _lib.MOE_ERR_ARG
+    # gathered up-projection: NULL perm; a bf16 token matrix beyond the 32-bit buffer offsets
+    assert L.moe_expert_up_gather(ctypes.byref(c), P, None, P, P, P, None, P, P, 1 << 40, None) == _lib.MOE_ERR_ARG
+    cbig = _cfg(n_tokens=1 << 20, d_model=1024)
+    assert L.moe_expert_up_gather(ctypes.byref(cbig), P, P, P, P, P, None, P, P, 1 << 40,
+                                  None) == _lib.MOE_ERR_UNSUPPORTED
+    # permute without x_perm needs no x (the workspace check is reached); with x_perm it does
+    assert L.moe_permute(ctypes.byref(c), P, None, P, P, P, P, None, None, P, 16, None) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_permute(ctypes.byref(c), P, None, P, P, P, P, None, P, P, 1 << 40, None) == _lib.MOE_ERR_ARG
     # negative gamma
     assert L.moe_bias_update(ctypes.byref(c), P, ctypes.c_float(-1.0), P, P, None) == _lib.MOE_ERR_ARG
     # forward: bias step without a selection bias

@@ -108,6 +108,18 @@ def test_steps_match_forward():
                        ("slot_pos", sp), ("drop_count", drop), ("out", out)):
             assert np.array_equal(host(t), o[key]), (name, key)
         assert np.array_equal(host(perm)[:kept], o["perm"][:kept])
+        # the fused dispatch: indices only, then the up GEMM gathers token rows through perm
+        perm2 = torch.full_like(perm, -7)
+        sp2 = torch.empty_like(sp)
+        counts2 = torch.empty_like(counts)
+        offs2 = torch.empty_like(offs)
+        M.permute(c, idx, None, counts2, offs2, perm2, sp2, None, ws=ws)
+        h2 = torch.empty_like(h)
+        M.expert_up_gather(c, dev["x"], perm2, offs2, dev["w1"], dev["w3"], h2, b1=dev["b1"], ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(counts2), host(counts)) and np.array_equal(host(offs2), host(offs))
+        assert np.array_equal(host(perm2)[:kept], perm_h) and np.array_equal(host(sp2), host(sp))
+        assert np.array_equal(host(h2)[:kept], host(h)[:kept]), (name, "gathered up-projection differs")
         if cfg.aux_loss:
             aux = torch.empty(1, dtype=torch.float32, device="cuda")
             M.aux_loss(c, counts, ps, aux)
