@@ -108,7 +108,11 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *   topk_idx   [N, k] int32  out: chosen experts, descending key, exact ties to the lower index
  *   gates      [N, k] fp32   out: gate weights by `gate_rule`
  *   probsum    [E] fp32 | NULL   out: sum over tokens of softmax(z)[t, e] (for moe_aux_loss)
- *   ws/ws_bytes scratch, at least moe_workspace_size(cfg) bytes
+ *   ws/ws_bytes workspace of moe_workspace_size(cfg) bytes; required when probsum is
+ *              requested.  When given (and large enough), routers with bf16 storage
+ *              and E a multiple of 64 compute the logits on the grouped-GEMM kernel
+ *              with its K-split scratch; otherwise a dedicated router kernel runs.
+ *              Both accumulate in fp32; their rounding orders differ.
  * Selection keys are formed and compared in fp64 from the fp32 logits and bias. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* logit_bias, const float* sel_bias, const float* logits_in,

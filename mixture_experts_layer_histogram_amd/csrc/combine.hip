@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   }
   const size_t trow = (size_t)t * d;
   if (d % VEC == 0) {
-    for (int c = lane * VEC; c < d; c += 64 * VEC) {
+#pragma unroll 2
+    for (int c = lane * VEC; c < d; c += 64 * VEC) {   // two chunks in flight per lane
       float acc[VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[v] = 0.f;

@@ -209,6 +209,8 @@ struct GemmParams {
   const uint16_t* W3;         // SwiGLU: [n_seg, Nn, K]
   const uint16_t* bias;       // [n_seg, Nn] or null
   uint16_t* out;              // [rows, Nn]
+  float* out_f;               // MODE_LOGITS: fp32 output
+  const float* bias_f;        // MODE_LOGITS: fp32 bias [Nn] or null
   float* partials;            // K-part tiles of the 256-row list
   float* partials_small;      // K-part tiles of the 64-row list
   int K, Nn, n_ntiles;
@@ -220,7 +222,8 @@ struct GemmParams {
 template <int MODE, bool HAS_BIAS>
 __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
                                             int wn, int r0, int r1, int n0, int Nn, int seg,
-                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
+                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+                                            const float* __restrict__ bias_f, float* __restrict__ out_f) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -229,7 +232,21 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
       for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
     __builtin_amdgcn_wave_barrier();
     const int rbase = r0 + wm * 128 + mi * 32;
-    if (MODE == MODE_SWIGLU_UP) {
+    if (MODE == MODE_LOGITS) {
+#pragma unroll 1
+      for (int pass = 0; pass < 16; ++pass) {
+        const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+        const int row = rbase + rr, col = n0 + wn * 128 + c4;
+        if (row < r1 && col < Nn) {
+          float4 v = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
+          if (HAS_BIAS) {
+            const float4 b = *reinterpret_cast<const float4*>(bias_f + col);
+            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          }
+          *reinterpret_cast<float4*>(out_f + (size_t)row * Nn + col) = v;
+        }
+      }
+    } else if (MODE == MODE_SWIGLU_UP) {
       // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
 #pragma unroll 1
       for (int pass = 0; pass < 4; ++pass) {
@@ -271,7 +288,8 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
 template <int MODE, bool HAS_BIAS>
 __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, int lane, int kh, int l32, int wn,
                                               int r0, int r1, int n0, int Nn, int seg,
-                                              const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
+                                              const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+                                              const float* __restrict__ bias_f, float* __restrict__ out_f) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
@@ -280,7 +298,21 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
       for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
     __builtin_amdgcn_wave_barrier();
     const int rbase = r0 + mi * 32;
-    if (MODE == MODE_SWIGLU_UP) {
+    if (MODE == MODE_LOGITS) {
+#pragma unroll 1
+      for (int pass = 0; pass < 8; ++pass) {
+        const int rr = pass * 4 + (lane >> 4), c4 = (lane & 15) * 4;
+        const int row = rbase + rr, col = n0 + wn * 64 + c4;
+        if (row < r1 && col < Nn) {
+          float4 v = *reinterpret_cast<const float4*>(ep + rr * 64 + c4);
+          if (HAS_BIAS) {
+            const float4 b = *reinterpret_cast<const float4*>(bias_f + col);
+            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          }
+          *reinterpret_cast<float4*>(out_f + (size_t)row * Nn + col) = v;
+        }
+      }
+    } else if (MODE == MODE_SWIGLU_UP) {
       // cols 0..31 hold x W1^T, cols 32..63 the matching x W3^T
 #pragma unroll 1
       for (int pass = 0; pass < 2; ++pass) {
@@ -444,7 +476,8 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-    store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out);
+    store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
+                                p.bias_f, p.out_f);
   } else {
     // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]
     float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2 + wn * 128 + l32;
@@ -580,7 +613,8 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
-    store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out);
+    store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
+                                  p.bias_f, p.out_f);
   } else {
     // fp32 partial tile, row-major [slot][64 rows][256 accumulator columns]
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
@@ -680,6 +714,18 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
         for (int e = 0; e < 8; ++e) v3[e] = q == 0 ? ys[e] : v3[e] + ys[e];
       }
     }
+    if (MODE == MODE_LOGITS) {
+      float4 o0 = make_float4(v1[0], v1[1], v1[2], v1[3]), o1 = make_float4(v1[4], v1[5], v1[6], v1[7]);
+      if (HAS_BIAS) {
+        const float4 b0 = *reinterpret_cast<const float4*>(p.bias_f + col);
+        const float4 b1 = *reinterpret_cast<const float4*>(p.bias_f + col + 4);
+        o0.x += b0.x; o0.y += b0.y; o0.z += b0.z; o0.w += b0.w;
+        o1.x += b1.x; o1.y += b1.y; o1.z += b1.z; o1.w += b1.w;
+      }
+      *reinterpret_cast<float4*>(p.out_f + (size_t)row * p.Nn + col) = o0;
+      *reinterpret_cast<float4*>(p.out_f + (size_t)row * p.Nn + col + 4) = o1;
+      continue;
+    }
     Vec8 b, o;
     if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(p.bias + (size_t)w.seg * p.Nn + col);
 #pragma unroll
@@ -769,6 +815,8 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.W3 = (const uint16_t*)g.w3;
   p.bias = (const uint16_t*)g.bias;
   p.out = (uint16_t*)g.out;
+  p.out_f = g.out_f32;
+  p.bias_f = g.bias_f32;
   p.partials = g.partials;
   p.partials_small = g.partials + (size_t)kMaxSplitUnits * kBM2 * kBN2;
   p.K = g.K;
@@ -798,8 +846,9 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
     return hipGetLastError();
   }
   const bool gather = g.perm != nullptr;
-  if (gather && (g.mode == MODE_DOWN || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
+  if (gather && (g.mode >= MODE_DOWN || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
     return hipErrorInvalidValue;
+  if (g.mode == MODE_LOGITS && (g.Nn % 8 != 0 || g.n_seg != 1)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, g.offsets, g.n_seg, g.max_rows, g.tiles,
                      g.max_tiles, g.tiles_small, g.max_tiles_small);
   hipError_t err = hipGetLastError();
@@ -809,8 +858,10 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   } else if (g.mode == MODE_GELU_UP) {
     if (hb) gather ? launch_bf16<MODE_GELU_UP, true, true>(g, s) : launch_bf16<MODE_GELU_UP, true, false>(g, s);
     else gather ? launch_bf16<MODE_GELU_UP, false, true>(g, s) : launch_bf16<MODE_GELU_UP, false, false>(g, s);
-  } else {
+  } else if (g.mode == MODE_DOWN) {
     hb ? launch_bf16<MODE_DOWN, true, false>(g, s) : launch_bf16<MODE_DOWN, false, false>(g, s);
+  } else {
+    g.bias_f32 ? launch_bf16<MODE_LOGITS, true, false>(g, s) : launch_bf16<MODE_LOGITS, false, false>(g, s);
   }
   return hipGetLastError();
 }

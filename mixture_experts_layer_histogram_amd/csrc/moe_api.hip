@@ -8,11 +8,6 @@ namespace moe {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-static int pow2ceil(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
 
 Workspace workspace_layout(const moe_config& c) {
   Workspace W{};
@@ -28,9 +23,7 @@ Workspace workspace_layout(const moe_config& c) {
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
 
   // top-k blocking: L lanes per token, 4 waves, iters rounds per block
-  int L = pow2ceil(c.n_experts);
-  if (L < 8) L = 8;
-  if (L > 64) L = 64;
+  const int L = topk_lanes(c.n_experts);
   const int per_iter = 4 * (64 / L);
   long long iters = ((long long)N + (long long)per_iter * 256 - 1) / ((long long)per_iter * 256);
   if (iters < 1) iters = 1;
@@ -117,31 +110,6 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // Internal step bodies (validated arguments).
-moe_status do_route(const moe_config& c, const Workspace& W, const void* x, const void* w_router,
-                    const float* logit_bias, const float* sel_bias, const float* logits_in, float* logits,
-                    int32_t* topk_idx, float* gates, float* probsum, void* ws, hipStream_t s) {
-  const float* zin = logits_in;
-  float* zout = nullptr;
-  if (!zin) {
-    MOE_HIP(launch_router_gemm(c, x, w_router, logit_bias, logits, s));
-    zin = logits;
-  } else if (logits && logits != logits_in) {
-    zout = logits;
-  }
-  MOE_HIP(launch_topk(c, W, zin, zout, sel_bias, topk_idx, gates,
-                      reinterpret_cast<float*>(wsp(ws, W.probsum_part)), probsum, s));
-  return MOE_OK;
-}
-
-moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx, const void* x,
-                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
-                      int64_t* drop_count, void* x_perm, void* ws, hipStream_t s) {
-  MOE_HIP(launch_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm,
-                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_rank)),
-                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_blocks)), s));
-  return MOE_OK;
-}
-
 GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, bool shared) {
   GroupedGemmArgs g{};
   g.dtype = c.dtype;
@@ -162,6 +130,50 @@ GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, boo
     g.max_tiles_small = W.max_tiles_small;
   }
   return g;
+}
+
+moe_status do_route(const moe_config& c, const Workspace& W, const void* x, const void* w_router,
+                    const float* logit_bias, const float* sel_bias, const float* logits_in, float* logits,
+                    int32_t* topk_idx, float* gates, float* probsum, void* ws, hipStream_t s) {
+  const float* zin = logits_in;
+  float* zout = nullptr;
+  if (!zin) {
+    // Wide routers (E a multiple of 64) run on the grouped GEMM with fp32 output; it needs the
+    // scratch part of the workspace.  Narrow ones use the router kernel, which needs none.
+    const bool wide = c.dtype == MOE_BF16 && c.n_experts % 64 == 0 && ws != nullptr && aligned16(logits) &&
+                      aligned16(logit_bias);
+    if (wide && c.n_tokens > 0) {
+      GroupedGemmArgs g = gemm_args(c, W, ws, false);
+      g.mode = MODE_LOGITS;
+      g.n_seg = 1;
+      g.max_rows = (int)c.n_tokens;
+      g.K = c.d_model;
+      g.Nn = c.n_experts;
+      g.a = x;
+      g.offsets = nullptr;
+      g.w = w_router;
+      g.out_f32 = logits;
+      g.bias_f32 = logit_bias;
+      MOE_HIP(launch_grouped_gemm(g, s));
+    } else {
+      MOE_HIP(launch_router_gemm(c, x, w_router, logit_bias, logits, s));
+    }
+    zin = logits;
+  } else if (logits && logits != logits_in) {
+    zout = logits;
+  }
+  MOE_HIP(launch_topk(c, W, zin, zout, sel_bias, topk_idx, gates,
+                      reinterpret_cast<float*>(wsp(ws, W.probsum_part)), probsum, s));
+  return MOE_OK;
+}
+
+moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx, const void* x,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                      int64_t* drop_count, void* x_perm, void* ws, hipStream_t s) {
+  MOE_HIP(launch_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm,
+                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_rank)),
+                         reinterpret_cast<int32_t*>(wsp(ws, W.hist_blocks)), s));
+  return MOE_OK;
 }
 
 // `perm` != NULL: `a` is the token matrix and row r of the expert order is
@@ -259,8 +271,10 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
     if (!logits_in && (!aligned16(x) || !aligned16(w_router))) return MOE_ERR_UNSUPPORTED;
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, probsum ? scratch_end(W) : 0));
+    // a workspace too small (or unaligned) for the scratch is simply not used
+    void* scratch = (ws && check_ws(ws, ws_bytes, scratch_end(W)) == MOE_OK) ? ws : nullptr;
     return do_route(c, W, x, w_router, logit_bias, sel_bias, logits_in, logits, topk_idx, gates, probsum,
-                    ws, stream);
+                    scratch, stream);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

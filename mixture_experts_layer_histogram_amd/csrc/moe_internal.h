@@ -46,6 +46,10 @@ template <> struct Store<uint16_t> {
 __device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
 __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 0.70710678118654752f); }
 
+// Top-k blocking: L lanes per token (each owning E / L consecutive experts, at
+// most 8), so a wavefront routes 64 / L tokens at once.
+inline int topk_lanes(int E) { return E <= 64 ? 8 : (E <= 128 ? 16 : 32); }
+
 // ----------------------------------------------------------------- workspace
 
 struct Workspace {
@@ -76,11 +80,12 @@ hipError_t launch_permute(const moe_config& c, const Workspace& L, const int32_t
                           int32_t* hist_rank, int32_t* hist_blocks, hipStream_t s);
 
 // GEMM modes
-enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2 };
+enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2, MODE_LOGITS = 3 };
 
 // Grouped GEMM over ragged segments [offsets[e], offsets[e+1]) of `a`.
 //   up   : h[r, :F]  = act(a[r, :K] W1_e^T [, a W3_e^T] [+ b1_e])
 //   down : y[r, :Nn] = a[r, :K] W2_e^T [+ b2_e]
+//   logits (one segment): z[r, :Nn] = a[r, :K] W^T [+ bias_f32] stored as fp32 (the router)
 // `offsets` has n_seg+1 entries; `tiles` is scratch for the device-built tile list.
 // With `perm` (up only), row r of the expert order is row perm[r] / gather_k
 // of `a`, which then holds a_rows token rows.
@@ -100,6 +105,8 @@ struct GroupedGemmArgs {
   const void* w3;        // SwiGLU up only
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
+  float* out_f32;        // MODE_LOGITS output [rows, Nn]
+  const float* bias_f32; // MODE_LOGITS bias [Nn] or NULL
   int32_t* tiles;        // scratch: 256-row tile list (4 header ints + 8 ints per tile)
   int max_tiles;
   int32_t* tiles_small;  // scratch: 64-row tile list

@@ -99,10 +99,15 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   if (tid < E) {
     int a = 0;
     int32_t* row = block_counts + (size_t)tid * nblk;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = row[b];
-      row[b] = a;
-      a += c;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {   // 16 loads in flight, then the running sum in order
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblk ? row[b0 + j] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nblk) row[b0 + j] = a;
+        a += c[j];
+      }
     }
     counts[tid] = a;
     kept = a < capacity ? a : capacity;

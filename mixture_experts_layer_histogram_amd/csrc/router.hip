@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
       }
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k && gl == j) {
+        if (j < k && (j % L) == gl) {   // k may exceed L
           idx_out[(size_t)t * k + j] = sel[j];
           gates_out[(size_t)t * k + j] = (float)gate[j];
         }
@@ -302,14 +302,17 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
 }
 
-// Sum the per-block partials in block order.
-__global__ __launch_bounds__(256) void probsum_reduce_kernel(const double* __restrict__ part, int nblk,
-                                                             int E, float* __restrict__ probsum) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += part[(size_t)b * E + e];
-    probsum[e] = (float)s;
-  }
+// Sum the per-block partials of expert e = blockIdx.x: lane l adds blocks
+// l, l + 64, ... in order, then a fixed xor tree combines the lanes, so the
+// result does not depend on timing.
+__global__ __launch_bounds__(64) void probsum_reduce_kernel(const double* __restrict__ part, int nblk,
+                                                            int E, float* __restrict__ probsum) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  double s = 0.0;
+  for (int b = lane; b < nblk; b += 64) s += part[(size_t)b * E + e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) probsum[e] = (float)s;
 }
 
 template <int L, int V>
@@ -326,18 +329,20 @@ hipError_t launch_topk(const moe_config& c, const Workspace& W, const float* zin
   double* part = probsum ? reinterpret_cast<double*>(probsum_part_f) : nullptr;
   if (c.n_tokens > 0) {
     const int E = c.n_experts;
+    // L = topk_lanes(E) lanes per token, V = experts per lane
     if (E <= 8) launch_topk_lv<8, 1>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else if (E <= 16) launch_topk_lv<16, 1>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else if (E <= 32) launch_topk_lv<32, 1>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else if (E <= 64) launch_topk_lv<64, 1>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else if (E <= 128) launch_topk_lv<64, 2>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else launch_topk_lv<64, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else if (E <= 16) launch_topk_lv<8, 2>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else if (E <= 32) launch_topk_lv<8, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else if (E <= 64) launch_topk_lv<8, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else if (E <= 128) launch_topk_lv<16, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else launch_topk_lv<32, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (probsum) {
     const int nblk = c.n_tokens > 0 ? W.topk_blocks : 0;
-    hipLaunchKernelGGL(probsum_reduce_kernel, dim3(1), dim3(256), 0, s, part, nblk, c.n_experts, probsum);
+    hipLaunchKernelGGL(probsum_reduce_kernel, dim3(c.n_experts), dim3(64), 0, s, part, nblk, c.n_experts,
+                       probsum);
     return hipGetLastError();
   }
   return hipSuccess;

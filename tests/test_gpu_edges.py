@@ -1,5 +1,6 @@
-"""GPU edge cases: empty and one-token batches, a single expert, k = E, a
-capacity that drops every slot, exact logit ties, odd expert counts."""
+"""GPU edge cases: empty and one-token batches, a single expert, k = E, k
+above the top-k lane group, a capacity that drops every slot, exact logit
+ties, odd expert counts, K-split tails, the GEMM router's short tail."""
 import numpy as np
 import pytest
 
@@ -30,6 +31,10 @@ EDGE = {
     "swiglu_big_segments": BASE.scaled(name="swiglu_big_segments", n_tokens=1500, n_experts=4, d_model=192,
                                        d_ff=320),
     # more tiles than one round of workgroups with a partial last round: the K-split tail path
+    # k larger than the top-k lane group (8 lanes per token for E <= 64)
+    "k16_e32": BASE.scaled(name="k16_e32", n_tokens=300, n_experts=32, top_k=16),
+    # E = 64 router on the grouped GEMM with a logit bias and a short tail (64-row tiles)
+    "router_gemm_tail": SWITCH_SKEWED.scaled(name="router_gemm_tail", n_tokens=600, d_model=256, d_ff=256),
     "split_k_up": BASE.scaled(name="split_k_up", n_tokens=2048, n_experts=4, d_model=256, d_ff=2240),
     "split_k_down_gelu": SWITCH_SKEWED.scaled(name="split_k_down_gelu", n_tokens=2048, n_experts=4, d_model=8448,
                                               d_ff=256, capacity_factor=0.0, logit_offset=None),
