@@ -7,4 +7,6 @@ for it.
 from .moe_oracle import (to_f64, router_logits, softmax_rows, top_k_desc, route, selection_gap,
                          dispatch, Dispatch, silu, gelu, ffn_swiglu, ffn_gelu, expert_apply,
                          aux_loss, bias_step, oracle_route, oracle_layer, RouteResult,
-                         GATE_TOPK_SOFTMAX, GATE_SOFTMAX_RENORM, GATE_SWITCH_TOP1)
+                         GATE_TOPK_SOFTMAX, GATE_SOFTMAX_RENORM, GATE_SWITCH_TOP1,
+                         E4M3_MAX, e4m3_value, e4m3_round, quantize_fp8_rows, dequantize_fp8_rows,
+                         fp8_expert_weights)

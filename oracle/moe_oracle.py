@@ -21,6 +21,8 @@ Sources (the pages describing the method; cited by title and section):
     printed output).
 [X] "Expert Parallelism for MoE Serving" (aiunderstanding.org): "Deep dive",
     "Technical insight" (dispatch groups tokens by expert; capacity).
+[S] "How sparse models scale" (ircnf.com): the part on running large MoE
+    models, where quantised weights are the remedy for their memory size.
 
 Readings taken where the pages leave a step open (each is also listed in the
 design notes):
@@ -38,7 +40,10 @@ design notes):
   the pre-drop counts and ``P_e`` the full-softmax probability averaged over
   all N tokens;
 * bias step ``b_e <- b_e - gamma * sign(counts_e * E - N k)``, sign(0) = 0,
-  applied after the forward pass (it feeds the next call only).
+  applied after the forward pass (it feeds the next call only);
+* fp8 weight-only experts ([S]; the pages name 8-bit weights, no format): OCP
+  E4M3 codes, round to nearest with ties to even, saturating at 448, one fp32
+  scale per output row (amax / 448), activations and accumulation unchanged.
 """
 from __future__ import annotations
 
@@ -288,13 +293,16 @@ def oracle_route(cfg, logits: np.ndarray, sel_bias=None) -> RouteResult:
                        signs=signs, new_bias=new_bias, min_gap=float(gap.min()) if gap.size else math.inf)
 
 
-def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"):
+def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs", expert_weights="stored"):
     """The whole forward pass in fp64.
 
     ``inputs`` is a :class:`workloads.LayerInputs`.  ``logits_override`` replaces
     the router product (parity hook: the GPU's fp32 logits decide routing on
     both sides).  ``rows`` restricts the expert work and the output to those
     tokens (routing, counts and capacity still cover all N).
+    ``expert_weights="fp8"`` runs the routed experts on their fp8 round trip
+    (``fp8_expert_weights``); the router and the shared expert keep the stored
+    weights.
 
     [L] "Concept / FFN swap": h + sum over the chosen experts of gate * expert(h);
     [G] example: out[tokens of e] += weight * expert_e(tokens of e) for each e;
@@ -324,6 +332,8 @@ def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"
             continue
         assert np.all(expert_of_slot[slots] == e)
         w = {n: to_f64(v, dt) for n, v in inputs.expert(e).items()}
+        if expert_weights == "fp8":
+            w = fp8_expert_weights(w)
         Y = expert_apply(cfg.act, x[slots // k], w)
         for s, yrow in zip(slots, Y):
             y_slot[int(s)] = yrow
@@ -340,3 +350,71 @@ def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"
             if r.disp.slot_pos[s] >= 0:
                 out[i] += r.gates[t, j] * y_slot[s]
     return r, out
+
+
+# --------------------------------------------------------------------------- fp8 weight-only experts
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return s * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(127))          # codes 0..126: every non-negative finite value, ascending
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 code to each value (compared exactly in fp64), an exact tie
+    going to the code with an even mantissa; magnitudes above 448 saturate to
+    448.  The sign bit follows the sign of x (so -0.0 and negative values that
+    round to zero give 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_rows(w) -> tuple[np.ndarray, np.ndarray]:
+    """Round-to-nearest fp8 weights with one scale per output row (a row of a
+    weight stored [out, in]).  In fp32, as the kernel computes it:
+    amax = max |w|, scale = amax / 448, inv = 448 / amax (scale = inv = 1 for
+    an all-zero row), code = e4m3_round(w * inv)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=1)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    codes = e4m3_round((w * inv[:, None]).astype(np.float32))
+    return codes, scale
+
+
+def dequantize_fp8_rows(codes, scales) -> np.ndarray:
+    """fp64 weights the fp8 experts compute with: value(code) * row scale (exact)."""
+    return e4m3_value(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+def fp8_expert_weights(w: dict) -> dict:
+    """An expert's weight dict with every matrix replaced by its fp8 round trip
+    (biases unchanged).  Input matrices are the exact fp64 values of bf16/fp32
+    storage, hence exactly representable in fp32."""
+    out = {}
+    for n, v in w.items():
+        if n.startswith("b"):
+            out[n] = v
+        else:
+            q, sc = quantize_fp8_rows(np.asarray(v, dtype=np.float32))
+            out[n] = dequantize_fp8_rows(q, sc)
+    return out

@@ -384,4 +384,83 @@ def check_activation_library():
     assert np.allclose(mo.gelu(v), TF.gelu(V, approximate="none").numpy(), rtol=1e-12, atol=1e-14)
 
 
+# ----------------------------------------------------------------- fp8 weight-only experts
+
+def check_e4m3_closed_forms():
+    """OCP E4M3 values fixed by the format: 448 the largest finite, 2^-6 the
+    smallest normal, 2^-9 the smallest subnormal, 1.0 = 0x38, S.1111.111 NaN;
+    the 127 non-negative finite codes increase strictly with the code."""
+    v = mo.e4m3_value(np.arange(256))
+    assert v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x38] == 1.0
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0x3F] == 1.875 and v[0xB8] == -1.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert np.all(np.diff(v[:127]) > 0)
+    fin = ~np.isnan(v)
+    assert np.array_equal(mo.e4m3_round(v[fin]), np.arange(256)[fin].astype(np.uint8))
+
+
+def check_e4m3_ties_to_even():
+    """A value halfway between two neighbouring codes takes the even one."""
+    v = mo.e4m3_value(np.arange(127))
+    mid = (v[:-1] + v[1:]) / 2
+    got = mo.e4m3_round(mid.astype(np.float32))
+    want = np.where(np.arange(126) % 2 == 0, np.arange(126), np.arange(1, 127))
+    assert np.array_equal(got, want.astype(np.uint8)), np.nonzero(got != want)
+    assert np.array_equal(mo.e4m3_round(-mid.astype(np.float32)), (want | 0x80).astype(np.uint8))
+
+
+def check_e4m3_rounding_library():
+    """Against torch's float8_e4m3fn cast (round to nearest even) on values of
+    every binade, the subnormal range and exact midpoints, all within +-448."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * 40.0, rng.uniform(-2 ** -5, 2 ** -5, 20000),
+                        np.exp2(rng.uniform(-12, 8.8, 20000)) * rng.choice([-1, 1], 20000)])
+    v = mo.e4m3_value(np.arange(127))
+    x = np.concatenate([x, (v[:-1] + v[1:]) / 2, v]).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mo.e4m3_round(x), lib)
+
+
+def check_fp8_quantize_rows():
+    """Per-row round trip: the row maximum lands on +-448 exactly, every element
+    is within half a code step of the original, an all-zero row stays zero."""
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((40, 96)) * np.exp2(rng.uniform(-8, 4, (40, 1)))).astype(np.float32)
+    w[3] = 0.0
+    q, sc = mo.quantize_fp8_rows(w)
+    assert q.dtype == np.uint8 and sc.dtype == np.float32
+    amax = np.abs(w).max(axis=1)
+    nz = amax > 0
+    assert np.array_equal(sc[nz], (amax[nz] / np.float32(448)).astype(np.float32))
+    j = np.abs(w).argmax(axis=1)
+    assert np.all(np.abs(mo.e4m3_value(q[np.arange(40), j]))[nz] == 448.0)
+    deq = mo.dequantize_fp8_rows(q, sc)
+    bound = np.maximum(2.0 ** -4 * np.abs(w), 2.0 ** -10 * sc[:, None].astype(np.float64)) * (1 + 1e-6)
+    assert np.all(np.abs(deq - w) <= bound)
+    assert np.all(q[3] == 0) and sc[3] == 1.0
+
+
+def check_fp8_expert_is_dense_fp8_ffn():
+    """One expert, k = 1: the layer with fp8 experts equals a dense SwiGLU FFN
+    whose weights went through torch's own per-row fp8 round trip (fp32 scale
+    amax / 448 and multiplier 448 / amax, float8_e4m3fn cast, back to fp64)."""
+    cfg = MoEConfig(name="fp8_dense", n_tokens=9, d_model=64, n_experts=1, top_k=1, d_ff=96, act="swiglu",
+                    gate_rule=GATE_TOPK_SOFTMAX, dtype="bf16", residual=False, seed=5)
+    inp = make_inputs(cfg)
+    _, out = mo.oracle_layer(cfg, inp, expert_weights="fp8")
+    x = mo.to_f64(inp.x, "bf16")
+
+    def rt(wb):
+        w = torch.from_numpy(mo.to_f64(wb, "bf16").astype(np.float32))
+        amax = w.abs().amax(dim=1, keepdim=True).double()
+        # correctly rounded fp32 quotients (fp64 quotient rounded once to fp32)
+        scale, inv = (amax / 448.0).float(), (448.0 / amax).float()
+        return ((w * inv).to(torch.float8_e4m3fn).to(torch.float64) * scale.to(torch.float64)).numpy()
+    e = inp.expert(0)
+    w1, w3, w2 = rt(e["w1"]), rt(e["w3"]), rt(e["w2"])
+    ref = (x @ w1.T) / (1 + np.exp(-(x @ w1.T))) * (x @ w3.T) @ w2.T
+    assert np.abs(out - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

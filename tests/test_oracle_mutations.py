@@ -11,7 +11,7 @@ import pytest
 import oracle.moe_oracle as mo
 import pin_checks as pc
 
-_orig = {n: getattr(mo, n) for n in ("top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
+_orig = {n: getattr(mo, n) for n in ("e4m3_round", "quantize_fp8_rows", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
                                        "aux_loss", "bias_step", "softmax_rows", "oracle_layer")}
 
 
@@ -94,7 +94,23 @@ def _layer_no_residual(cfg, inputs, *a, **kw):
     return _orig["oracle_layer"](dataclasses.replace(cfg, residual=False), inputs, *a, **kw)
 
 
+def _e4m3_ties_away(x):
+    xa = np.asarray(x, dtype=np.float64)
+    c = _orig["e4m3_round"](xa)
+    v = mo.e4m3_value(np.arange(127))
+    mid = np.isin(np.abs(xa), (v[:-1] + v[1:]) / 2)
+    up = np.searchsorted(v, np.abs(xa)).clip(0, 126)
+    return np.where(mid, up | np.where(np.signbit(xa), 0x80, 0), c).astype(np.uint8)
+
+
+def _quantize_fnuz_max(w):
+    q, sc = _orig["quantize_fp8_rows"](np.asarray(w, dtype=np.float32) * np.float32(240.0 / 448.0))
+    return q, (sc * np.float32(448.0 / 240.0)).astype(np.float32)
+
+
 MUTATIONS = [
+    ("e4m3_round", _e4m3_ties_away, [pc.check_e4m3_ties_to_even, pc.check_e4m3_rounding_library]),
+    ("quantize_fp8_rows", _quantize_fnuz_max, [pc.check_fp8_quantize_rows]),
     ("top_k_desc", _ties_to_higher, [pc.check_topk_brute_force]),
     ("route", _gates_from_biased_key, [pc.check_bias_moves_selection_not_gates]),
     ("ffn_swiglu", _silu_on_w3, [pc.check_single_expert_is_dense, pc.check_identical_experts_are_dense]),
