@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/sec @DeepSeek-V3 & Mixtral shapes; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", "grouped_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--oracle-tokens", type=int, default=None,
                     help="tokens in the CPU-baseline sample (default: whole batch for prefill shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-experts", action="store_true",
+                    help="routed experts with fp8 (E4M3) weights and per-row scales, quantised before timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -119,6 +122,22 @@ def main():
     out = torch.empty((N, d), dtype=st, device=dev_name)
     aux = torch.empty(1, dtype=f32, device=dev_name) if cfg.aux_loss else None
     signs = torch.empty(E, dtype=torch.int8, device=dev_name)
+    fp8 = None
+    if args.fp8_experts:
+        if cfg.dtype != "bf16":
+            print("--fp8-experts needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        fp8 = {}
+        for n in ("w1", "w3", "w2"):
+            t = dev[n]
+            if t is None:
+                fp8[n] = (None, None)
+                continue
+            q = torch.empty(t.shape, dtype=torch.uint8, device=dev_name)
+            sc = torch.empty(t.shape[:-1], dtype=torch.float32, device=dev_name)
+            M.quantize_fp8(t, q, sc)
+            fp8[n] = (q, sc)
+        torch.cuda.synchronize()
     # the bias step writes a copy, so every timed step routes with the same selection bias
     sel_next = dev["sel_bias"].clone() if dev["sel_bias"] is not None else None
     residual = dev["x"] if cfg.residual else None
@@ -135,9 +154,16 @@ def main():
         mark(1)
         M.permute(c, idx, None, counts, offs, perm, slot_pos, None, drop_count=drop, ws=ws)
         mark(2)
-        M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+        if fp8 is None:
+            M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+        else:
+            M.expert_up_fp8(c, dev["x"], perm, offs, fp8["w1"][0], fp8["w3"][0], fp8["w1"][1], fp8["w3"][1], h,
+                            b1=dev["b1"], ws=ws)
         mark(3)
-        M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
+        if fp8 is None:
+            M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
+        else:
+            M.expert_down_fp8(c, h, offs, fp8["w2"][0], fp8["w2"][1], y, b2=dev["b2"], ws=ws)
         mark(4)
         if Fs:
             M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], h_sh, y_sh, ws=ws)
@@ -171,12 +197,30 @@ def main():
              for j, n in enumerate(names)}
 
     kept = int(offs[-1].item())
+    used = int((counts > 0).sum().item())
     n_up = 2 if cfg.act == "swiglu" else 1
     up_flop = 2.0 * n_up * d * F * kept
     down_flop = 2.0 * F * d * kept
-    up_tflops = up_flop / (parts["expert_up"] * 1e-3) / 1e12
+    t_up = parts["expert_up"] * 1e-3
+    up_tflops = up_flop / t_up / 1e12
     expert_tflops = (up_flop + down_flop) / ((parts["expert_up"] + parts["expert_down"]) * 1e-3) / 1e12
-    traffic = measured_traffic(cfg.name)
+    # algorithmic bytes of the up call: each used expert's weights once (+ fp8 row scales), the
+    # token rows once, h written once, b1 rows of used experts
+    esz = 2 if cfg.dtype == "bf16" else 4
+    wsz = 1 if fp8 is not None else esz
+    up_bytes = (used * n_up * F * (d * wsz + (4 if fp8 is not None else 0)) + N * d * esz + kept * F * esz
+                + (used * F * esz if cfg.ffn_bias else 0))
+    if cfg.dtype == "bf16":
+        t_mfma, t_hbm = up_flop / (PEAK_BF16_TFLOPS * 1e12), up_bytes / (PEAK_HBM_GBS * 1e9)
+        if t_mfma >= t_hbm:
+            roof = {"bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            gbs = up_bytes / t_up / 1e9
+            roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:   # fp32 storage runs on the vector ALUs
+        roof = {"bound": "alu", "achieved": up_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = measured_traffic(cfg.name) if fp8 is None else None
 
     result = {
         "metric": METRIC,
@@ -193,12 +237,12 @@ def main():
         "data": "synthetic (seeded; random weights of the named shapes)",
         "config": {"workload": cfg.name, "n_tokens": N, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
                    "d_ff_shared": Fs, "act": cfg.act, "gate_rule": cfg.gate_rule,
-                   "capacity_factor": cfg.capacity_factor, "kept_slots": kept},
+                   "capacity_factor": cfg.capacity_factor, "kept_slots": kept, "used_experts": used,
+                   "expert_weights": "fp8_e4m3_row_scaled" if fp8 is not None else cfg.dtype},
         "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
                                "(build_tiles_kernel, grouped_gemm_kernel, split_fixup_kernel; one "
-                               "moe_expert_up_gather call)",
-                     "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": up_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+                               f"{'moe_expert_up_gather' if fp8 is None else 'moe_expert_up_fp8'} call)",
+                     **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop},
         "expert_gemm_tflops": expert_tflops,
         "breakdown_ms": parts,
         "wall_s_timed": wall_s,
@@ -206,11 +250,11 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens, fp8 is not None)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cfg, inp, n_tok):
+def cpu_baseline(cfg, inp, n_tok, fp8=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
     import oracle
     try:
@@ -227,11 +271,12 @@ def cpu_baseline(cfg, inp, n_tok):
                         sel_bias=inp.sel_bias, w1=inp.w1, w3=inp.w3, w2=inp.w2, b1=inp.b1, b2=inp.b2,
                         sh_w1=inp.sh_w1, sh_w3=inp.sh_w3, sh_w2=inp.sh_w2)
     t0 = time.perf_counter()
-    oracle.oracle_layer(sub, sub_inp)
+    oracle.oracle_layer(sub, sub_inp, expert_weights="fp8" if fp8 else "stored")
     dt = time.perf_counter() - t0
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
-            "sample": f"first {n_tok} of {N} tokens of {cfg.name}, whole layer in fp64 "
+            "sample": f"first {n_tok} of {N} tokens of {cfg.name}, whole layer in fp64"
+                      f"{' with the fp8 round trip of the expert weights' if fp8 else ''} "
                       f"(routing, capacity and aux computed over the sample)"}
 
 

@@ -14,6 +14,8 @@
  *       layer works", "Load balancing and expert capacity".
  *   [X] "Expert Parallelism for MoE Serving" (aiunderstanding.org):
  *       "Deep dive", "Technical insight" (dispatch by expert, capacity).
+ *   [S] "How sparse models scale" (ircnf.com): quantised weights as the
+ *       remedy for the memory size of large MoE models.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument except `cfg` (and the struct pointers of
@@ -173,6 +175,38 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* x, const int3
 moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
                            const void* w2, const void* b2, void* y_perm,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* fp8 weight-only experts ([S] "How sparse models scale": quantised weights are
+ * how large MoE models fit in memory; the format here is OCP E4M3, round to
+ * nearest).  Each row of a weight matrix stored [out, in] gets one fp32 scale:
+ * scale = amax / 448 (1 for an all-zero row), code = nearest E4M3 value to
+ * w * (448 / amax), ties to the even code, saturating at +-448.  The product
+ * then uses w = value(code) * scale; activations stay bf16, accumulation fp32.
+ *
+ * moe_quantize_fp8: quantise a bf16 matrix w [rows, cols] (device) into codes
+ *   q [rows, cols] uint8 and scales [rows] fp32 (both device, caller-owned).
+ *   For cols % 4 == 0, w must be 16-byte and q 4-byte aligned.  Codes are a
+ *   deterministic function of w (fp32 arithmetic with correctly rounded
+ *   division).  Expert weights W1, W3 [E, F, d] are rows = E*F, cols = d;
+ *   W2 [E, d, F] is rows = E*d, cols = F. */
+moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                            hipStream_t stream);
+
+/* moe_expert_up_gather with fp8 weights: h = act(x[perm] (W1q*s1)^T [, x[perm] (W3q*s3)^T] [+ b1]).
+ *   w1q, w3q [E, F, d] uint8 codes, 16-byte aligned; s1, s3 [E, F] fp32 scales;
+ *   w3q / s3 NULL for MOE_ACT_GELU.  bf16 storage only (else MOE_ERR_UNSUPPORTED).
+ * Every segment runs on 64-row tiles: the kernel streams the codes (half the
+ * bytes of bf16) and expands them to bf16 exactly before the bf16 MFMA. */
+moe_status moe_expert_up_fp8(const moe_config* cfg, const void* x, const int32_t* perm,
+                             const int32_t* offsets, const uint8_t* w1q, const uint8_t* w3q,
+                             const float* s1, const float* s3, const void* b1, void* h_tmp,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_expert_down with fp8 weights: y = h (W2q*s2)^T [+ b2]; w2q [E, d, F] codes,
+ * s2 [E, d] scales. */
+moe_status moe_expert_down_fp8(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
+                               const uint8_t* w2q, const float* s2, const void* b2, void* y_perm,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Shared expert ([L] "Shared experts": every token passes through it, weight 1):
  * y_sh[N, d] = (SiLU(x sh_w1^T) * (x sh_w3^T)) sh_w2^T.  h_tmp is [N, Fs]. */

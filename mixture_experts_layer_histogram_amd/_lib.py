@@ -56,6 +56,9 @@ _SIGS = {
     "moe_expert_up": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up_gather": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P],
+    "moe_expert_up_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_expert_down_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_shared_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_combine": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P],
     "moe_bias_update": [ctypes.POINTER(MoeConfig), _P, c_float, _P, _P, _P],
@@ -155,6 +158,25 @@ def expert_up_gather(cfg, x, perm, offsets, w1, w3, h_tmp, b1=None, ws=None, str
     wp, wb = _ws(ws)
     _call("moe_expert_up_gather", ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(w1), _ptr(w3),
           _ptr(b1), _ptr(h_tmp), wp, wb, _stream(stream))
+
+
+def quantize_fp8(w, q, scales, stream=None):
+    """Per-row E4M3 codes and fp32 scales of a bf16 matrix (rows = all leading dims)."""
+    cols = int(w.shape[-1])
+    rows = int(w.numel() // cols) if cols else 0
+    _call("moe_quantize_fp8", _ptr(w), rows, cols, _ptr(q), _ptr(scales), _stream(stream))
+
+
+def expert_up_fp8(cfg, x, perm, offsets, w1q, w3q, s1, s3, h_tmp, b1=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _call("moe_expert_up_fp8", ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(w1q), _ptr(w3q),
+          _ptr(s1), _ptr(s3), _ptr(b1), _ptr(h_tmp), wp, wb, _stream(stream))
+
+
+def expert_down_fp8(cfg, h_tmp, offsets, w2q, s2, y_perm, b2=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _call("moe_expert_down_fp8", ctypes.byref(cfg), _ptr(h_tmp), _ptr(offsets), _ptr(w2q), _ptr(s2), _ptr(b2),
+          _ptr(y_perm), wp, wb, _stream(stream))
 
 
 def expert_down(cfg, h_tmp, offsets, w2, y_perm, b2=None, ws=None, stream=None):

@@ -18,6 +18,8 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     # keep the compiler from forming packed-fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # fp32 division and square root correctly rounded (the fp8 quantiser depends on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]

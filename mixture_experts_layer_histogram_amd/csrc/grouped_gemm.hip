@@ -25,7 +25,7 @@ namespace moe {
 
 // Splits every segment into 256-row tiles and 64-row tiles: floor(rows / 256)
 // full tiles, one more 256-row tile when at least kBigTailMin rows remain,
-// otherwise ceil(rest / 64) 64-row tiles.  Each list: [0] = tile count; tile i
+// otherwise ceil(rest / 64) 64-row tiles (only 64-row tiles with small_only).  Each list: [0] = tile count; tile i
 // at [4 + 8 i] = (segment, row_begin, row_end, first tile of the segment in
 // this list, tiles of the segment in this list, 0, 0, 0).
 constexpr int kBigTailMin = 128;
@@ -33,7 +33,7 @@ constexpr int kBigTailMin = 128;
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int n_seg,
                                                           int dense_rows, int32_t* __restrict__ big,
                                                           int max_big, int32_t* __restrict__ small,
-                                                          int max_small) {
+                                                          int max_small, int small_only) {
   __shared__ int tot_b[4], tot_s[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int lo = 0, hi = 0, nb = 0, ns = 0, split = 0;
@@ -41,9 +41,9 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
     lo = offsets ? offsets[tid] : 0;
     hi = offsets ? offsets[tid + 1] : dense_rows;
     const int rows = hi - lo;
-    nb = rows / 256;
+    nb = small_only ? 0 : rows / 256;
     const int rest = rows - nb * 256;
-    if (rest >= kBigTailMin) { nb += 1; }
+    if (!small_only && rest >= kBigTailMin) { nb += 1; }
     else { ns = (rest + 63) / 64; }
     split = min(hi, lo + nb * 256);
   }
@@ -129,8 +129,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) leaving lgkmcnt / expcnt alone (gfx9 encoding).
-#define MOE_WAIT_VM0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+// s_waitcnt vmcnt(n), n < 64, leaving lgkmcnt / expcnt alone (gfx9 encoding: vmcnt
+// bits 3:0 in bits 3:0 and bits 5:4 in bits 15:14; expcnt 6:4; lgkmcnt 11:8).
+#define MOE_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+#define MOE_WAIT_VM0() __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0))
 
 // How the units of one tile list are laid out: T tiles of KT steps; the
 // first `full` tiles run whole, the remaining `rem` tiles run in s K-parts.
@@ -208,6 +210,10 @@ struct GemmParams {
   const uint16_t* W;          // [n_seg, Nn, K]
   const uint16_t* W3;         // SwiGLU: [n_seg, Nn, K]
   const uint16_t* bias;       // [n_seg, Nn] or null
+  const uint8_t* W8;          // fp8 weights [n_seg, Nn, K] (E4M3 codes)
+  const uint8_t* W8_3;        // fp8 SwiGLU W3
+  const float* scale1;        // fp8 row scales of W8 [n_seg, Nn]
+  const float* scale3;        // fp8 row scales of W8_3
   uint16_t* out;              // [rows, Nn]
   float* out_f;               // MODE_LOGITS: fp32 output
   const float* bias_f;        // MODE_LOGITS: fp32 bias [Nn] or null
@@ -564,7 +570,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
   }
   for (int kt = kt0; kt < kt1; ++kt) {
     // outstanding in issue order: step kt, then step kt + 1 (10 loads) if it exists
-    if (kt + 1 < kt1) __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8));
+    if (kt + 1 < kt1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(10));
     else MOE_WAIT_VM0();
     __builtin_amdgcn_s_barrier();          // step kt landed everywhere; the slot of kt - 1 is free
     const uint16_t* st = lds + (kt % kStages3) * kStage3Elems;
@@ -629,6 +635,164 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
   __syncthreads();   // the next unit's first loads must not overtake this epilogue
 }
 
+// ---------------------------------------------------------------------------
+// 64 x 256 tile with fp8 (E4M3) weights ([S]: quantised expert weights halve
+// the bytes a weight-streaming GEMM moves).  The B tile arrives as codes
+// (256 rows x 64 bytes per K step) through the same direct-to-LDS loads, so a
+// stage is 24 KB and a 5-stage ring keeps four K steps of loads in flight.
+// Fragments are expanded to bf16 exactly (every E4M3 value is a bf16 value)
+// with v_cvt_scalef32_pk_bf16_fp8 at scale 1 and fed to the bf16 MFMA; each
+// output column is multiplied by its weight row's scale before the epilogue.
+// B LDS layout: row r holds four 16-byte chunks, chunk c in slot
+// c ^ ((r >> 2) & 3), which spreads the 8-byte fragment reads of 16
+// consecutive rows over all banks.
+constexpr int kStages8 = 5;
+constexpr int kStage8Elems = kBM3 * kBK2 + (kBN2 * kBK2) / 2;   // bf16 A rows + fp8 B rows, in bf16 units
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
+  union {
+    bf16x2v h[4];
+    bf16x8 o;
+  } u;
+  u.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  u.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  u.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  u.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return u.o;
+}
+
+template <int MODE, bool HAS_BIAS, bool GATHER>
+__device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& w, uint16_t* lds, int wn,
+                                               int lane) {
+  constexpr int P = kStages8 - 1;            // K steps in flight ahead of the one computed
+  constexpr int kLoads = 6;                  // per wavefront and K step: 2 A + 4 B
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int rowbytes = p.K * 2;
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+
+  int voffa[2], voffb[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * wn + 8 * u + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(row);
+    if (GATHER) {
+      const int r = w.r0 + row;
+      voffa[u] = (r < w.r1 ? (p.perm[r] / p.gk) * rowbytes : kOobOffset) + chunk * 16;
+    } else {
+      voffa[u] = row * rowbytes + chunk * 16;
+    }
+  }
+  // B: instruction u of wavefront wn fills rows 64 wn + 16 u + (lane >> 2), slot lane & 3
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 64 * wn + 16 * u + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * p.K + chunk * 16;
+  }
+  const int h = kh ^ swz8(l32);
+  const int brow0 = MODE == MODE_SWIGLU_UP ? (32 * wn + l32) : (64 * wn + l32);
+  const int bstep = MODE == MODE_SWIGLU_UP ? 128 : 32;
+  const int bsw = (l32 >> 2) & 3;            // (row >> 2) & 3 of both fragment rows (bases are multiples of 32)
+
+  const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(p.A, p.a_bytes)
+                                           : make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
+  const int nb_rows = min(cols_per_tile, p.Nn - w.n0);
+  const uint8_t* wsrc = (MODE == MODE_SWIGLU_UP && wn >= 2) ? p.W8_3 : p.W8;
+  const __amdgpu_buffer_rsrc_t rb =
+      make_rsrc(wsrc + (size_t)w.seg * p.Nn * p.K + (size_t)w.n0 * p.K, (uint32_t)nb_rows * p.K);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int kt0 = w.kt0, kt1 = w.kt1;
+#define FP8_LOAD_A(u, st, kt) dma16(ra, (st) + (16 * wn + 8 * (u)) * kBK2, voffa[u], (kt) * kBK2 * 2)
+#define FP8_LOAD_B(u, st, kt) dma16(rb, (st) + kBM3 * kBK2 + (64 * wn + 16 * (u)) * (kBK2 / 2), voffb[u], (kt) * kBK2)
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {           // prologue: steps kt0 .. kt0 + P - 1
+    const int kt = kt0 + pp;
+    if (kt < kt1) {
+      uint16_t* st = lds + (kt % kStages8) * kStage8Elems;
+      FP8_LOAD_A(0, st, kt); FP8_LOAD_A(1, st, kt);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) FP8_LOAD_B(u, st, kt);
+    }
+  }
+  for (int kt = kt0; kt < kt1; ++kt) {
+    // outstanding in issue order: steps kt .. kt + r, r = min(P - 1, kt1 - 1 - kt)
+    const int r = min(P - 1, kt1 - 1 - kt);
+    if (r >= 3) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(3 * kLoads));
+    else if (r == 2) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(2 * kLoads));
+    else if (r == 1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(kLoads));
+    else MOE_WAIT_VM0();
+    __builtin_amdgcn_s_barrier();            // step kt landed everywhere; the slot of kt - 1 is free
+    const uint16_t* st = lds + (kt % kStages8) * kStage8Elems;
+    uint16_t* nx = lds + ((kt + P) % kStages8) * kStage8Elems;
+    const bool more = kt + P < kt1;
+    bf16x8 fa[2], fb[2];
+#pragma unroll
+    for (int kk = 0; kk < kBK2 / 16; ++kk) {
+      if (more && kk < 3) {                   // next loads: 2 / 2 / 2 over the first three sub-steps
+        if (kk == 0) { FP8_LOAD_A(0, nx, kt + P); FP8_LOAD_A(1, nx, kt + P); }
+        else { FP8_LOAD_B(2 * kk - 2, nx, kt + P); FP8_LOAD_B(2 * kk - 1, nx, kt + P); }
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        fa[x] = *reinterpret_cast<const bf16x8*>(st + (32 * x + l32) * kBK2 + ((h ^ (4 * x) ^ (2 * kk)) << 3));
+        const int brow = brow0 + bstep * x;
+        // 8 code bytes read with the same element type as the A fragments (the compiler then
+        // keeps them apart from the in-flight LDS loads as it does for A)
+        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(
+            st + kBM3 * kBK2 + ((brow * kBK2 + ((kk ^ bsw) << 4) + kh * 8) >> 1));
+        fb[x] = fp8x8_to_bf16(__builtin_bit_cast(uint2, b4));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+#undef FP8_LOAD_A
+#undef FP8_LOAD_B
+  // per-column weight scales (lane's column l32 of each 32-wide block)
+  float sc[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int col = MODE == MODE_SWIGLU_UP ? w.n0 + 32 * wn + l32 : w.n0 + 64 * wn + 32 * ni + l32;
+    const float* sp = (MODE == MODE_SWIGLU_UP && ni == 1) ? p.scale3 : p.scale1;
+    sc[ni] = col < p.Nn ? sp[(size_t)w.seg * p.Nn + col] : 0.f;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] *= sc[ni];
+  __syncthreads();   // every wavefront is done with the ring before the epilogue reuses it
+
+  if (w.slot < 0) {
+    float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
+    store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
+                                  p.bias_f, p.out_f);
+  } else {
+    float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
+  }
+  __syncthreads();   // the next unit's first loads must not overtake this epilogue
+}
+
 // The persistent kernel: grid = CUs rounded up to a multiple of 8, one
 // workgroup per CU.  Workgroup q of XCD x walks items q, q + G/8, ... of its
 // XCD's sequence: first the cb 256-row units of its range, then its 64-row
@@ -636,7 +800,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 // while the others finish.  (Interleaving the two kinds finely measured
 // slower: the weight streams of the short tiles evict the long tiles'
 // operands from L2.)
-template <int MODE, bool HAS_BIAS, bool GATHER>
+template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
@@ -656,12 +820,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
   const int lane = tid & 63;
   for (int i = q; i < n; i += per_xcd) {
-    if (i < cb) {
+    if (!FP8 && i < cb) {   // fp8 weights use 64-row tiles only
       const Unit w = decode_unit(p.tiles, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
       big_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
     } else {
       const Unit w = decode_unit(p.tiles_small, ps, s0 + (i - cb), p.n_ntiles, KT, cols_per_tile);
-      small_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
+      if (FP8) small_unit_fp8<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
+      else small_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
     }
   }
 }
@@ -783,7 +948,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 }
 
 int grouped_gemm_max_tiles(int max_rows, int n_seg) { return max_rows / 256 + n_seg; }
-int grouped_gemm_max_small_tiles(int n_seg) { return 2 * n_seg; }
+int grouped_gemm_max_small_tiles(int max_rows, int n_seg) { return max_rows / 64 + n_seg; }
 size_t grouped_gemm_partials_bytes() {
   return (size_t)kMaxSplitUnits * (kBM2 + kBM3) * kBN2 * sizeof(float);
 }
@@ -801,7 +966,7 @@ static int device_cus() {
   return cus[dev];
 }
 
-template <int MODE, bool HAS_BIAS, bool GATHER>
+template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8 = false>
 static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   const int cols = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   GemmParams p;
@@ -817,13 +982,17 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.out = (uint16_t*)g.out;
   p.out_f = g.out_f32;
   p.bias_f = g.bias_f32;
+  p.W8 = g.w8;
+  p.W8_3 = g.w8_3;
+  p.scale1 = g.scale1;
+  p.scale3 = g.scale3;
   p.partials = g.partials;
   p.partials_small = g.partials + (size_t)kMaxSplitUnits * kBM2 * kBN2;
   p.K = g.K;
   p.Nn = g.Nn;
   p.n_ntiles = (g.Nn + cols - 1) / cols;
   const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, HAS_BIAS, GATHER>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
   hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(2 * grid), dim3(256), 0, s, p, grid);
 }
 
@@ -849,10 +1018,20 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   if (gather && (g.mode >= MODE_DOWN || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
     return hipErrorInvalidValue;
   if (g.mode == MODE_LOGITS && (g.Nn % 8 != 0 || g.n_seg != 1)) return hipErrorInvalidValue;
+  if (g.fp8 && (g.mode == MODE_LOGITS || (g.mode != MODE_DOWN && !gather) || !g.w8 || !g.scale1 ||
+                (g.mode == MODE_SWIGLU_UP && (!g.w8_3 || !g.scale3))))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, g.offsets, g.n_seg, g.max_rows, g.tiles,
-                     g.max_tiles, g.tiles_small, g.max_tiles_small);
+                     g.max_tiles, g.tiles_small, g.max_tiles_small, g.fp8 ? 1 : 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (g.fp8) {   // fp8 weights: up with the row gather, or down
+    if (g.mode == MODE_SWIGLU_UP) launch_bf16<MODE_SWIGLU_UP, false, true, true>(g, s);
+    else if (g.mode == MODE_GELU_UP)
+      hb ? launch_bf16<MODE_GELU_UP, true, true, true>(g, s) : launch_bf16<MODE_GELU_UP, false, true, true>(g, s);
+    else hb ? launch_bf16<MODE_DOWN, true, false, true>(g, s) : launch_bf16<MODE_DOWN, false, false, true>(g, s);
+    return hipGetLastError();
+  }
   if (g.mode == MODE_SWIGLU_UP) {
     gather ? launch_bf16<MODE_SWIGLU_UP, false, true>(g, s) : launch_bf16<MODE_SWIGLU_UP, false, false>(g, s);
   } else if (g.mode == MODE_GELU_UP) {

@@ -33,9 +33,9 @@ Workspace workspace_layout(const moe_config& c) {
   W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
   W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
   W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E);
-  W.max_tiles_small = grouped_gemm_max_small_tiles((int)E);
+  W.max_tiles_small = grouped_gemm_max_small_tiles((int)slots, (int)E);
   W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1) : 0;
-  W.max_tiles_sh_small = Fs ? grouped_gemm_max_small_tiles(1) : 0;
+  W.max_tiles_sh_small = Fs ? grouped_gemm_max_small_tiles((int)N, 1) : 0;
 
   W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
   W.hist_rank = take(slots * 4);
@@ -195,6 +195,48 @@ moe_status do_up(const moe_config& c, const Workspace& W, const void* a, const i
   g.w3 = swiglu ? w3 : nullptr;
   g.bias = (!shared && c.ffn_bias) ? b1 : nullptr;
   g.out = h;
+  MOE_HIP(launch_grouped_gemm(g, s));
+  return MOE_OK;
+}
+
+// fp8 experts: weights are E4M3 codes with per-row scales; up always gathers token rows.
+moe_status do_up_fp8(const moe_config& c, const Workspace& W, const void* x, const int32_t* perm,
+                     const int32_t* offsets, const uint8_t* w1q, const uint8_t* w3q, const float* s1,
+                     const float* s3, const void* b1, void* h, void* ws, hipStream_t s) {
+  GroupedGemmArgs g = gemm_args(c, W, ws, false);
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  g.mode = swiglu ? MODE_SWIGLU_UP : MODE_GELU_UP;
+  g.perm = perm;
+  g.gather_k = c.top_k;
+  g.a_rows = (int)c.n_tokens;
+  g.K = c.d_model;
+  g.Nn = c.d_ff;
+  g.a = x;
+  g.offsets = offsets;
+  g.fp8 = true;
+  g.w8 = w1q;
+  g.w8_3 = swiglu ? w3q : nullptr;
+  g.scale1 = s1;
+  g.scale3 = swiglu ? s3 : nullptr;
+  g.bias = c.ffn_bias ? b1 : nullptr;
+  g.out = h;
+  MOE_HIP(launch_grouped_gemm(g, s));
+  return MOE_OK;
+}
+
+moe_status do_down_fp8(const moe_config& c, const Workspace& W, const void* h, const int32_t* offsets,
+                       const uint8_t* w2q, const float* s2, const void* b2, void* y, void* ws, hipStream_t s) {
+  GroupedGemmArgs g = gemm_args(c, W, ws, false);
+  g.mode = MODE_DOWN;
+  g.K = c.d_ff;
+  g.Nn = c.d_model;
+  g.a = h;
+  g.offsets = offsets;
+  g.fp8 = true;
+  g.w8 = w2q;
+  g.scale1 = s2;
+  g.bias = c.ffn_bias ? b2 : nullptr;
+  g.out = y;
   MOE_HIP(launch_grouped_gemm(g, s));
   return MOE_OK;
 }
@@ -373,6 +415,64 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
     MOE_TRY(moe_expert_up(cfg, x_perm, offsets, w1, w3, b1, h_tmp, ws, ws_bytes, stream));
     const Workspace W = workspace_layout(c);
     return do_down(c, W, h_tmp, offsets, w2, b2, y_perm, ws, stream, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                            hipStream_t stream) {
+  try {
+    if (rows < 0 || cols <= 0 || cols > (1 << 24)) return MOE_ERR_ARG;
+    if (rows > 0 && (!w || !q || !scales)) return MOE_ERR_ARG;
+    if (cols % 4 == 0 && (!aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 3u)))
+      return MOE_ERR_UNSUPPORTED;
+    MOE_HIP(launch_quantize_fp8(reinterpret_cast<const uint16_t*>(w), rows, cols, q, scales, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_up_fp8(const moe_config* cfg, const void* x, const int32_t* perm, const int32_t* offsets,
+                             const uint8_t* w1q, const uint8_t* w3q, const float* s1, const float* s3,
+                             const void* b1, void* h_tmp, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!offsets || !w1q || !s1 || (any && (!x || !perm || !h_tmp))) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_SWIGLU && (!w3q || !s3)) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_GELU && (w3q || s3)) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b1) return MOE_ERR_ARG;
+    if (!gather_ok(c)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w1q) || !aligned16(w3q) || !aligned16(h_tmp) || !aligned16(b1))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    if (!any) return MOE_OK;
+    return do_up_fp8(c, W, x, perm, offsets, w1q, w3q, s1, s3, b1, h_tmp, ws, stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_down_fp8(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
+                               const uint8_t* w2q, const float* s2, const void* b2, void* y_perm, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!offsets || !w2q || !s2 || (any && (!h_tmp || !y_perm))) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b2) return MOE_ERR_ARG;
+    if (!aligned16(h_tmp) || !aligned16(w2q) || !aligned16(y_perm) || !aligned16(b2)) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    if (!any) return MOE_OK;
+    return do_down_fp8(c, W, h_tmp, offsets, w2q, s2, b2, y_perm, ws, stream);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

@@ -105,6 +105,11 @@ struct GroupedGemmArgs {
   const void* w3;        // SwiGLU up only
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
+  bool fp8;              // weights are E4M3 codes (w8, w8_3) with row scales (64-row tiles only)
+  const uint8_t* w8;     // fp8 W1 (up) or W2 (down): [n_seg, Nn, K]
+  const uint8_t* w8_3;   // fp8 W3 (SwiGLU up)
+  const float* scale1;   // row scales of w8 [n_seg, Nn]
+  const float* scale3;   // row scales of w8_3
   float* out_f32;        // MODE_LOGITS output [rows, Nn]
   const float* bias_f32; // MODE_LOGITS bias [Nn] or NULL
   int32_t* tiles;        // scratch: 256-row tile list (4 header ints + 8 ints per tile)
@@ -115,9 +120,13 @@ struct GroupedGemmArgs {
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
 int grouped_gemm_max_tiles(int max_rows, int n_seg);
-int grouped_gemm_max_small_tiles(int n_seg);
+int grouped_gemm_max_small_tiles(int max_rows, int n_seg);
 size_t grouped_gemm_partials_bytes();
 size_t grouped_gemm_gather_max_bytes();   // largest token matrix (bytes) the bf16 gather path addresses
+
+// Per-row fp8 (E4M3) quantisation of a bf16 [rows, cols] matrix: codes and fp32 scales.
+hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint8_t* q, float* scales,
+                               hipStream_t s);
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,

@@ -1,0 +1,120 @@
+"""GPU parity of the fp8 (E4M3) weight-only experts.
+
+The quantiser must reproduce the oracle's codes and scales bit for bit (both
+compute in fp32 with correctly rounded division).  The layer with fp8
+experts must match the oracle run on the same fp8 round-trip weights within
+the bf16 tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_harness import SMALL, TOL, host, rel_err, say
+from workloads import MIXTRAL_DECODE, SWITCH_SKEWED, DEEPSEEK_V3, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "decode_swiglu": MIXTRAL_DECODE.scaled(name="fp8_decode_swiglu", d_model=256, d_ff=384),
+    "gelu_bias_capacity": SWITCH_SKEWED.scaled(name="fp8_gelu_bias_capacity", n_tokens=700, d_model=192,
+                                               d_ff=320),
+    "ragged_e64": DEEPSEEK_V3.scaled(name="fp8_ragged_e64", n_tokens=300, n_experts=64, top_k=4, d_model=320,
+                                     d_ff=192, d_ff_shared=0),
+    "long_segments": SMALL["mixtral_prefill_small"].scaled(name="fp8_long_segments", n_tokens=700),
+}
+
+
+def _bf16_tensor(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_quantize_matches_oracle():
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    rng = np.random.default_rng(11)
+    mats = []
+    cfg = CASES["decode_swiglu"]
+    inp = make_inputs(cfg)
+    mats.append(inp.w1.reshape(-1, cfg.d_model))
+    mats.append(inp.w2.reshape(-1, cfg.d_ff))
+    # rows of every magnitude, an all-zero row, an odd column count (scalar path)
+    w = (rng.standard_normal((64, 100)) * np.exp2(rng.uniform(-20, 10, (64, 1)))).astype(np.float32)
+    w[5] = 0.0
+    w[6, :50] = 0.0
+    bits = (w.view(np.uint32) + 0x7FFF + ((w.view(np.uint32) >> 16) & 1)) >> 16
+    mats.append(bits.astype(np.uint16))
+    for m in mats:
+        rows, cols = m.shape
+        say(f"quantize {rows}x{cols}")
+        wt = _bf16_tensor(m)
+        q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+        M.quantize_fp8(wt, q, sc)
+        torch.cuda.synchronize()
+        q_ref, sc_ref = oracle.quantize_fp8_rows(oracle.to_f64(m, "bf16").astype(np.float32))
+        assert np.array_equal(host(sc), sc_ref), "scales differ"
+        qg = host(q)
+        assert np.array_equal(qg, q_ref), np.argwhere(qg != q_ref)[:5]
+
+
+def _quantize(M, t):
+    import torch
+    cols = t.shape[-1]
+    q = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(t.shape[:-1], dtype=torch.float32, device="cuda")
+    M.quantize_fp8(t, q, sc)
+    return q, sc
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fp8_layer_parity(name):
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from mixture_experts_layer_histogram_amd import MoELayer, upload_inputs
+    cfg = CASES[name]
+    say(f"fp8 case {name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} F={cfg.d_ff}")
+    inp = make_inputs(cfg)
+    dev = upload_inputs(inp, "cuda")
+    layer = MoELayer(cfg, dev, "cuda")
+    c, ws = layer.cfg, layer.ws
+    N, E, k, d, F = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff
+    st = torch.bfloat16
+    z = torch.empty((N, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    g = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    M.route(c, dev["x"], dev["w_router"], idx, g, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"],
+            logits=z, ws=ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    sp = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    M.permute(c, idx, None, counts, offs, perm, sp, None, ws=ws)
+    w1q, s1 = _quantize(M, dev["w1"])
+    w2q, s2 = _quantize(M, dev["w2"])
+    w3q = s3 = None
+    if cfg.act == "swiglu":
+        w3q, s3 = _quantize(M, dev["w3"])
+    h = torch.empty((N * k, F), dtype=st, device="cuda")
+    y = torch.empty((N * k, d), dtype=st, device="cuda")
+    M.expert_up_fp8(c, dev["x"], perm, offs, w1q, w3q, s1, s3, h, b1=dev["b1"], ws=ws)
+    M.expert_down_fp8(c, h, offs, w2q, s2, y, b2=dev["b2"], ws=ws)
+    out = torch.empty((N, d), dtype=st, device="cuda")
+    M.combine(c, y, sp, g, out, residual=dev["x"] if cfg.residual else None)
+    torch.cuda.synchronize()
+    # the quantised weights are the oracle's own
+    q_ref, s_ref = oracle.quantize_fp8_rows(oracle.to_f64(inp.w1.reshape(-1, d), "bf16").astype(np.float32))
+    assert np.array_equal(host(w1q).reshape(-1, d), q_ref) and np.array_equal(host(s1).reshape(-1), s_ref)
+    logits = host(z)
+    r, ref = oracle.oracle_layer(cfg, inp, logits_override=logits, expert_weights="fp8")
+    assert np.array_equal(host(idx), r.topk_idx)
+    assert np.array_equal(host(offs), r.disp.offsets)
+    err = rel_err(host(out), ref)
+    say(f"{name}: fp8 out rel err {err:.3e}")
+    assert err <= TOL["bf16"], err
+    # determinism: a second run gives the same bits
+    y2 = torch.empty_like(y)
+    M.expert_down_fp8(c, h, offs, w2q, s2, y2, b2=dev["b2"], ws=ws)
+    torch.cuda.synchronize()
+    kept = int(host(offs)[-1])
+    assert np.array_equal(host(y2)[:kept], host(y)[:kept])
