@@ -33,8 +33,10 @@ design notes):
 * SwiGLU expert: ``(SiLU(X W1^T) * (X W3^T)) W2^T``, SiLU on W1, no biases;
 * GELU expert: ``GELU(X W1^T + b1) W2^T + b2`` with the exact erf GELU;
 * capacity ``C = floor(cf * N / E)``; each expert keeps its first C slots in
-  ascending slot id ``s = t*k + j``; a dropped slot contributes nothing and the
-  kept gates of that token are not renormalised;
+  ascending slot id ``s = t*k + j`` (or, as a variant, in choice order: all
+  first choices by token, then second choices, ...); a dropped slot
+  contributes nothing and the kept gates of that token are not renormalised;
+  the kept rows are packed back to back or placed in fixed [E, C] buffers;
 * dropped tokens still receive the residual (and the shared expert, if any);
 * auxiliary loss ``E * sum_e f_e * P_e`` with ``f_e = counts_e / (N k)`` from
   the pre-drop counts and ``P_e`` the full-softmax probability averaged over
@@ -161,40 +163,66 @@ def selection_gap(z: np.ndarray, k: int, rule: str, sel_bias=None) -> np.ndarray
 @dataclass
 class Dispatch:
     counts: np.ndarray      # [E] pre-drop tokens per expert (sum = N k)
-    offsets: np.ndarray     # [E+1] exclusive scan of kept counts
-    perm: np.ndarray        # [sum kept] slot id s = t*k + j, grouped by expert, ascending within
-    slot_pos: np.ndarray    # [N k] position of slot s in perm, -1 if dropped
+    offsets: np.ndarray     # [E+1] start row of each expert's segment (packed: scan of kept counts; padded: e*C)
+    perm: np.ndarray        # slot id s = t*k + j per row, grouped by expert (padded: -1 on padding rows)
+    slot_pos: np.ndarray    # [N k] row of slot s, -1 if dropped
     drop_count: int
+    kept: np.ndarray        # [E] kept slots per expert, min(counts, C)
 
 
-def dispatch(idx: np.ndarray, n_experts: int, capacity: int | None) -> Dispatch:
+def dispatch(idx: np.ndarray, n_experts: int, capacity: int | None, layout: str = "packed",
+             priority: str = "slot") -> Dispatch:
     """Group the N*k slots by expert ([G] example: per expert, the tokens that
     chose it; [X] "Deep dive": tokens are sent to the holder of their expert).
 
-    Within an expert, slots keep ascending slot id.  With a capacity C
-    ([N] Load balancing item 2: each expert takes at most C * N / E tokens;
-    the overflow skips the experts), only the first C slots of each expert
-    are kept.
+    Within an expert, slots are ordered by priority: ascending slot id
+    s = t*k + j ("slot"), or by choice rank first and token second
+    ("choice": every token's first choice before any second choice).  With a
+    capacity C ([N] Load balancing item 2: each expert takes at most C * N / E
+    tokens; the overflow skips the experts), only the first C slots of each
+    expert in that order are kept.
+
+    Layout ([X] "Technical insight": fixed per-expert buffers, padded or
+    dropped to a uniform shape): "packed" puts the experts' kept rows back to
+    back; "padded" gives expert e rows [e*C, (e+1)*C), kept rows first and
+    padding rows (perm = -1) after them.
     """
     expert_of_slot = idx.reshape(-1)
     n_slots = expert_of_slot.size
+    k = idx.shape[1] if idx.ndim == 2 else 1
     counts = np.zeros(n_experts, dtype=np.int64)
     kept_lists = []
     drop = 0
     for e in range(n_experts):
         slots = np.nonzero(expert_of_slot == e)[0]          # ascending slot id
+        if priority == "choice":
+            slots = slots[np.lexsort((slots // k, slots % k))]   # by choice j, then token t
+        elif priority != "slot":
+            raise ValueError(priority)
         counts[e] = slots.size
         if capacity is not None and slots.size > capacity:
             drop += slots.size - capacity
             slots = slots[:capacity]
         kept_lists.append(slots)
+    kept = np.array([len(s) for s in kept_lists], dtype=np.int64)
     offsets = np.zeros(n_experts + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum([len(s) for s in kept_lists])
-    perm = np.concatenate(kept_lists) if kept_lists else np.zeros(0, np.int64)
+    if layout == "packed":
+        offsets[1:] = np.cumsum(kept)
+        perm = np.concatenate(kept_lists) if kept_lists else np.zeros(0, np.int64)
+    elif layout == "padded":
+        if capacity is None:
+            raise ValueError("the padded layout needs a finite capacity")
+        offsets = np.arange(n_experts + 1, dtype=np.int64) * capacity
+        perm = np.full(n_experts * capacity, -1, dtype=np.int64)
+        for e, sl in enumerate(kept_lists):
+            perm[e * capacity:e * capacity + sl.size] = sl
+    else:
+        raise ValueError(layout)
     slot_pos = np.full(n_slots, -1, dtype=np.int64)
-    slot_pos[perm] = np.arange(perm.size)
+    rows = np.nonzero(perm >= 0)[0]
+    slot_pos[perm[rows]] = rows
     return Dispatch(counts=counts, offsets=offsets, perm=perm.astype(np.int64),
-                    slot_pos=slot_pos, drop_count=int(drop))
+                    slot_pos=slot_pos, drop_count=int(drop), kept=kept)
 
 
 # --------------------------------------------------------------------------- experts
@@ -282,7 +310,8 @@ def oracle_route(cfg, logits: np.ndarray, sel_bias=None) -> RouteResult:
     counts, permutation, capacity, aux loss and the bias step."""
     z = np.asarray(logits, dtype=np.float64)
     idx, gates, p = route(z, cfg.top_k, cfg.gate_rule, sel_bias)
-    d = dispatch(idx, cfg.n_experts, cfg.capacity)
+    d = dispatch(idx, cfg.n_experts, cfg.capacity, getattr(cfg, "capacity_layout", "packed"),
+                 getattr(cfg, "capacity_priority", "slot"))
     aux = aux_loss(d.counts, p, cfg.top_k) if cfg.aux_loss else None
     signs = new_bias = None
     if cfg.gamma > 0:
@@ -327,6 +356,7 @@ def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"
     for e in range(E):
         lo, hi = r.disp.offsets[e], r.disp.offsets[e + 1]
         slots = r.disp.perm[lo:hi]
+        slots = slots[slots >= 0]                       # padded layout: skip padding rows
         slots = slots[want[slots // k]]
         if slots.size == 0:
             continue

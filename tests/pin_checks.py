@@ -223,6 +223,60 @@ def check_capacity_brute_force():
         assert d.drop_count == int(np.maximum(d.counts - C, 0).sum())
 
 
+def check_capacity_choice_priority_brute_force():
+    """Choice priority: an over-full expert keeps the slots with the smallest
+    (choice rank j, token t); its rows hold them in that order.  With k = 1 it
+    coincides with slot priority."""
+    rng = np.random.default_rng(22)
+    for E, k, N, C in ((4, 2, 30, 6), (5, 3, 24, 4), (4, 1, 40, 7), (6, 3, 20, 0)):
+        z = rng.standard_normal((N, E))
+        z[:, 1] += 1.0
+        idx, _, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, None)
+        d = mo.dispatch(idx, E, C, "packed", "choice")
+        es = idx.reshape(-1)
+        for s in range(N * k):
+            t, j = divmod(s, k)
+            ahead = sum(1 for s2 in range(N * k) if es[s2] == es[s] and (s2 % k, s2 // k) < (j, t))
+            assert (d.slot_pos[s] >= 0) == (ahead < C), (s, ahead, C)
+            if d.slot_pos[s] >= 0:
+                assert d.slot_pos[s] == d.offsets[es[s]] + ahead
+        assert d.drop_count == int(np.maximum(d.counts - C, 0).sum())
+        if k == 1:
+            d0 = mo.dispatch(idx, E, C)
+            assert np.array_equal(d.perm, d0.perm) and np.array_equal(d.slot_pos, d0.slot_pos)
+
+
+def check_padded_capacity_layout():
+    """Padded layout: expert e owns rows [e C, (e+1) C), its kept slots first
+    (same order as packed), padding rows marked -1; the layer output does not
+    depend on the layout."""
+    rng = np.random.default_rng(23)
+    E, k, N, C = 4, 2, 30, 9
+    z = rng.standard_normal((N, E))
+    z[:, 2] += 1.5
+    idx, _, _ = mo.route(z, k, GATE_TOPK_SOFTMAX, None)
+    for pr in ("slot", "choice"):
+        pk = mo.dispatch(idx, E, C, "packed", pr)
+        pd = mo.dispatch(idx, E, C, "padded", pr)
+        assert np.array_equal(pd.offsets, np.arange(E + 1) * C)
+        for e in range(E):
+            n = pk.kept[e]
+            assert np.array_equal(pd.perm[e * C:e * C + n], pk.perm[pk.offsets[e]:pk.offsets[e + 1]])
+            assert np.all(pd.perm[e * C + n:(e + 1) * C] == -1)
+        assert np.array_equal(pd.slot_pos >= 0, pk.slot_pos >= 0)
+        ok = pd.slot_pos >= 0
+        assert np.array_equal(pd.perm[pd.slot_pos[ok]], np.nonzero(ok)[0])
+    cfg = MoEConfig(name="padded", n_tokens=N, d_model=16, n_experts=E, top_k=k, d_ff=24, act="swiglu",
+                    gate_rule=GATE_TOPK_SOFTMAX, dtype="f32", capacity_factor=C * E / N, residual=True)
+    assert cfg.capacity == C
+    inp, _ = _small_inputs(cfg, seed=4)
+    import dataclasses
+    _, out_packed = mo.oracle_layer(cfg, inp, logits_override=z.astype(np.float32))
+    _, out_padded = mo.oracle_layer(dataclasses.replace(cfg, capacity_layout="padded"), inp,
+                                    logits_override=z.astype(np.float32))
+    assert np.array_equal(out_packed, out_padded)
+
+
 # ----------------------------------------------------------------- layer reductions
 
 def _small_inputs(cfg, w_override=None, seed=0):

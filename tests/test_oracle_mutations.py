@@ -43,7 +43,7 @@ def _gelu_no_b2(X, w1, b1, w2, b2):
     return _orig["ffn_gelu"](X, w1, b1, w2, None)
 
 
-def _keep_last(idx, E, C):
+def _keep_last(idx, E, C, *a):
     d = _orig["dispatch"](idx, E, None)
     if C is None:
         return d
@@ -60,17 +60,21 @@ def _keep_last(idx, E, C):
     offs[1:] = np.cumsum([len(s) for s in lists])
     sp = np.full(es.size, -1, np.int64)
     sp[perm] = np.arange(perm.size)
-    return mo.Dispatch(d.counts, offs, perm, sp, drop)
+    return mo.Dispatch(d.counts, offs, perm, sp, drop, np.diff(offs))
 
 
-def _descending_segments(idx, E, C):
-    d = _orig["dispatch"](idx, E, C)
+def _descending_segments(idx, E, C, *a):
+    d = _orig["dispatch"](idx, E, C, *a)
     perm = d.perm.copy()
     for e in range(E):
         perm[d.offsets[e]:d.offsets[e + 1]] = perm[d.offsets[e]:d.offsets[e + 1]][::-1]
     sp = np.full(d.slot_pos.size, -1, np.int64)
     sp[perm] = np.arange(perm.size)
-    return mo.Dispatch(d.counts, d.offsets, perm, sp, d.drop_count)
+    return mo.Dispatch(d.counts, d.offsets, perm, sp, d.drop_count, d.kept)
+
+
+def _choice_as_slot(idx, E, C, layout="packed", priority="slot"):
+    return _orig["dispatch"](idx, E, C, layout, "slot")
 
 
 def _aux_post_drop(counts, p, k):
@@ -118,6 +122,7 @@ MUTATIONS = [
     ("ffn_gelu", _gelu_no_b2, [pc.check_single_expert_is_dense, pc.check_printed_example_output]),
     ("dispatch", _keep_last, [pc.check_capacity_brute_force]),
     ("dispatch", _descending_segments, [pc.check_dispatch_invariants]),
+    ("dispatch", _choice_as_slot, [pc.check_capacity_choice_priority_brute_force]),
     ("aux_loss", _aux_post_drop, [pc.check_aux_uniform_is_one]),
     ("bias_step", _bias_sign_flipped, [pc.check_bias_step_signs, pc.check_bias_loop_equalises]),
     ("softmax_rows", _softmax_no_max, [pc.check_softmax_library]),

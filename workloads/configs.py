@@ -45,6 +45,9 @@ class MoEConfig:
     ffn_bias: bool = False            # expert Linear layers carry biases (GELU form only)
     gate_rule: str = GATE_TOPK_SOFTMAX
     capacity_factor: float = 0.0      # <= 0: unlimited capacity
+    capacity_layout: str = "packed"   # "packed": experts' kept rows back to back; "padded": [E, C] rows
+    capacity_priority: str = "slot"   # which slots an over-full expert keeps: "slot" (ascending t*k+j)
+                                      # or "choice" (all first choices, then second choices, ...)
     dtype: str = "bf16"               # storage type of x, weights and out ("bf16" or "f32")
     residual: bool = True             # out = x + MoE(x)
     sel_bias_range: float = 0.0       # > 0: selection bias ~ U(-r, r) per expert
