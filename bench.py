@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8-experts", action="store_true",
                     help="routed experts with fp8 (E4M3) weights and per-row scales, quantised before timing")
+    ap.add_argument("--capacity-layout", choices=["packed", "padded"], default=None,
+                    help="override the workload's capacity layout (padded: [E, C] expert buffers)")
+    ap.add_argument("--capacity-priority", choices=["slot", "choice"], default=None,
+                    help="override which slots an over-full expert keeps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -84,6 +88,12 @@ def main():
     from workloads import BY_NAME, make_inputs
 
     cfg = BY_NAME[args.config]
+    if args.capacity_layout or args.capacity_priority:
+        if args.capacity_layout == "padded" and cfg.capacity is None:
+            print("--capacity-layout padded needs a workload with a capacity factor", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.scaled(capacity_layout=args.capacity_layout or cfg.capacity_layout,
+                         capacity_priority=args.capacity_priority or cfg.capacity_priority)
     dev_name = "cuda:0"
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
@@ -112,11 +122,12 @@ def main():
     probsum = torch.empty(E, dtype=f32, device=dev_name) if cfg.aux_loss else None
     counts = torch.empty(E, dtype=i32, device=dev_name)
     offs = torch.empty(E + 1, dtype=i32, device=dev_name)
-    perm = torch.empty(N * k, dtype=i32, device=dev_name)
+    R = M._lib.expert_rows(c)           # rows of the expert-ordered buffers
+    perm = torch.empty(max(R, 1), dtype=i32, device=dev_name)
     slot_pos = torch.empty(N * k, dtype=i32, device=dev_name)
     drop = torch.empty(1, dtype=torch.int64, device=dev_name)
-    h = torch.empty((N * k, F), dtype=st, device=dev_name)
-    y = torch.empty((N * k, d), dtype=st, device=dev_name)
+    h = torch.empty((max(R, 1), F), dtype=st, device=dev_name)
+    y = torch.empty((max(R, 1), d), dtype=st, device=dev_name)
     h_sh = torch.empty((N, Fs), dtype=st, device=dev_name) if Fs else None
     y_sh = torch.empty((N, d), dtype=st, device=dev_name) if Fs else None
     out = torch.empty((N, d), dtype=st, device=dev_name)
@@ -196,7 +207,7 @@ def main():
     parts = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
              for j, n in enumerate(names)}
 
-    kept = int(offs[-1].item())
+    kept = int((slot_pos >= 0).sum().item())     # kept slots (the padded layout's padding rows excluded)
     used = int((counts > 0).sum().item())
     n_up = 2 if cfg.act == "swiglu" else 1
     up_flop = 2.0 * n_up * d * F * kept
@@ -237,7 +248,9 @@ def main():
         "data": "synthetic (seeded; random weights of the named shapes)",
         "config": {"workload": cfg.name, "n_tokens": N, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
                    "d_ff_shared": Fs, "act": cfg.act, "gate_rule": cfg.gate_rule,
-                   "capacity_factor": cfg.capacity_factor, "kept_slots": kept, "used_experts": used,
+                   "capacity_factor": cfg.capacity_factor, "capacity_layout": cfg.capacity_layout,
+                   "capacity_priority": cfg.capacity_priority, "expert_rows": R, "kept_slots": kept,
+                   "used_experts": used,
                    "expert_weights": "fp8_e4m3_row_scaled" if fp8 is not None else cfg.dtype},
         "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
                                "(build_tiles_kernel, grouped_gemm_kernel, split_fixup_kernel; one "

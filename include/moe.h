@@ -81,6 +81,18 @@ typedef enum {
   MOE_ACT_GELU = 1     /* [G] example: GELU(x W1^T + b1) W2^T + b2, exact erf GELU */
 } moe_act;
 
+/* Where the kept rows of each expert live ([X] "Technical insight": per-expert
+ * buffers, padded or dropped to a uniform shape).  PACKED: back to back,
+ * offsets = exclusive scan of kept counts, N k rows at most.  PADDED: expert e
+ * owns rows [e C, (e+1) C) (needs a finite capacity), kept rows first, padding
+ * rows have perm = -1 and read as zero; every expert segment has C rows. */
+typedef enum { MOE_CAPACITY_PACKED = 0, MOE_CAPACITY_PADDED = 1 } moe_capacity_layout;
+
+/* Which slots an over-full expert keeps.  SLOT: the first C in slot order
+ * s = t k + j.  CHOICE: the first C in (j, t) order - every token's first
+ * choice before any second choice.  Rows of an expert follow the same order. */
+typedef enum { MOE_PRIORITY_SLOT = 0, MOE_PRIORITY_CHOICE = 1 } moe_capacity_priority;
+
 typedef struct moe_config {
   int64_t n_tokens;        /* N >= 0 */
   int32_t d_model;         /* d > 0 */
@@ -94,7 +106,12 @@ typedef struct moe_config {
   float   capacity_factor; /* <= 0: unlimited; else C = floor(cf * N / E) ([N] item 2) */
   int32_t dtype;           /* moe_dtype */
   int32_t add_residual;    /* 1: out = x + MoE(x) ([L] "FFN swap": h + ...) */
+  int32_t capacity_layout; /* moe_capacity_layout */
+  int32_t capacity_priority; /* moe_capacity_priority */
 } moe_config;
+
+/* Rows R of the expert-ordered buffers (perm, x_perm, h_tmp, y_perm):
+ * N k for MOE_CAPACITY_PACKED, E C for MOE_CAPACITY_PADDED. */
 
 /* Bytes of scratch that moe_forward needs for `cfg` (the step entry points
  * need at most this much too).  Host only, launches nothing. */
@@ -127,12 +144,15 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   topk_idx  [N, k] int32     from moe_route
  *   x         [N, d] | NULL    rows to gather (may be NULL when x_perm is NULL)
  *   counts    [E] int32        out: slots per expert before dropping (sum = N k)
- *   offsets   [E+1] int32      out: exclusive scan of kept counts min(counts, C)
- *   perm      [N k] int32      out: perm[p] = slot id at expert-sorted position p
- *                              (p < offsets[E]); ascending slot id within an expert
+ *   offsets   [E+1] int32      out: start row of each expert's segment: exclusive scan of
+ *                              kept counts min(counts, C) (packed) or e C (padded)
+ *   perm      [R] int32        out: perm[p] = slot id at expert-sorted position p
+ *                              (p < offsets[E]), in priority order within an expert;
+ *                              -1 on padding rows (R = N k packed, E C padded)
  *   slot_pos  [N k] int32      out: position of slot s in perm, -1 if dropped
  *   drop_count int64 | NULL    out: sum_e max(0, counts_e - C)
- *   x_perm    [N k, d] | NULL  out: x_perm[p] = x[perm[p] / k] for p < offsets[E];
+ *   x_perm    [R, d] | NULL    out: x_perm[p] = x[perm[p] / k] for p < offsets[E] (zero rows
+ *                              where perm[p] = -1);
  *                              NULL skips the row copy (moe_expert_up_gather then
  *                              reads the token rows through perm)
  * Each expert keeps its first C slots in ascending slot id. */

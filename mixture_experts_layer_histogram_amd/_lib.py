@@ -26,7 +26,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("n_tokens", c_int64), ("d_model", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
                 ("d_ff", c_int32), ("d_ff_shared", c_int32), ("act", c_int32), ("ffn_bias", c_int32),
                 ("gate_rule", c_int32), ("capacity_factor", c_float), ("dtype", c_int32),
-                ("add_residual", c_int32)]
+                ("add_residual", c_int32), ("capacity_layout", c_int32), ("capacity_priority", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -111,11 +111,26 @@ def _call(name, *args):
         raise MoeError(name, st)
 
 
+LAYOUTS = {"packed": 0, "padded": 1}
+PRIORITIES = {"slot": 0, "choice": 1}
+
+
 def make_config(n_tokens, d_model, n_experts, top_k, d_ff, d_ff_shared=0, act="swiglu", ffn_bias=False,
-                gate_rule="topk_softmax", capacity_factor=0.0, dtype="bf16", add_residual=True) -> MoeConfig:
+                gate_rule="topk_softmax", capacity_factor=0.0, dtype="bf16", add_residual=True,
+                capacity_layout="packed", capacity_priority="slot") -> MoeConfig:
     return MoeConfig(int(n_tokens), int(d_model), int(n_experts), int(top_k), int(d_ff), int(d_ff_shared),
                      ACTS[act], int(bool(ffn_bias)), GATE_RULES[gate_rule], float(capacity_factor),
-                     DTYPES[dtype], int(bool(add_residual)))
+                     DTYPES[dtype], int(bool(add_residual)), LAYOUTS[capacity_layout],
+                     PRIORITIES[capacity_priority])
+
+
+def expert_rows(cfg: MoeConfig) -> int:
+    """Rows of the expert-ordered buffers (perm, x_perm, h, y) for this config."""
+    if cfg.capacity_layout == LAYOUTS["padded"]:
+        # same arithmetic as the library: double(cf) * N / E, truncated
+        cap = int(float(cfg.capacity_factor) * cfg.n_tokens / cfg.n_experts) if cfg.capacity_factor > 0 else 0
+        return cfg.n_experts * cap
+    return cfg.n_tokens * cfg.top_k
 
 
 def workspace_size(cfg: MoeConfig) -> int:

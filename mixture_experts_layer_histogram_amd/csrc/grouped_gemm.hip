@@ -390,7 +390,8 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
       const int r = w.r0 + row;
-      voff[u] = (r < w.r1 ? (p.perm[r] / p.gk) * rowbytes : kOobOffset) + chunk * 16;
+      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      voff[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voff[u] = row * rowbytes + chunk * 16;
     }
@@ -521,7 +522,8 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
       const int r = w.r0 + row;
-      voffa[u] = (r < w.r1 ? (p.perm[r] / p.gk) * rowbytes : kOobOffset) + chunk * 16;
+      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      voffa[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voffa[u] = row * rowbytes + chunk * 16;
     }
@@ -680,7 +682,8 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
       const int r = w.r0 + row;
-      voffa[u] = (r < w.r1 ? (p.perm[r] / p.gk) * rowbytes : kOobOffset) + chunk * 16;
+      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      voffa[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voffa[u] = row * rowbytes + chunk * 16;
     }
@@ -909,7 +912,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
 }
 
 // fp32 storage: one thread per output element, sequential fp32 FMA over K.
-// With `perm`, row r of the expert order reads token row perm[r] / gk of A.
+// With `perm`, row r of the expert order reads token row perm[r] / gk of A
+// (perm[r] = -1: a padding row, all zeros).
 template <int MODE, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ perm, int gk, const int32_t* __restrict__ offsets,
@@ -928,16 +932,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     }
     seg = lo;
   }
-  const int arow = perm ? perm[row] / gk : row;
-  const float* a = A + (size_t)arow * K;
+  const int pr = perm ? perm[row] : row;        // -1: a padding row (reads as zeros)
+  const int kk = pr >= 0 ? K : 0;
+  const float* a = A + (size_t)(pr >= 0 ? (perm ? pr / gk : pr) : 0) * K;
   const float* w = W + (size_t)seg * Nn * K + (size_t)col * K;
   float acc = 0.f;
-  for (int j = 0; j < K; ++j) acc = fmaf(a[j], w[j], acc);
+  for (int j = 0; j < kk; ++j) acc = fmaf(a[j], w[j], acc);
   float v;
   if (MODE == MODE_SWIGLU_UP) {
     const float* w3 = W3 + (size_t)seg * Nn * K + (size_t)col * K;
     float acc3 = 0.f;
-    for (int j = 0; j < K; ++j) acc3 = fmaf(a[j], w3[j], acc3);
+    for (int j = 0; j < kk; ++j) acc3 = fmaf(a[j], w3[j], acc3);
     v = silu_f(acc) * acc3;
   } else {
     v = acc;

@@ -20,6 +20,7 @@ Workspace workspace_layout(const moe_config& c) {
   const size_t N = (size_t)c.n_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
   const size_t d = (size_t)c.d_model, F = (size_t)c.d_ff, Fs = (size_t)(c.d_ff_shared > 0 ? c.d_ff_shared : 0);
   const size_t slots = N * k;
+  const size_t rows = (size_t)expert_rows(c);   // expert-ordered buffer rows
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
 
   // top-k blocking: L lanes per token, 4 waves, iters rounds per block
@@ -32,8 +33,8 @@ Workspace workspace_layout(const moe_config& c) {
   W.topk_tokens_per_block = per_iter * W.topk_iters;
   W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
   W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
-  W.max_tiles = grouped_gemm_max_tiles((int)slots, (int)E);
-  W.max_tiles_small = grouped_gemm_max_small_tiles((int)slots, (int)E);
+  W.max_tiles = grouped_gemm_max_tiles((int)(rows > slots ? rows : slots), (int)E);
+  W.max_tiles_small = grouped_gemm_max_small_tiles((int)(rows > slots ? rows : slots), (int)E);
   W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1) : 0;
   W.max_tiles_sh_small = Fs ? grouped_gemm_max_small_tiles((int)N, 1) : 0;
 
@@ -51,14 +52,14 @@ Workspace workspace_layout(const moe_config& c) {
   W.probsum = take(E * 4);
   W.counts = take(E * 4);
   W.offsets = take((E + 1) * 4);
-  W.perm = take(slots * 4);
+  W.perm = take(rows * 4);
   W.slot_pos = take(slots * 4);
   W.drop_count = take(8);
   W.aux = take(4);
   W.signs = take(E);
-  W.x_perm = take(slots * d * esz);
-  W.h = take(slots * F * esz);
-  W.y = take(slots * d * esz);
+  W.x_perm = take(rows * d * esz);
+  W.h = take(rows * F * esz);
+  W.y = take(rows * d * esz);
   W.h_sh = take(N * Fs * esz);
   W.y_sh = take(Fs ? N * d * esz : 0);
   W.total = off;
@@ -84,6 +85,10 @@ moe_status check_config(const moe_config* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_ARG;
   if (isnan(c->capacity_factor)) return MOE_ERR_ARG;
   if (c->gate_rule == MOE_GATE_SWITCH_TOP1 && c->top_k != 1) return MOE_ERR_ARG;
+  if (c->capacity_layout != MOE_CAPACITY_PACKED && c->capacity_layout != MOE_CAPACITY_PADDED) return MOE_ERR_ARG;
+  if (c->capacity_priority != MOE_PRIORITY_SLOT && c->capacity_priority != MOE_PRIORITY_CHOICE) return MOE_ERR_ARG;
+  if (c->capacity_layout == MOE_CAPACITY_PADDED && !(c->capacity_factor > 0.f)) return MOE_ERR_ARG;
+  if (expert_rows(*c) >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (c->ffn_bias && c->act != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_BF16) {
     if (c->d_model % 64 || c->d_ff % 64 || c->d_ff_shared % 64) return MOE_ERR_UNSUPPORTED;
@@ -123,7 +128,7 @@ GroupedGemmArgs gemm_args(const moe_config& c, const Workspace& W, void* ws, boo
     g.max_tiles_small = W.max_tiles_sh_small;
   } else {
     g.n_seg = c.n_experts;
-    g.max_rows = (int)(c.n_tokens * c.top_k);
+    g.max_rows = (int)expert_rows(c);
     g.tiles = reinterpret_cast<int32_t*>(wsp(ws, W.tiles));
     g.max_tiles = W.max_tiles;
     g.tiles_small = reinterpret_cast<int32_t*>(wsp(ws, W.tiles_small));

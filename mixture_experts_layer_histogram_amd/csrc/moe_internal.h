@@ -50,6 +50,19 @@ __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 
 // most 8), so a wavefront routes 64 / L tokens at once.
 inline int topk_lanes(int E) { return E <= 64 ? 8 : (E <= 128 ? 16 : 32); }
 
+// Per-expert capacity C = floor(cf * N / E) in double (0x7fffffff when unlimited).
+inline int capacity_of(const moe_config& c) {
+  if (!(c.capacity_factor > 0.f)) return 0x7fffffff;
+  const double cap = (double)c.capacity_factor * (double)c.n_tokens / (double)c.n_experts;
+  return cap >= 2147483647.0 ? 0x7fffffff : (int)cap;
+}
+
+// Rows of the expert-ordered buffers (perm, x_perm, h, y): N k packed, E C padded.
+inline long long expert_rows(const moe_config& c) {
+  return c.capacity_layout == MOE_CAPACITY_PADDED ? (long long)c.n_experts * capacity_of(c)
+                                                  : c.n_tokens * (long long)c.top_k;
+}
+
 // ----------------------------------------------------------------- workspace
 
 struct Workspace {

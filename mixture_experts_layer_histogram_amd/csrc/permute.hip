@@ -8,6 +8,13 @@
 // expert takes.  [N] "Load balancing" item 2: at most C * N / E tokens per
 // expert, the overflow skips the experts.
 //
+// Priority: slots are ranked in "priority order" i = 0 .. N k - 1: slot order
+// (i = s = t k + j) or choice order (i = j N + t: every first choice before
+// any second choice).  Ranks, the capacity cut and the row order inside an
+// expert all follow i.  Layout: packed rows (offsets = scan of kept counts)
+// or fixed [E, C] buffers (offsets = e C; rows past an expert's kept count
+// get perm = -1 and, when x_perm is written, zero rows).
+//
 // Three passes, no atomics on values that decide positions:
 //   1. hist_rank   : per block of 1024 slots, the stable rank of every slot
 //                    among the block's slots of the same expert, and the
@@ -26,6 +33,10 @@
 namespace moe {
 
 constexpr int kHistWaves = 4;
+
+// slot of priority index i, and priority index of slot s
+__device__ __forceinline__ int slot_of(int i, int N, int k, bool choice) { return choice ? (i % N) * k + i / N : i; }
+__device__ __forceinline__ int index_of(int s, int N, int k, bool choice) { return choice ? (s % k) * N + s / k : s; }
 constexpr int kHistChunks = kHistSlotsPerBlock / (64 * kHistWaves);   // 64-slot chunks per wave
 
 // Pass 1.  Wave w of block b owns slots [b*1024 + w*256, +256) and walks them
@@ -36,7 +47,8 @@ constexpr int kHistChunks = kHistSlotsPerBlock / (64 * kHistWaves);   // 64-slot
 __global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restrict__ topk_idx,
                                                         int n_slots, int E, int nblk,
                                                         int32_t* __restrict__ local_rank,
-                                                        int32_t* __restrict__ block_counts) {
+                                                        int32_t* __restrict__ block_counts, int N, int k,
+                                                        int choice) {
   __shared__ int cnt[kHistWaves][kMaxExperts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < kHistWaves * kMaxExperts; i += blockDim.x) (&cnt[0][0])[i] = 0;
@@ -47,8 +59,8 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restric
   int rank[kHistChunks], eid[kHistChunks];
 #pragma unroll
   for (int ch = 0; ch < kHistChunks; ++ch) {
-    const int s = base + ch * 64 + lane;
-    const int e = s < n_slots ? topk_idx[s] : -1;
+    const int i = base + ch * 64 + lane;
+    const int e = i < n_slots ? topk_idx[slot_of(i, N, k, choice)] : -1;
     uint64_t match = __ballot(e >= 0);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
@@ -79,15 +91,15 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restric
   __syncthreads();
 #pragma unroll
   for (int ch = 0; ch < kHistChunks; ++ch) {
-    const int s = base + ch * 64 + lane;
-    if (s < n_slots) local_rank[s] = cnt[wave][eid[ch]] + rank[ch];
+    const int i = base + ch * 64 + lane;
+    if (i < n_slots) local_rank[slot_of(i, N, k, choice)] = cnt[wave][eid[ch]] + rank[ch];
   }
 }
 
 // Pass 2 (one workgroup).  Thread e walks expert e's block counts in block
 // order; then a workgroup scan over experts gives the offsets.
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ block_counts,
-                                                            int nblk, int E, int capacity,
+                                                            int nblk, int E, int capacity, int padded,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int64_t* __restrict__ drop_count) {
@@ -128,12 +140,12 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   __syncthreads();
   int prefix = 0;
   for (int w = 0; w < wave; ++w) prefix += wave_tot[w];
-  if (tid < E) offsets[tid] = prefix + incl - kept;
+  if (tid < E) offsets[tid] = padded ? tid * capacity : prefix + incl - kept;
   if (tid == 0) {
     int tot = 0;
     long long dt = 0;
     for (int w = 0; w < 4; ++w) { tot += wave_tot[w]; dt += wave_drop[w]; }
-    offsets[E] = tot;
+    offsets[E] = padded ? E * capacity : tot;
     if (drop_count) *drop_count = dt;
   }
 }
@@ -144,12 +156,13 @@ __global__ __launch_bounds__(256) void scatter_gather_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
     const int32_t* __restrict__ rank_base, const int32_t* __restrict__ offsets, int n_slots, int k,
     int nblk, int capacity, const char* __restrict__ x, size_t row_bytes, int32_t* __restrict__ perm,
-    int32_t* __restrict__ slot_pos, char* __restrict__ x_perm) {
+    int32_t* __restrict__ slot_pos, char* __restrict__ x_perm, int N, int choice) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + wave;
   if (s >= n_slots) return;
   const int e = topk_idx[s];
-  const int r = rank_base[(size_t)e * nblk + s / kHistSlotsPerBlock] + local_rank[s];
+  const int blk = index_of(s, N, k, choice) / kHistSlotsPerBlock;
+  const int r = rank_base[(size_t)e * nblk + blk] + local_rank[s];
   if (r >= capacity) {
     if (lane == 0) slot_pos[s] = -1;
     return;
@@ -176,11 +189,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ rank_base,
                                                       const int32_t* __restrict__ offsets, int n_slots,
                                                       int nblk, int capacity, int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ slot_pos) {
+                                                      int32_t* __restrict__ slot_pos, int N, int k, int choice) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n_slots) return;
   const int e = topk_idx[s];
-  const int r = rank_base[(size_t)e * nblk + s / kHistSlotsPerBlock] + local_rank[s];
+  const int blk = index_of(s, N, k, choice) / kHistSlotsPerBlock;
+  const int r = rank_base[(size_t)e * nblk + blk] + local_rank[s];
   if (r >= capacity) {
     slot_pos[s] = -1;
     return;
@@ -188,6 +202,27 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int pos = offsets[e] + r;
   perm[pos] = s;
   slot_pos[s] = pos;
+}
+
+// Padded layout: rows of expert e past its kept count get perm = -1 and, when
+// x_perm is written, a zero row.  One wavefront per buffer row.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ counts, int E, int capacity,
+                                                       int32_t* __restrict__ perm, char* __restrict__ x_perm,
+                                                       size_t row_bytes) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long r = (long long)blockIdx.x * 4 + wave;
+  if (r >= (long long)E * capacity) return;
+  const int e = (int)(r / capacity), j = (int)(r % capacity);
+  const int kept = min(counts[e], capacity);
+  if (j < kept) return;
+  if (lane == 0) perm[r] = -1;
+  if (x_perm == nullptr) return;
+  char* dst = x_perm + (size_t)r * row_bytes;
+  if ((row_bytes & 15) == 0) {
+    for (size_t i = (size_t)lane * 16; i < row_bytes; i += 64 * 16) *reinterpret_cast<uint4*>(dst + i) = uint4{0, 0, 0, 0};
+  } else {
+    for (size_t i = (size_t)lane * 2; i < row_bytes; i += 64 * 2) *reinterpret_cast<uint16_t*>(dst + i) = 0;
+  }
 }
 
 hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx,
@@ -198,30 +233,39 @@ hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t
   const int n_slots = (int)n_slots_ll;
   const int nblk = W.hist_blocks_n;
   const int E = c.n_experts;
-  int capacity = 0x7fffffff;
-  if (c.capacity_factor > 0.f) {
-    const double cap = (double)c.capacity_factor * (double)c.n_tokens / (double)E;
-    capacity = cap >= 2147483647.0 ? 0x7fffffff : (int)cap;   // floor (cap >= 0)
-  }
+  const int capacity = capacity_of(c);
+  const int N = (int)c.n_tokens, k = c.top_k;
+  const int choice = c.capacity_priority == MOE_PRIORITY_CHOICE ? 1 : 0;
+  const int padded = c.capacity_layout == MOE_CAPACITY_PADDED ? 1 : 0;
   if (n_slots > 0) {
     hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, n_slots, E, nblk,
-                       hist_rank, hist_blocks);
+                       hist_rank, hist_blocks, N, k, choice);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, hist_blocks, n_slots > 0 ? nblk : 0,
-                     E, capacity, counts, offsets, drop_count);
+                     E, capacity, padded, counts, offsets, drop_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_slots == 0) return err;
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)c.d_model * esz;
+  if (padded) {
+    const long long rows = expert_rows(c);
+    if (rows > 0) {
+      hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, counts, E, capacity,
+                         perm, (char*)x_perm, row_bytes);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+  }
   if (x_perm == nullptr) {
     hipLaunchKernelGGL(scatter_kernel, dim3((n_slots + 255) / 256), dim3(256), 0, s, topk_idx, hist_rank,
-                       hist_blocks, offsets, n_slots, nblk, capacity, perm, slot_pos);
+                       hist_blocks, offsets, n_slots, nblk, capacity, perm, slot_pos, N, k, choice);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(scatter_gather_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s, topk_idx,
                      hist_rank, hist_blocks, offsets, n_slots, c.top_k, nblk, capacity,
-                     (const char*)x, (size_t)c.d_model * esz, perm, slot_pos, (char*)x_perm);
+                     (const char*)x, row_bytes, perm, slot_pos, (char*)x_perm, N, choice);
   return hipGetLastError();
 }
 

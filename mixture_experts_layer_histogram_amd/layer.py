@@ -14,7 +14,8 @@ def config_from(c, n_tokens: int | None = None) -> _lib.MoeConfig:
     residual."""
     return _lib.make_config(c.n_tokens if n_tokens is None else n_tokens, c.d_model, c.n_experts, c.top_k,
                             c.d_ff, c.d_ff_shared, c.act, c.ffn_bias, c.gate_rule, c.capacity_factor,
-                            c.dtype, c.residual)
+                            c.dtype, c.residual, getattr(c, "capacity_layout", "packed"),
+                            getattr(c, "capacity_priority", "slot"))
 
 
 def to_device(a, device, dtype: str):
@@ -64,7 +65,7 @@ class MoELayer:
             "gates": torch.empty((N, k), dtype=f32, device=device),
             "counts": torch.empty(E, dtype=i32, device=device),
             "offsets": torch.empty(E + 1, dtype=i32, device=device),
-            "perm": torch.empty(N * k, dtype=i32, device=device),
+            "perm": torch.empty(max(_lib.expert_rows(self.cfg), 1), dtype=i32, device=device),
             "slot_pos": torch.empty(N * k, dtype=i32, device=device),
             "drop_count": torch.empty(1, dtype=torch.int64, device=device),
             "probsum": torch.empty(E, dtype=f32, device=device),

@@ -35,6 +35,17 @@ EDGE = {
     "k16_e32": BASE.scaled(name="k16_e32", n_tokens=300, n_experts=32, top_k=16),
     # E = 64 router on the grouped GEMM with a logit bias and a short tail (64-row tiles)
     "router_gemm_tail": SWITCH_SKEWED.scaled(name="router_gemm_tail", n_tokens=600, d_model=256, d_ff=256),
+    # capacity-buffer layout ([E, C] rows, padding rows read as zero) and choice-major priority
+    "padded_capacity": BASE.scaled(name="padded_capacity", n_tokens=600, capacity_factor=1.25,
+                                   capacity_layout="padded"),
+    "choice_priority": BASE.scaled(name="choice_priority", n_tokens=600, capacity_factor=1.25,
+                                   capacity_priority="choice"),
+    "padded_choice_f32": DEEPSEEK_V3.scaled(name="padded_choice_f32", n_tokens=77, d_model=48, d_ff=40,
+                                            d_ff_shared=24, n_experts=16, top_k=4, dtype="f32",
+                                            capacity_factor=1.5, capacity_layout="padded",
+                                            capacity_priority="choice"),
+    "padded_gelu_bias": SWITCH_SKEWED.scaled(name="padded_gelu_bias", n_tokens=700, d_model=192, d_ff=320,
+                                             capacity_layout="padded"),
     "split_k_up": BASE.scaled(name="split_k_up", n_tokens=2048, n_experts=4, d_model=256, d_ff=2240),
     "split_k_down_gelu": SWITCH_SKEWED.scaled(name="split_k_down_gelu", n_tokens=2048, n_experts=4, d_model=8448,
                                               d_ff=256, capacity_factor=0.0, logit_offset=None),
@@ -54,6 +65,11 @@ def test_edge_parity(name):
     assert int(o["drop_count"][0]) == r.disp.drop_count
     _, ref = oracle.oracle_layer(cfg, inp, logits_override=o["logits"])
     assert rel_err(o["out"], ref) <= TOL[cfg.dtype], rel_err(o["out"], ref)
+    if cfg.capacity_layout == "padded":      # padding rows carry -1 in perm
+        assert np.array_equal(o["perm"], r.disp.perm)
+    else:
+        kept = int(r.disp.offsets[-1])
+        assert np.array_equal(o["perm"][:kept], r.disp.perm)
     if name == "all_dropped":
         assert r.disp.drop_count == cfg.n_tokens
         assert np.array_equal(o["out"], host_x(inp))      # residual passes through unchanged

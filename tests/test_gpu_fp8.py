@@ -21,6 +21,9 @@ CASES = {
     "ragged_e64": DEEPSEEK_V3.scaled(name="fp8_ragged_e64", n_tokens=300, n_experts=64, top_k=4, d_model=320,
                                      d_ff=192, d_ff_shared=0),
     "long_segments": SMALL["mixtral_prefill_small"].scaled(name="fp8_long_segments", n_tokens=700),
+    "padded_choice": SMALL["mixtral_prefill_small"].scaled(name="fp8_padded_choice", n_tokens=500,
+                                                           capacity_factor=1.25, capacity_layout="padded",
+                                                           capacity_priority="choice"),
 }
 
 
@@ -87,7 +90,8 @@ def test_fp8_layer_parity(name):
             logits=z, ws=ws)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    R = M._lib.expert_rows(c)
+    perm = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
     sp = torch.empty(N * k, dtype=torch.int32, device="cuda")
     M.permute(c, idx, None, counts, offs, perm, sp, None, ws=ws)
     w1q, s1 = _quantize(M, dev["w1"])
@@ -95,8 +99,8 @@ def test_fp8_layer_parity(name):
     w3q = s3 = None
     if cfg.act == "swiglu":
         w3q, s3 = _quantize(M, dev["w3"])
-    h = torch.empty((N * k, F), dtype=st, device="cuda")
-    y = torch.empty((N * k, d), dtype=st, device="cuda")
+    h = torch.empty((R, F), dtype=st, device="cuda")
+    y = torch.empty((R, d), dtype=st, device="cuda")
     M.expert_up_fp8(c, dev["x"], perm, offs, w1q, w3q, s1, s3, h, b1=dev["b1"], ws=ws)
     M.expert_down_fp8(c, h, offs, w2q, s2, y, b2=dev["b2"], ws=ws)
     out = torch.empty((N, d), dtype=st, device="cuda")

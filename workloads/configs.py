@@ -21,6 +21,8 @@ Only shapes and options live here; :mod:`workloads.gen` draws the values.
 from __future__ import annotations
 
 import dataclasses
+
+import numpy as np
 from dataclasses import dataclass
 
 # Gate rules (what the router does with the logits z of one token).
@@ -70,7 +72,8 @@ class MoEConfig:
         """Per-expert capacity floor(cf * N / E), or None when unlimited."""
         if self.capacity_factor <= 0:
             return None
-        return int((float(self.capacity_factor) * self.n_tokens) // self.n_experts)
+        # the factor as the C ABI carries it (fp32), then floor(cf * N / E) in double
+        return int(float(np.float32(self.capacity_factor)) * self.n_tokens / self.n_experts)
 
 
 TINY_TOP2_FP32 = MoEConfig(
