@@ -448,3 +448,159 @@ def fp8_expert_weights(w: dict) -> dict:
             q, sc = quantize_fp8_rows(np.asarray(v, dtype=np.float32))
             out[n] = dequantize_fp8_rows(q, sc)
     return out
+
+
+# --------------------------------------------------------------------------- backward
+
+def silu_grad(u: np.ndarray) -> np.ndarray:
+    """d/du u*sigmoid(u) = sigmoid(u) * (1 + u * (1 - sigmoid(u)))."""
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * (1.0 - s))
+
+
+def gelu_grad(u: np.ndarray) -> np.ndarray:
+    """d/du u*Phi(u) = Phi(u) + u*phi(u) (exact erf GELU)."""
+    return 0.5 * erfc(-u / math.sqrt(2.0)) + u * np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
+
+
+def softmax_backward(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """Row softmax Jacobian-vector product: dz = p * (dp - <p, dp>)."""
+    return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+
+
+def gate_backward(rule: str, z: np.ndarray, idx: np.ndarray, gates: np.ndarray, p: np.ndarray,
+                  dg: np.ndarray) -> np.ndarray:
+    """dL/dz from dL/dgates; the selection itself is piecewise constant in z.
+
+    rule A (gate = softmax of the selected raw logits): dz_S = g * (dg - <g, dg>);
+    rule B (gate = p_S / sum p_S, p = softmax(z)): dp_S = (dg - <g, dg>) / sum p_S,
+    then the full softmax Jacobian; rule C (gate = p of the argmax): dp = dg at
+    the argmax, then the softmax Jacobian."""
+    N, E = z.shape
+    dz = np.zeros((N, E))
+    if rule == GATE_TOPK_SOFTMAX:
+        dzs = gates * (dg - np.sum(gates * dg, axis=1, keepdims=True))
+        np.put_along_axis(dz, idx, dzs, axis=1)
+    elif rule == GATE_SOFTMAX_RENORM:
+        ps = np.take_along_axis(p, idx, axis=1)
+        dps = (dg - np.sum(gates * dg, axis=1, keepdims=True)) / ps.sum(axis=1, keepdims=True)
+        dp = np.zeros((N, E))
+        np.put_along_axis(dp, idx, dps, axis=1)
+        dz = softmax_backward(p, dp)
+    elif rule == GATE_SWITCH_TOP1:
+        dp = np.zeros((N, E))
+        np.put_along_axis(dp, idx, dg, axis=1)
+        dz = softmax_backward(p, dp)
+    else:
+        raise ValueError(rule)
+    return dz
+
+
+def aux_loss_backward(counts: np.ndarray, p: np.ndarray, k: int, d_aux: float) -> np.ndarray:
+    """dL/dz of d_aux * E * sum_e f_e P_e: f (from the discrete counts) is constant,
+    dP_e/dp[t,e] = 1/N, then the softmax Jacobian."""
+    N, E = p.shape
+    f = counts.astype(np.float64) / float(N * k)
+    dp = np.broadcast_to(d_aux * E * f / float(N), (N, E))
+    return softmax_backward(p, dp)
+
+
+def expert_backward(act: str, X: np.ndarray, w: dict, dY: np.ndarray) -> dict:
+    """Gradients of one expert FFN on its rows X given dL/dY: dX and the weight
+    (and bias) gradients.  SwiGLU: H = SiLU(A1) * A3, A1 = X W1^T, A3 = X W3^T,
+    Y = H W2^T.  GELU: H = GELU(A), A = X W1^T + b1, Y = H W2^T + b2."""
+    g = {}
+    if act == "swiglu":
+        A1, A3 = X @ w["w1"].T, X @ w["w3"].T
+        H = silu(A1) * A3
+        dH = dY @ w["w2"]
+        dA1 = dH * A3 * silu_grad(A1)
+        dA3 = dH * silu(A1)
+        g["w2"] = dY.T @ H
+        g["w1"] = dA1.T @ X
+        g["w3"] = dA3.T @ X
+        g["x"] = dA1 @ w["w1"] + dA3 @ w["w3"]
+    elif act == "gelu":
+        A = X @ w["w1"].T
+        if w.get("b1") is not None:
+            A = A + w["b1"][None, :]
+        H = gelu(A)
+        dH = dY @ w["w2"]
+        dA = dH * gelu_grad(A)
+        g["w2"] = dY.T @ H
+        g["w1"] = dA.T @ X
+        if w.get("b1") is not None:
+            g["b1"] = dA.sum(axis=0)
+        if w.get("b2") is not None:
+            g["b2"] = dY.sum(axis=0)
+        g["x"] = dA @ w["w1"]
+    else:
+        raise ValueError(act)
+    return g
+
+
+def oracle_layer_backward(cfg, inputs, dout, d_aux: float = 0.0, logits_override=None,
+                          expert_weights="stored") -> dict:
+    """Gradients of the layer's forward pass (``oracle_layer``) in fp64, for an
+    upstream gradient ``dout`` [N, d] of ``out`` and ``d_aux`` of the aux loss.
+
+    The routing decisions (selection, capacity) are taken as fixed, since they
+    are piecewise constant in the inputs; gradients flow through the gate
+    weights into the logits and the router, through the kept slots' expert
+    FFNs, the shared expert and the residual ([L] "The load balance problem":
+    the auxiliary loss is a second gradient signal into the router).
+
+    Returns dx [N, d], w_router [E, d], logit_bias [E], w1/w3 [E, F, d],
+    w2 [E, d, F], b1 [E, F] / b2 [E, d] (GELU with biases), sh_w1/sh_w3
+    [Fs, d] and sh_w2 [d, Fs] (with a shared expert)."""
+    dt = cfg.dtype
+    N, E, k, d, F = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff
+    x = to_f64(inputs.x, dt)
+    wr = to_f64(inputs.w_router, dt)
+    z = router_logits(x, wr, inputs.logit_bias) if logits_override is None else \
+        np.asarray(logits_override, dtype=np.float32).astype(np.float64)
+    r = oracle_route(cfg, z, inputs.sel_bias)
+    dout = np.asarray(dout, dtype=np.float64)
+    grads = {"x": np.zeros((N, d)), "w1": np.zeros((E, F, d)), "w2": np.zeros((E, d, F))}
+    if cfg.act == "swiglu":
+        grads["w3"] = np.zeros((E, F, d))
+    if cfg.ffn_bias:
+        grads["b1"] = np.zeros((E, F))
+        grads["b2"] = np.zeros((E, d))
+    if cfg.residual:
+        grads["x"] += dout
+    dg = np.zeros((N, k))
+    for e in range(E):
+        lo, hi = r.disp.offsets[e], r.disp.offsets[e + 1]
+        slots = r.disp.perm[lo:hi]
+        slots = slots[slots >= 0]
+        if slots.size == 0:
+            continue
+        w = {n: to_f64(v, dt) for n, v in inputs.expert(e).items()}
+        if expert_weights == "fp8":
+            w = fp8_expert_weights(w)
+        t, j = slots // k, slots % k
+        X = x[t]
+        Y = expert_apply(cfg.act, X, w)
+        dg[t, j] = np.sum(dout[t] * Y, axis=1)
+        dY = r.gates[t, j][:, None] * dout[t]
+        g = expert_backward(cfg.act, X, w, dY)
+        np.add.at(grads["x"], t, g["x"])
+        for n in ("w1", "w3", "w2", "b1", "b2"):
+            if n in g:
+                grads[n][e] += g[n]
+    dz = gate_backward(cfg.gate_rule, z, r.topk_idx, r.gates, r.probs, dg)
+    if cfg.aux_loss and d_aux != 0.0:
+        dz = dz + aux_loss_backward(r.disp.counts, r.probs, k, d_aux)
+    grads["logits"] = dz
+    grads["w_router"] = dz.T @ x
+    grads["logit_bias"] = dz.sum(axis=0)
+    grads["x"] += dz @ wr
+    if cfg.d_ff_shared > 0:
+        sw = {"w1": to_f64(inputs.sh_w1, dt), "w3": to_f64(inputs.sh_w3, dt), "w2": to_f64(inputs.sh_w2, dt)}
+        g = expert_backward("swiglu", x, sw, dout)
+        grads["x"] += g["x"]
+        grads["sh_w1"], grads["sh_w3"], grads["sh_w2"] = g["w1"], g["w3"], g["w2"]
+    grads["gates"] = dg
+    return grads

@@ -438,6 +438,110 @@ def check_activation_library():
     assert np.allclose(mo.gelu(v), TF.gelu(V, approximate="none").numpy(), rtol=1e-12, atol=1e-14)
 
 
+# ----------------------------------------------------------------- backward
+
+def _torch_layer_loss(cfg, inp, idx, kept, counts, dout, d_aux, params):
+    """The layer's forward written with torch ops (fp64) for fixed routing
+    decisions, and the scalar <out, dout> + d_aux * aux whose gradients
+    torch.autograd computes."""
+    E, k = cfg.n_experts, cfg.top_k
+    x, wr = params["x"], params["w_router"]
+    z = x @ wr.T + params["logit_bias"][None, :]
+    p = torch.softmax(z, dim=1)
+    it = torch.from_numpy(idx)
+    if cfg.gate_rule == GATE_TOPK_SOFTMAX:
+        g = torch.softmax(z.gather(1, it), dim=1)
+    elif cfg.gate_rule == GATE_SOFTMAX_RENORM:
+        ps = p.gather(1, it)
+        g = ps / ps.sum(dim=1, keepdim=True)
+    else:
+        g = p.gather(1, it)
+    out = x.clone() if cfg.residual else torch.zeros_like(x)
+    if cfg.d_ff_shared:
+        out = out + TF.linear(TF.silu(TF.linear(x, params["sh_w1"])) * TF.linear(x, params["sh_w3"]),
+                              params["sh_w2"])
+    for t in range(cfg.n_tokens):
+        for j in range(k):
+            if not kept[t, j]:
+                continue
+            e = int(idx[t, j])
+            xt = x[t:t + 1]
+            if cfg.act == "swiglu":
+                y = TF.linear(TF.silu(TF.linear(xt, params[f"w1_{e}"])) * TF.linear(xt, params[f"w3_{e}"]),
+                              params[f"w2_{e}"])
+            else:
+                h = TF.gelu(TF.linear(xt, params[f"w1_{e}"], params.get(f"b1_{e}")), approximate="none")
+                y = TF.linear(h, params[f"w2_{e}"], params.get(f"b2_{e}"))
+            out = out.index_add(0, torch.tensor([t]), g[t, j] * y)
+    loss = (out * torch.from_numpy(dout)).sum()
+    if cfg.aux_loss:
+        f = torch.from_numpy(counts.astype(np.float64)) / float(cfg.n_tokens * k)
+        loss = loss + d_aux * E * (f * p.mean(dim=0)).sum()
+    return loss
+
+
+def check_backward_autograd():
+    """The fp64 backward (router, gates for every rule, aux loss, experts with
+    capacity drops, GELU biases, shared expert, residual) against
+    torch.autograd on the same forward written with torch ops."""
+    cases = [
+        MoEConfig(name="bw_a", n_tokens=20, d_model=12, n_experts=5, top_k=2, d_ff=16, act="swiglu",
+                  gate_rule=GATE_TOPK_SOFTMAX, dtype="f32", capacity_factor=1.5, residual=True, seed=31),
+        MoEConfig(name="bw_b", n_tokens=18, d_model=12, n_experts=6, top_k=3, d_ff=10, d_ff_shared=14,
+                  act="swiglu", gate_rule=GATE_SOFTMAX_RENORM, dtype="f32", residual=True,
+                  sel_bias_range=0.05, seed=32),
+        MoEConfig(name="bw_c", n_tokens=22, d_model=10, n_experts=4, top_k=1, d_ff=14, act="gelu", ffn_bias=True,
+                  gate_rule=GATE_SWITCH_TOP1, dtype="f32", capacity_factor=1.0, residual=True, aux_loss=True,
+                  logit_offset=(1, 0.7), init="uniform_experts", seed=33),
+    ]
+    rng = np.random.default_rng(34)
+    for cfg in cases:
+        inp = make_inputs(cfg)
+        dout = rng.standard_normal((cfg.n_tokens, cfg.d_model))
+        d_aux = 0.37 if cfg.aux_loss else 0.0
+        gr = mo.oracle_layer_backward(cfg, inp, dout, d_aux=d_aux)
+        r, _ = mo.oracle_layer(cfg, inp)
+        kept = (r.disp.slot_pos >= 0).reshape(cfg.n_tokens, cfg.top_k)
+        dt = cfg.dtype
+        P = {"x": mo.to_f64(inp.x, dt), "w_router": mo.to_f64(inp.w_router, dt),
+             "logit_bias": np.zeros(cfg.n_experts) if inp.logit_bias is None
+             else np.asarray(inp.logit_bias, np.float64)}
+        for e in range(cfg.n_experts):
+            for n, v in inp.expert(e).items():
+                P[f"{n}_{e}"] = mo.to_f64(v, dt)
+        if cfg.d_ff_shared:
+            for n in ("sh_w1", "sh_w3", "sh_w2"):
+                P[n] = mo.to_f64(getattr(inp, n), dt)
+        T = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True) for n, v in P.items()}
+        loss = _torch_layer_loss(cfg, inp, r.topk_idx, kept, r.disp.counts, dout, d_aux, T)
+        loss.backward()
+
+        def close(a, b, what):
+            a, b = np.asarray(a), np.asarray(b)
+            assert np.abs(a - b).max() <= 1e-11 * max(1.0, np.abs(b).max()), (cfg.name, what)
+        close(gr["x"], T["x"].grad.numpy(), "x")
+        close(gr["w_router"], T["w_router"].grad.numpy(), "w_router")
+        close(gr["logit_bias"], T["logit_bias"].grad.numpy(), "logit_bias")
+        for e in range(cfg.n_experts):
+            for n in ("w1", "w3", "w2", "b1", "b2"):
+                if f"{n}_{e}" in T:
+                    close(gr[n][e], T[f"{n}_{e}"].grad.numpy(), f"{n}_{e}")
+        if cfg.d_ff_shared:
+            for n in ("sh_w1", "sh_w3", "sh_w2"):
+                close(gr[n], T[n].grad.numpy(), n)
+
+
+def check_activation_grads_library():
+    """SiLU' and GELU' against torch.autograd on a grid, including the tails."""
+    u = np.linspace(-12, 12, 2001)
+    ut = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    TF.silu(ut).sum().backward()
+    assert np.abs(mo.silu_grad(u) - ut.grad.numpy()).max() <= 1e-14
+    ut = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    TF.gelu(ut, approximate="none").sum().backward()
+    assert np.abs(mo.gelu_grad(u) - ut.grad.numpy()).max() <= 1e-14
+
+
 # ----------------------------------------------------------------- fp8 weight-only experts
 
 def check_e4m3_closed_forms():

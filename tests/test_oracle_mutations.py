@@ -11,7 +11,7 @@ import pytest
 import oracle.moe_oracle as mo
 import pin_checks as pc
 
-_orig = {n: getattr(mo, n) for n in ("e4m3_round", "quantize_fp8_rows", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
+_orig = {n: getattr(mo, n) for n in ("e4m3_round", "quantize_fp8_rows", "gate_backward", "silu_grad", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
                                        "aux_loss", "bias_step", "softmax_rows", "oracle_layer")}
 
 
@@ -77,6 +77,18 @@ def _choice_as_slot(idx, E, C, layout="packed", priority="slot"):
     return _orig["dispatch"](idx, E, C, layout, "slot")
 
 
+def _gate_backward_no_centering(rule, z, idx, gates, p, dg):
+    if rule != "topk_softmax":
+        return _orig["gate_backward"](rule, z, idx, gates, p, dg)
+    dz = np.zeros(z.shape)
+    np.put_along_axis(dz, idx, gates * dg, axis=1)          # drops the -<g, dg> term
+    return dz
+
+
+def _silu_grad_sigmoid_only(u):
+    return 1.0 / (1.0 + np.exp(-u))
+
+
 def _aux_post_drop(counts, p, k):
     N, E = p.shape
     C = max(1, N // (4 * E))
@@ -113,6 +125,8 @@ def _quantize_fnuz_max(w):
 
 
 MUTATIONS = [
+    ("gate_backward", _gate_backward_no_centering, [pc.check_backward_autograd]),
+    ("silu_grad", _silu_grad_sigmoid_only, [pc.check_activation_grads_library, pc.check_backward_autograd]),
     ("e4m3_round", _e4m3_ties_away, [pc.check_e4m3_ties_to_even, pc.check_e4m3_rounding_library]),
     ("quantize_fp8_rows", _quantize_fnuz_max, [pc.check_fp8_quantize_rows]),
     ("top_k_desc", _ties_to_higher, [pc.check_topk_brute_force]),
