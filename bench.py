@@ -51,6 +51,9 @@ def parse():
                     help="override the workload's capacity layout (padded: [E, C] expert buffers)")
     ap.add_argument("--capacity-priority", choices=["slot", "choice"], default=None,
                     help="override which slots an over-full expert keeps")
+    ap.add_argument("--backward", action="store_true",
+                    help="a step is the forward pass plus moe_backward (dout = ones-scaled noise, d_aux = 1 with an "
+                         "aux loss); reports the backward's time and algorithmic TFLOP/s")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -154,6 +157,32 @@ def main():
     residual = dev["x"] if cfg.residual else None
 
     names = ["route", "permute", "expert_up", "expert_down", "shared", "combine", "aux_bias"]
+    bw = None
+    if args.backward:
+        if fp8 is not None or cfg.dtype != "bf16":
+            print("--backward runs on bf16 weights", file=sys.stderr)
+            sys.exit(2)
+        names.append("backward")
+        gen = torch.Generator(device=dev_name).manual_seed(7)
+        dout = (torch.randn((N, d), device=dev_name, generator=gen) * 0.1).to(st)
+        bw_grads = {"dx": torch.empty((N, d), dtype=st, device=dev_name),
+                    "dw_router": torch.empty((E, d), dtype=f32, device=dev_name),
+                    "dlogit_bias": torch.empty(E, dtype=f32, device=dev_name),
+                    "dw1": torch.empty((E, F, d), dtype=f32, device=dev_name),
+                    "dw2": torch.empty((E, d, F), dtype=f32, device=dev_name)}
+        if cfg.act == "swiglu":
+            bw_grads["dw3"] = torch.empty((E, F, d), dtype=f32, device=dev_name)
+        if cfg.ffn_bias:
+            bw_grads["db1"] = torch.empty((E, F), dtype=f32, device=dev_name)
+            bw_grads["db2"] = torch.empty((E, d), dtype=f32, device=dev_name)
+        if Fs:
+            bw_grads["dsh_w1"] = torch.empty((Fs, d), dtype=f32, device=dev_name)
+            bw_grads["dsh_w3"] = torch.empty((Fs, d), dtype=f32, device=dev_name)
+            bw_grads["dsh_w2"] = torch.empty((d, Fs), dtype=f32, device=dev_name)
+        bw_ws = torch.empty(M.backward_workspace_size(c), dtype=torch.uint8, device=dev_name)
+        bw_saved = {"logits": z, "topk_idx": idx, "gates": gates, "counts": counts, "offsets": offs,
+                    "perm": perm, "slot_pos": slot_pos, "y_perm": y}
+        bw = (dout, bw_grads, bw_ws, bw_saved)
 
     def step(ev=None):
         def mark(i):
@@ -186,13 +215,16 @@ def main():
         if cfg.gamma > 0:
             M.bias_update(c, counts, cfg.gamma, sel_next, signs)
         mark(7)
+        if bw is not None:
+            M.backward(c, dev, dev["x"], bw[0], bw[3], bw[1], d_aux=1.0 if cfg.aux_loss else 0.0, ws=bw[2])
+            mark(8)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -231,6 +263,7 @@ def main():
     else:   # fp32 storage runs on the vector ALUs
         roof = {"bound": "alu", "achieved": up_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    bw_flop = 2.0 * (up_flop + down_flop + 2.0 * N * d * E + 6.0 * d * Fs * N)
     traffic = measured_traffic(cfg.name) if fp8 is None else None
 
     result = {
@@ -257,6 +290,12 @@ def main():
                                f"{'moe_expert_up_gather' if fp8 is None else 'moe_expert_up_fp8'} call)",
                      **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop},
         "expert_gemm_tflops": expert_tflops,
+        **({"backward": {"ms": parts["backward"],
+                         "algorithmic_tflop": bw_flop / 1e12,
+                         "tflops": bw_flop / (parts["backward"] * 1e-3) / 1e12,
+                         "note": "dx, router, expert and shared-expert gradients; algorithmic FLOPs = the two "
+                                 "products per forward product (input and weight gradients); pre-activation "
+                                 "recompute and weight transposes are overhead"}} if bw is not None else {}),
         "breakdown_ms": parts,
         "wall_s_timed": wall_s,
         "input_gen_s": gen_s,

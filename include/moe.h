@@ -301,6 +301,55 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
+/* ------------------------------------------------------------------ backward
+ * Gradients of the layer for an upstream gradient `dout` of `out` and `d_aux`
+ * of the auxiliary loss ([L] "The load balance problem": the aux loss is a
+ * second gradient signal into the router; the bias step, moe_bias_update,
+ * follows each training step).  The routing decisions (selection, capacity)
+ * are taken as fixed: they are piecewise constant in the inputs.  Gradients
+ * flow through the gate weights (rule A: softmax over the selected logits;
+ * rule B: renormalised softmax probabilities; rule C: the argmax probability)
+ * into the logits, the router weight, the logit bias and the input; through
+ * the kept slots' expert FFNs (pre-activations recomputed); the shared expert;
+ * and the residual.  bf16 storage only (MOE_ERR_UNSUPPORTED otherwise):
+ * bf16 operands and intermediates, fp32 accumulation, fp32 weight gradients.
+ */
+typedef struct moe_saved {      /* forward state of the same call, as the step entry points return it */
+  const float*   logits;        /* [N, E] fp32 */
+  const int32_t* topk_idx;      /* [N, k] */
+  const float*   gates;         /* [N, k] */
+  const int32_t* counts;        /* [E] (used for the aux-loss gradient) */
+  const int32_t* offsets;       /* [E+1] */
+  const int32_t* perm;          /* [R] */
+  const int32_t* slot_pos;      /* [N k] */
+  const void*    y_perm;        /* [R, d] expert outputs (storage dtype) */
+} moe_saved;
+
+typedef struct moe_grads {      /* device outputs; fp32 unless noted */
+  void*  dx;                    /* [N, d] storage dtype (required) */
+  float* dw_router;             /* [E, d] | NULL */
+  float* dlogit_bias;           /* [E] | NULL */
+  float* dw1;                   /* [E, F, d] (required) */
+  float* dw3;                   /* [E, F, d] (required for SwiGLU) */
+  float* dw2;                   /* [E, d, F] (required) */
+  float* db1;                   /* [E, F] (required with ffn_bias) */
+  float* db2;                   /* [E, d] (required with ffn_bias) */
+  float* dsh_w1;                /* [Fs, d] (required with a shared expert) */
+  float* dsh_w3;                /* [Fs, d] */
+  float* dsh_w2;                /* [d, Fs] */
+  float* dgates;                /* [N, k] | NULL: dL/dgates */
+} moe_grads;
+
+/* Workspace bytes moe_backward needs (transposed weight copies, recomputed
+ * pre-activations and intermediate gradients).  Host only. */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* x [N, d], dout [N, d] (storage dtype), weights as for moe_forward.  d_aux is
+ * used when the router's aux loss is wanted (pass 0 otherwise). */
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, const void* dout,
+                        float d_aux, const moe_saved* saved, const moe_grads* grads, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 const char* moe_status_str(moe_status s);
 
 #ifdef __cplusplus

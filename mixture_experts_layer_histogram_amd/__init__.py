@@ -5,11 +5,11 @@ behind the C ABI in ``include/moe.h``; this package only marshals arguments.
 """
 from . import _lib
 from ._lib import (MoeConfig, MoeError, make_config, workspace_size, route, permute, expert_ffn, expert_up, expert_up_gather,
-                   quantize_fp8, expert_up_fp8, expert_down_fp8,
+                   quantize_fp8, expert_up_fp8, expert_down_fp8, backward, backward_workspace_size,
                    expert_down, shared_ffn, combine, bias_update, aux_loss, forward, status_str, lib)
 from .layer import MoELayer, config_from, upload_inputs, to_device
 
 __all__ = ["MoeConfig", "MoeError", "make_config", "workspace_size", "route", "permute", "expert_ffn",
            "expert_up", "expert_up_gather", "expert_down",
-           "quantize_fp8", "expert_up_fp8", "expert_down_fp8", "shared_ffn", "combine", "bias_update", "aux_loss", "forward",
+           "quantize_fp8", "expert_up_fp8", "expert_down_fp8", "backward", "backward_workspace_size", "shared_ffn", "combine", "bias_update", "aux_loss", "forward",
            "status_str", "lib", "MoELayer", "config_from", "upload_inputs", "to_device"]

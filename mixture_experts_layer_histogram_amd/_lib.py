@@ -40,6 +40,16 @@ class MoeOutputs(ctypes.Structure):
                                         "sel_bias_next")] + [("bias_gamma", c_float)]
 
 
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm", "slot_pos",
+                                        "y_perm")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("dx", "dw_router", "dlogit_bias", "dw1", "dw3", "dw2", "db1", "db2",
+                                        "dsh_w1", "dsh_w3", "dsh_w2", "dgates")]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn, status):
         self.status = status
@@ -65,6 +75,9 @@ _SIGS = {
     "moe_aux_loss": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P],
     "moe_forward": [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), _P, _P, _P,
                     ctypes.POINTER(MoeOutputs), _P, c_size_t, _P],
+    "moe_backward_workspace_size": [ctypes.POINTER(MoeConfig), ctypes.POINTER(c_size_t)],
+    "moe_backward": [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), _P, _P, c_float,
+                     ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), _P, c_size_t, _P],
 }
 
 
@@ -231,3 +244,23 @@ def forward(cfg, weights: dict, x, out, residual=None, sel_bias=None, outputs: d
     wp, wb = _ws(ws)
     _call("moe_forward", ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(residual), _ptr(sel_bias),
           ctypes.byref(O), wp, wb, _stream(stream))
+
+
+def backward_workspace_size(cfg: MoeConfig) -> int:
+    n = c_size_t(0)
+    _call("moe_backward_workspace_size", ctypes.byref(cfg), ctypes.byref(n))
+    return n.value
+
+
+def backward(cfg, weights: dict, x, dout, saved: dict, grads: dict, d_aux=0.0, ws=None, stream=None):
+    """moe_backward: `weights` as for forward(); `saved` holds logits, topk_idx, gates, counts,
+    offsets, perm, slot_pos, y_perm of the forward; `grads` the output tensors (see moe_grads)."""
+    W = MoeWeights(*[_ptr(weights.get(n)) for n in ("w_router", "logit_bias", "w1", "w3", "w2", "b1", "b2",
+                                                    "sh_w1", "sh_w3", "sh_w2")])
+    S = MoeSaved(*[_ptr(saved.get(n)) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm",
+                                                "slot_pos", "y_perm")])
+    G = MoeGrads(*[_ptr(grads.get(n)) for n in ("dx", "dw_router", "dlogit_bias", "dw1", "dw3", "dw2", "db1", "db2",
+                                                "dsh_w1", "dsh_w3", "dsh_w2", "dgates")])
+    wp, wb = _ws(ws)
+    _call("moe_backward", ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(dout), c_float(d_aux), ctypes.byref(S),
+          ctypes.byref(G), wp, wb, _stream(stream))

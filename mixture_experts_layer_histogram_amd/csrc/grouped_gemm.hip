@@ -1020,7 +1020,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
     return hipGetLastError();
   }
   const bool gather = g.perm != nullptr;
-  if (gather && (g.mode >= MODE_DOWN || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
+  if (gather && (g.mode == MODE_LOGITS || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
     return hipErrorInvalidValue;
   if (g.mode == MODE_LOGITS && (g.Nn % 8 != 0 || g.n_seg != 1)) return hipErrorInvalidValue;
   if (g.fp8 && (g.mode == MODE_LOGITS || (g.mode != MODE_DOWN && !gather) || !g.w8 || !g.scale1 ||
@@ -1043,7 +1043,9 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
     if (hb) gather ? launch_bf16<MODE_GELU_UP, true, true>(g, s) : launch_bf16<MODE_GELU_UP, true, false>(g, s);
     else gather ? launch_bf16<MODE_GELU_UP, false, true>(g, s) : launch_bf16<MODE_GELU_UP, false, false>(g, s);
   } else if (g.mode == MODE_DOWN) {
-    hb ? launch_bf16<MODE_DOWN, true, false>(g, s) : launch_bf16<MODE_DOWN, false, false>(g, s);
+    if (gather)   // plain product of gathered token rows (the backward recomputes pre-activations)
+      hb ? launch_bf16<MODE_DOWN, true, true>(g, s) : launch_bf16<MODE_DOWN, false, true>(g, s);
+    else hb ? launch_bf16<MODE_DOWN, true, false>(g, s) : launch_bf16<MODE_DOWN, false, false>(g, s);
   } else {
     g.bias_f32 ? launch_bf16<MODE_LOGITS, true, false>(g, s) : launch_bf16<MODE_LOGITS, false, false>(g, s);
   }

@@ -611,3 +611,213 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
 }
 
 }  // extern "C"
+
+// ===================================================================== backward
+
+namespace {
+
+// Backward workspace: the forward scratch first (tile lists, K-split partials),
+// then the backward's own buffers.
+struct BwdLayout {
+  size_t wt2, wtcat, a1, a3, h, dy, dh, da, dX, dg, dz, dz16, wrt, dxr;
+  size_t wts2, wtscat, a1s, a3s, hs, dhs, das, dxs;
+  size_t total;
+  int ldz;   // K-padded router width for the dx GEMM
+};
+
+BwdLayout backward_layout(const moe_config& c) {
+  BwdLayout B{};
+  const Workspace W = workspace_layout(c);
+  size_t off = scratch_end(W);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t N = (size_t)c.n_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
+  const size_t d = (size_t)c.d_model, F = (size_t)c.d_ff, Fs = (size_t)(c.d_ff_shared > 0 ? c.d_ff_shared : 0);
+  const size_t R = (size_t)expert_rows(c);
+  const bool sw = c.act == MOE_ACT_SWIGLU;
+  const size_t nA = sw ? 2 : 1;
+  B.ldz = ((c.n_experts + 63) / 64) * 64;
+  B.wt2 = take(E * F * d * 2);
+  B.wtcat = take(E * d * nA * F * 2);
+  B.a1 = take(R * F * 2);
+  B.a3 = take(sw ? R * F * 2 : 0);
+  B.h = take(R * F * 2);
+  B.dy = take(R * d * 2);
+  B.dh = take(R * F * 2);
+  B.da = take(R * nA * F * 2);
+  B.dX = take(R * d * 2);
+  B.dg = take(N * k * 4);
+  B.dz = take(N * E * 4);
+  B.dz16 = take(N * (size_t)B.ldz * 2);
+  B.wrt = take(d * (size_t)B.ldz * 2);
+  B.dxr = take(N * d * 2);
+  B.wts2 = take(Fs * d * 2);
+  B.wtscat = take(d * 2 * Fs * 2);
+  B.a1s = take(N * Fs * 2);
+  B.a3s = take(N * Fs * 2);
+  B.hs = take(N * Fs * 2);
+  B.dhs = take(N * Fs * 2);
+  B.das = take(N * 2 * Fs * 2);
+  B.dxs = take(Fs ? N * d * 2 : 0);
+  B.total = off;
+  return B;
+}
+
+// Plain product out[r, :Nn] = a[r, :K] W^T (+ bias) on the grouped GEMM (mode down): segments of
+// the routed layout (shared = false) or one dense segment of N rows (shared = true / router).
+moe_status plain_gemm(const moe_config& c, const Workspace& W, void* ws, bool dense, const void* a,
+                      const int32_t* perm, const int32_t* offsets, const void* w, const void* bias, int K, int Nn,
+                      void* out, hipStream_t s) {
+  GroupedGemmArgs g = gemm_args(c, W, ws, false);
+  if (dense) {
+    g.n_seg = 1;
+    g.max_rows = (int)c.n_tokens;
+    g.offsets = nullptr;
+  } else {
+    g.offsets = offsets;
+  }
+  g.mode = MODE_DOWN;
+  g.perm = perm;
+  g.gather_k = c.top_k;
+  g.a_rows = (int)c.n_tokens;
+  g.K = K;
+  g.Nn = Nn;
+  g.a = a;
+  g.w = w;
+  g.bias = bias;
+  g.out = out;
+  MOE_HIP(launch_grouped_gemm(g, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+  try {
+    MOE_TRY(check_config(cfg));
+    if (!bytes) return MOE_ERR_ARG;
+    *bytes = backward_layout(*cfg).total;
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, const void* dout, float d_aux,
+                        const moe_saved* sv, const moe_grads* gr, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!w || !sv || !gr) return MOE_ERR_ARG;
+    if (isnan(d_aux)) return MOE_ERR_ARG;
+    const bool any = c.n_tokens > 0;
+    const bool sw = c.act == MOE_ACT_SWIGLU;
+    const bool shared = c.d_ff_shared > 0;
+    if (!w->w_router || !w->w1 || !w->w2 || (sw && !w->w3)) return MOE_ERR_ARG;
+    if (c.ffn_bias && (!w->b1 || !w->b2 || !gr->db1 || !gr->db2)) return MOE_ERR_ARG;
+    if (!gr->dw1 || !gr->dw2 || (sw && !gr->dw3)) return MOE_ERR_ARG;
+    if (shared && (!w->sh_w1 || !w->sh_w3 || !w->sh_w2 || !gr->dsh_w1 || !gr->dsh_w3 || !gr->dsh_w2))
+      return MOE_ERR_ARG;
+    if (any && (!x || !dout || !gr->dx || !sv->logits || !sv->topk_idx || !sv->gates || !sv->counts ||
+                !sv->offsets || !sv->perm || !sv->slot_pos || !sv->y_perm))
+      return MOE_ERR_ARG;
+    if (!gather_ok(c)) return MOE_ERR_UNSUPPORTED;
+    const void* ptrs[] = {x, dout, gr->dx, sv->y_perm, w->w_router, w->w1, w->w3, w->w2, w->b1, w->b2,
+                          w->sh_w1, w->sh_w3, w->sh_w2, gr->dw1, gr->dw3, gr->dw2, gr->dw_router};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    const BwdLayout B = backward_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, B.total));
+    const int N = (int)c.n_tokens, E = c.n_experts, k = c.top_k, d = c.d_model, F = c.d_ff;
+    const int Fs = shared ? c.d_ff_shared : 0;
+    const long long R = expert_rows(c);
+    const int nA = sw ? 2 : 1;
+    auto P = [&](size_t o) { return wsp(ws, o); };
+    float* dg = gr->dgates ? gr->dgates : reinterpret_cast<float*>(P(B.dg));
+
+    // weight-only work that does not depend on the batch: transposed copies
+    MOE_HIP(launch_transpose(w->w2, E, d, F, P(B.wt2), d, 0, stream));                  // W2^T [E, F, d]
+    MOE_HIP(launch_transpose(w->w1, E, F, d, P(B.wtcat), nA * F, 0, stream));           // [W1^T | W3^T] [E, d, nA F]
+    if (sw) MOE_HIP(launch_transpose(w->w3, E, F, d, P(B.wtcat), nA * F, F, stream));
+    if (!any) return MOE_OK;
+
+    // combine backward: dL/dgates and dY = g dout on the kept rows
+    MOE_HIP(launch_combine_backward(c, dout, sv->y_perm, sv->slot_pos, sv->gates, dg, P(B.dy), stream));
+    // routed experts: recompute pre-activations, dH, activation backward, dX
+    MOE_TRY(plain_gemm(c, W, ws, false, x, sv->perm, sv->offsets, w->w1, c.ffn_bias ? w->b1 : nullptr, d, F,
+                       P(B.a1), stream));
+    if (sw)
+      MOE_TRY(plain_gemm(c, W, ws, false, x, sv->perm, sv->offsets, w->w3, nullptr, d, F, P(B.a3), stream));
+    MOE_TRY(plain_gemm(c, W, ws, false, P(B.dy), nullptr, sv->offsets, P(B.wt2), nullptr, d, F, P(B.dh), stream));
+    MOE_HIP(launch_act_backward(sw, P(B.a1), sw ? P(B.a3) : nullptr, P(B.dh), R, F, P(B.h), P(B.da), stream));
+    MOE_TRY(plain_gemm(c, W, ws, false, P(B.da), nullptr, sv->offsets, P(B.wtcat), nullptr, nA * F, d, P(B.dX),
+                       stream));
+    // expert weight gradients (reduction over each expert's kept rows)
+    MOE_HIP(launch_wgrad(P(B.dy), d, P(B.h), F, false, sv->offsets, sv->perm, k, 0, E, d, F, gr->dw2, F,
+                         (long long)d * F, stream));
+    MOE_HIP(launch_wgrad(P(B.da), nA * F, x, d, true, sv->offsets, sv->perm, k, 0, E, F, d, gr->dw1, d,
+                         (long long)F * d, stream));
+    if (sw)
+      MOE_HIP(launch_wgrad(reinterpret_cast<uint16_t*>(P(B.da)) + F, nA * F, x, d, true, sv->offsets, sv->perm, k, 0, E,
+                           F, d, gr->dw3, d, (long long)F * d, stream));
+    if (c.ffn_bias) {
+      MOE_HIP(launch_segment_colsum(P(B.da), nA * F, 0, F, sv->offsets, sv->perm, 0, E, gr->db1, stream));
+      MOE_HIP(launch_segment_colsum(P(B.dy), d, 0, d, sv->offsets, sv->perm, 0, E, gr->db2, stream));
+    }
+    // router: dz from the gate gradients (+ aux), then dW_r = dz^T x, d logit_bias, dx_r = dz W_r
+    float* dz = reinterpret_cast<float*>(P(B.dz));
+    MOE_HIP(launch_router_backward(c, sv->logits, sv->topk_idx, sv->gates, dg, d_aux != 0.f ? sv->counts : nullptr,
+                                   d_aux, dz, P(B.dz16), B.ldz, stream));
+    if (gr->dw_router)
+      MOE_HIP(launch_wgrad(P(B.dz16), B.ldz, x, d, false, nullptr, nullptr, 1, N, 1, E, d, gr->dw_router, d, 0,
+                           stream));
+    if (gr->dlogit_bias) MOE_HIP(launch_colsum_f32(dz, N, E, gr->dlogit_bias, stream));
+    MOE_HIP(launch_transpose(w->w_router, 1, E, d, P(B.wrt), B.ldz, 0, stream));       // W_r^T [d, ldz]
+    MOE_HIP(launch_zero_cols(P(B.wrt), d, B.ldz, E, B.ldz, stream));
+    MOE_TRY(plain_gemm(c, W, ws, true, P(B.dz16), nullptr, nullptr, P(B.wrt), nullptr, B.ldz, d, P(B.dxr), stream));
+    // shared expert (dense SwiGLU over all tokens, weight 1)
+    const void* dxs = nullptr;
+    if (shared) {
+      MOE_HIP(launch_transpose(w->sh_w2, 1, d, Fs, P(B.wts2), d, 0, stream));          // sh_w2^T [Fs, d]
+      MOE_HIP(launch_transpose(w->sh_w1, 1, Fs, d, P(B.wtscat), 2 * Fs, 0, stream));   // [sh_w1^T | sh_w3^T] [d, 2Fs]
+      MOE_HIP(launch_transpose(w->sh_w3, 1, Fs, d, P(B.wtscat), 2 * Fs, Fs, stream));
+      auto shared_gemm = [&](const void* a, const void* wt, int K, int Nn, void* out) {
+        GroupedGemmArgs g = gemm_args(c, W, ws, true);
+        g.mode = MODE_DOWN;
+        g.K = K;
+        g.Nn = Nn;
+        g.a = a;
+        g.offsets = nullptr;
+        g.w = wt;
+        g.out = out;
+        return launch_grouped_gemm(g, stream);
+      };
+      MOE_HIP(shared_gemm(x, w->sh_w1, d, Fs, P(B.a1s)));
+      MOE_HIP(shared_gemm(x, w->sh_w3, d, Fs, P(B.a3s)));
+      MOE_HIP(shared_gemm(dout, P(B.wts2), d, Fs, P(B.dhs)));
+      MOE_HIP(launch_act_backward(true, P(B.a1s), P(B.a3s), P(B.dhs), N, Fs, P(B.hs), P(B.das), stream));
+      MOE_HIP(shared_gemm(P(B.das), P(B.wtscat), 2 * Fs, d, P(B.dxs)));
+      MOE_HIP(launch_wgrad(dout, d, P(B.hs), Fs, false, nullptr, nullptr, 1, N, 1, d, Fs, gr->dsh_w2, Fs, 0, stream));
+      MOE_HIP(launch_wgrad(P(B.das), 2 * Fs, x, d, false, nullptr, nullptr, 1, N, 1, Fs, d, gr->dsh_w1, d, 0,
+                           stream));
+      MOE_HIP(launch_wgrad(reinterpret_cast<uint16_t*>(P(B.das)) + Fs, 2 * Fs, x, d, false, nullptr, nullptr, 1, N, 1, Fs,
+                           d, gr->dsh_w3, d, 0, stream));
+      dxs = P(B.dxs);
+    }
+    // dx = residual + scattered expert input gradients + shared + router
+    MOE_HIP(launch_dx_gather(c, c.add_residual ? dout : nullptr, P(B.dX), sv->slot_pos, dxs, P(B.dxr), gr->dx,
+                             stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

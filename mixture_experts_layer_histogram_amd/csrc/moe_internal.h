@@ -141,6 +141,25 @@ size_t grouped_gemm_gather_max_bytes();   // largest token matrix (bytes) the bf
 hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint8_t* q, float* scales,
                                hipStream_t s);
 
+// Backward kernels (backward.hip); bf16 storage.
+hipError_t launch_combine_backward(const moe_config& c, const void* dout, const void* y, const int32_t* slot_pos,
+                                   const float* gates, float* dg, void* dy, hipStream_t s);
+hipError_t launch_transpose(const void* src, int batch, int R, int C, void* dst, int ldd, int col0, hipStream_t s);
+hipError_t launch_zero_cols(void* a, long long rows, int ld, int c0, int c1, hipStream_t s);
+hipError_t launch_act_backward(bool swiglu, const void* a1, const void* a3, const void* dh, long long rows, int F,
+                               void* h, void* da, hipStream_t s);
+hipError_t launch_wgrad(const void* P, int ldp, const void* Q, int ldq, bool gather_q, const int32_t* offsets,
+                        const int32_t* perm, int gk, int dense_rows, int n_seg, int M, int N, float* C, int ldc,
+                        long long strideC, hipStream_t s);
+hipError_t launch_segment_colsum(const void* a, int lda, int col0, int ncols, const int32_t* offsets,
+                                 const int32_t* perm, int dense_rows, int n_seg, float* out, hipStream_t s);
+hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* out, hipStream_t s);
+hipError_t launch_router_backward(const moe_config& c, const float* z, const int32_t* idx, const float* gates,
+                                  const float* dg, const int32_t* counts, float d_aux, float* dz, void* dz16,
+                                  int ldz, hipStream_t s);
+hipError_t launch_dx_gather(const moe_config& c, const void* dout, const void* dX, const int32_t* slot_pos,
+                            const void* dxs, const void* dxr, void* dx, hipStream_t s);
+
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,
                           void* out, hipStream_t s);

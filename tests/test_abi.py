@@ -104,3 +104,30 @@ def test_null_and_workspace_errors_before_launch():
     O = _lib.MoeOutputs(P, *([None] * 12), 0.0)
     assert L.moe_forward(ctypes.byref(cs), ctypes.byref(W), P, None, None, ctypes.byref(O), P, 1 << 40,
                          None) == _lib.MOE_ERR_ARG
+
+
+def test_backward_errors_before_launch():
+    L = M.lib()
+    c = _cfg()
+    P = 4096  # a non-NULL, 256-aligned address that is never dereferenced
+    W = _lib.MoeWeights(P, None, P, P, P, None, None, None, None, None)
+    S = _lib.MoeSaved(*([P] * 8))
+    G = _lib.MoeGrads(P, P, None, P, P, P, *([None] * 6))
+    f = ctypes.c_float
+
+    def call(cfg, Wt=W, Gt=G, dout=P, d_aux=0.0, ws_bytes=1 << 40):
+        return L.moe_backward(ctypes.byref(cfg), ctypes.byref(Wt), P, dout, f(d_aux), ctypes.byref(S),
+                              ctypes.byref(Gt), P, ws_bytes, None)
+
+    n = ctypes.c_size_t(0)
+    assert L.moe_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)) == _lib.MOE_OK and n.value > 0
+    assert call(c, ws_bytes=16) == _lib.MOE_ERR_WORKSPACE
+    assert call(_cfg(dtype="f32")) == _lib.MOE_ERR_UNSUPPORTED          # bf16 storage only
+    assert call(c, d_aux=float("nan")) == _lib.MOE_ERR_ARG
+    assert call(c, dout=None) == _lib.MOE_ERR_ARG
+    assert call(c, dout=P + 2) == _lib.MOE_ERR_UNSUPPORTED              # misaligned
+    G3 = _lib.MoeGrads(P, P, None, P, None, P, *([None] * 6))           # SwiGLU without dW3
+    assert call(c, Gt=G3) == _lib.MOE_ERR_ARG
+    cb = _cfg(act="gelu", ffn_bias=1)                                    # biases without their gradients
+    Wg = _lib.MoeWeights(P, None, P, None, P, P, P, None, None, None)
+    assert call(cb, Wt=Wg) == _lib.MOE_ERR_ARG
