@@ -10,4 +10,5 @@ from .moe_oracle import (to_f64, router_logits, softmax_rows, top_k_desc, route,
                          GATE_TOPK_SOFTMAX, GATE_SOFTMAX_RENORM, GATE_SWITCH_TOP1,
                          E4M3_MAX, e4m3_value, e4m3_round, quantize_fp8_rows, dequantize_fp8_rows,
                          fp8_expert_weights, silu_grad, gelu_grad, softmax_backward, gate_backward,
-                         aux_loss_backward, expert_backward, oracle_layer_backward)
+                         aux_loss_backward, expert_backward, oracle_layer_backward, oracle_backward_rows,
+                         oracle_expert_grad_columns, oracle_shared_grad_columns)

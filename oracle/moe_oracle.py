@@ -497,19 +497,22 @@ def gate_backward(rule: str, z: np.ndarray, idx: np.ndarray, gates: np.ndarray, 
     return dz
 
 
-def aux_loss_backward(counts: np.ndarray, p: np.ndarray, k: int, d_aux: float) -> np.ndarray:
+def aux_loss_backward(counts: np.ndarray, p: np.ndarray, k: int, d_aux: float, n_tokens=None) -> np.ndarray:
     """dL/dz of d_aux * E * sum_e f_e P_e: f (from the discrete counts) is constant,
-    dP_e/dp[t,e] = 1/N, then the softmax Jacobian."""
+    dP_e/dp[t,e] = 1/N, then the softmax Jacobian.  ``p`` may hold a subset of
+    the N tokens' rows when ``n_tokens`` gives N."""
     N, E = p.shape
+    N = N if n_tokens is None else int(n_tokens)
     f = counts.astype(np.float64) / float(N * k)
-    dp = np.broadcast_to(d_aux * E * f / float(N), (N, E))
+    dp = np.broadcast_to(d_aux * E * f / float(N), p.shape)
     return softmax_backward(p, dp)
 
 
-def expert_backward(act: str, X: np.ndarray, w: dict, dY: np.ndarray) -> dict:
-    """Gradients of one expert FFN on its rows X given dL/dY: dX and the weight
-    (and bias) gradients.  SwiGLU: H = SiLU(A1) * A3, A1 = X W1^T, A3 = X W3^T,
-    Y = H W2^T.  GELU: H = GELU(A), A = X W1^T + b1, Y = H W2^T + b2."""
+def expert_backward(act: str, X: np.ndarray, w: dict, dY: np.ndarray, weights: bool = True) -> dict:
+    """Gradients of one expert FFN on its rows X given dL/dY: dX and (unless
+    ``weights`` is False) the weight and bias gradients.  SwiGLU: H = SiLU(A1)
+    * A3, A1 = X W1^T, A3 = X W3^T, Y = H W2^T.  GELU: H = GELU(A), A = X W1^T
+    + b1, Y = H W2^T + b2."""
     g = {}
     if act == "swiglu":
         A1, A3 = X @ w["w1"].T, X @ w["w3"].T
@@ -517,10 +520,12 @@ def expert_backward(act: str, X: np.ndarray, w: dict, dY: np.ndarray) -> dict:
         dH = dY @ w["w2"]
         dA1 = dH * A3 * silu_grad(A1)
         dA3 = dH * silu(A1)
+        g["x"] = dA1 @ w["w1"] + dA3 @ w["w3"]
+        if not weights:
+            return g
         g["w2"] = dY.T @ H
         g["w1"] = dA1.T @ X
         g["w3"] = dA3.T @ X
-        g["x"] = dA1 @ w["w1"] + dA3 @ w["w3"]
     elif act == "gelu":
         A = X @ w["w1"].T
         if w.get("b1") is not None:
@@ -528,13 +533,15 @@ def expert_backward(act: str, X: np.ndarray, w: dict, dY: np.ndarray) -> dict:
         H = gelu(A)
         dH = dY @ w["w2"]
         dA = dH * gelu_grad(A)
+        g["x"] = dA @ w["w1"]
+        if not weights:
+            return g
         g["w2"] = dY.T @ H
         g["w1"] = dA.T @ X
         if w.get("b1") is not None:
             g["b1"] = dA.sum(axis=0)
         if w.get("b2") is not None:
             g["b2"] = dY.sum(axis=0)
-        g["x"] = dA @ w["w1"]
     else:
         raise ValueError(act)
     return g
@@ -604,3 +611,84 @@ def oracle_layer_backward(cfg, inputs, dout, d_aux: float = 0.0, logits_override
         grads["sh_w1"], grads["sh_w3"], grads["sh_w2"] = g["w1"], g["w3"], g["w2"]
     grads["gates"] = dg
     return grads
+
+
+# --------------------------------------------------------------------------- sampled backward (full sizes)
+
+def oracle_backward_rows(cfg, inputs, dout, rows, d_aux: float = 0.0, logits_override=None) -> dict:
+    """The per-token part of ``oracle_layer_backward`` for the tokens ``rows``
+    only: dx [rows, d], the gate gradients [rows, k] and dL/dlogits [rows, E].
+
+    Each of these rows depends on its own token alone once routing is fixed
+    (the aux-loss gradient only through the batch counts): the token's kept
+    experts give dgates and their input gradient, the gate rule maps dgates
+    to dlogits, the router adds dz W_router, plus the shared expert and the
+    residual.  Routing, counts and capacity still cover all N tokens."""
+    dt = cfg.dtype
+    N, k = cfg.n_tokens, cfg.top_k
+    rows = np.asarray(rows, dtype=np.int64)
+    x = to_f64(inputs.x, dt)
+    wr = to_f64(inputs.w_router, dt)
+    z = router_logits(x, wr, inputs.logit_bias) if logits_override is None else \
+        np.asarray(logits_override, dtype=np.float32).astype(np.float64)
+    r = oracle_route(cfg, z, inputs.sel_bias)
+    xr = x[rows]
+    dr = np.asarray(dout, dtype=np.float64)[rows]
+    dx = dr.copy() if cfg.residual else np.zeros_like(xr)
+    dg = np.zeros((rows.size, k))
+    chosen = r.topk_idx[rows]
+    kept = r.disp.slot_pos[rows[:, None] * k + np.arange(k)[None, :]] >= 0
+    for e in np.unique(chosen[kept]):
+        ii, jj = np.nonzero(kept & (chosen == e))
+        w = {n: to_f64(v, dt) for n, v in inputs.expert(int(e)).items()}
+        dg[ii, jj] = np.sum(dr[ii] * expert_apply(cfg.act, xr[ii], w), axis=1)
+        dY = r.gates[rows[ii], jj][:, None] * dr[ii]
+        np.add.at(dx, ii, expert_backward(cfg.act, xr[ii], w, dY, weights=False)["x"])
+    dz = gate_backward(cfg.gate_rule, z[rows], chosen, r.gates[rows], r.probs[rows], dg)
+    if cfg.aux_loss and d_aux != 0.0:
+        dz = dz + aux_loss_backward(r.disp.counts, r.probs[rows], k, d_aux, n_tokens=N)
+    dx += dz @ wr
+    if cfg.d_ff_shared > 0:
+        sw = {"w1": to_f64(inputs.sh_w1, dt), "w3": to_f64(inputs.sh_w3, dt), "w2": to_f64(inputs.sh_w2, dt)}
+        dx += expert_backward("swiglu", xr, sw, dr, weights=False)["x"]
+    return {"x": dx, "gates": dg, "logits": dz, "route": r}
+
+
+def _hidden_subset(w: dict, cols, dt: str) -> dict:
+    cols = np.asarray(cols, dtype=np.int64)
+    sub = {"w1": to_f64(w["w1"][cols], dt), "w2": to_f64(w["w2"][:, cols], dt)}
+    if w.get("w3") is not None:
+        sub["w3"] = to_f64(w["w3"][cols], dt)
+    if w.get("b1") is not None:
+        sub["b1"] = to_f64(w["b1"][cols], dt)
+        sub["b2"] = to_f64(w["b2"], dt)
+    return sub
+
+
+def oracle_expert_grad_columns(cfg, inputs, dout, e: int, cols, route: RouteResult) -> dict:
+    """Weight gradients of routed expert ``e`` restricted to its hidden units
+    ``cols``: w1 / w3 [cols, d], w2 [d, cols], b1 [cols], and b2 [d].
+
+    The activation acts on each hidden unit alone, so these entries are the
+    weight gradients of the smaller FFN that keeps only the units ``cols``,
+    fed the same rows (every kept slot of e) and the same dL/dY = gate * dout."""
+    k = cfg.top_k
+    lo, hi = route.disp.offsets[e], route.disp.offsets[e + 1]
+    slots = route.disp.perm[lo:hi]
+    slots = slots[slots >= 0]
+    t, j = slots // k, slots % k
+    X = to_f64(inputs.x[t], cfg.dtype)
+    dY = route.gates[t, j][:, None] * np.asarray(dout, dtype=np.float64)[t]
+    g = expert_backward(cfg.act, X, _hidden_subset(inputs.expert(e), cols, cfg.dtype), dY)
+    g.pop("x")
+    return g
+
+
+def oracle_shared_grad_columns(cfg, inputs, dout, cols) -> dict:
+    """Shared-expert weight gradients restricted to its hidden units ``cols``
+    (the same argument as ``oracle_expert_grad_columns``; every token's row)."""
+    w = {"w1": inputs.sh_w1, "w3": inputs.sh_w3, "w2": inputs.sh_w2}
+    g = expert_backward("swiglu", to_f64(inputs.x, cfg.dtype), _hidden_subset(w, cols, cfg.dtype),
+                        np.asarray(dout, dtype=np.float64))
+    g.pop("x")
+    return g

@@ -480,26 +480,27 @@ def _torch_layer_loss(cfg, inp, idx, kept, counts, dout, d_aux, params):
     return loss
 
 
-def check_backward_autograd():
-    """The fp64 backward (router, gates for every rule, aux loss, experts with
-    capacity drops, GELU biases, shared expert, residual) against
-    torch.autograd on the same forward written with torch ops."""
-    cases = [
-        MoEConfig(name="bw_a", n_tokens=20, d_model=12, n_experts=5, top_k=2, d_ff=16, act="swiglu",
-                  gate_rule=GATE_TOPK_SOFTMAX, dtype="f32", capacity_factor=1.5, residual=True, seed=31),
-        MoEConfig(name="bw_b", n_tokens=18, d_model=12, n_experts=6, top_k=3, d_ff=10, d_ff_shared=14,
-                  act="swiglu", gate_rule=GATE_SOFTMAX_RENORM, dtype="f32", residual=True,
-                  sel_bias_range=0.05, seed=32),
-        MoEConfig(name="bw_c", n_tokens=22, d_model=10, n_experts=4, top_k=1, d_ff=14, act="gelu", ffn_bias=True,
-                  gate_rule=GATE_SWITCH_TOP1, dtype="f32", capacity_factor=1.0, residual=True, aux_loss=True,
-                  logit_offset=(1, 0.7), init="uniform_experts", seed=33),
-    ]
+_BW_CASES = [
+    MoEConfig(name="bw_a", n_tokens=20, d_model=12, n_experts=5, top_k=2, d_ff=16, act="swiglu",
+              gate_rule=GATE_TOPK_SOFTMAX, dtype="f32", capacity_factor=1.5, residual=True, seed=31),
+    MoEConfig(name="bw_b", n_tokens=18, d_model=12, n_experts=6, top_k=3, d_ff=10, d_ff_shared=14,
+              act="swiglu", gate_rule=GATE_SOFTMAX_RENORM, dtype="f32", residual=True,
+              sel_bias_range=0.05, seed=32),
+    MoEConfig(name="bw_c", n_tokens=22, d_model=10, n_experts=4, top_k=1, d_ff=14, act="gelu", ffn_bias=True,
+              gate_rule=GATE_SWITCH_TOP1, dtype="f32", capacity_factor=1.0, residual=True, aux_loss=True,
+              logit_offset=(1, 0.7), init="uniform_experts", seed=33),
+]
+
+
+def _autograd_cases():
+    """For each backward case: inputs, dout, d_aux and the torch.autograd leaves
+    (x, w_router, logit_bias, every expert's weights, shared weights) after
+    backward() of the layer's forward written with torch ops."""
     rng = np.random.default_rng(34)
-    for cfg in cases:
+    for cfg in _BW_CASES:
         inp = make_inputs(cfg)
         dout = rng.standard_normal((cfg.n_tokens, cfg.d_model))
         d_aux = 0.37 if cfg.aux_loss else 0.0
-        gr = mo.oracle_layer_backward(cfg, inp, dout, d_aux=d_aux)
         r, _ = mo.oracle_layer(cfg, inp)
         kept = (r.disp.slot_pos >= 0).reshape(cfg.n_tokens, cfg.top_k)
         dt = cfg.dtype
@@ -515,20 +516,62 @@ def check_backward_autograd():
         T = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True) for n, v in P.items()}
         loss = _torch_layer_loss(cfg, inp, r.topk_idx, kept, r.disp.counts, dout, d_aux, T)
         loss.backward()
+        yield cfg, inp, dout, d_aux, {n: t.grad.numpy() for n, t in T.items()}
 
-        def close(a, b, what):
-            a, b = np.asarray(a), np.asarray(b)
-            assert np.abs(a - b).max() <= 1e-11 * max(1.0, np.abs(b).max()), (cfg.name, what)
-        close(gr["x"], T["x"].grad.numpy(), "x")
-        close(gr["w_router"], T["w_router"].grad.numpy(), "w_router")
-        close(gr["logit_bias"], T["logit_bias"].grad.numpy(), "logit_bias")
+
+def _close(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, what
+    assert np.abs(a - b).max() <= 1e-11 * max(1.0, np.abs(b).max()), what
+
+
+def check_backward_autograd():
+    """The fp64 backward (router, gates for every rule, aux loss, experts with
+    capacity drops, GELU biases, shared expert, residual) against
+    torch.autograd on the same forward written with torch ops."""
+    for cfg, inp, dout, d_aux, G in _autograd_cases():
+        gr = mo.oracle_layer_backward(cfg, inp, dout, d_aux=d_aux)
+        _close(gr["x"], G["x"], (cfg.name, "x"))
+        _close(gr["w_router"], G["w_router"], (cfg.name, "w_router"))
+        _close(gr["logit_bias"], G["logit_bias"], (cfg.name, "logit_bias"))
         for e in range(cfg.n_experts):
             for n in ("w1", "w3", "w2", "b1", "b2"):
-                if f"{n}_{e}" in T:
-                    close(gr[n][e], T[f"{n}_{e}"].grad.numpy(), f"{n}_{e}")
+                if f"{n}_{e}" in G:
+                    _close(gr[n][e], G[f"{n}_{e}"], (cfg.name, f"{n}_{e}"))
         if cfg.d_ff_shared:
             for n in ("sh_w1", "sh_w3", "sh_w2"):
-                close(gr[n], T[n].grad.numpy(), n)
+                _close(gr[n], G[n], (cfg.name, n))
+
+
+def check_sampled_backward_autograd():
+    """The sampled backward used at full sizes (a subset of token rows; a
+    subset of each expert's hidden units) against torch.autograd: dx rows,
+    expert and shared-expert weight-gradient columns and biases.  Its gate and
+    logit gradients equal the whole-batch oracle's rows."""
+    for cfg, inp, dout, d_aux, G in _autograd_cases():
+        N, F = cfg.n_tokens, cfg.d_ff
+        rows = np.arange(1, N, 3)                       # a strict subset (the aux term's N must stay N)
+        rb = mo.oracle_backward_rows(cfg, inp, dout, rows, d_aux=d_aux)
+        _close(rb["x"], G["x"][rows], (cfg.name, "rows x"))
+        full = mo.oracle_layer_backward(cfg, inp, dout, d_aux=d_aux)
+        _close(rb["gates"], full["gates"][rows], (cfg.name, "rows gates"))
+        _close(rb["logits"], full["logits"][rows], (cfg.name, "rows logits"))
+        cols = np.array([F - 1, 0, F // 2])
+        for e in range(cfg.n_experts):
+            gc = mo.oracle_expert_grad_columns(cfg, inp, dout, e, cols, rb["route"])
+            _close(gc["w1"], G[f"w1_{e}"][cols], (cfg.name, e, "w1 cols"))
+            _close(gc["w2"], G[f"w2_{e}"][:, cols], (cfg.name, e, "w2 cols"))
+            if cfg.act == "swiglu":
+                _close(gc["w3"], G[f"w3_{e}"][cols], (cfg.name, e, "w3 cols"))
+            if cfg.ffn_bias:
+                _close(gc["b1"], G[f"b1_{e}"][cols], (cfg.name, e, "b1 cols"))
+                _close(gc["b2"], G[f"b2_{e}"], (cfg.name, e, "b2"))
+        if cfg.d_ff_shared:
+            sc = np.array([cfg.d_ff_shared - 1, 2])
+            gs = mo.oracle_shared_grad_columns(cfg, inp, dout, sc)
+            _close(gs["w1"], G["sh_w1"][sc], (cfg.name, "sh_w1 cols"))
+            _close(gs["w3"], G["sh_w3"][sc], (cfg.name, "sh_w3 cols"))
+            _close(gs["w2"], G["sh_w2"][:, sc], (cfg.name, "sh_w2 cols"))
 
 
 def check_activation_grads_library():

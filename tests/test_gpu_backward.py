@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import SMALL, TOL, host, rel_err, say
+from gpu_harness import FULL, SMALL, TOL, host, rel_err, say
 from workloads import make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -29,14 +29,11 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).astype(np.float32)).to(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_backward_parity(name):
+def _run_backward(cfg, inp, dout, d_aux):
+    """Forward through the step entry points, then moe_backward; returns the
+    device gradients, the device logits and a callable that repeats the backward."""
     import torch
     import mixture_experts_layer_histogram_amd as M
-    cfg = CASES[name]
-    say(f"backward {name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} F={cfg.d_ff} "
-        f"Fs={cfg.d_ff_shared} rule={cfg.gate_rule}")
-    inp = make_inputs(cfg)
     dev = M.upload_inputs(inp, "cuda")
     c = M.config_from(cfg)
     N, E, k, d, F, Fs = cfg.n_tokens, cfg.n_experts, cfg.top_k, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
@@ -57,11 +54,7 @@ def test_backward_parity(name):
     M.permute(c, idx, None, counts, offs, perm, sp, None, ws=ws)
     M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
     M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
-
-    rng = np.random.default_rng(99)
-    dout_np = rng.standard_normal((N, d)).astype(np.float32)
-    dout = _bf16(dout_np)
-    d_aux = 0.5 if cfg.aux_loss else 0.0
+    del h, ws
     grads = {"dx": torch.empty((N, d), dtype=st, device="cuda"),
              "dw_router": torch.empty((E, d), dtype=f32, device="cuda"),
              "dlogit_bias": torch.empty(E, dtype=f32, device="cuda"),
@@ -80,17 +73,32 @@ def test_backward_parity(name):
     bws = torch.empty(M.backward_workspace_size(c), dtype=torch.uint8, device="cuda")
     saved = {"logits": z, "topk_idx": idx, "gates": g, "counts": counts, "offsets": offs, "perm": perm,
              "slot_pos": sp, "y_perm": y}
-    M.backward(c, dev, dev["x"], dout, saved, grads, d_aux=d_aux, ws=bws)
-    torch.cuda.synchronize()
 
-    dout_ref = host(dout)
-    ref = oracle.oracle_layer_backward(cfg, inp, dout_ref, d_aux=d_aux, logits_override=host(z))
+    def again():
+        M.backward(c, dev, dev["x"], dout, saved, grads, d_aux=d_aux, ws=bws)
+        torch.cuda.synchronize()
+    again()
+    return grads, z, sp, again
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(name):
+    cfg = CASES[name]
+    say(f"backward {name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} F={cfg.d_ff} "
+        f"Fs={cfg.d_ff_shared} rule={cfg.gate_rule}")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(99)
+    dout = _bf16(rng.standard_normal((cfg.n_tokens, cfg.d_model)).astype(np.float32))
+    d_aux = 0.5 if cfg.aux_loss else 0.0
+    grads, z, _, again = _run_backward(cfg, inp, dout, d_aux)
+
+    ref = oracle.oracle_layer_backward(cfg, inp, host(dout), d_aux=d_aux, logits_override=host(z))
     tol = TOL["bf16"]
     checks = [("dx", "x"), ("dw_router", "w_router"), ("dlogit_bias", "logit_bias"), ("dw1", "w1"), ("dw2", "w2"),
               ("dgates", "gates")]
     checks += [("dw3", "w3")] if cfg.act == "swiglu" else []
     checks += [("db1", "b1"), ("db2", "b2")] if cfg.ffn_bias else []
-    checks += [("dsh_w1", "sh_w1"), ("dsh_w3", "sh_w3"), ("dsh_w2", "sh_w2")] if Fs else []
+    checks += [("dsh_w1", "sh_w1"), ("dsh_w3", "sh_w3"), ("dsh_w2", "sh_w2")] if cfg.d_ff_shared else []
     for gk, rk in checks:
         err = rel_err(host(grads[gk]), ref[rk])
         say(f"  {gk}: rel err {err:.3e}")
@@ -98,6 +106,82 @@ def test_backward_parity(name):
     # deterministic: a second call gives the same bits
     dx1 = host(grads["dx"]).copy()
     w1a = host(grads["dw1"]).copy()
-    M.backward(c, dev, dev["x"], dout, saved, grads, d_aux=d_aux, ws=bws)
-    torch.cuda.synchronize()
+    again()
     assert np.array_equal(host(grads["dx"]), dx1) and np.array_equal(host(grads["dw1"]), w1a)
+
+
+def _sample_rows(cfg, slot_pos, n=12):
+    N = cfg.n_tokens
+    rows = set(np.linspace(0, N - 1, min(n, N)).astype(int).tolist())
+    dropped = np.nonzero((slot_pos.reshape(N, cfg.top_k) < 0).any(axis=1))[0]
+    rows.update(dropped[:4].tolist())                       # tokens with a dropped slot
+    return np.array(sorted(rows))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral_prefill", "mixtral_decode", "switch_skewed", "deepseek_v3"])
+def test_backward_full_size(name):
+    """Full sizes: dx and dgates on sampled tokens, the weight gradients of
+    sampled hidden units of the busiest, the least busy and the first expert
+    (and of the shared expert), each computed by the oracle one by one; the
+    router gradients through a property of every softmax-based gate rule
+    (each token's logit gradient sums to zero over the experts, so the expert
+    sums of dlogit_bias and of dw_router vanish)."""
+    import torch
+    cfg = FULL[name]
+    say(f"backward full {name}: generating inputs")
+    inp = make_inputs(cfg)
+    N, E, d, F, Fs = cfg.n_tokens, cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    gen = torch.Generator(device="cuda").manual_seed(98)
+    dout = (torch.randn((N, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    d_aux = 0.5 if cfg.aux_loss else 0.0
+    say(f"backward full {name}: forward + backward")
+    grads, z, sp, _ = _run_backward(cfg, inp, dout, d_aux)
+    dout_h, sp_h = host(dout), host(sp)
+    tol = TOL["bf16"]
+
+    rows = _sample_rows(cfg, sp_h)
+    say(f"backward full {name}: oracle on {rows.size} sampled tokens")
+    rb = oracle.oracle_backward_rows(cfg, inp, dout_h, rows, d_aux=d_aux, logits_override=host(z))
+    rows_t = torch.from_numpy(rows).cuda()
+    for gk, ref in (("dx", rb["x"]), ("dgates", rb["gates"])):
+        err = rel_err(host(grads[gk].index_select(0, rows_t)), ref)
+        say(f"  {gk} rows: rel err {err:.3e}")
+        assert err <= tol, (name, gk, err)
+
+    kept = rb["route"].disp.offsets[1:] - rb["route"].disp.offsets[:-1]
+    busy = [int(np.argmax(kept)), int(np.argmin(np.where(kept > 0, kept, kept.max() + 1))), 0]
+    cols = np.array(sorted({0, F // 3, F - 1}))
+    cols_t = torch.from_numpy(cols).cuda()
+    for e in dict.fromkeys(busy):
+        if kept[e] == 0:
+            continue
+        gc = oracle.oracle_expert_grad_columns(cfg, inp, dout_h, e, cols, rb["route"])
+        got = {"w1": grads["dw1"][e].index_select(0, cols_t), "w2": grads["dw2"][e].index_select(1, cols_t)}
+        if cfg.act == "swiglu":
+            got["w3"] = grads["dw3"][e].index_select(0, cols_t)
+        if cfg.ffn_bias:
+            got["b1"] = grads["db1"][e].index_select(0, cols_t)
+            got["b2"] = grads["db2"][e]
+        for n, t in got.items():
+            err = rel_err(host(t), gc[n])
+            say(f"  expert {e} ({kept[e]} rows) d{n} cols: rel err {err:.3e}")
+            assert err <= tol, (name, e, n, err)
+    if Fs:
+        sc = np.array([0, Fs // 2, Fs - 1])
+        sc_t = torch.from_numpy(sc).cuda()
+        gs = oracle.oracle_shared_grad_columns(cfg, inp, dout_h, sc)
+        for n, t in (("w1", grads["dsh_w1"].index_select(0, sc_t)), ("w3", grads["dsh_w3"].index_select(0, sc_t)),
+                     ("w2", grads["dsh_w2"].index_select(1, sc_t))):
+            err = rel_err(host(t), gs[n])
+            say(f"  shared dsh_{n} cols: rel err {err:.3e}")
+            assert err <= tol, (name, "sh", n, err)
+
+    # router: sum over experts of each token's dlogits is zero
+    db = host(grads["dlogit_bias"])
+    dwr = grads["dw_router"]
+    s_db = abs(float(db.sum())) / max(float(np.abs(db).max()), 1e-30)
+    s_wr = float(dwr.double().sum(0).abs().max()) / max(float(dwr.abs().max()), 1e-30)
+    say(f"  router: |sum_e dlogit_bias| {s_db:.3e}, |sum_e dw_router| {s_wr:.3e} (relative)")
+    assert s_db <= 1e-3 and s_wr <= tol

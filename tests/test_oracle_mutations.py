@@ -11,7 +11,7 @@ import pytest
 import oracle.moe_oracle as mo
 import pin_checks as pc
 
-_orig = {n: getattr(mo, n) for n in ("e4m3_round", "quantize_fp8_rows", "gate_backward", "silu_grad", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
+_orig = {n: getattr(mo, n) for n in ("aux_loss_backward", "e4m3_round", "quantize_fp8_rows", "gate_backward", "silu_grad", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
                                        "aux_loss", "bias_step", "softmax_rows", "oracle_layer")}
 
 
@@ -85,6 +85,10 @@ def _gate_backward_no_centering(rule, z, idx, gates, p, dg):
     return dz
 
 
+def _aux_backward_subset_n(counts, p, k, d_aux, n_tokens=None):
+    return _orig["aux_loss_backward"](counts, p, k, d_aux)     # takes N from the rows it was given
+
+
 def _silu_grad_sigmoid_only(u):
     return 1.0 / (1.0 + np.exp(-u))
 
@@ -126,6 +130,7 @@ def _quantize_fnuz_max(w):
 
 MUTATIONS = [
     ("gate_backward", _gate_backward_no_centering, [pc.check_backward_autograd]),
+    ("aux_loss_backward", _aux_backward_subset_n, [pc.check_sampled_backward_autograd]),
     ("silu_grad", _silu_grad_sigmoid_only, [pc.check_activation_grads_library, pc.check_backward_autograd]),
     ("e4m3_round", _e4m3_ties_away, [pc.check_e4m3_ties_to_even, pc.check_e4m3_rounding_library]),
     ("quantize_fp8_rows", _quantize_fnuz_max, [pc.check_fp8_quantize_rows]),
