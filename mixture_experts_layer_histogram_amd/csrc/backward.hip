@@ -54,7 +54,41 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const T* __restri
 
 // ----------------------------------------------------------------- transposes
 // dst[b][c][col0 + r] = src[b][r][c] for a batch of [R, C] matrices (bf16),
-// dst row stride ldd.  64 x 64 tiles through LDS.
+// dst row stride ldd, through 64 x 64 LDS tiles.
+//
+// 16-byte form (R, C, ldd, col0 multiples of 8): each thread moves two
+// 8-element row chunks in and two 8-element column chunks out, so global
+// reads and writes are whole 128-byte lines per 8 lanes.  In LDS the 16-byte
+// chunk c of tile row r sits at chunk c ^ ((r >> 3) & 7): the eight lanes
+// that read one column at rows 8i + j then hit eight different chunks.
+__global__ __launch_bounds__(256) void transpose8_kernel(const uint16_t* __restrict__ src, int R, int C,
+                                                         uint16_t* __restrict__ dst, int ldd, int col0) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + (size_t)b * R * C;
+  uint16_t* o = dst + (size_t)b * C * ldd;
+#pragma unroll
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int rr = q >> 3, ch = q & 7;
+    if (r0 + rr < R && c0 + ch * 8 < C)
+      *reinterpret_cast<uint4*>(tile + rr * 64 + ((ch ^ ((rr >> 3) & 7)) << 3)) =
+          *reinterpret_cast<const uint4*>(s + (size_t)(r0 + rr) * C + c0 + ch * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int cc = q >> 3, i = q & 7;      // output row c0 + cc, source rows 8 i .. 8 i + 7
+    if (c0 + cc < C && r0 + 8 * i < R) {
+      Vec8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v.e[j] = tile[(8 * i + j) * 64 + ((((cc >> 3) ^ i) & 7) << 3) + (cc & 7)];
+      *reinterpret_cast<uint4*>(o + (size_t)(c0 + cc) * ldd + col0 + r0 + 8 * i) = v.u;
+    }
+  }
+}
+
+// Element form for other shapes.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int R, int C,
                                                         uint16_t* __restrict__ dst, int ldd, int col0) {
   __shared__ uint16_t tile[64][65];
@@ -89,27 +123,46 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ a
 // [dA] (stride F).
 __device__ __forceinline__ float sigmoid_f(float u) { return 1.0f / (1.0f + __expf(-u)); }
 
+// One thread per 8 consecutive hidden units of a row (F a multiple of 8).
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void act_backward_kernel(const uint16_t* __restrict__ a1,
                                                            const uint16_t* __restrict__ a3,
                                                            const uint16_t* __restrict__ dh, long long rows, int F,
                                                            uint16_t* __restrict__ h, uint16_t* __restrict__ da) {
+  const int F8 = F >> 3;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * F) return;
-  const long long r = i / F;
-  const int f = (int)(i % F);
-  const float u = bf16_to_f32(a1[i]), g = bf16_to_f32(dh[i]);
+  if (i >= rows * F8) return;
+  const long long r = i / F8;
+  const int f = (int)(i % F8) * 8;
+  const size_t e = (size_t)r * F + f;
+  Vec8 u, g, hv, d1, d3;
+  u.u = *reinterpret_cast<const uint4*>(a1 + e);
+  g.u = *reinterpret_cast<const uint4*>(dh + e);
   if (SWIGLU) {
-    const float v = bf16_to_f32(a3[i]);
-    const float sg = sigmoid_f(u), si = u * sg;
-    h[i] = f32_to_bf16(si * v);
-    da[(size_t)r * 2 * F + f] = f32_to_bf16(g * v * (sg * (1.0f + u * (1.0f - sg))));
-    da[(size_t)r * 2 * F + F + f] = f32_to_bf16(g * si);
+    Vec8 v;
+    v.u = *reinterpret_cast<const uint4*>(a3 + e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float uu = bf16_to_f32(u.e[j]), gg = bf16_to_f32(g.e[j]), vv = bf16_to_f32(v.e[j]);
+      const float sg = sigmoid_f(uu), si = uu * sg;
+      hv.e[j] = f32_to_bf16(si * vv);
+      d1.e[j] = f32_to_bf16(gg * vv * (sg * (1.0f + uu * (1.0f - sg))));
+      d3.e[j] = f32_to_bf16(gg * si);
+    }
+    *reinterpret_cast<uint4*>(h + e) = hv.u;
+    *reinterpret_cast<uint4*>(da + (size_t)r * 2 * F + f) = d1.u;
+    *reinterpret_cast<uint4*>(da + (size_t)r * 2 * F + F + f) = d3.u;
   } else {
-    const float cdf = 0.5f * erfcf(-u * 0.70710678118654752f);
-    const float pdf = 0.39894228040143268f * __expf(-0.5f * u * u);
-    h[i] = f32_to_bf16(u * cdf);
-    da[i] = f32_to_bf16(g * (cdf + u * pdf));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float uu = bf16_to_f32(u.e[j]), gg = bf16_to_f32(g.e[j]);
+      const float cdf = 0.5f * erfcf(-uu * 0.70710678118654752f);
+      const float pdf = 0.39894228040143268f * __expf(-0.5f * uu * uu);
+      hv.e[j] = f32_to_bf16(uu * cdf);
+      d1.e[j] = f32_to_bf16(gg * (cdf + uu * pdf));
+    }
+    *reinterpret_cast<uint4*>(h + e) = hv.u;
+    *reinterpret_cast<uint4*>(da + e) = d1.u;
   }
 }
 
@@ -230,7 +283,47 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const uint16_t* __restric
 
 // ----------------------------------------------------------------- column sums per segment
 // Bias gradients: out[e][c] = sum over the segment's valid rows of a[r][col0 + c]
-// (fp32, rows in ascending order).  One thread per (segment, column).
+// (fp32).  Block = (512-column group, segment): each thread owns 8 adjacent
+// columns (one 16-byte load per row), the 8 waves take every 8th row, and the
+// wave partials are added in wave order, so the result is deterministic.
+// Needs lda, col0 and ncols multiples of 8 (the scalar kernel below otherwise).
+__global__ __launch_bounds__(512) void segment_colsum8_kernel(const uint16_t* __restrict__ a, int lda, int col0,
+                                                              int ncols, const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ perm, int dense_rows,
+                                                              float* __restrict__ out) {
+  __shared__ float red[8][512];
+  const int e = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c0 = blockIdx.x * 512 + lane * 8;
+  const int lo = offsets ? offsets[e] : 0, hi = offsets ? offsets[e + 1] : dense_rows;
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.f;
+  if (c0 < ncols) {
+    for (int r = lo + wave; r < hi; r += 8) {
+      if (perm != nullptr && perm[r] < 0) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(a + (size_t)r * lda + col0 + c0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[2 * i] += __uint_as_float(w[i] << 16);
+        s[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = s[i];
+  __syncthreads();
+  const int c = blockIdx.x * 512 + threadIdx.x;
+  if (c < ncols) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) t += red[w][threadIdx.x];
+    out[(size_t)e * ncols + c] = t;
+  }
+}
+
+// Scalar form for unaligned strides: one thread per (segment, column), rows in order.
 __global__ __launch_bounds__(256) void segment_colsum_kernel(const uint16_t* __restrict__ a, int lda, int col0,
                                                              int ncols, const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ perm, int dense_rows,
@@ -245,13 +338,40 @@ __global__ __launch_bounds__(256) void segment_colsum_kernel(const uint16_t* __r
   out[i] = s;
 }
 
-__global__ __launch_bounds__(256) void colsum_f32_kernel(const float* __restrict__ a, int rows, int cols,
-                                                         float* __restrict__ out) {
-  const int cc = blockIdx.x * blockDim.x + threadIdx.x;
-  if (cc >= cols) return;
+// Column sums of an fp32 [rows, cols] matrix in two deterministic passes:
+// block b adds rows [256 b, 256 b + 256) of every column (wave w takes the
+// rows = w mod 4; the four wave sums are added in order) into part[b][c];
+// the second pass adds the chunk sums in ascending chunk order.
+constexpr int kColsumChunk = 256;
+
+__global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ a, int rows, int cols,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.x * kColsumChunk, r1 = min(rows, r0 + kColsumChunk);
+  for (int cb = 0; cb < cols; cb += 64) {
+    const int c = cb + lane;
+    float s = 0.f;
+    if (c < cols) {
+#pragma unroll 8
+      for (int r = r0 + wave; r < r1; r += 4) s += a[(size_t)r * cols + c];
+    }
+    red[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && c < cols)
+      part[(size_t)blockIdx.x * cols + c] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nchunk, int cols,
+                                                           float* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
   float s = 0.f;
-  for (int r = 0; r < rows; ++r) s += a[(size_t)r * cols + cc];
-  out[cc] = s;
+#pragma unroll 8
+  for (int i = 0; i < nchunk; ++i) s += part[(size_t)i * cols + c];
+  out[c] = s;
 }
 
 // ----------------------------------------------------------------- router backward
@@ -357,7 +477,9 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dout, const 
 
 hipError_t launch_transpose(const void* src, int batch, int R, int C, void* dst, int ldd, int col0, hipStream_t s) {
   if (batch == 0 || R == 0 || C == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64, batch), dim3(256), 0, s,
+  const bool vec = R % 8 == 0 && C % 8 == 0 && ldd % 8 == 0 && col0 % 8 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+  hipLaunchKernelGGL(vec ? transpose8_kernel : transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64, batch), dim3(256), 0, s,
                      (const uint16_t*)src, R, C, (uint16_t*)dst, ldd, col0);
   return hipGetLastError();
 }
@@ -372,7 +494,8 @@ hipError_t launch_zero_cols(void* a, long long rows, int ld, int c0, int c1, hip
 
 hipError_t launch_act_backward(bool swiglu, const void* a1, const void* a3, const void* dh, long long rows, int F,
                                void* h, void* da, hipStream_t s) {
-  const long long n = rows * F;
+  if (F % 8 != 0) return hipErrorInvalidValue;
+  const long long n = rows * (F / 8);
   if (n == 0) return hipSuccess;
   const dim3 g((unsigned)((n + 255) / 256));
   if (swiglu)
@@ -402,14 +525,26 @@ hipError_t launch_segment_colsum(const void* a, int lda, int col0, int ncols, co
                                  const int32_t* perm, int dense_rows, int n_seg, float* out, hipStream_t s) {
   const long long n = (long long)n_seg * ncols;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint16_t*)a,
-                     lda, col0, ncols, offsets, perm, dense_rows, n_seg, out);
+  if (lda % 8 == 0 && col0 % 8 == 0 && ncols % 8 == 0 && (reinterpret_cast<uintptr_t>(a) & 15) == 0) {
+    hipLaunchKernelGGL(segment_colsum8_kernel, dim3((unsigned)((ncols + 511) / 512), (unsigned)n_seg), dim3(512), 0,
+                       s, (const uint16_t*)a, lda, col0, ncols, offsets, perm, dense_rows, out);
+  } else {
+    hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)a, lda, col0, ncols, offsets, perm, dense_rows, n_seg, out);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* out, hipStream_t s) {
+size_t colsum_part_floats(int rows, int cols) {
+  return (size_t)((rows + kColsumChunk - 1) / kColsumChunk) * (size_t)cols;
+}
+
+hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* part, float* out, hipStream_t s) {
   if (cols == 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_f32_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, a, rows, cols, out);
+  const int nchunk = (rows + kColsumChunk - 1) / kColsumChunk;
+  if (nchunk > 0)
+    hipLaunchKernelGGL(colsum_part_kernel, dim3(nchunk), dim3(256), 0, s, a, rows, cols, part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part, nchunk, cols, out);
   return hipGetLastError();
 }
 

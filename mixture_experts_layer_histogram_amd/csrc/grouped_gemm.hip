@@ -113,10 +113,6 @@ constexpr int kOobOffset = 0x7fff0000;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-union Vec8 {
-  uint4 u;
-  uint16_t e[8];
-};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);

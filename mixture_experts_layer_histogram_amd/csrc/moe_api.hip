@@ -619,7 +619,7 @@ namespace {
 // Backward workspace: the forward scratch first (tile lists, K-split partials),
 // then the backward's own buffers.
 struct BwdLayout {
-  size_t wt2, wtcat, a1, a3, h, dy, dh, da, dX, dg, dz, dz16, wrt, dxr;
+  size_t wt2, wtcat, a1, a3, h, dy, dh, da, dX, dg, dz, dz16, wrt, dxr, zpart;
   size_t wts2, wtscat, a1s, a3s, hs, dhs, das, dxs;
   size_t total;
   int ldz;   // K-padded router width for the dx GEMM
@@ -654,6 +654,7 @@ BwdLayout backward_layout(const moe_config& c) {
   B.dz16 = take(N * (size_t)B.ldz * 2);
   B.wrt = take(d * (size_t)B.ldz * 2);
   B.dxr = take(N * d * 2);
+  B.zpart = take(colsum_part_floats((int)N, (int)E) * 4);
   B.wts2 = take(Fs * d * 2);
   B.wtscat = take(d * 2 * Fs * 2);
   B.a1s = take(N * Fs * 2);
@@ -778,7 +779,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     if (gr->dw_router)
       MOE_HIP(launch_wgrad(P(B.dz16), B.ldz, x, d, false, nullptr, nullptr, 1, N, 1, E, d, gr->dw_router, d, 0,
                            stream));
-    if (gr->dlogit_bias) MOE_HIP(launch_colsum_f32(dz, N, E, gr->dlogit_bias, stream));
+    if (gr->dlogit_bias)
+      MOE_HIP(launch_colsum_f32(dz, N, E, reinterpret_cast<float*>(P(B.zpart)), gr->dlogit_bias, stream));
     MOE_HIP(launch_transpose(w->w_router, 1, E, d, P(B.wrt), B.ldz, 0, stream));       // W_r^T [d, ldz]
     MOE_HIP(launch_zero_cols(P(B.wrt), d, B.ldz, E, B.ldz, stream));
     MOE_TRY(plain_gemm(c, W, ws, true, P(B.dz16), nullptr, nullptr, P(B.wrt), nullptr, B.ldz, d, P(B.dxr), stream));

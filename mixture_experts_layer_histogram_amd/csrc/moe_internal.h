@@ -33,6 +33,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Eight bf16 values as one 16-byte load or store.
+union Vec8 {
+  uint4 u;
+  uint16_t e[8];
+};
+
 template <typename T> struct Store;
 template <> struct Store<float> {
   static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
@@ -153,7 +159,8 @@ hipError_t launch_wgrad(const void* P, int ldp, const void* Q, int ldq, bool gat
                         long long strideC, hipStream_t s);
 hipError_t launch_segment_colsum(const void* a, int lda, int col0, int ncols, const int32_t* offsets,
                                  const int32_t* perm, int dense_rows, int n_seg, float* out, hipStream_t s);
-hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* out, hipStream_t s);
+size_t colsum_part_floats(int rows, int cols);   // scratch of launch_colsum_f32
+hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* part, float* out, hipStream_t s);
 hipError_t launch_router_backward(const moe_config& c, const float* z, const int32_t* idx, const float* gates,
                                   const float* dg, const int32_t* counts, float d_aux, float* dz, void* dz16,
                                   int ldz, hipStream_t s);
