@@ -300,7 +300,6 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        const void* residual, const float* sel_bias, const moe_outputs* o,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Static text for a status code. */
 /* ------------------------------------------------------------------ backward
  * Gradients of the layer for an upstream gradient `dout` of `out` and `d_aux`
  * of the auxiliary loss ([L] "The load balance problem": the aux loss is a
@@ -344,12 +343,20 @@ typedef struct moe_grads {      /* device outputs; fp32 unless noted */
  * pre-activations and intermediate gradients).  Host only. */
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 
-/* x [N, d], dout [N, d] (storage dtype), weights as for moe_forward.  d_aux is
- * used when the router's aux loss is wanted (pass 0 otherwise). */
+/* x [N, d], dout [N, d] (storage dtype), weights as for moe_forward; `saved`
+ * holds the forward state of the same inputs (caller-owned device buffers,
+ * read only).  d_aux multiplies the aux-loss gradient (pass 0 when the loss is
+ * not used).  Every gradient is overwritten, not accumulated; unused experts
+ * get zero weight gradients.  The call is deterministic (no atomics).
+ * Errors, before any launch: MOE_ERR_ARG for a missing required pointer or a
+ * NaN d_aux; MOE_ERR_UNSUPPORTED for fp32 storage, a pointer not 16-byte
+ * aligned, or a token matrix beyond the 32-bit gather offsets; MOE_ERR_WORKSPACE
+ * when ws_bytes is below moe_backward_workspace_size. */
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, const void* dout,
                         float d_aux, const moe_saved* saved, const moe_grads* grads, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Static text for a status code. */
 const char* moe_status_str(moe_status s);
 
 #ifdef __cplusplus

@@ -9,10 +9,12 @@
 // taken as fixed; gradients flow through the gate weights, the kept slots'
 // expert FFNs, the shared expert and the residual.
 //
-// Products run on the grouped GEMM of the forward pass (transposed weight
-// copies make every operand contiguous along its reduction axis) and on the
-// ragged-reduction kernel below for the weight gradients, whose reduction
-// runs over each expert's rows.
+// Products with the weights in their stored layout and the weight gradients
+// (reductions over each expert's rows) run on the K-major tile kernels of
+// xgemm.hip; the pre-activations are recomputed on the forward's grouped GEMM.
+// The element kernels here: combine backward, activation backward, router
+// backward, bias and logit-bias column sums, the expert-order row gather, and
+// the final scatter of dx.
 #include "moe_internal.h"
 
 #include <math.h>
@@ -52,68 +54,31 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const T* __restri
   if (lane == 0) dg[s] = acc;
 }
 
-// ----------------------------------------------------------------- transposes
-// dst[b][c][col0 + r] = src[b][r][c] for a batch of [R, C] matrices (bf16),
-// dst row stride ldd, through 64 x 64 LDS tiles.
-//
-// 16-byte form (R, C, ldd, col0 multiples of 8): each thread moves two
-// 8-element row chunks in and two 8-element column chunks out, so global
-// reads and writes are whole 128-byte lines per 8 lanes.  In LDS the 16-byte
-// chunk c of tile row r sits at chunk c ^ ((r >> 3) & 7): the eight lanes
-// that read one column at rows 8i + j then hit eight different chunks.
-__global__ __launch_bounds__(256) void transpose8_kernel(const uint16_t* __restrict__ src, int R, int C,
-                                                         uint16_t* __restrict__ dst, int ldd, int col0) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
-  const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* s = src + (size_t)b * R * C;
-  uint16_t* o = dst + (size_t)b * C * ldd;
-#pragma unroll
-  for (int q = threadIdx.x; q < 512; q += 256) {
-    const int rr = q >> 3, ch = q & 7;
-    if (r0 + rr < R && c0 + ch * 8 < C)
-      *reinterpret_cast<uint4*>(tile + rr * 64 + ((ch ^ ((rr >> 3) & 7)) << 3)) =
-          *reinterpret_cast<const uint4*>(s + (size_t)(r0 + rr) * C + c0 + ch * 8);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = threadIdx.x; q < 512; q += 256) {
-    const int cc = q >> 3, i = q & 7;      // output row c0 + cc, source rows 8 i .. 8 i + 7
-    if (c0 + cc < C && r0 + 8 * i < R) {
-      Vec8 v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v.e[j] = tile[(8 * i + j) * 64 + ((((cc >> 3) ^ i) & 7) << 3) + (cc & 7)];
-      *reinterpret_cast<uint4*>(o + (size_t)(c0 + cc) * ldd + col0 + r0 + 8 * i) = v.u;
+// ----------------------------------------------------------------- expert-order rows
+// For the expert-order rows r < offsets[n_seg]: xg[r] = x[perm[r] / k] (the
+// token row of the slot), and for padding rows of the [E, C] layout (perm < 0)
+// xg[r] = 0 and dy[r] = 0, so every product over expert-order rows sees zeros
+// there.  One wavefront per row, 16-byte lanes (d a multiple of 8).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets, int n_seg, int k,
+                                                          int d, uint16_t* __restrict__ xg, uint16_t* __restrict__ dy) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long r = (long long)blockIdx.x * 4 + wave;
+  if (r >= offsets[n_seg]) return;
+  const int pr = perm[r];
+  uint4* dst = reinterpret_cast<uint4*>(xg + (size_t)r * d);
+  const int n8 = d / 8;
+  if (pr >= 0) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)(pr / k) * d);
+    for (int c = lane; c < n8; c += 64) dst[c] = src[c];
+  } else {
+    uint4* dyr = reinterpret_cast<uint4*>(dy + (size_t)r * d);
+    for (int c = lane; c < n8; c += 64) {
+      dst[c] = uint4{0, 0, 0, 0};
+      dyr[c] = uint4{0, 0, 0, 0};
     }
   }
-}
-
-// Element form for other shapes.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int R, int C,
-                                                        uint16_t* __restrict__ dst, int ldd, int col0) {
-  __shared__ uint16_t tile[64][65];
-  const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* s = src + (size_t)b * R * C;
-  uint16_t* o = dst + (size_t)b * C * ldd;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;
-    if (r0 + rr < R && c0 + cc < C) tile[rr][cc] = s[(size_t)(r0 + rr) * C + c0 + cc];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    if (r0 + rr < R && c0 + cc < C) o[(size_t)(c0 + cc) * ldd + col0 + r0 + rr] = tile[rr][cc];
-  }
-}
-
-// Zero columns [c0, c1) of a [rows, ld] bf16 matrix (K padding of a GEMM operand).
-__global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ a, long long rows, int ld, int c0,
-                                                        int c1) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int w = c1 - c0;
-  if (w <= 0 || i >= rows * w) return;
-  a[(size_t)(i / w) * ld + c0 + (int)(i % w)] = 0;
 }
 
 // ----------------------------------------------------------------- activation backward
@@ -164,121 +129,6 @@ __global__ __launch_bounds__(256) void act_backward_kernel(const uint16_t* __res
     *reinterpret_cast<uint4*>(h + e) = hv.u;
     *reinterpret_cast<uint4*>(da + e) = d1.u;
   }
-}
-
-// ----------------------------------------------------------------- ragged-reduction GEMM
-// Weight gradients: for each segment e (rows [offsets[e], offsets[e+1]), rows
-// with perm < 0 skipped), C_e[m, n] = sum_r P[r, m] Q[r, n] in fp32, written
-// to C + e * strideC (row stride ldc).  Q rows may be gathered token rows
-// (Q row r = Qsrc[perm[r] / gk]).  P and Q are bf16 row-major with row
-// strides ldp, ldq.
-//
-// 128 x 128 output tile per workgroup (4 wavefronts 2 x 2, each 64 x 64 =
-// 2 x 2 MFMA 32x32x16 blocks).  K step = 32 rows: each thread loads two
-// 16-byte pieces (rows r, r+1 of one 8-column chunk) per operand into
-// registers, then writes them to LDS transposed ([column][row], rows padded
-// to 40 elements) as 8 packed row pairs, so the MFMA fragments (8
-// consecutive rows of one column) are single 16-byte LDS reads.  Two LDS
-// stages; the next step's global loads are in flight during this step's
-// MFMAs.
-constexpr int kWgLd = 40;                       // LDS row length (elements) of the transposed tiles
-
-template <bool GATHER_Q>
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(const uint16_t* __restrict__ P, int ldp,
-                                                       const uint16_t* __restrict__ Q, int ldq,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ perm, int gk, int dense_rows,
-                                                       int M, int N, float* __restrict__ C, int ldc,
-                                                       long long strideC) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][128 * kWgLd];
-  const int tiles_n = (N + 127) / 128;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int e = blockIdx.y;
-  const int m0 = tm * 128, n0 = tn * 128;
-  const int r_lo = offsets ? offsets[e] : 0;
-  const int r_hi = offsets ? offsets[e + 1] : dense_rows;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, kh = lane >> 5;
-  // loader: thread -> row pair rp (rows 2rp, 2rp+1 of the step), column chunk c (8 columns)
-  const int rp = tid & 15, c = tid >> 4;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  uint4 pv[2], qv[2];
-  auto load = [&](int r0) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = r0 + 2 * rp + h;
-      bool ok = r < r_hi;
-      int qrow = r;
-      if (ok && perm != nullptr) {
-        const int pr = perm[r];
-        ok = pr >= 0;
-        if (GATHER_Q) qrow = pr / gk;
-      }
-      const int mc = m0 + 8 * c, nc = n0 + 8 * c;
-      pv[h] = (ok && mc < M) ? *reinterpret_cast<const uint4*>(P + (size_t)r * ldp + mc) : uint4{0, 0, 0, 0};
-      qv[h] = (ok && nc < N) ? *reinterpret_cast<const uint4*>(Q + (size_t)qrow * ldq + nc) : uint4{0, 0, 0, 0};
-    }
-  };
-  auto store = [&](int st) {
-    uint32_t* lp = reinterpret_cast<uint32_t*>(lds[st][0]);
-    uint32_t* lq = reinterpret_cast<uint32_t*>(lds[st][1]);
-    const uint16_t* p0 = reinterpret_cast<const uint16_t*>(&pv[0]);
-    const uint16_t* p1 = reinterpret_cast<const uint16_t*>(&pv[1]);
-    const uint16_t* q0 = reinterpret_cast<const uint16_t*>(&qv[0]);
-    const uint16_t* q1 = reinterpret_cast<const uint16_t*>(&qv[1]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lp[((8 * c + i) * kWgLd) / 2 + rp] = (uint32_t)p0[i] | ((uint32_t)p1[i] << 16);
-      lq[((8 * c + i) * kWgLd) / 2 + rp] = (uint32_t)q0[i] | ((uint32_t)q1[i] << 16);
-    }
-  };
-
-  const int steps = (r_hi - r_lo + 31) / 32;
-  if (steps > 0) {
-    load(r_lo);
-    store(0);
-    __syncthreads();
-  }
-  for (int s = 0; s < steps; ++s) {
-    const int st = s & 1;
-    if (s + 1 < steps) load(r_lo + 32 * (s + 1));
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        fa[x] = *reinterpret_cast<const bf16x8*>(&lds[st][0][(wm * 64 + 32 * x + l32) * kWgLd + 16 * kk + 8 * kh]);
-        fb[x] = *reinterpret_cast<const bf16x8*>(&lds[st][1][(wn * 64 + 32 * x + l32) * kWgLd + 16 * kk + 8 * kh]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (s + 1 < steps) store(st ^ 1);
-    __syncthreads();
-  }
-  float* out = C + (size_t)e * strideC;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int n = n0 + wn * 64 + ni * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (m < M && n < N) out[(size_t)m * ldc + n] = acc[mi][ni][r];
-      }
-    }
 }
 
 // ----------------------------------------------------------------- column sums per segment
@@ -475,20 +325,12 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dout, const 
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, int batch, int R, int C, void* dst, int ldd, int col0, hipStream_t s) {
-  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
-  const bool vec = R % 8 == 0 && C % 8 == 0 && ldd % 8 == 0 && col0 % 8 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
-  hipLaunchKernelGGL(vec ? transpose8_kernel : transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64, batch), dim3(256), 0, s,
-                     (const uint16_t*)src, R, C, (uint16_t*)dst, ldd, col0);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_cols(void* a, long long rows, int ld, int c0, int c1, hipStream_t s) {
-  const long long n = rows * (long long)(c1 - c0);
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (uint16_t*)a, rows, ld,
-                     c0, c1);
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int n_seg, int k, int d,
+                              long long max_rows, void* xg, void* dy, hipStream_t s) {
+  if (max_rows == 0) return hipSuccess;
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, (const uint16_t*)x,
+                     perm, offsets, n_seg, k, d, (uint16_t*)xg, (uint16_t*)dy);
   return hipGetLastError();
 }
 
@@ -504,20 +346,6 @@ hipError_t launch_act_backward(bool swiglu, const void* a1, const void* a3, cons
   else
     hipLaunchKernelGGL(act_backward_kernel<false>, g, dim3(256), 0, s, (const uint16_t*)a1, nullptr,
                        (const uint16_t*)dh, rows, F, (uint16_t*)h, (uint16_t*)da);
-  return hipGetLastError();
-}
-
-hipError_t launch_wgrad(const void* P, int ldp, const void* Q, int ldq, bool gather_q, const int32_t* offsets,
-                        const int32_t* perm, int gk, int dense_rows, int n_seg, int M, int N, float* C, int ldc,
-                        long long strideC, hipStream_t s) {
-  if (n_seg == 0 || M == 0 || N == 0) return hipSuccess;
-  const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)), (unsigned)n_seg);
-  if (gather_q)
-    hipLaunchKernelGGL(wgrad_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)P, ldp, (const uint16_t*)Q, ldq,
-                       offsets, perm, gk, dense_rows, M, N, C, ldc, strideC);
-  else
-    hipLaunchKernelGGL(wgrad_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)P, ldp, (const uint16_t*)Q,
-                       ldq, offsets, perm, gk, dense_rows, M, N, C, ldc, strideC);
   return hipGetLastError();
 }
 

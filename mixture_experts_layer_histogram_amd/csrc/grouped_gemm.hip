@@ -18,14 +18,15 @@
 //
 // MFMA 32x32x16 layout (lane l): A row l%32, k = 8*(l/32)..+7; B column l%32,
 // same k; D column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
-#include "moe_internal.h"
+#include "gemm_tile.h"
 
 namespace moe {
 
 
 // Splits every segment into 256-row tiles and 64-row tiles: floor(rows / 256)
 // full tiles, one more 256-row tile when at least kBigTailMin rows remain,
-// otherwise ceil(rest / 64) 64-row tiles (only 64-row tiles with small_only).  Each list: [0] = tile count; tile i
+// otherwise ceil(rest / 64) 64-row tiles.  kind 1: 64-row tiles only; kind 2:
+// 256-row tiles only (ceil(rows / 256)).  Each list: [0] = tile count; tile i
 // at [4 + 8 i] = (segment, row_begin, row_end, first tile of the segment in
 // this list, tiles of the segment in this list, 0, 0, 0).
 constexpr int kBigTailMin = 128;
@@ -33,7 +34,7 @@ constexpr int kBigTailMin = 128;
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int n_seg,
                                                           int dense_rows, int32_t* __restrict__ big,
                                                           int max_big, int32_t* __restrict__ small,
-                                                          int max_small, int small_only) {
+                                                          int max_small, int kind) {
   __shared__ int tot_b[4], tot_s[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int lo = 0, hi = 0, nb = 0, ns = 0, split = 0;
@@ -41,10 +42,10 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
     lo = offsets ? offsets[tid] : 0;
     hi = offsets ? offsets[tid + 1] : dense_rows;
     const int rows = hi - lo;
-    nb = small_only ? 0 : rows / 256;
+    nb = kind == 1 ? 0 : (kind == 2 ? (rows + 255) / 256 : rows / 256);
     const int rest = rows - nb * 256;
-    if (!small_only && rest >= kBigTailMin) { nb += 1; }
-    else { ns = (rest + 63) / 64; }
+    if (kind == 0 && rest >= kBigTailMin) { nb += 1; }
+    else if (rest > 0) { ns = (rest + 63) / 64; }
     split = min(hi, lo + nb * 256);
   }
   int ib = nb, is = ns;
@@ -77,124 +78,6 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   }
 }
 
-// ---------------------------------------------------------------------------
-// Common pieces of the bf16 tile code.
-//
-// Operand pipeline.  BK = 64 (one 128-byte cache line per operand row and K
-// step).  LDS stages are filled by direct-to-LDS buffer loads: each
-// wavefront instruction moves 8 rows x 128 bytes straight into 1 KB of LDS,
-// with no staging registers.  Rows past the segment (or past the weight
-// matrix) read as zero through the buffer range check, so ragged tails need
-// no clamping.
-//
-// LDS layout: row r of a stage occupies 128 bytes = eight 16-byte chunks;
-// chunk c sits in slot c ^ g(r), g(r) = (r ^ (r >> 3)) & 7, which keeps the
-// 16-byte fragment reads of 16 consecutive rows on distinct banks.
-//
-// Work order.  Units enumerate each list's tiles expert by expert and, inside
-// one expert, N-tile by N-tile over all of its M tiles.  Each XCD (XCD =
-// workgroup id % 8) takes a contiguous range of each list, so the tiles that
-// share an expert's weight tile run close together on one XCD (its L2 holds
-// the tile once).  When a list leaves a last, partly filled round, those last
-// tiles are split along K into s parts (s = floor(grid / leftover), at least
-// 4 K steps per part); the parts write fp32 partial tiles (row-major) and a
-// fix-up kernel adds them in part order, so results do not depend on timing.
-constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 64;
-constexpr int kXcds = 8;
-constexpr int kStageElems = 256 * kBK2;          // one 256-row operand tile of one stage (bf16 elements)
-constexpr int kMaxSplitUnits = 256;              // partial tiles the workspace holds per list
-constexpr int kTileInts = 8;                     // tile entry: seg, r0, r1, first tile of seg, tiles of seg
-constexpr int kBM3 = 64, kStages3 = 3;           // short-tile shape and ring depth
-constexpr int kStage3Elems = (kBM3 + kBN2) * kBK2;
-constexpr int kLdsElems = 2 * 2 * kStageElems > kStages3 * kStage3Elems ? 2 * 2 * kStageElems
-                                                                        : kStages3 * kStage3Elems;
-// voffset of a row that must read as zero in gather mode (beyond every A buffer)
-constexpr int kOobOffset = 0x7fff0000;
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
-
-// 16 bytes per lane from `voff + soff` of the buffer straight into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt vmcnt(n), n < 64, leaving lgkmcnt / expcnt alone (gfx9 encoding: vmcnt
-// bits 3:0 in bits 3:0 and bits 5:4 in bits 15:14; expcnt 6:4; lgkmcnt 11:8).
-#define MOE_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
-#define MOE_WAIT_VM0() __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0))
-
-// How the units of one tile list are laid out: T tiles of KT steps; the
-// first `full` tiles run whole, the remaining `rem` tiles run in s K-parts.
-struct UnitPlan {
-  int full, rem, s;
-  __device__ __host__ int units() const { return full + rem * s; }
-};
-
-__device__ __forceinline__ UnitPlan plan_units(int T, int G, int KT) {
-  UnitPlan p;
-  const int rounds = T / G;
-  p.rem = T - rounds * G;
-  p.s = 1;
-  if (p.rem > 0) {
-    p.s = G / p.rem;
-    if (p.s * p.rem > kMaxSplitUnits) p.s = kMaxSplitUnits / p.rem;
-    if (p.s > KT / 4) p.s = KT / 4;
-    if (p.s < 1) p.s = 1;
-  }
-  if (p.s == 1) p.rem = 0;
-  p.full = T - p.rem;
-  return p;
-}
-
-// One unit of work: rows [r0, r1) of segment `seg`, output columns from n0,
-// K steps [kt0, kt1); slot >= 0 marks a K-part that writes partial tile `slot`.
-struct Unit {
-  int seg, r0, r1, n0, kt0, kt1, slot;
-};
-
-__device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, const UnitPlan& plan, int u,
-                                            int n_ntiles, int KT, int cols_per_tile) {
-  Unit w;
-  int tile_lin;
-  w.kt0 = 0;
-  w.kt1 = KT;
-  w.slot = -1;
-  if (u < plan.full) {
-    tile_lin = u;
-  } else {
-    const int v = u - plan.full;
-    tile_lin = plan.full + v / plan.s;
-    const int part = v % plan.s;
-    w.kt0 = (int)((long long)KT * part / plan.s);
-    w.kt1 = (int)((long long)KT * (part + 1) / plan.s);
-    w.slot = v;
-  }
-  const int ti = tile_lin / n_ntiles;          // the expert's tiles occupy [first, first + cnt) * n_ntiles
-  const int* te = tiles + 4 + kTileInts * ti;
-  const int first = te[3], cnt = te[4];
-  const int o = tile_lin - first * n_ntiles;
-  const int j = o / cnt;
-  const int i = first + o % cnt;
-  const int* td = tiles + 4 + kTileInts * i;
-  // readfirstlane: the tile entry is the same for every lane; saying so keeps
-  // the buffer descriptors built from it in scalar registers
-  w.seg = __builtin_amdgcn_readfirstlane(td[0]);
-  w.r0 = __builtin_amdgcn_readfirstlane(td[1]);
-  w.r1 = __builtin_amdgcn_readfirstlane(td[2]);
-  w.n0 = __builtin_amdgcn_readfirstlane(j * cols_per_tile);
-  w.kt0 = __builtin_amdgcn_readfirstlane(w.kt0);
-  w.kt1 = __builtin_amdgcn_readfirstlane(w.kt1);
-  w.slot = __builtin_amdgcn_readfirstlane(w.slot);
-  return w;
-}
-
 // Kernel arguments of the bf16 grouped GEMM.
 struct GemmParams {
   const uint16_t* A;          // rows in expert order, or (gather) the token rows
@@ -217,75 +100,6 @@ struct GemmParams {
   float* partials_small;      // K-part tiles of the 64-row list
   int K, Nn, n_ntiles;
 };
-
-// Epilogue of one 128 x 128 wavefront block (rows r0 + wm*128 .., columns of
-// the output n0 ..): activation, bias, bf16 rounding, 16-byte stores.
-// `ep` is this wavefront's 16 KB of LDS; `src_acc` the accumulators.
-template <int MODE, bool HAS_BIAS>
-__device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
-                                            int wn, int r0, int r1, int n0, int Nn, int seg,
-                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                            const float* __restrict__ bias_f, float* __restrict__ out_f) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
-    __builtin_amdgcn_wave_barrier();
-    const int rbase = r0 + wm * 128 + mi * 32;
-    if (MODE == MODE_LOGITS) {
-#pragma unroll 1
-      for (int pass = 0; pass < 16; ++pass) {
-        const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-        const int row = rbase + rr, col = n0 + wn * 128 + c4;
-        if (row < r1 && col < Nn) {
-          float4 v = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
-          if (HAS_BIAS) {
-            const float4 b = *reinterpret_cast<const float4*>(bias_f + col);
-            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-          }
-          *reinterpret_cast<float4*>(out_f + (size_t)row * Nn + col) = v;
-        }
-      }
-    } else if (MODE == MODE_SWIGLU_UP) {
-      // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
-#pragma unroll 1
-      for (int pass = 0; pass < 4; ++pass) {
-        const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-        const int row = rbase + rr, col = n0 + wn * 64 + c8;
-        if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 128 + c8;
-          Vec8 o;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-        }
-      }
-    } else {
-#pragma unroll 1
-      for (int pass = 0; pass < 8; ++pass) {
-        const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
-        const int row = rbase + rr, col = n0 + wn * 128 + c8;
-        if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 128 + c8;
-          Vec8 b;
-          if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-          Vec8 o;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            float x = src[v];
-            if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
-            if (MODE == MODE_GELU_UP) x = gelu_f(x);
-            o.e[v] = f32_to_bf16(x);
-          }
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
 
 template <int MODE, bool HAS_BIAS>
 __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, int lane, int kh, int l32, int wn,
@@ -946,6 +760,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     if (MODE == MODE_GELU_UP) v = gelu_f(v);
   }
   out[i] = v;
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int n_seg, int dense_rows, int32_t* big, int max_big,
+                              int32_t* small, int max_small, int kind, hipStream_t s) {
+  if (n_seg > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, n_seg, dense_rows, big, max_big, small,
+                     max_small, kind);
+  return hipGetLastError();
 }
 
 int grouped_gemm_max_tiles(int max_rows, int n_seg) { return max_rows / 256 + n_seg; }

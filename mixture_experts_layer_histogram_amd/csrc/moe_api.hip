@@ -4,6 +4,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace moe {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -619,10 +621,11 @@ namespace {
 // Backward workspace: the forward scratch first (tile lists, K-split partials),
 // then the backward's own buffers.
 struct BwdLayout {
-  size_t wt2, wtcat, a1, a3, h, dy, dh, da, dX, dg, dz, dz16, wrt, dxr, zpart;
-  size_t wts2, wtscat, a1s, a3s, hs, dhs, das, dxs;
+  size_t a1, a3, h, dy, dh, da, dX, xg, dg, dz, dz16, zpart, dxr;
+  size_t a1s, a3s, hs, dhs, das, dxs, tiles_dense, tiles_none;
   size_t total;
-  int ldz;   // K-padded router width for the dx GEMM
+  int ldz;          // K-padded router width (a multiple of 64) for the dx product
+  int max_tiles_dense;
 };
 
 BwdLayout backward_layout(const moe_config& c) {
@@ -640,8 +643,7 @@ BwdLayout backward_layout(const moe_config& c) {
   const bool sw = c.act == MOE_ACT_SWIGLU;
   const size_t nA = sw ? 2 : 1;
   B.ldz = ((c.n_experts + 63) / 64) * 64;
-  B.wt2 = take(E * F * d * 2);
-  B.wtcat = take(E * d * nA * F * 2);
+  B.max_tiles_dense = grouped_gemm_max_tiles((int)N, 1);
   B.a1 = take(R * F * 2);
   B.a3 = take(sw ? R * F * 2 : 0);
   B.h = take(R * F * 2);
@@ -649,20 +651,20 @@ BwdLayout backward_layout(const moe_config& c) {
   B.dh = take(R * F * 2);
   B.da = take(R * nA * F * 2);
   B.dX = take(R * d * 2);
+  B.xg = take(R * d * 2);
   B.dg = take(N * k * 4);
   B.dz = take(N * E * 4);
   B.dz16 = take(N * (size_t)B.ldz * 2);
-  B.wrt = take(d * (size_t)B.ldz * 2);
-  B.dxr = take(N * d * 2);
   B.zpart = take(colsum_part_floats((int)N, (int)E) * 4);
-  B.wts2 = take(Fs * d * 2);
-  B.wtscat = take(d * 2 * Fs * 2);
+  B.dxr = take(N * d * 2);
   B.a1s = take(N * Fs * 2);
   B.a3s = take(N * Fs * 2);
   B.hs = take(N * Fs * 2);
   B.dhs = take(N * Fs * 2);
   B.das = take(N * 2 * Fs * 2);
   B.dxs = take(Fs ? N * d * 2 : 0);
+  B.tiles_dense = take((4 + 8 * (size_t)B.max_tiles_dense) * 4);
+  B.tiles_none = take(64);
   B.total = off;
   return B;
 }
@@ -743,31 +745,46 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     auto P = [&](size_t o) { return wsp(ws, o); };
     float* dg = gr->dgates ? gr->dgates : reinterpret_cast<float*>(P(B.dg));
 
-    // weight-only work that does not depend on the batch: transposed copies
-    MOE_HIP(launch_transpose(w->w2, E, d, F, P(B.wt2), d, 0, stream));                  // W2^T [E, F, d]
-    MOE_HIP(launch_transpose(w->w1, E, F, d, P(B.wtcat), nA * F, 0, stream));           // [W1^T | W3^T] [E, d, nA F]
-    if (sw) MOE_HIP(launch_transpose(w->w3, E, F, d, P(B.wtcat), nA * F, F, stream));
     if (!any) return MOE_OK;
+    // every K-major row range the products address stays below 2^31 bytes
+    const size_t lim = 0x7fffffffull;
+    const size_t ld_routed = (size_t)std::max(d, nA * F), ld_dense = (size_t)std::max(std::max(B.ldz, d), 2 * Fs);
+    if ((size_t)R * ld_routed * 2 >= lim || (size_t)N * ld_dense * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+    int32_t* tiles = reinterpret_cast<int32_t*>(P(W.tiles));
+    int32_t* tiles_small = reinterpret_cast<int32_t*>(P(W.tiles_small));
+    int32_t* tiles_dense = reinterpret_cast<int32_t*>(P(B.tiles_dense));
+    int32_t* tiles_none = reinterpret_cast<int32_t*>(P(B.tiles_none));
+    // out[rows of each expert] = a B_e, B_e in its stored [K, N] layout (rows k >= K1 from B2)
+    auto nn_routed = [&](const void* a, const void* B1, const void* B2, int K, int K1, int Nn, void* out) {
+      return launch_gemm_nn(a, sv->offsets, E, 0, (int)R, tiles, W.max_tiles, tiles_small, W.max_tiles_small, B1,
+                            B2, (long long)K1 * Nn, K, K1, K1, K - K1, Nn, out, stream);
+    };
+    auto nn_dense = [&](const void* a, const void* B1, const void* B2, int K, int K1, int b_rows1, int Nn,
+                        void* out) {
+      return launch_gemm_nn(a, nullptr, 1, N, N, tiles_dense, B.max_tiles_dense, tiles_none, 0, B1, B2, 0, K, K1,
+                            b_rows1, K - K1, Nn, out, stream);
+    };
 
     // combine backward: dL/dgates and dY = g dout on the kept rows
     MOE_HIP(launch_combine_backward(c, dout, sv->y_perm, sv->slot_pos, sv->gates, dg, P(B.dy), stream));
-    // routed experts: recompute pre-activations, dH, activation backward, dX
-    MOE_TRY(plain_gemm(c, W, ws, false, x, sv->perm, sv->offsets, w->w1, c.ffn_bias ? w->b1 : nullptr, d, F,
+    // token rows in expert order (zero rows, and zero dY, for padding rows)
+    MOE_HIP(launch_gather_rows(x, sv->perm, sv->offsets, E, k, d, R, P(B.xg), P(B.dy), stream));
+    // routed experts: recompute pre-activations, dH = dY W2_e, activation backward, dX = dA [W1_e ; W3_e]
+    MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w1, c.ffn_bias ? w->b1 : nullptr, d, F,
                        P(B.a1), stream));
     if (sw)
-      MOE_TRY(plain_gemm(c, W, ws, false, x, sv->perm, sv->offsets, w->w3, nullptr, d, F, P(B.a3), stream));
-    MOE_TRY(plain_gemm(c, W, ws, false, P(B.dy), nullptr, sv->offsets, P(B.wt2), nullptr, d, F, P(B.dh), stream));
+      MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w3, nullptr, d, F, P(B.a3), stream));
+    MOE_HIP(nn_routed(P(B.dy), w->w2, nullptr, d, d, F, P(B.dh)));
     MOE_HIP(launch_act_backward(sw, P(B.a1), sw ? P(B.a3) : nullptr, P(B.dh), R, F, P(B.h), P(B.da), stream));
-    MOE_TRY(plain_gemm(c, W, ws, false, P(B.da), nullptr, sv->offsets, P(B.wtcat), nullptr, nA * F, d, P(B.dX),
-                       stream));
-    // expert weight gradients (reduction over each expert's kept rows)
-    MOE_HIP(launch_wgrad(P(B.dy), d, P(B.h), F, false, sv->offsets, sv->perm, k, 0, E, d, F, gr->dw2, F,
-                         (long long)d * F, stream));
-    MOE_HIP(launch_wgrad(P(B.da), nA * F, x, d, true, sv->offsets, sv->perm, k, 0, E, F, d, gr->dw1, d,
-                         (long long)F * d, stream));
+    MOE_HIP(nn_routed(P(B.da), w->w1, sw ? w->w3 : nullptr, nA * F, F, d, P(B.dX)));
+    // expert weight gradients: reductions over each expert's rows
+    MOE_HIP(launch_gemm_tn(P(B.dy), d, 0, P(B.h), F, sv->offsets, E, 0, (int)R, d, F, gr->dw2, (long long)d * F,
+                           stream));
+    MOE_HIP(launch_gemm_tn(P(B.da), nA * F, 0, P(B.xg), d, sv->offsets, E, 0, (int)R, F, d, gr->dw1,
+                           (long long)F * d, stream));
     if (sw)
-      MOE_HIP(launch_wgrad(reinterpret_cast<uint16_t*>(P(B.da)) + F, nA * F, x, d, true, sv->offsets, sv->perm, k, 0, E,
-                           F, d, gr->dw3, d, (long long)F * d, stream));
+      MOE_HIP(launch_gemm_tn(P(B.da), nA * F, F, P(B.xg), d, sv->offsets, E, 0, (int)R, F, d, gr->dw3,
+                             (long long)F * d, stream));
     if (c.ffn_bias) {
       MOE_HIP(launch_segment_colsum(P(B.da), nA * F, 0, F, sv->offsets, sv->perm, 0, E, gr->db1, stream));
       MOE_HIP(launch_segment_colsum(P(B.dy), d, 0, d, sv->offsets, sv->perm, 0, E, gr->db2, stream));
@@ -777,40 +794,32 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     MOE_HIP(launch_router_backward(c, sv->logits, sv->topk_idx, sv->gates, dg, d_aux != 0.f ? sv->counts : nullptr,
                                    d_aux, dz, P(B.dz16), B.ldz, stream));
     if (gr->dw_router)
-      MOE_HIP(launch_wgrad(P(B.dz16), B.ldz, x, d, false, nullptr, nullptr, 1, N, 1, E, d, gr->dw_router, d, 0,
-                           stream));
+      MOE_HIP(launch_gemm_tn(P(B.dz16), B.ldz, 0, x, d, nullptr, 1, N, N, E, d, gr->dw_router, 0, stream));
     if (gr->dlogit_bias)
       MOE_HIP(launch_colsum_f32(dz, N, E, reinterpret_cast<float*>(P(B.zpart)), gr->dlogit_bias, stream));
-    MOE_HIP(launch_transpose(w->w_router, 1, E, d, P(B.wrt), B.ldz, 0, stream));       // W_r^T [d, ldz]
-    MOE_HIP(launch_zero_cols(P(B.wrt), d, B.ldz, E, B.ldz, stream));
-    MOE_TRY(plain_gemm(c, W, ws, true, P(B.dz16), nullptr, nullptr, P(B.wrt), nullptr, B.ldz, d, P(B.dxr), stream));
+    MOE_HIP(nn_dense(P(B.dz16), w->w_router, nullptr, B.ldz, B.ldz, E, d, P(B.dxr)));
     // shared expert (dense SwiGLU over all tokens, weight 1)
     const void* dxs = nullptr;
     if (shared) {
-      MOE_HIP(launch_transpose(w->sh_w2, 1, d, Fs, P(B.wts2), d, 0, stream));          // sh_w2^T [Fs, d]
-      MOE_HIP(launch_transpose(w->sh_w1, 1, Fs, d, P(B.wtscat), 2 * Fs, 0, stream));   // [sh_w1^T | sh_w3^T] [d, 2Fs]
-      MOE_HIP(launch_transpose(w->sh_w3, 1, Fs, d, P(B.wtscat), 2 * Fs, Fs, stream));
-      auto shared_gemm = [&](const void* a, const void* wt, int K, int Nn, void* out) {
+      auto shared_up = [&](const void* wt, void* out) {
         GroupedGemmArgs g = gemm_args(c, W, ws, true);
         g.mode = MODE_DOWN;
-        g.K = K;
-        g.Nn = Nn;
-        g.a = a;
+        g.K = d;
+        g.Nn = Fs;
+        g.a = x;
         g.offsets = nullptr;
         g.w = wt;
         g.out = out;
         return launch_grouped_gemm(g, stream);
       };
-      MOE_HIP(shared_gemm(x, w->sh_w1, d, Fs, P(B.a1s)));
-      MOE_HIP(shared_gemm(x, w->sh_w3, d, Fs, P(B.a3s)));
-      MOE_HIP(shared_gemm(dout, P(B.wts2), d, Fs, P(B.dhs)));
+      MOE_HIP(shared_up(w->sh_w1, P(B.a1s)));
+      MOE_HIP(shared_up(w->sh_w3, P(B.a3s)));
+      MOE_HIP(nn_dense(dout, w->sh_w2, nullptr, d, d, d, Fs, P(B.dhs)));
       MOE_HIP(launch_act_backward(true, P(B.a1s), P(B.a3s), P(B.dhs), N, Fs, P(B.hs), P(B.das), stream));
-      MOE_HIP(shared_gemm(P(B.das), P(B.wtscat), 2 * Fs, d, P(B.dxs)));
-      MOE_HIP(launch_wgrad(dout, d, P(B.hs), Fs, false, nullptr, nullptr, 1, N, 1, d, Fs, gr->dsh_w2, Fs, 0, stream));
-      MOE_HIP(launch_wgrad(P(B.das), 2 * Fs, x, d, false, nullptr, nullptr, 1, N, 1, Fs, d, gr->dsh_w1, d, 0,
-                           stream));
-      MOE_HIP(launch_wgrad(reinterpret_cast<uint16_t*>(P(B.das)) + Fs, 2 * Fs, x, d, false, nullptr, nullptr, 1, N, 1, Fs,
-                           d, gr->dsh_w3, d, 0, stream));
+      MOE_HIP(nn_dense(P(B.das), w->sh_w1, w->sh_w3, 2 * Fs, Fs, Fs, d, P(B.dxs)));
+      MOE_HIP(launch_gemm_tn(dout, d, 0, P(B.hs), Fs, nullptr, 1, N, N, d, Fs, gr->dsh_w2, 0, stream));
+      MOE_HIP(launch_gemm_tn(P(B.das), 2 * Fs, 0, x, d, nullptr, 1, N, N, Fs, d, gr->dsh_w1, 0, stream));
+      MOE_HIP(launch_gemm_tn(P(B.das), 2 * Fs, Fs, x, d, nullptr, 1, N, N, Fs, d, gr->dsh_w3, 0, stream));
       dxs = P(B.dxs);
     }
     // dx = residual + scattered expert input gradients + shared + router

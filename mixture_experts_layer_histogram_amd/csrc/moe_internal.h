@@ -150,17 +150,28 @@ hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint
 // Backward kernels (backward.hip); bf16 storage.
 hipError_t launch_combine_backward(const moe_config& c, const void* dout, const void* y, const int32_t* slot_pos,
                                    const float* gates, float* dg, void* dy, hipStream_t s);
-hipError_t launch_transpose(const void* src, int batch, int R, int C, void* dst, int ldd, int col0, hipStream_t s);
-hipError_t launch_zero_cols(void* a, long long rows, int ld, int c0, int c1, hipStream_t s);
 hipError_t launch_act_backward(bool swiglu, const void* a1, const void* a3, const void* dh, long long rows, int F,
                                void* h, void* da, hipStream_t s);
-hipError_t launch_wgrad(const void* P, int ldp, const void* Q, int ldq, bool gather_q, const int32_t* offsets,
-                        const int32_t* perm, int gk, int dense_rows, int n_seg, int M, int N, float* C, int ldc,
-                        long long strideC, hipStream_t s);
 hipError_t launch_segment_colsum(const void* a, int lda, int col0, int ncols, const int32_t* offsets,
                                  const int32_t* perm, int dense_rows, int n_seg, float* out, hipStream_t s);
 size_t colsum_part_floats(int rows, int cols);   // scratch of launch_colsum_f32
 hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* part, float* out, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int n_seg, int k, int d,
+                              long long max_rows, void* xg, void* dy, hipStream_t s);
+// Tile lists of the grouped GEMM (kind 0: 256- and 64-row tiles, 1: 64-row only, 2: 256-row only).
+hipError_t launch_build_tiles(const int32_t* offsets, int n_seg, int dense_rows, int32_t* big, int max_big,
+                              int32_t* small, int max_small, int kind, hipStream_t s);
+// Backward products with K-major operands (xgemm.hip).
+//   NN: out[r, :N] (bf16) = A[r, :K] B_s[K, N] for the rows of segment s; B_s rows k < K1 at
+//       B1 + s strideB + k N, rows k >= K1 at B2 + s strideB + (k - K1) N; rows beyond b_rows1 /
+//       b_rows2 of either part read as zero.  Needs K, K1 multiples of 64.
+//   TN: C_s[m, n] (fp32, row-major [M, N]) = sum over the rows r of segment s of P[r, pc0 + m] Q[r, n].
+hipError_t launch_gemm_nn(const void* A, const int32_t* offsets, int n_seg, int dense_rows, int max_rows,
+                          int32_t* tiles, int max_tiles, int32_t* tiles_small, int max_tiles_small, const void* B1,
+                          const void* B2, long long strideB, int K, int K1, int b_rows1, int b_rows2, int N, void* out,
+                          hipStream_t s);
+hipError_t launch_gemm_tn(const void* P, int ldp, int pc0, const void* Q, int ldq, const int32_t* offsets, int n_seg,
+                          int dense_rows, int max_seg_rows, int M, int N, float* C, long long strideC, hipStream_t s);
 hipError_t launch_router_backward(const moe_config& c, const float* z, const int32_t* idx, const float* gates,
                                   const float* dg, const int32_t* counts, float d_aux, float* dz, void* dz16,
                                   int ldz, hipStream_t s);

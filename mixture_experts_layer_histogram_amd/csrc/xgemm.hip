@@ -1,0 +1,363 @@
+// Products of the layer backward whose operands are K-major in memory.
+//
+//   NN (ragged rows):  out[r, n] = sum_k A[r, k] B_s[k, n] for the rows r of
+//       segment s.  A is row-major [rows, K] in expert order; B_s is a weight
+//       matrix in its stored layout, [K, N] with N contiguous, so
+//       dH = dY W2_e (W2_e is [d, F]) and dX = [dA1 | dA3] [W1_e ; W3_e]
+//       (W1_e, W3_e are [F, d]) need no transposed weight copies.
+//   TN (ragged reduction): C_s[m, n] = sum over the rows r of segment s of
+//       P[r, m] Q[r, n] in fp32: the weight gradients dW2_e = dY^T H,
+//       dW1_e = dA1^T X, dW_router = dZ^T X.
+//
+// Both run the 256 x 256 x 64 tile of the forward's grouped GEMM (4
+// wavefronts of 128 x 128, MFMA 32x32x16 bf16, two 64 KB LDS stages filled by
+// direct-to-LDS buffer loads, one barrier per K step).  What changes is how a
+// K-major operand sits in LDS and reaches the MFMA:
+//
+// K-major stage: 64 K rows x 256 columns, 512 bytes per row; the 16-byte
+// chunk c of row r sits in slot c ^ (4 (r & 3)).  A direct-to-LDS load moves
+// two such rows (64 lanes x 16 bytes); the lane that fills slot s fetches
+// source chunk s ^ (4 (r & 3)).
+//
+// Transposing fragment read: ds_read_b64_tr_b16 works on groups of 16 lanes;
+// lane i of a group receives element i % 4 of the 8-byte blocks that lanes
+// 4 j + i / 4 (j = 0..3) address.  So if lane i addresses row kb + i / 4,
+// columns c0 + 4 (i % 4) .. + 3, it receives column c0 + i at rows kb .. kb + 3.
+// The MFMA operand (column l % 32, K 8 (l / 32) .. + 7 for lane l) is two such
+// reads: group G = l / 16 takes c0 = 16 (G & 1), kb = 8 (G >> 1) and kb + 4.
+// Per half-wave the 16 (row, chunk) pairs of one read fall on 16 distinct
+// 4-bank groups under the slot swizzle above.
+#include "gemm_tile.h"
+
+namespace moe {
+
+typedef __bf16 bf16x4t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4t lds_bf16x4;
+
+__device__ __forceinline__ bf16x4t read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// Lane constants of the transposing fragment reads of a K-major stage whose
+// 128-column block for this wavefront starts at column `cblk`:
+// element offset of fragment x (32 columns each) in sub-step kk, half h =
+//   (16 kk + 4 h) * 256 + base + xo[x].
+struct TrLane {
+  int base;
+  int xo[4];
+};
+
+__device__ __forceinline__ TrLane tr_lane(int lane, int cblk) {
+  const int G = lane >> 4, i = lane & 15;
+  const int row = 8 * (G >> 1) + (i >> 2);             // row within the sub-step
+  const int chunk = 2 * (G & 1) + ((i & 3) >> 1);      // 16-byte chunk within the 32-column fragment
+  const int sw = 4 * (i >> 2);                          // = 4 (row & 3)
+  TrLane t;
+  t.base = row * 256 + cblk + 4 * (i & 1);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) t.xo[x] = ((4 * x + chunk) ^ sw) * 8;
+  return t;
+}
+
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* st, const TrLane& t, int kk, int x) {
+  const uint16_t* p = st + kk * 16 * 256 + t.base + t.xo[x];
+  const bf16x4t lo = read_tr(p);
+  const bf16x4t hi = read_tr(p + 4 * 256);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Direct-to-LDS loads of a K-major operand: wavefront w fills K rows
+// 16 w .. 16 w + 15 of the stage, two rows per instruction.  voff[u] is the
+// byte offset of this lane's source chunk for instruction u at K row 0 of the
+// operand (rows advance by `rowbytes`).
+__device__ __forceinline__ void tr_dma_offsets(int wave, int lane, int rowbytes, int col0, int (&voff)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int lr = 16 * wave + 2 * u + (lane >> 5);
+    const int chunk = (lane & 31) ^ (4 * (lr & 3));
+    voff[u] = lr * rowbytes + col0 * 2 + chunk * 16;
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+}
+
+__device__ __forceinline__ void mfma_block(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// NN: persistent over the units of a 256-row tile list (expert-major, N-tile
+// by N-tile over the expert's row tiles; each XCD a contiguous range).
+struct NnParams {
+  const uint16_t* A;        // [rows, K] in segment order
+  const int32_t* tiles;     // 256-row tiles covering every row (kind 2)
+  const uint16_t* B1;       // rows k < K1 of B_s: B1 + s * strideB + k * N
+  const uint16_t* B2;       // rows k >= K1: B2 + s * strideB + (k - K1) * N (or null)
+  long long strideB;
+  int K, K1, N;
+  int b_rows1, b_rows2;     // rows of B1 / B2 per segment that exist (beyond: zero)
+  uint16_t* out;            // [rows, N]
+  int n_ntiles;
+};
+
+__global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
+  const int G = gridDim.x;
+  const int KT = p.K / kBK2;
+  UnitPlan plan;
+  plan.full = p.tiles[0] * p.n_ntiles;
+  plan.rem = 0;
+  plan.s = 1;
+  const int U = plan.full;
+  const int per_xcd = G / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  const int span = (U + kXcds - 1) / kXcds;
+  const int u0 = min(U, xcd * span), cnt = min(U, u0 + span) - u0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int rowbytes = p.K * 2, browbytes = p.N * 2;
+  const int h = kh ^ swz8(l32);
+  const int abase = (wm * 128 + l32) * kBK2;
+  const TrLane tb = tr_lane(lane, wn * 128);
+
+  for (int it = q; it < cnt; it += per_xcd) {
+    const Unit w = decode_unit(p.tiles, plan, u0 + it, p.n_ntiles, KT, kBN2);
+    int voff[8], voffb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = 64 * wave + 8 * u + (lane >> 3);
+      voff[u] = row * rowbytes + (((lane & 7) ^ swz8(row)) * 16);
+    }
+    tr_dma_offsets(wave, lane, browbytes, w.n0, voffb);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
+    const __amdgpu_buffer_rsrc_t rb1 =
+        make_rsrc(p.B1 + (size_t)w.seg * p.strideB, (uint32_t)p.b_rows1 * browbytes);
+    const __amdgpu_buffer_rsrc_t rb2 =
+        make_rsrc(p.B2 ? p.B2 + (size_t)w.seg * p.strideB : p.B1, p.B2 ? (uint32_t)p.b_rows2 * browbytes : 0u);
+
+    auto issue = [&](uint16_t* st, int kt, int u) {
+      dma16(ra, st + (64 * wave + 8 * u) * kBK2, voff[u], kt * kBK2 * 2);
+      const int k0 = kt * kBK2;
+      const bool second = k0 >= p.K1;
+      const int kb = second ? k0 - p.K1 : k0;
+      dma16(second ? rb2 : rb1, st + kStageElems + (16 * wave + 2 * u) * 256, voffb[u] + kb * browbytes, 0);
+    };
+
+    f32x16 acc[4][4];
+    zero_acc(acc);
+    // One K step: fragments from stage `st`, the next step's loads into `nx`.
+    // The restrict-qualified stage pointers tell the compiler that the reads
+    // of one stage never alias the direct-to-LDS loads into the other, so it
+    // does not wait for those loads before each transposing read.
+    auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {
+      MOE_WAIT_VM0();
+      __builtin_amdgcn_s_barrier();
+      const bool more = kt + 1 < KT;
+      bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
+        fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kBK2 / 16; ++kk) {
+        const int c = kk & 1;
+        if (more && kk < 3) {
+#pragma unroll
+          for (int u = 3 * kk; u < 3 * kk + 3; ++u)
+            if (u < 8) issue(nx, kt + 1, u);
+        }
+        if (kk + 1 < kBK2 / 16) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x +
+                                                             ((h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3));
+            fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
+          }
+        }
+        mfma_block(acc, fa[c], fb[c]);
+      }
+    };
+
+    if (KT > 0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) issue(lds, 0, u);
+    }
+    for (int kt = 0; kt < KT; ++kt)
+      step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
+    __syncthreads();
+    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
+    store_block<MODE_DOWN, false>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.N, w.seg, nullptr, p.out,
+                                  nullptr, nullptr);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// TN: one workgroup per (segment, M tile, N tile); workgroup b of XCD b % 8
+// takes item (b % 8) * span + b / 8 of the segment-major, M-tile-major order,
+// so an XCD's concurrent tiles share their P and Q column blocks in its L2.
+struct TnParams {
+  const uint16_t* P;        // [rows, ldp], columns pc0 .. pc0 + M
+  const uint16_t* Q;        // [rows, ldq], columns 0 .. N
+  const int32_t* offsets;   // segment row ranges, or null: one segment of dense_rows rows
+  int dense_rows;
+  int ldp, pc0, ldq;
+  int M, N;
+  float* C;                 // C_s = C + s * strideC, [M, N] row-major
+  long long strideC;
+  int tiles_m, tiles_n, units, span;
+};
+
+__global__ __launch_bounds__(256, 1) void gemm_tn_kernel(TnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
+  const int item = (blockIdx.x % kXcds) * p.span + blockIdx.x / kXcds;
+  if (item >= p.units) return;
+  const int per_seg = p.tiles_m * p.tiles_n;
+  const int s = item / per_seg;
+  const int m0 = ((item % per_seg) / p.tiles_n) * 256;
+  const int n0 = (item % p.tiles_n) * 256;
+  const int lo = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s] : 0);
+  const int hi = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s + 1] : p.dense_rows);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int pbytes = p.ldp * 2, qbytes = p.ldq * 2;
+  int voffp[8], voffq[8];
+  tr_dma_offsets(wave, lane, pbytes, p.pc0 + m0, voffp);
+  tr_dma_offsets(wave, lane, qbytes, n0, voffq);
+  const TrLane ta = tr_lane(lane, wm * 128), tb = tr_lane(lane, wn * 128);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.P + (size_t)lo * p.ldp, (uint32_t)(hi - lo) * pbytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (size_t)lo * p.ldq, (uint32_t)(hi - lo) * qbytes);
+
+  auto issue = [&](uint16_t* st, int kt, int u) {
+    const int r = kt * kBK2;
+    dma16(rp, st + (16 * wave + 2 * u) * 256, voffp[u] + r * pbytes, 0);
+    dma16(rq, st + kStageElems + (16 * wave + 2 * u) * 256, voffq[u] + r * qbytes, 0);
+  };
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  const int KT = (hi - lo + kBK2 - 1) / kBK2;
+  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {   // as in NN
+    MOE_WAIT_VM0();
+    __builtin_amdgcn_s_barrier();
+    const bool more = kt + 1 < KT;
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      fa[0][x] = frag_tr(st, ta, 0, x);
+      fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK2 / 16; ++kk) {
+      const int c = kk & 1;
+      if (more && kk < 3) {
+#pragma unroll
+        for (int u = 3 * kk; u < 3 * kk + 3; ++u)
+          if (u < 8) issue(nx, kt + 1, u);
+      }
+      if (kk + 1 < kBK2 / 16) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          fa[c ^ 1][x] = frag_tr(st, ta, kk + 1, x);
+          fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
+        }
+      }
+      mfma_block(acc, fa[c], fb[c]);
+    }
+  };
+  if (KT > 0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) issue(lds, 0, u);
+  }
+  for (int kt = 0; kt < KT; ++kt)
+    step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
+  __syncthreads();
+  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
+  store_block<MODE_LOGITS, false>(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, s, nullptr, nullptr, nullptr,
+                                  p.C + (size_t)s * p.strideC);
+}
+
+static int cus_rounded() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  return ((v + kXcds - 1) / kXcds) * kXcds;
+}
+
+hipError_t launch_gemm_nn(const void* A, const int32_t* offsets, int n_seg, int dense_rows, int max_rows,
+                          int32_t* tiles, int max_tiles, int32_t* tiles_small, int max_tiles_small, const void* B1,
+                          const void* B2, long long strideB, int K, int K1, int b_rows1, int b_rows2, int N, void* out,
+                          hipStream_t s) {
+  if (K % kBK2 != 0 || K1 % kBK2 != 0 || N % 8 != 0 || (B2 == nullptr && K1 < K)) return hipErrorInvalidValue;
+  if ((size_t)b_rows1 * N * 2 >= 0x80000000ull || (size_t)b_rows2 * N * 2 >= 0x80000000ull ||
+      (size_t)max_rows * K * 2 >= 0x80000000ull || max_tiles < max_rows / 256 + n_seg)
+    return hipErrorInvalidValue;
+  hipError_t e = launch_build_tiles(offsets, n_seg, dense_rows, tiles, max_tiles, tiles_small, max_tiles_small, 2, s);
+  if (e != hipSuccess) return e;
+  NnParams p;
+  p.A = (const uint16_t*)A;
+  p.tiles = tiles;
+  p.B1 = (const uint16_t*)B1;
+  p.B2 = (const uint16_t*)B2;
+  p.strideB = strideB;
+  p.K = K;
+  p.K1 = K1;
+  p.N = N;
+  p.b_rows1 = b_rows1;
+  p.b_rows2 = b_rows2;
+  p.out = (uint16_t*)out;
+  p.n_ntiles = (N + kBN2 - 1) / kBN2;
+  hipLaunchKernelGGL(gemm_nn_kernel, dim3(cus_rounded()), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const void* P, int ldp, int pc0, const void* Q, int ldq, const int32_t* offsets, int n_seg,
+                          int dense_rows, int max_seg_rows, int M, int N, float* C, long long strideC,
+                          hipStream_t s) {
+  if (n_seg == 0 || M == 0 || N == 0) return hipSuccess;
+  if (ldp % 8 != 0 || pc0 % 8 != 0 || ldq % 8 != 0 || N % 8 != 0) return hipErrorInvalidValue;
+  if ((size_t)max_seg_rows * ldp * 2 >= 0x80000000ull || (size_t)max_seg_rows * ldq * 2 >= 0x80000000ull)
+    return hipErrorInvalidValue;
+  TnParams p;
+  p.P = (const uint16_t*)P;
+  p.Q = (const uint16_t*)Q;
+  p.offsets = offsets;
+  p.dense_rows = dense_rows;
+  p.ldp = ldp;
+  p.pc0 = pc0;
+  p.ldq = ldq;
+  p.M = M;
+  p.N = N;
+  p.C = C;
+  p.strideC = strideC;
+  p.tiles_m = (M + 255) / 256;
+  p.tiles_n = (N + 255) / 256;
+  p.units = n_seg * p.tiles_m * p.tiles_n;
+  p.span = (p.units + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)(p.span * kXcds)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe
