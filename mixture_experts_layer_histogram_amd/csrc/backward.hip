@@ -24,12 +24,13 @@ namespace moe {
 // ----------------------------------------------------------------- combine backward
 // One wavefront per slot s = t k + j.  Kept slots: dg[t, j] = <dout_t, y_row>
 // (fp32, lane-strided partial sums then a fixed xor tree) and dY_row =
-// g[t, j] * dout_t.  Dropped slots: dg = 0.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_backward_kernel(const T* __restrict__ dout, const T* __restrict__ y,
+// g[t, j] * dout_t.  Dropped slots: dg = 0.  16-byte lanes (d a multiple of 8).
+__global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* __restrict__ dout,
+                                                               const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ slot_pos,
                                                                const float* __restrict__ gates, int n_slots, int k,
-                                                               int d, float* __restrict__ dg, T* __restrict__ dy) {
+                                                               int d, float* __restrict__ dg,
+                                                               uint16_t* __restrict__ dy) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + wave;
   if (s >= n_slots) return;
@@ -40,14 +41,21 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const T* __restri
   }
   const int t = s / k;
   const float g = gates[s];
-  const T* dr = dout + (size_t)t * d;
-  const T* yr = y + (size_t)pos * d;
-  T* dyr = dy + (size_t)pos * d;
+  const uint4* dr = reinterpret_cast<const uint4*>(dout + (size_t)t * d);
+  const uint4* yr = reinterpret_cast<const uint4*>(y + (size_t)pos * d);
+  uint4* dyr = reinterpret_cast<uint4*>(dy + (size_t)pos * d);
   float acc = 0.f;
-  for (int c = lane; c < d; c += 64) {
-    const float go = Store<T>::load(dr, c);
-    acc = fmaf(go, Store<T>::load(yr, c), acc);
-    Store<T>::store(dyr, c, g * go);
+  for (int c = lane; c < d / 8; c += 64) {
+    Vec8 go, yv, o;
+    go.u = dr[c];
+    yv.u = yr[c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gv = bf16_to_f32(go.e[e]);
+      acc = fmaf(gv, bf16_to_f32(yv.e[e]), acc);
+      o.e[e] = f32_to_bf16(g * gv);
+    }
+    dyr[c] = o.u;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
@@ -293,24 +301,37 @@ __global__ __launch_bounds__(256) void router_backward_kernel(const float* __res
 
 // ----------------------------------------------------------------- dx
 // dx[t] = [dout_t] + sum_j dX[slot_pos[t k + j]] + [dxs_t] + [dxr_t], fp32 accumulation in a
-// fixed order, rounded once to the storage type.  One wavefront per token.
-template <typename T>
-__global__ __launch_bounds__(256) void dx_gather_kernel(const T* __restrict__ dout, const T* __restrict__ dX,
+// fixed order, rounded once to bf16.  One wavefront per token, 16-byte lanes.
+__device__ __forceinline__ void add8(float (&a)[8], const uint4& v) {
+  Vec8 x;
+  x.u = v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] += bf16_to_f32(x.e[e]);
+}
+
+__global__ __launch_bounds__(256) void dx_gather_kernel(const uint16_t* __restrict__ dout,
+                                                        const uint16_t* __restrict__ dX,
                                                         const int32_t* __restrict__ slot_pos,
-                                                        const T* __restrict__ dxs, const T* __restrict__ dxr,
-                                                        int N, int k, int d, T* __restrict__ dx) {
+                                                        const uint16_t* __restrict__ dxs,
+                                                        const uint16_t* __restrict__ dxr, int N, int k, int d,
+                                                        uint16_t* __restrict__ dx) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= N) return;
-  for (int c = lane; c < d; c += 64) {
-    float a = dout ? Store<T>::load(dout, (size_t)t * d + c) : 0.f;
+  const size_t row = (size_t)t * d;
+  for (int c = lane; c < d / 8; c += 64) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (dout) add8(a, reinterpret_cast<const uint4*>(dout + row)[c]);
     for (int j = 0; j < k; ++j) {
       const int pos = slot_pos[(size_t)t * k + j];
-      if (pos >= 0) a += Store<T>::load(dX, (size_t)pos * d + c);
+      if (pos >= 0) add8(a, reinterpret_cast<const uint4*>(dX + (size_t)pos * d)[c]);
     }
-    if (dxs) a += Store<T>::load(dxs, (size_t)t * d + c);
-    if (dxr) a += Store<T>::load(dxr, (size_t)t * d + c);
-    Store<T>::store(dx, (size_t)t * d + c, a);
+    if (dxs) add8(a, reinterpret_cast<const uint4*>(dxs + row)[c]);
+    if (dxr) add8(a, reinterpret_cast<const uint4*>(dxr + row)[c]);
+    Vec8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.e[e] = f32_to_bf16(a[e]);
+    reinterpret_cast<uint4*>(dx + row)[c] = o.u;
   }
 }
 
@@ -319,7 +340,8 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dout, const 
                                    const float* gates, float* dg, void* dy, hipStream_t s) {
   const int n_slots = (int)(c.n_tokens * c.top_k);
   if (n_slots == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_backward_kernel<uint16_t>, dim3((n_slots + 3) / 4), dim3(256), 0, s,
+  if (c.d_model % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_backward_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s,
                      (const uint16_t*)dout, (const uint16_t*)y, slot_pos, gates, n_slots, c.top_k, c.d_model, dg,
                      (uint16_t*)dy);
   return hipGetLastError();
@@ -390,7 +412,8 @@ hipError_t launch_dx_gather(const moe_config& c, const void* dout, const void* d
                             const void* dxs, const void* dxr, void* dx, hipStream_t s) {
   const int N = (int)c.n_tokens;
   if (N == 0) return hipSuccess;
-  hipLaunchKernelGGL(dx_gather_kernel<uint16_t>, dim3((N + 3) / 4), dim3(256), 0, s, (const uint16_t*)dout,
+  if (c.d_model % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dx_gather_kernel, dim3((N + 3) / 4), dim3(256), 0, s, (const uint16_t*)dout,
                      (const uint16_t*)dX, slot_pos, (const uint16_t*)dxs, (const uint16_t*)dxr, N, c.top_k,
                      c.d_model, (uint16_t*)dx);
   return hipGetLastError();
