@@ -32,7 +32,9 @@ METRIC = "MoE layer tokens/sec @DeepSeek-V3 & Mixtral shapes; % MFMA/HBM rooflin
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", "grouped_gemm.hip")
+# sources the up-projection kernel is compiled from (the traffic counters are tied to them)
+GEMM_SRC = [os.path.join(ROOT, "mixture_experts_layer_histogram_amd", "csrc", f)
+            for f in ("grouped_gemm.hip", "gemm_tile.h", "moe_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -52,17 +54,21 @@ def parse():
     ap.add_argument("--capacity-priority", choices=["slot", "choice"], default=None,
                     help="override which slots an over-full expert keeps")
     ap.add_argument("--backward", action="store_true",
-                    help="a step is the forward pass plus moe_backward (dout = ones-scaled noise, d_aux = 1 with an "
-                         "aux loss); reports the backward's time and algorithmic TFLOP/s")
+                    help="a training step: the forward (its up-projection keeping the pre-activations) plus "
+                         "moe_backward (dout = seeded noise, d_aux = 1 with an aux loss); reports the backward's "
+                         "time and algorithmic TFLOP/s")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
@@ -180,8 +186,10 @@ def main():
             bw_grads["dsh_w3"] = torch.empty((Fs, d), dtype=f32, device=dev_name)
             bw_grads["dsh_w2"] = torch.empty((d, Fs), dtype=f32, device=dev_name)
         bw_ws = torch.empty(M.backward_workspace_size(c), dtype=torch.uint8, device=dev_name)
+        # the training forward keeps the up-projection's pre-activations for the backward
+        pre_act = torch.empty((2 if cfg.act == "swiglu" else 1, max(R, 1), F), dtype=st, device=dev_name)
         bw_saved = {"logits": z, "topk_idx": idx, "gates": gates, "counts": counts, "offsets": offs,
-                    "perm": perm, "slot_pos": slot_pos, "y_perm": y}
+                    "perm": perm, "slot_pos": slot_pos, "y_perm": y, "pre_act": pre_act}
         bw = (dout, bw_grads, bw_ws, bw_saved)
 
     def step(ev=None):
@@ -194,7 +202,9 @@ def main():
         mark(1)
         M.permute(c, idx, None, counts, offs, perm, slot_pos, None, drop_count=drop, ws=ws)
         mark(2)
-        if fp8 is None:
+        if bw is not None:
+            M.expert_up_save(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, bw[3]["pre_act"], b1=dev["b1"], ws=ws)
+        elif fp8 is None:
             M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
         else:
             M.expert_up_fp8(c, dev["x"], perm, offs, fp8["w1"][0], fp8["w3"][0], fp8["w1"][1], fp8["w3"][1], h,
@@ -287,15 +297,16 @@ def main():
                    "expert_weights": "fp8_e4m3_row_scaled" if fp8 is not None else cfg.dtype},
         "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
                                "(build_tiles_kernel, grouped_gemm_kernel, split_fixup_kernel; one "
-                               f"{'moe_expert_up_gather' if fp8 is None else 'moe_expert_up_fp8'} call)",
+                               f"{'moe_expert_up_fp8' if fp8 is not None else ('moe_expert_up_save' if bw is not None else 'moe_expert_up_gather')} call)",
                      **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop},
         "expert_gemm_tflops": expert_tflops,
         **({"backward": {"ms": parts["backward"],
                          "algorithmic_tflop": bw_flop / 1e12,
                          "tflops": bw_flop / (parts["backward"] * 1e-3) / 1e12,
                          "note": "dx, router, expert and shared-expert gradients; algorithmic FLOPs = the two "
-                                 "products per forward product (input and weight gradients); pre-activation "
-                                 "recompute and weight transposes are overhead"}} if bw is not None else {}),
+                                 "products per forward product (input and weight gradients); the routed "
+                                 "pre-activations come from the forward (moe_expert_up_save), the shared "
+                                 "expert's are recomputed"}} if bw is not None else {}),
         "breakdown_ms": parts,
         "wall_s_timed": wall_s,
         "input_gen_s": gen_s,

@@ -191,6 +191,18 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* x, const int3
                                 const void* b1, void* h_tmp, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* moe_expert_up_gather that also keeps the pre-activations for moe_backward
+ * (the training forward; [L] "The load balance problem" trains the layer):
+ *   pre_act [n, R, F] bf16 out: plane 0 = x W1_e^T (+ b1_e for GELU), plane 1 =
+ *   x W3_e^T (SwiGLU only; n = 2 for SwiGLU, 1 for GELU), rows in expert order,
+ *   R = rows of the expert-ordered buffers.  Caller-owned device memory.
+ * bf16 storage only (MOE_ERR_UNSUPPORTED otherwise); other arguments and errors
+ * as moe_expert_up_gather; pre_act NULL is MOE_ERR_ARG when N > 0. */
+moe_status moe_expert_up_save(const moe_config* cfg, const void* x, const int32_t* perm,
+                              const int32_t* offsets, const void* w1, const void* w3,
+                              const void* b1, void* h_tmp, void* pre_act, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* Second half of moe_expert_ffn: y = h W2_e^T [+ b2_e]. */
 moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
                            const void* w2, const void* b2, void* y_perm,
@@ -322,6 +334,7 @@ typedef struct moe_saved {      /* forward state of the same call, as the step e
   const int32_t* perm;          /* [R] */
   const int32_t* slot_pos;      /* [N k] */
   const void*    y_perm;        /* [R, d] expert outputs (storage dtype) */
+  const void*    pre_act;       /* [n, R, F] from moe_expert_up_save, or NULL: recomputed */
 } moe_saved;
 
 typedef struct moe_grads {      /* device outputs; fp32 unless noted */

@@ -42,7 +42,7 @@ class MoeOutputs(ctypes.Structure):
 
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm", "slot_pos",
-                                        "y_perm")]
+                                        "y_perm", "pre_act")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -65,6 +65,7 @@ _SIGS = {
     "moe_expert_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up_gather": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_expert_up_save": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P],
     "moe_expert_up_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
@@ -188,6 +189,13 @@ def expert_up_gather(cfg, x, perm, offsets, w1, w3, h_tmp, b1=None, ws=None, str
           _ptr(b1), _ptr(h_tmp), wp, wb, _stream(stream))
 
 
+def expert_up_save(cfg, x, perm, offsets, w1, w3, h_tmp, pre_act, b1=None, ws=None, stream=None):
+    """moe_expert_up_save: expert_up_gather that also writes the pre-activations [n, R, F] for backward()."""
+    wp, wb = _ws(ws)
+    _call("moe_expert_up_save", ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(w1), _ptr(w3),
+          _ptr(b1), _ptr(h_tmp), _ptr(pre_act), wp, wb, _stream(stream))
+
+
 def quantize_fp8(w, q, scales, stream=None):
     """Per-row E4M3 codes and fp32 scales of a bf16 matrix (rows = all leading dims)."""
     cols = int(w.shape[-1])
@@ -254,11 +262,12 @@ def backward_workspace_size(cfg: MoeConfig) -> int:
 
 def backward(cfg, weights: dict, x, dout, saved: dict, grads: dict, d_aux=0.0, ws=None, stream=None):
     """moe_backward: `weights` as for forward(); `saved` holds logits, topk_idx, gates, counts,
-    offsets, perm, slot_pos, y_perm of the forward; `grads` the output tensors (see moe_grads)."""
+    offsets, perm, slot_pos, y_perm of the forward and optionally pre_act (from expert_up_save);
+    `grads` the output tensors (see moe_grads)."""
     W = MoeWeights(*[_ptr(weights.get(n)) for n in ("w_router", "logit_bias", "w1", "w3", "w2", "b1", "b2",
                                                     "sh_w1", "sh_w3", "sh_w2")])
     S = MoeSaved(*[_ptr(saved.get(n)) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm",
-                                                "slot_pos", "y_perm")])
+                                                "slot_pos", "y_perm", "pre_act")])
     G = MoeGrads(*[_ptr(grads.get(n)) for n in ("dx", "dw_router", "dlogit_bias", "dw1", "dw3", "dw2", "db1", "db2",
                                                 "dsh_w1", "dsh_w3", "dsh_w2", "dgates")])
     wp, wb = _ws(ws)

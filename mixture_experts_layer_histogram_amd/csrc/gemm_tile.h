@@ -134,7 +134,8 @@ template <int MODE, bool HAS_BIAS>
 __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
                                             int wn, int r0, int r1, int n0, int Nn, int seg,
                                             const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                            const float* __restrict__ bias_f, float* __restrict__ out_f) {
+                                            const float* __restrict__ bias_f, float* __restrict__ out_f,
+                                            uint16_t* __restrict__ pre = nullptr, long long pre_plane = 0) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -169,6 +170,16 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
 #pragma unroll
           for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
           *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (pre != nullptr) {   // pre-activations x W1^T, x W3^T for the backward
+            Vec8 a1, a3;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              a1.e[v] = f32_to_bf16(src[v]);
+              a3.e[v] = f32_to_bf16(src[64 + v]);
+            }
+            *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a1.u;
+            *reinterpret_cast<uint4*>(pre + pre_plane + (size_t)row * Nn + col) = a3.u;
+          }
         }
       }
     } else {
@@ -180,15 +191,17 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
           const float* src = ep + rr * 128 + c8;
           Vec8 b;
           if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-          Vec8 o;
+          Vec8 o, a;
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
             float x = src[v];
             if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+            a.e[v] = f32_to_bf16(x);
             if (MODE == MODE_GELU_UP) x = gelu_f(x);
             o.e[v] = f32_to_bf16(x);
           }
           *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (MODE == MODE_GELU_UP && pre != nullptr) *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a.u;
         }
       }
     }

@@ -94,6 +94,8 @@ struct GemmParams {
   const float* scale1;        // fp8 row scales of W8 [n_seg, Nn]
   const float* scale3;        // fp8 row scales of W8_3
   uint16_t* out;              // [rows, Nn]
+  uint16_t* pre;              // up modes: pre-activations [n_mat][rows, Nn] (bf16) or null
+  long long pre_plane;        // elements per plane of `pre`
   float* out_f;               // MODE_LOGITS: fp32 output
   const float* bias_f;        // MODE_LOGITS: fp32 bias [Nn] or null
   float* partials;            // K-part tiles of the 256-row list
@@ -105,7 +107,8 @@ template <int MODE, bool HAS_BIAS>
 __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, int lane, int kh, int l32, int wn,
                                               int r0, int r1, int n0, int Nn, int seg,
                                               const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                              const float* __restrict__ bias_f, float* __restrict__ out_f) {
+                                              const float* __restrict__ bias_f, float* __restrict__ out_f,
+                                              uint16_t* __restrict__ pre, long long pre_plane) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
@@ -140,6 +143,16 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
 #pragma unroll
           for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[32 + v]);
           *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (pre != nullptr) {
+            Vec8 a1, a3;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              a1.e[v] = f32_to_bf16(src[v]);
+              a3.e[v] = f32_to_bf16(src[32 + v]);
+            }
+            *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a1.u;
+            *reinterpret_cast<uint4*>(pre + pre_plane + (size_t)row * Nn + col) = a3.u;
+          }
         }
       }
     } else {
@@ -151,15 +164,17 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
           const float* src = ep + rr * 64 + c8;
           Vec8 b;
           if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-          Vec8 o;
+          Vec8 o, a;
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
             float x = src[v];
             if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+            a.e[v] = f32_to_bf16(x);
             if (MODE == MODE_GELU_UP) x = gelu_f(x);
             o.e[v] = f32_to_bf16(x);
           }
           *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (MODE == MODE_GELU_UP && pre != nullptr) *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a.u;
         }
       }
     }
@@ -294,7 +309,7 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
     store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                p.bias_f, p.out_f);
+                                p.bias_f, p.out_f, p.pre, p.pre_plane);
   } else {
     // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]
     float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2 + wn * 128 + l32;
@@ -432,7 +447,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
     store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                  p.bias_f, p.out_f);
+                                  p.bias_f, p.out_f, p.pre, p.pre_plane);
   } else {
     // fp32 partial tile, row-major [slot][64 rows][256 accumulator columns]
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
@@ -592,7 +607,7 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
     store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                  p.bias_f, p.out_f);
+                                  p.bias_f, p.out_f, p.pre, p.pre_plane);
   } else {
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
 #pragma unroll
@@ -704,20 +719,27 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
       *reinterpret_cast<float4*>(p.out_f + (size_t)row * p.Nn + col + 4) = o1;
       continue;
     }
-    Vec8 b, o;
+    Vec8 b, o, s1, s3;
     if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(p.bias + (size_t)w.seg * p.Nn + col);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = v1[e];
       if (MODE == MODE_SWIGLU_UP) {
+        s1.e[e] = f32_to_bf16(x);
+        s3.e[e] = f32_to_bf16(v3[e]);
         x = silu_f(x) * v3[e];
       } else {
         if (HAS_BIAS) x += bf16_to_f32(b.e[e]);
+        s1.e[e] = f32_to_bf16(x);
         if (MODE == MODE_GELU_UP) x = gelu_f(x);
       }
       o.e[e] = f32_to_bf16(x);
     }
     *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
+    if ((MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP) && p.pre != nullptr) {
+      *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = s1.u;
+      if (MODE == MODE_SWIGLU_UP) *reinterpret_cast<uint4*>(p.pre + p.pre_plane + (size_t)row * p.Nn + col) = s3.u;
+    }
   }
 }
 
@@ -803,6 +825,8 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.W3 = (const uint16_t*)g.w3;
   p.bias = (const uint16_t*)g.bias;
   p.out = (uint16_t*)g.out;
+  p.pre = (MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP) ? (uint16_t*)g.pre : nullptr;
+  p.pre_plane = (long long)g.max_rows * g.Nn;
   p.out_f = g.out_f32;
   p.bias_f = g.bias_f32;
   p.W8 = g.w8;

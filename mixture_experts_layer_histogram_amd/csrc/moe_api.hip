@@ -187,8 +187,9 @@ moe_status do_permute(const moe_config& c, const Workspace& W, const int32_t* to
 // token perm[r] / top_k (the gather of the dispatch done inside the GEMM).
 moe_status do_up(const moe_config& c, const Workspace& W, const void* a, const int32_t* offsets,
                  const void* w1, const void* w3, const void* b1, void* h, void* ws, hipStream_t s,
-                 bool shared, const int32_t* perm = nullptr) {
+                 bool shared, const int32_t* perm = nullptr, void* pre = nullptr) {
   GroupedGemmArgs g = gemm_args(c, W, ws, shared);
+  g.pre = pre;
   g.perm = perm;
   g.gather_k = c.top_k;
   g.a_rows = (int)c.n_tokens;
@@ -387,6 +388,31 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* x, const int3
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
     if (!any) return MOE_OK;
     return do_up(c, W, x, offsets, w1, w3, b1, h_tmp, ws, stream, false, perm);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_up_save(const moe_config* cfg, const void* x, const int32_t* perm, const int32_t* offsets,
+                              const void* w1, const void* w3, const void* b1, void* h_tmp, void* pre_act, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const bool any = c.n_tokens > 0;
+    if (!offsets || !w1 || (any && (!x || !perm || !h_tmp || !pre_act))) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_ARG;
+    if (c.act == MOE_ACT_GELU && w3) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b1) return MOE_ERR_ARG;
+    if (!gather_ok(c)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w1) || (w3 && !aligned16(w3)) || !aligned16(h_tmp) || !aligned16(pre_act) ||
+        (b1 && !aligned16(b1)))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    if (!any) return MOE_OK;
+    return do_up(c, W, x, offsets, w1, w3, b1, h_tmp, ws, stream, false, perm, pre_act);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -731,7 +757,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                 !sv->offsets || !sv->perm || !sv->slot_pos || !sv->y_perm))
       return MOE_ERR_ARG;
     if (!gather_ok(c)) return MOE_ERR_UNSUPPORTED;
-    const void* ptrs[] = {x, dout, gr->dx, sv->y_perm, w->w_router, w->w1, w->w3, w->w2, w->b1, w->b2,
+    const void* ptrs[] = {x, dout, gr->dx, sv->y_perm, sv->pre_act, w->w_router, w->w1, w->w3, w->w2, w->b1, w->b2,
                           w->sh_w1, w->sh_w3, w->sh_w2, gr->dw1, gr->dw3, gr->dw2, gr->dw_router};
     for (const void* p : ptrs)
       if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
@@ -770,12 +796,20 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     // token rows in expert order (zero rows, and zero dY, for padding rows)
     MOE_HIP(launch_gather_rows(x, sv->perm, sv->offsets, E, k, d, R, P(B.xg), P(B.dy), stream));
     // routed experts: recompute pre-activations, dH = dY W2_e, activation backward, dX = dA [W1_e ; W3_e]
-    MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w1, c.ffn_bias ? w->b1 : nullptr, d, F,
-                       P(B.a1), stream));
-    if (sw)
-      MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w3, nullptr, d, F, P(B.a3), stream));
+    // pre-activations: saved by moe_expert_up_save, or recomputed from the expert-ordered rows
+    const void* a1 = P(B.a1);
+    const void* a3 = sw ? P(B.a3) : nullptr;
+    if (sv->pre_act) {
+      a1 = sv->pre_act;
+      if (sw) a3 = static_cast<const uint16_t*>(sv->pre_act) + (size_t)R * F;
+    } else {
+      MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w1, c.ffn_bias ? w->b1 : nullptr, d, F,
+                         P(B.a1), stream));
+      if (sw)
+        MOE_TRY(plain_gemm(c, W, ws, false, P(B.xg), nullptr, sv->offsets, w->w3, nullptr, d, F, P(B.a3), stream));
+    }
     MOE_HIP(nn_routed(P(B.dy), w->w2, nullptr, d, d, F, P(B.dh)));
-    MOE_HIP(launch_act_backward(sw, P(B.a1), sw ? P(B.a3) : nullptr, P(B.dh), R, F, P(B.h), P(B.da), stream));
+    MOE_HIP(launch_act_backward(sw, a1, a3, P(B.dh), R, F, P(B.h), P(B.da), stream));
     MOE_HIP(nn_routed(P(B.da), w->w1, sw ? w->w3 : nullptr, nA * F, F, d, P(B.dX)));
     // expert weight gradients: reductions over each expert's rows
     MOE_HIP(launch_gemm_tn(P(B.dy), d, 0, P(B.h), F, sv->offsets, E, 0, (int)R, d, F, gr->dw2, (long long)d * F,

@@ -124,6 +124,7 @@ struct GroupedGemmArgs {
   const void* w3;        // SwiGLU up only
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
+  void* pre;             // up modes, bf16: pre-activations [n_mat][max_rows, Nn] (x W1^T (+ b1) [, x W3^T]) or NULL
   bool fp8;              // weights are E4M3 codes (w8, w8_3) with row scales (64-row tiles only)
   const uint8_t* w8;     // fp8 W1 (up) or W2 (down): [n_seg, Nn, K]
   const uint8_t* w8_3;   // fp8 W3 (SwiGLU up)

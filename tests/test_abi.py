@@ -131,3 +131,16 @@ def test_backward_errors_before_launch():
     cb = _cfg(act="gelu", ffn_bias=1)                                    # biases without their gradients
     Wg = _lib.MoeWeights(P, None, P, None, P, P, P, None, None, None)
     assert call(cb, Wt=Wg) == _lib.MOE_ERR_ARG
+
+
+def test_up_save_errors_before_launch():
+    L = M.lib()
+    P = 4096
+    c = _cfg()
+    # pre_act NULL, fp32 storage, misaligned pre_act
+    assert L.moe_expert_up_save(ctypes.byref(c), P, P, P, P, P, None, P, None, P, 1 << 40, None) == _lib.MOE_ERR_ARG
+    cf = _cfg(dtype="f32")
+    assert L.moe_expert_up_save(ctypes.byref(cf), P, P, P, P, P, None, P, P, P, 1 << 40,
+                                None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_up_save(ctypes.byref(c), P, P, P, P, P, None, P, P + 2, P, 1 << 40,
+                                None) == _lib.MOE_ERR_UNSUPPORTED

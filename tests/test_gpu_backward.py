@@ -29,9 +29,11 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).astype(np.float32)).to(torch.bfloat16).cuda()
 
 
-def _run_backward(cfg, inp, dout, d_aux):
+def _run_backward(cfg, inp, dout, d_aux, save_pre=False):
     """Forward through the step entry points, then moe_backward; returns the
-    device gradients, the device logits and a callable that repeats the backward."""
+    device gradients, the device logits and a callable that repeats the backward.
+    save_pre: the up-projection is moe_expert_up_save and the backward reuses its
+    pre-activations instead of recomputing them."""
     import torch
     import mixture_experts_layer_histogram_amd as M
     dev = M.upload_inputs(inp, "cuda")
@@ -52,7 +54,19 @@ def _run_backward(cfg, inp, dout, d_aux):
     M.route(c, dev["x"], dev["w_router"], idx, g, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"],
             logits=z, ws=ws)
     M.permute(c, idx, None, counts, offs, perm, sp, None, ws=ws)
-    M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+    pre = None
+    if save_pre:
+        n_mat = 2 if cfg.act == "swiglu" else 1
+        pre = torch.empty((n_mat, max(R, 1), F), dtype=st, device="cuda")
+        M.expert_up_save(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, pre, b1=dev["b1"], ws=ws)
+        h_ref = torch.empty_like(h)
+        M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h_ref, b1=dev["b1"], ws=ws)
+        torch.cuda.synchronize()
+        kept = int(offs[-1].item())
+        assert torch.equal(h[:kept], h_ref[:kept])      # saving changes nothing else
+        del h_ref
+    else:
+        M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
     M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
     del h, ws
     grads = {"dx": torch.empty((N, d), dtype=st, device="cuda"),
@@ -72,7 +86,7 @@ def _run_backward(cfg, inp, dout, d_aux):
         grads["dsh_w2"] = torch.empty((d, Fs), dtype=f32, device="cuda")
     bws = torch.empty(M.backward_workspace_size(c), dtype=torch.uint8, device="cuda")
     saved = {"logits": z, "topk_idx": idx, "gates": g, "counts": counts, "offsets": offs, "perm": perm,
-             "slot_pos": sp, "y_perm": y}
+             "slot_pos": sp, "y_perm": y, "pre_act": pre}
 
     def again():
         M.backward(c, dev, dev["x"], dout, saved, grads, d_aux=d_aux, ws=bws)
@@ -81,16 +95,20 @@ def _run_backward(cfg, inp, dout, d_aux):
     return grads, z, sp, again
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_backward_parity(name):
+SAVED = ["swiglu_rule_a", "gelu_bias_aux_capacity", "padded_choice"]
+
+
+@pytest.mark.parametrize("name,save_pre", [(n, False) for n in sorted(CASES)] + [(n, True) for n in SAVED],
+                         ids=[n for n in sorted(CASES)] + [n + "-saved_pre" for n in SAVED])
+def test_backward_parity(name, save_pre):
     cfg = CASES[name]
     say(f"backward {name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} F={cfg.d_ff} "
-        f"Fs={cfg.d_ff_shared} rule={cfg.gate_rule}")
+        f"Fs={cfg.d_ff_shared} rule={cfg.gate_rule} saved pre-activations={save_pre}")
     inp = make_inputs(cfg)
     rng = np.random.default_rng(99)
     dout = _bf16(rng.standard_normal((cfg.n_tokens, cfg.d_model)).astype(np.float32))
     d_aux = 0.5 if cfg.aux_loss else 0.0
-    grads, z, _, again = _run_backward(cfg, inp, dout, d_aux)
+    grads, z, _, again = _run_backward(cfg, inp, dout, d_aux, save_pre)
 
     ref = oracle.oracle_layer_backward(cfg, inp, host(dout), d_aux=d_aux, logits_override=host(z))
     tol = TOL["bf16"]
