@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace moe {
 
 // ----------------------------------------------------------------- combine backward
@@ -335,6 +337,13 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const uint16_t* __restri
   }
 }
 
+// Zero fill of an fp32 array (a kernel rather than a memset node, so callers
+// may capture it in a graph).
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
 // ----------------------------------------------------------------- launches
 hipError_t launch_combine_backward(const moe_config& c, const void* dout, const void* y, const int32_t* slot_pos,
                                    const float* gates, float* dg, void* dy, hipStream_t s) {
@@ -344,6 +353,13 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dout, const 
   hipLaunchKernelGGL(combine_backward_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s,
                      (const uint16_t*)dout, (const uint16_t*)y, slot_pos, gates, n_slots, c.top_k, c.d_model, dg,
                      (uint16_t*)dy);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

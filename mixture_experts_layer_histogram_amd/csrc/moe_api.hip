@@ -771,7 +771,24 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     auto P = [&](size_t o) { return wsp(ws, o); };
     float* dg = gr->dgates ? gr->dgates : reinterpret_cast<float*>(P(B.dg));
 
-    if (!any) return MOE_OK;
+    if (!any) {   // an empty batch: every weight gradient is zero
+      const size_t Fd = (size_t)F * d;
+      MOE_HIP(launch_fill_zero(gr->dw1, (size_t)E * Fd, stream));
+      MOE_HIP(launch_fill_zero(gr->dw2, (size_t)E * Fd, stream));
+      if (sw) MOE_HIP(launch_fill_zero(gr->dw3, (size_t)E * Fd, stream));
+      if (c.ffn_bias) {
+        MOE_HIP(launch_fill_zero(gr->db1, (size_t)E * F, stream));
+        MOE_HIP(launch_fill_zero(gr->db2, (size_t)E * d, stream));
+      }
+      if (gr->dw_router) MOE_HIP(launch_fill_zero(gr->dw_router, (size_t)E * d, stream));
+      if (gr->dlogit_bias) MOE_HIP(launch_fill_zero(gr->dlogit_bias, (size_t)E, stream));
+      if (shared) {
+        MOE_HIP(launch_fill_zero(gr->dsh_w1, (size_t)Fs * d, stream));
+        MOE_HIP(launch_fill_zero(gr->dsh_w3, (size_t)Fs * d, stream));
+        MOE_HIP(launch_fill_zero(gr->dsh_w2, (size_t)Fs * d, stream));
+      }
+      return MOE_OK;
+    }
     // every K-major row range the products address stays below 2^31 bytes
     const size_t lim = 0x7fffffffull;
     const size_t ld_routed = (size_t)std::max(d, nA * F), ld_dense = (size_t)std::max(std::max(B.ldz, d), 2 * Fs);

@@ -157,6 +157,7 @@ hipError_t launch_segment_colsum(const void* a, int lda, int col0, int ncols, co
                                  const int32_t* perm, int dense_rows, int n_seg, float* out, hipStream_t s);
 size_t colsum_part_floats(int rows, int cols);   // scratch of launch_colsum_f32
 hipError_t launch_colsum_f32(const float* a, int rows, int cols, float* part, float* out, hipStream_t s);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);   // n fp32 zeros
 hipError_t launch_gather_rows(const void* x, const int32_t* perm, const int32_t* offsets, int n_seg, int k, int d,
                               long long max_rows, void* xg, void* dy, hipStream_t s);
 // Tile lists of the grouped GEMM (kind 0: 256- and 64-row tiles, 1: 64-row only, 2: 256-row only).

@@ -21,6 +21,9 @@ CASES = {
     "padded_choice": SMALL["mixtral_prefill_small"].scaled(name="bw_padded_choice", n_tokens=500,
                                                            capacity_factor=1.25, capacity_layout="padded",
                                                            capacity_priority="choice"),
+    # E not a multiple of 64 (padded router width), k = 3, a ragged token count
+    "e100_k3": SMALL["mixtral_prefill_small"].scaled(name="bw_e100_k3", n_tokens=333, n_experts=100, top_k=3),
+    "one_token": SMALL["deepseek_v3_small"].scaled(name="bw_one_token", n_tokens=1),
 }
 
 
@@ -203,3 +206,24 @@ def test_backward_full_size(name):
     s_wr = float(dwr.double().sum(0).abs().max()) / max(float(dwr.abs().max()), 1e-30)
     say(f"  router: |sum_e dlogit_bias| {s_db:.3e}, |sum_e dw_router| {s_wr:.3e} (relative)")
     assert s_db <= 1e-3 and s_wr <= tol
+
+
+def test_backward_empty_batch():
+    """N = 0: no launches on token buffers; every weight gradient comes back zero."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    cfg = SMALL["deepseek_v3_small"].scaled(name="bw_empty", n_tokens=0)
+    inp = make_inputs(cfg)
+    dev = M.upload_inputs(inp, "cuda")
+    c = M.config_from(cfg)
+    E, d, F, Fs = cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    nan = float("nan")
+    grads = {"dw_router": torch.full((E, d), nan, device="cuda"), "dlogit_bias": torch.full((E,), nan, device="cuda"),
+             "dw1": torch.full((E, F, d), nan, device="cuda"), "dw3": torch.full((E, F, d), nan, device="cuda"),
+             "dw2": torch.full((E, d, F), nan, device="cuda"), "dsh_w1": torch.full((Fs, d), nan, device="cuda"),
+             "dsh_w3": torch.full((Fs, d), nan, device="cuda"), "dsh_w2": torch.full((d, Fs), nan, device="cuda")}
+    bws = torch.empty(max(M.backward_workspace_size(c), 1), dtype=torch.uint8, device="cuda")
+    M.backward(c, dev, None, None, {}, grads, d_aux=0.0, ws=bws)
+    torch.cuda.synchronize()
+    for n, t in grads.items():
+        assert torch.count_nonzero(t).item() == 0, n
