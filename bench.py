@@ -2,9 +2,10 @@
 
 One step = one pass of the whole layer over one batch of synthetic input:
 router GEMM + top-k -> histogram/scan/permute -> grouped expert GEMMs (up with
-the token-row gather and the activation fused, down) -> [shared expert] ->
-combine -> [aux loss] -> [bias step], each a C-ABI call into libmoe_hip.so on
-one HIP stream.
+the token-row gather and the activation fused) -> [shared expert] -> down
+projection -> combine (fused into the down projection's epilogue for top-1
+routing) -> [aux loss] -> [bias step], each a C-ABI call into libmoe_hip.so
+on one HIP stream.
 Inputs are resident in HBM before the timed region starts.
 
 Prints ONE JSON line.  `value` is layer tokens/s; `roofline` describes the
@@ -162,7 +163,7 @@ def main():
     sel_next = dev["sel_bias"].clone() if dev["sel_bias"] is not None else None
     residual = dev["x"] if cfg.residual else None
 
-    names = ["route", "permute", "expert_up", "expert_down", "shared", "combine", "aux_bias"]
+    names = ["route", "permute", "expert_up", "shared", "expert_down", "combine", "aux_bias"]
     bw = None
     if args.backward:
         if fp8 is not None or cfg.dtype != "bf16":
@@ -192,6 +193,8 @@ def main():
                     "perm": perm, "slot_pos": slot_pos, "y_perm": y, "pre_act": pre_act}
         bw = (dout, bw_grads, bw_ws, bw_saved)
 
+    fuse_combine = k == 1 and fp8 is None and bw is None and cfg.dtype == "bf16"
+
     def step(ev=None):
         def mark(i):
             if ev is not None:
@@ -210,15 +213,19 @@ def main():
             M.expert_up_fp8(c, dev["x"], perm, offs, fp8["w1"][0], fp8["w3"][0], fp8["w1"][1], fp8["w3"][1], h,
                             b1=dev["b1"], ws=ws)
         mark(3)
-        if fp8 is None:
+        if Fs:
+            M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], h_sh, y_sh, ws=ws)
+        mark(4)
+        if fuse_combine:   # top-1: the combine runs in the down projection's epilogue
+            M.expert_down_combine(c, h, offs, perm, slot_pos, gates, dev["w2"], out, b2=dev["b2"],
+                                  residual=residual, shared_y=y_sh, ws=ws)
+        elif fp8 is None:
             M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
         else:
             M.expert_down_fp8(c, h, offs, fp8["w2"][0], fp8["w2"][1], y, b2=dev["b2"], ws=ws)
-        mark(4)
-        if Fs:
-            M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], h_sh, y_sh, ws=ws)
         mark(5)
-        M.combine(c, y, slot_pos, gates, out, residual=residual, shared_y=y_sh)
+        if not fuse_combine:
+            M.combine(c, y, slot_pos, gates, out, residual=residual, shared_y=y_sh)
         mark(6)
         if cfg.aux_loss:
             M.aux_loss(c, counts, probsum, aux)

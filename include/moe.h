@@ -208,6 +208,26 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32
                            const void* w2, const void* b2, void* y_perm,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_expert_down with the combine fused into its epilogue, for top-1 routing
+ * (top_k = 1; [X] "Deep dive": dispatch and combine fused into the expert
+ * compute; [G] "Load balancing and expert capacity": a token over capacity
+ * keeps the residual).  Each token has at most one slot, so the row holding
+ * it is the token's only writer:
+ *   out[t] = [residual_t] + [shared_y_t] + gates[t] * Y_row   (kept slot)
+ *   out[t] = [residual_t] + [shared_y_t]                       (dropped)
+ * with Y_row = h_row W2_e^T [+ b2_e] rounded to bf16 first, fp32 sums, one
+ * rounding: bit-identical to moe_expert_down followed by moe_combine.
+ *   perm [R], slot_pos [N], gates [N] from moe_route / moe_permute;
+ *   residual, shared_y [N, d] or NULL; out [N, d].  No y_perm is written
+ *   (moe_backward needs the unfused moe_expert_down).
+ * Errors: MOE_ERR_UNSUPPORTED for top_k != 1, fp32 storage or a pointer not
+ * 16-byte aligned; otherwise as moe_expert_down. */
+moe_status moe_expert_down_combine(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
+                                   const int32_t* perm, const int32_t* slot_pos, const float* gates,
+                                   const void* w2, const void* b2, const void* residual,
+                                   const void* shared_y, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* fp8 weight-only experts ([S] "How sparse models scale": quantised weights are
  * how large MoE models fit in memory; the format here is OCP E4M3, round to
  * nearest).  Each row of a weight matrix stored [out, in] gets one fp32 scale:

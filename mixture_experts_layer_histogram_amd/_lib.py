@@ -67,6 +67,8 @@ _SIGS = {
     "moe_expert_up_gather": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up_save": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_expert_down_combine": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t,
+                                _P],
     "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P],
     "moe_expert_up_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
@@ -194,6 +196,14 @@ def expert_up_save(cfg, x, perm, offsets, w1, w3, h_tmp, pre_act, b1=None, ws=No
     wp, wb = _ws(ws)
     _call("moe_expert_up_save", ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(w1), _ptr(w3),
           _ptr(b1), _ptr(h_tmp), _ptr(pre_act), wp, wb, _stream(stream))
+
+
+def expert_down_combine(cfg, h_tmp, offsets, perm, slot_pos, gates, w2, out, b2=None, residual=None, shared_y=None,
+                        ws=None, stream=None):
+    """moe_expert_down_combine: top-1 down projection with the gate-weighted combine in its epilogue."""
+    wp, wb = _ws(ws)
+    _call("moe_expert_down_combine", ctypes.byref(cfg), _ptr(h_tmp), _ptr(offsets), _ptr(perm), _ptr(slot_pos),
+          _ptr(gates), _ptr(w2), _ptr(b2), _ptr(residual), _ptr(shared_y), _ptr(out), wp, wb, _stream(stream))
 
 
 def quantize_fp8(w, q, scales, stream=None):

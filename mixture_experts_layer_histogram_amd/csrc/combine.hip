@@ -75,6 +75,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   }
 }
 
+// Top-1 routing with the combine fused into the down projection: a token whose
+// slot was dropped gets out = [residual] + [shared_y] (the same fp32 sum and
+// single rounding as combine_kernel).  One wavefront per token, 16-byte lanes.
+__global__ __launch_bounds__(256) void combine_dropped_kernel(const int32_t* __restrict__ slot_pos,
+                                                              const uint16_t* __restrict__ res,
+                                                              const uint16_t* __restrict__ sh,
+                                                              uint16_t* __restrict__ out, int N, int d) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= N || slot_pos[t] >= 0) return;
+  const size_t trow = (size_t)t * d;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+    if (res) {
+      Vec8 r;
+      r.u = *reinterpret_cast<const uint4*>(res + trow + c);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[v] = bf16_to_f32(r.e[v]);
+    }
+    if (sh) {
+      Vec8 y;
+      y.u = *reinterpret_cast<const uint4*>(sh + trow + c);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[v] += bf16_to_f32(y.e[v]);
+    }
+    Vec8 o;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(acc[v]);
+    *reinterpret_cast<uint4*>(out + trow + c) = o.u;
+  }
+}
+
+hipError_t launch_combine_dropped(const moe_config& c, const int32_t* slot_pos, const void* residual,
+                                  const void* shared_y, void* out, hipStream_t s) {
+  const int N = (int)c.n_tokens;
+  if (N == 0) return hipSuccess;
+  if (c.top_k != 1 || c.d_model % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_dropped_kernel, dim3((N + 3) / 4), dim3(256), 0, s, slot_pos,
+                     (const uint16_t*)residual, (const uint16_t*)shared_y, (uint16_t*)out, N, c.d_model);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,
                           void* out, hipStream_t s) {

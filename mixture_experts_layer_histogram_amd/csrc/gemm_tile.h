@@ -127,6 +127,44 @@ __device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, c
   return w;
 }
 
+// Gate-weighted combine in the down projection's epilogue (top-1 routing: a
+// token has at most one slot, so the row holding it is the token's only
+// writer).  Same arithmetic as the separate combine: Y rounded to bf16, then
+// out = bf16(fma(g, Y, [residual] + [shared_y])).
+struct CombineOut {
+  const int32_t* perm;        // expert-order row -> slot id (= token); < 0: padding row
+  const float* gates;         // [N]
+  const uint16_t* residual;   // [N, Nn] or null
+  const uint16_t* shared_y;   // [N, Nn] or null
+  uint16_t* out;              // [N, Nn]; null: no fused combine
+};
+
+__device__ __forceinline__ void combine_store8(const CombineOut& cmb, int row, int col, int Nn, const Vec8& y) {
+  const int t = cmb.perm[row];
+  if (t < 0) return;
+  const float g = cmb.gates[t];
+  const size_t o = (size_t)t * Nn + col;
+  float acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+  if (cmb.residual) {
+    Vec8 r;
+    r.u = *reinterpret_cast<const uint4*>(cmb.residual + o);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = bf16_to_f32(r.e[v]);
+  }
+  if (cmb.shared_y) {
+    Vec8 sy;
+    sy.u = *reinterpret_cast<const uint4*>(cmb.shared_y + o);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] += bf16_to_f32(sy.e[v]);
+  }
+  Vec8 ov;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) ov.e[v] = f32_to_bf16(fmaf(g, bf16_to_f32(y.e[v]), acc[v]));
+  *reinterpret_cast<uint4*>(cmb.out + o) = ov.u;
+}
+
 // Epilogue of one 128 x 128 wavefront block (rows r0 + wm*128 .., columns of
 // the output n0 ..): activation, bias, bf16 rounding, 16-byte stores.
 // `ep` is this wavefront's 16 KB of LDS; `src_acc` the accumulators.
@@ -135,7 +173,8 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
                                             int wn, int r0, int r1, int n0, int Nn, int seg,
                                             const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                             const float* __restrict__ bias_f, float* __restrict__ out_f,
-                                            uint16_t* __restrict__ pre = nullptr, long long pre_plane = 0) {
+                                            uint16_t* __restrict__ pre = nullptr, long long pre_plane = 0,
+                                            const CombineOut* cmb = nullptr) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -200,7 +239,8 @@ __device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int 
             if (MODE == MODE_GELU_UP) x = gelu_f(x);
             o.e[v] = f32_to_bf16(x);
           }
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (MODE == MODE_DOWN && cmb != nullptr && cmb->out != nullptr) combine_store8(*cmb, row, col, Nn, o);
+          else *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
           if (MODE == MODE_GELU_UP && pre != nullptr) *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a.u;
         }
       }

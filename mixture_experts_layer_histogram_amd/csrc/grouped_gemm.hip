@@ -95,6 +95,7 @@ struct GemmParams {
   const float* scale3;        // fp8 row scales of W8_3
   uint16_t* out;              // [rows, Nn]
   uint16_t* pre;              // up modes: pre-activations [n_mat][rows, Nn] (bf16) or null
+  CombineOut cmb;             // down mode: fused top-1 combine (cmb.out null: plain Y)
   long long pre_plane;        // elements per plane of `pre`
   float* out_f;               // MODE_LOGITS: fp32 output
   const float* bias_f;        // MODE_LOGITS: fp32 bias [Nn] or null
@@ -108,7 +109,8 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
                                               int r0, int r1, int n0, int Nn, int seg,
                                               const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                               const float* __restrict__ bias_f, float* __restrict__ out_f,
-                                              uint16_t* __restrict__ pre, long long pre_plane) {
+                                              uint16_t* __restrict__ pre, long long pre_plane,
+                                              const CombineOut* cmb) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
@@ -173,7 +175,8 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
             if (MODE == MODE_GELU_UP) x = gelu_f(x);
             o.e[v] = f32_to_bf16(x);
           }
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          if (MODE == MODE_DOWN && cmb->out != nullptr) combine_store8(*cmb, row, col, Nn, o);
+          else *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
           if (MODE == MODE_GELU_UP && pre != nullptr) *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a.u;
         }
       }
@@ -309,7 +312,7 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
     store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                p.bias_f, p.out_f, p.pre, p.pre_plane);
+                                p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
   } else {
     // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]
     float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2 + wn * 128 + l32;
@@ -447,7 +450,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
     store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                  p.bias_f, p.out_f, p.pre, p.pre_plane);
+                                  p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
   } else {
     // fp32 partial tile, row-major [slot][64 rows][256 accumulator columns]
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
@@ -607,7 +610,7 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
   if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wn * (32 * 64);
     store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                  p.bias_f, p.out_f, p.pre, p.pre_plane);
+                                  p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
   } else {
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
 #pragma unroll
@@ -735,7 +738,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
       }
       o.e[e] = f32_to_bf16(x);
     }
-    *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
+    if (MODE == MODE_DOWN && p.cmb.out != nullptr) combine_store8(p.cmb, row, col, p.Nn, o);
+    else *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
     if ((MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP) && p.pre != nullptr) {
       *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = s1.u;
       if (MODE == MODE_SWIGLU_UP) *reinterpret_cast<uint4*>(p.pre + p.pre_plane + (size_t)row * p.Nn + col) = s3.u;
@@ -827,6 +831,11 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.out = (uint16_t*)g.out;
   p.pre = (MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP) ? (uint16_t*)g.pre : nullptr;
   p.pre_plane = (long long)g.max_rows * g.Nn;
+  p.cmb.perm = g.comb_perm;
+  p.cmb.gates = g.comb_gates;
+  p.cmb.residual = (const uint16_t*)g.comb_residual;
+  p.cmb.shared_y = (const uint16_t*)g.comb_shared;
+  p.cmb.out = MODE == MODE_DOWN ? (uint16_t*)g.comb_out : nullptr;
   p.out_f = g.out_f32;
   p.bias_f = g.bias_f32;
   p.W8 = g.w8;
@@ -854,6 +863,8 @@ static void launch_f32(const GroupedGemmArgs& g, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   if (g.max_rows <= 0) return hipSuccess;
+  if (g.comb_out && (g.dtype != MOE_BF16 || g.mode != MODE_DOWN || !g.comb_perm || !g.comb_gates))
+    return hipErrorInvalidValue;
   const bool hb = g.bias != nullptr;
   if (g.dtype == MOE_F32) {
     if (g.mode == MODE_SWIGLU_UP) launch_f32<MODE_SWIGLU_UP, false>(g, s);

@@ -249,9 +249,26 @@ moe_status do_down_fp8(const moe_config& c, const Workspace& W, const void* h, c
   return MOE_OK;
 }
 
+// Top-1 combine fused into the routed down projection (see moe_expert_down_combine).
+struct FusedCombine {
+  const int32_t* perm;
+  const float* gates;
+  const void* residual;
+  const void* shared_y;
+  void* out;
+};
+
 moe_status do_down(const moe_config& c, const Workspace& W, const void* h, const int32_t* offsets,
-                   const void* w2, const void* b2, void* y, void* ws, hipStream_t s, bool shared) {
+                   const void* w2, const void* b2, void* y, void* ws, hipStream_t s, bool shared,
+                   const FusedCombine* fc = nullptr) {
   GroupedGemmArgs g = gemm_args(c, W, ws, shared);
+  if (fc) {
+    g.comb_perm = fc->perm;
+    g.comb_gates = fc->gates;
+    g.comb_residual = fc->residual;
+    g.comb_shared = fc->shared_y;
+    g.comb_out = fc->out;
+  }
   g.mode = MODE_DOWN;
   g.K = shared ? c.d_ff_shared : c.d_ff;
   g.Nn = c.d_model;
@@ -413,6 +430,31 @@ moe_status moe_expert_up_save(const moe_config* cfg, const void* x, const int32_
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
     if (!any) return MOE_OK;
     return do_up(c, W, x, offsets, w1, w3, b1, h_tmp, ws, stream, false, perm, pre_act);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_down_combine(const moe_config* cfg, const void* h_tmp, const int32_t* offsets,
+                                   const int32_t* perm, const int32_t* slot_pos, const float* gates, const void* w2,
+                                   const void* b2, const void* residual, const void* shared_y, void* out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    if (c.top_k != 1 || c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const bool any = c.n_tokens > 0;
+    if (!offsets || !w2 || (any && (!h_tmp || !perm || !slot_pos || !gates || !out))) return MOE_ERR_ARG;
+    if (c.ffn_bias && !b2) return MOE_ERR_ARG;
+    if (!aligned16(h_tmp) || !aligned16(w2) || !aligned16(out) || (b2 && !aligned16(b2)) ||
+        (residual && !aligned16(residual)) || (shared_y && !aligned16(shared_y)))
+      return MOE_ERR_UNSUPPORTED;
+    const Workspace W = workspace_layout(c);
+    MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
+    if (!any) return MOE_OK;
+    MOE_HIP(launch_combine_dropped(c, slot_pos, residual, shared_y, out, stream));
+    const FusedCombine fc{perm, gates, residual, shared_y, out};
+    return do_down(c, W, h_tmp, offsets, w2, b2, nullptr, ws, stream, false, &fc);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -615,7 +657,6 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     MOE_TRY(do_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop, x_perm, ws, stream));
     if (fused) MOE_TRY(do_up(c, W, x, offsets, w->w1, w->w3, w->b1, h, ws, stream, false, perm));
     else MOE_TRY(do_up(c, W, x_perm, offsets, w->w1, w->w3, w->b1, h, ws, stream, false));
-    MOE_TRY(do_down(c, W, h, offsets, w->w2, w->b2, y, ws, stream, false));
     const void* shared_y = nullptr;
     if (c.d_ff_shared > 0) {
       void* h_sh = wsp(ws, W.h_sh);
@@ -624,7 +665,14 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
       MOE_TRY(do_down(c, W, h_sh, nullptr, w->sh_w2, nullptr, y_sh, ws, stream, true));
       shared_y = y_sh;
     }
-    MOE_HIP(launch_combine(c, y, slot_pos, gates, res, shared_y, o->out, stream));
+    if (c.top_k == 1 && c.dtype == MOE_BF16) {   // one slot per token: combine in the down projection
+      MOE_HIP(launch_combine_dropped(c, slot_pos, res, shared_y, o->out, stream));
+      const FusedCombine fc{perm, gates, res, shared_y, o->out};
+      MOE_TRY(do_down(c, W, h, offsets, w->w2, w->b2, y, ws, stream, false, &fc));
+    } else {
+      MOE_TRY(do_down(c, W, h, offsets, w->w2, w->b2, y, ws, stream, false));
+      MOE_HIP(launch_combine(c, y, slot_pos, gates, res, shared_y, o->out, stream));
+    }
     if (want_aux) MOE_HIP(launch_aux_loss(c, counts, probsum, o->aux, stream));
     if (o->bias_gamma > 0.f) {
       int8_t* signs = o->signs ? o->signs : reinterpret_cast<int8_t*>(wsp(ws, W.signs));

@@ -125,6 +125,13 @@ struct GroupedGemmArgs {
   const void* bias;      // b1 (up) / b2 (down) or NULL: [n_seg, Nn]
   void* out;             // [rows, Nn]
   void* pre;             // up modes, bf16: pre-activations [n_mat][max_rows, Nn] (x W1^T (+ b1) [, x W3^T]) or NULL
+  // down mode, bf16, top-1 routing: gate-weighted combine in the epilogue instead of writing `out`:
+  // out_tok[t] = [residual_t] + [shared_y_t] + gate_t * Y_row for the row whose slot is t = comb_perm[row]
+  const int32_t* comb_perm;
+  const float* comb_gates;
+  const void* comb_residual;
+  const void* comb_shared;
+  void* comb_out;
   bool fp8;              // weights are E4M3 codes (w8, w8_3) with row scales (64-row tiles only)
   const uint8_t* w8;     // fp8 W1 (up) or W2 (down): [n_seg, Nn, K]
   const uint8_t* w8_3;   // fp8 W3 (SwiGLU up)
@@ -180,6 +187,10 @@ hipError_t launch_router_backward(const moe_config& c, const float* z, const int
 hipError_t launch_dx_gather(const moe_config& c, const void* dout, const void* dX, const int32_t* slot_pos,
                             const void* dxs, const void* dxr, void* dx, hipStream_t s);
 
+// Top-1 routing with the combine fused into the down projection: the tokens that
+// kept no slot get out = [residual] + [shared_y] here.
+hipError_t launch_combine_dropped(const moe_config& c, const int32_t* slot_pos, const void* residual,
+                                  const void* shared_y, void* out, hipStream_t s);
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_pos,
                           const float* gates, const void* residual, const void* shared_y,
                           void* out, hipStream_t s);

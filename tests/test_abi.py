@@ -144,3 +144,17 @@ def test_up_save_errors_before_launch():
                                 None) == _lib.MOE_ERR_UNSUPPORTED
     assert L.moe_expert_up_save(ctypes.byref(c), P, P, P, P, P, None, P, P + 2, P, 1 << 40,
                                 None) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_down_combine_errors_before_launch():
+    L = M.lib()
+    P = 4096
+    c2 = _cfg()                       # top_k = 2: the fused combine needs one slot per token
+    args = (P, P, P, P, P, P, None, None, None, P, P, 1 << 40, None)
+    assert L.moe_expert_down_combine(ctypes.byref(c2), *args) == _lib.MOE_ERR_UNSUPPORTED
+    c1 = _cfg(top_k=1)
+    assert L.moe_expert_down_combine(ctypes.byref(_cfg(top_k=1, dtype="f32")), *args) == _lib.MOE_ERR_UNSUPPORTED
+    bad = (P, P, P, P, P, P, None, None, None, None, P, 1 << 40, None)   # NULL out
+    assert L.moe_expert_down_combine(ctypes.byref(c1), *bad) == _lib.MOE_ERR_ARG
+    mis = (P, P, P, P, P, P, None, None, None, P + 2, P, 1 << 40, None)  # misaligned out
+    assert L.moe_expert_down_combine(ctypes.byref(c1), *mis) == _lib.MOE_ERR_UNSUPPORTED

@@ -195,3 +195,52 @@ def test_router_paths_agree():
             zs.append(zh)
         assert rel_err(zs[0], zs[1]) <= 1e-5, (name, rel_err(zs[0], zs[1]))
         assert np.array_equal(zs[0], o["logits"]), name   # moe_forward takes the GEMM path
+
+
+@pytest.mark.parametrize("variant", ["shared_no_residual", "padded_capacity"])
+def test_down_combine_matches_unfused(variant):
+    """moe_expert_down_combine (top-1: the gate-weighted combine in the down
+    projection's epilogue) gives the bits of moe_expert_down + moe_combine,
+    including dropped tokens, padding rows and a shared expert."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    if variant == "shared_no_residual":
+        cfg = SMALL["deepseek_v3_small"].scaled(name="top1_shared", top_k=1, residual=False, n_tokens=700)
+    else:
+        cfg = SMALL["switch_skewed_small"].scaled(name="top1_padded", capacity_layout="padded",
+                                                  capacity_priority="choice")
+    inp = make_inputs(cfg)
+    dev = M.upload_inputs(inp, "cuda")
+    c = M.config_from(cfg)
+    N, E, d, F, Fs = cfg.n_tokens, cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    R = M._lib.expert_rows(c)
+    st = torch.bfloat16
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((N, 1), dtype=torch.int32, device="cuda")
+    g = torch.empty((N, 1), dtype=torch.float32, device="cuda")
+    z = torch.empty((N, E), dtype=torch.float32, device="cuda")
+    M.route(c, dev["x"], dev["w_router"], idx, g, logit_bias=dev["logit_bias"], sel_bias=dev["sel_bias"], logits=z,
+            ws=ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(max(R, 1), dtype=torch.int32, device="cuda")
+    sp = torch.empty(N, dtype=torch.int32, device="cuda")
+    M.permute(c, idx, None, counts, offs, perm, sp, None, ws=ws)
+    h = torch.empty((max(R, 1), F), dtype=st, device="cuda")
+    M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h, b1=dev["b1"], ws=ws)
+    ysh = None
+    if Fs:
+        hsh = torch.empty((N, Fs), dtype=st, device="cuda")
+        ysh = torch.empty((N, d), dtype=st, device="cuda")
+        M.shared_ffn(c, dev["x"], dev["sh_w1"], dev["sh_w3"], dev["sh_w2"], hsh, ysh, ws=ws)
+    res = dev["x"] if cfg.residual else None
+    y = torch.empty((max(R, 1), d), dtype=st, device="cuda")
+    M.expert_down(c, h, offs, dev["w2"], y, b2=dev["b2"], ws=ws)
+    ref = torch.empty((N, d), dtype=st, device="cuda")
+    M.combine(c, y, sp, g, ref, residual=res, shared_y=ysh)
+    out = torch.full((N, d), float("nan"), dtype=st, device="cuda")
+    M.expert_down_combine(c, h, offs, perm, sp, g, dev["w2"], out, b2=dev["b2"], residual=res, shared_y=ysh, ws=ws)
+    torch.cuda.synchronize()
+    dropped = int((host(sp) < 0).sum())
+    say(f"down_combine {variant}: N={N} E={E} dropped={dropped}")
+    assert np.array_equal(host(out), host(ref))
