@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of a single-GPU sparse Mixture-of-Experts FFN layer (forward
- * pass) for AMD Instinct MI355X (gfx950).
+ * pass, and its backward for training) for AMD Instinct MI355X (gfx950).
  *
  * The layer, as the pages describing it define it:
  *   [L] "Mixture of Experts (MoE)", AI Engineering from Scratch, Phase 07
@@ -13,7 +13,9 @@
  *   [G] "Mixture of Experts (MoE)" glossary (ultralytics.com): "How an MoE
  *       layer works", "Load balancing and expert capacity".
  *   [X] "Expert Parallelism for MoE Serving" (aiunderstanding.org):
- *       "Deep dive", "Technical insight" (dispatch by expert, capacity).
+ *       "Deep dive", "Technical insight" (dispatch by expert, capacity),
+ *       "Future of expert parallelism for MoE serving" (fused dispatch and
+ *       compute kernels, grouped GEMMs over many experts).
  *   [S] "How sparse models scale" (ircnf.com): quantised weights as the
  *       remedy for the memory size of large MoE models.
  *
@@ -123,7 +125,8 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *   logit_bias [E] fp32 | NULL   fixed offset added to every token's logits
  *   sel_bias   [E] fp32 | NULL   selection-only bias ([L] DeepSeek-V3 approach); never enters a gate
  *   logits_in  [N, E] fp32 | NULL  if given, used as the logits (the GEMM is skipped)
- *   logits     [N, E] fp32 | NULL  out: z = x W_r^T + logit_bias (copied from logits_in if given)
+ *   logits     [N, E] fp32   out: z = x W_r^T + logit_bias (required when N > 0 unless logits_in is
+ *              given; with logits_in it may be NULL, else receives a copy)
  *   topk_idx   [N, k] int32  out: chosen experts, descending key, exact ties to the lower index
  *   gates      [N, k] fp32   out: gate weights by `gate_rule`
  *   probsum    [E] fp32 | NULL   out: sum over tokens of softmax(z)[t, e] (for moe_aux_loss)
@@ -155,18 +158,19 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *                              where perm[p] = -1);
  *                              NULL skips the row copy (moe_expert_up_gather then
  *                              reads the token rows through perm)
- * Each expert keeps its first C slots in ascending slot id. */
+ * Each expert keeps its first C slots in the order cfg->capacity_priority
+ * names (ascending slot id by default). */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
                        int64_t* drop_count, void* x_perm, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
 /* Grouped expert FFN over the ragged expert segments of x_perm ([L] "FFN swap";
- * [X] "Future": grouped GEMMs that batch many experts).  Rows
+ * [X] "Future of expert parallelism": grouped GEMMs that batch many experts).  Rows
  * [offsets[e], offsets[e+1]) of x_perm go through expert e.
  *   w3 must be NULL for MOE_ACT_GELU; b1, b2 are NULL unless cfg->ffn_bias.
- *   h_tmp  [N k, F]  scratch/out: activated hidden rows (storage dtype)
- *   y_perm [N k, d]  out: expert outputs in x_perm's row order (storage dtype)
+ *   h_tmp  [R, F]  scratch/out: activated hidden rows (storage dtype)
+ *   y_perm [R, d]  out: expert outputs in x_perm's row order (storage dtype)
  * Equivalent to moe_expert_up followed by moe_expert_down. */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
                           const void* w1, const void* w3, const void* w2,
@@ -179,10 +183,10 @@ moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_expert_up with the dispatch gather fused into the GEMM's operand loads
- * ([X] "Future": fused dispatch and compute kernels): row p of the expert order
+ * ([X] "Future of expert parallelism": fused dispatch and compute kernels): row p of the expert order
  * is token row x[perm[p] / k], so no x_perm copy is made.
  *   x     [N, d]     token rows
- *   perm  [N k] int32  from moe_permute
+ *   perm  [R] int32  from moe_permute
  * Results are bit-identical to moe_expert_up on the gathered x_perm.
  * MOE_ERR_UNSUPPORTED when a bf16 x exceeds 2 GiB - 1 MiB (the kernel's 32-bit
  * buffer offsets); moe_forward then falls back to the copy. */
@@ -209,7 +213,7 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h_tmp, const int32
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_expert_down with the combine fused into its epilogue, for top-1 routing
- * (top_k = 1; [X] "Deep dive": dispatch and combine fused into the expert
+ * (top_k = 1; [X] "Future of expert parallelism": dispatch and combine fused into the expert
  * compute; [G] "Load balancing and expert capacity": a token over capacity
  * keeps the residual).  Each token has at most one slot, so the row holding
  * it is the token's only writer:
