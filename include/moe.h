@@ -317,7 +317,7 @@ typedef struct moe_outputs {
   float*   gates;            /* [N, k] */
   int32_t* counts;           /* [E] pre-drop */
   int32_t* offsets;          /* [E+1] */
-  int32_t* perm;             /* [N k] */
+  int32_t* perm;             /* [R] */
   int32_t* slot_pos;         /* [N k] */
   int64_t* drop_count;       /* scalar */
   float*   probsum;          /* [E] */
@@ -329,7 +329,11 @@ typedef struct moe_outputs {
 } moe_outputs;
 
 /* The whole layer: route -> permute -> grouped expert FFN -> [shared expert]
- * -> combine -> [aux loss] -> [bias step], all enqueued on `stream`.
+ * -> combine -> [aux loss] -> [bias step], all enqueued on `stream`.  The
+ * up projection gathers the token rows itself (moe_expert_up_gather) when
+ * the token matrix fits its 32-bit offsets; with top_k = 1 and bf16 storage
+ * the combine runs in the down projection's epilogue
+ * (moe_expert_down_combine).  Both are bit-identical to the unfused steps.
  *   x        [N, d]; residual [N, d] | NULL (NULL with add_residual = 1 uses x)
  *   sel_bias [E] fp32 | NULL (selection bias used by this pass) */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
