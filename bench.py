@@ -303,7 +303,8 @@ def main():
                    "used_experts": used,
                    "expert_weights": "fp8_e4m3_row_scaled" if fp8 is not None else cfg.dtype},
         "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
-                               "(build_tiles_kernel, grouped_gemm_kernel, split_fixup_kernel; one "
+                               "(build_tiles_kernel, grouped_gemm_big_kernel, grouped_gemm_small_kernel, "
+                               "split_fixup_kernel; one "
                                f"{'moe_expert_up_fp8' if fp8 is not None else ('moe_expert_up_save' if bw is not None else 'moe_expert_up_gather')} call)",
                      **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop},
         "expert_gemm_tflops": expert_tflops,

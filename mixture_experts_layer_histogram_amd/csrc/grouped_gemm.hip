@@ -12,9 +12,10 @@
 // Work decomposition.  A one-workgroup kernel turns `offsets` into two tile
 // lists on the device (256-row tiles for long segments, 64-row tiles for
 // short segments and short tails), so the host never waits for the routing
-// result.  One persistent kernel runs both kinds of tile: the 256-row tiles
-// are bound by the matrix cores, the 64-row tiles by streaming the expert's
-// weights, and interleaving them on every XCD lets one kind hide the other.
+// result.  Two persistent kernels follow it on the stream, one per list: the
+// 256-row tiles are bound by the matrix cores and run on 8 wavefronts per CU,
+// the 64-row tiles are bound by streaming the expert's weights and run on 4.
+// A K-split fix-up kernel closes the call.
 //
 // MFMA 32x32x16 layout (lane l): A row l%32, k = 8*(l/32)..+7; B column l%32,
 // same k; D column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
@@ -104,15 +105,15 @@ struct GemmParams {
   int K, Nn, n_ntiles;
 };
 
-template <int MODE, bool HAS_BIAS>
-__device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, int lane, int kh, int l32, int wn,
+template <int MODE, bool HAS_BIAS, int NMI = 2>
+__device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, int lane, int kh, int l32, int wn,
                                               int r0, int r1, int n0, int Nn, int seg,
                                               const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
                                               const float* __restrict__ bias_f, float* __restrict__ out_f,
                                               uint16_t* __restrict__ pre, long long pre_plane,
                                               const CombineOut* cmb) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < NMI; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -186,145 +187,184 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[2][2], float* ep, in
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tile (long segments: the routed experts of prefill batches and
-// the shared expert).
+// 256 x 256 tile (long segments: the routed experts of prefill batches, the
+// shared expert, the router logits).
 //
-// 256 threads = 4 wavefronts in a 2x2 layout; each wavefront owns a 128 x 128
-// block = 4 x 4 MFMA 32x32x16 blocks whose 256 fp32 accumulators per lane
-// live in AGPRs (one workgroup per CU).  Two 64 KB LDS stages; the loads for
-// step k+1 are issued in slices between the MFMAs of the first three
-// sub-steps of step k, and the fragments of each 16-wide sub-step are read
-// from LDS while the previous sub-step's 16 MFMAs issue.  One fence-free
-// barrier per step.
-//   SwiGLU up : the B tile holds 128 rows of W1 and the same 128 rows of W3,
-//               and each wavefront owns matching W1/W3 column blocks, so the
-//               epilogue forms SiLU(a1) * a3 in registers and writes bf16 H.
+// 512 threads = 8 wavefronts, two per SIMD, in a 2 x 4 layout; each wavefront
+// owns a 128 x 64 block = 4 x 2 MFMA 32x32x16 blocks (128 fp32 accumulators
+// per lane), so while one wavefront of a SIMD waits on its loads or fragment
+// reads the other issues MFMAs; s_setprio favours the wavefront that is in
+// its MFMA run.  Two 64 KB LDS stages (A 256 rows, B 256 rows, 128 bytes
+// each); the loads for step k+1 are issued in slices between the MFMAs of the
+// first two sub-steps of step k, and the fragments of each 16-wide sub-step
+// are read from LDS while the previous sub-step's 8 MFMAs issue.  One
+// fence-free barrier per step.
+//   SwiGLU up : the B tile holds 128 rows of W1 and the same 128 rows of W3;
+//               wavefront wn owns W1 columns 32 wn .. 32 wn + 31 (B rows
+//               32 wn + ..) and the same W3 columns (B rows 128 + 32 wn + ..),
+//               so the epilogue forms SiLU(a1) * a3 in registers and writes
+//               bf16 H.
 //   GELU up   : GELU(acc + b1) -> bf16 H.
-//   down      : acc (+ b2) -> bf16 Y.
+//   down      : acc (+ b2) -> bf16 Y, or the fused top-1 combine.
+//   logits    : acc (+ fp32 bias) -> fp32.
 template <int MODE, bool HAS_BIAS, bool GATHER>
 __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uint16_t* lds, int wave, int lane) {
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, kh = lane >> 5;
   const size_t wstride = (size_t)p.Nn * p.K;
   const int rowbytes = p.K * 2;
-  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  constexpr bool SW = MODE == MODE_SWIGLU_UP;
+  constexpr int cols_per_tile = SW ? kBN2 / 2 : kBN2;
 
-  // DMA: wavefront w fills rows 64w..64w+63 of both operands, 8 rows per
-  // instruction; lane -> row (lane >> 3), slot lane & 7 holding chunk slot ^ g(row).
-  int voff[8], voffb[8];
+  // DMA: wavefront w fills rows 32w..32w+31 of both operands, 8 rows per instruction.
+  int voff[4], voffb[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int row = 64 * wave + 8 * u + (lane >> 3);
+  for (int u = 0; u < 4; ++u) {
+    const int row = 32 * wave + 8 * u + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
       const int r = w.r0 + row;
-      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      const int pr = r < w.r1 ? p.perm[r] : -1;
       voff[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voff[u] = row * rowbytes + chunk * 16;
     }
-    // SwiGLU: wavefronts 2 and 3 fill B rows 128..255 from W3, whose rows restart at 0
-    voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * rowbytes + chunk * 16;
+    voffb[u] = (SW ? (row & 127) : row) * rowbytes + chunk * 16;
   }
-  // Fragment reads: row r = base + 32 x + l32 (base a multiple of 128), chunk
-  // c = 2 kk + kh; g(r) = g(l32) ^ 4 (x & 1), so slot = (2 kk) ^ h ^ 4 (x & 1).
+  // Fragment reads: A rows wm 128 + 32 mi + l32 -> slot (2 kk + kh) ^ g(l32) ^ 4 (mi & 1);
+  // B rows (SwiGLU) 128 ni + 32 wn + l32 -> ^ 4 (wn & 1), else 64 wn + 32 ni + l32 -> ^ 4 (ni & 1).
   const int h = kh ^ swz8(l32);
   const int abase = (wm * 128 + l32) * kBK2;
-  const int bbase = kStageElems + (MODE == MODE_SWIGLU_UP ? (wn * 64 + l32) : (wn * 128 + l32)) * kBK2;
+  const int bb0 = kStageElems + (SW ? (32 * wn + l32) : (64 * wn + l32)) * kBK2;
+  const int bstep = (SW ? 128 : 32) * kBK2;
+  const int hb0 = SW ? (h ^ (4 * (wn & 1))) : h;
+  const int hb1 = SW ? hb0 : (h ^ 4);
 
   const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(p.A, p.a_bytes)
                                            : make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
   const int nb_rows = min(cols_per_tile, p.Nn - w.n0);
-  const uint16_t* wsrc = (MODE == MODE_SWIGLU_UP && wave >= 2) ? p.W3 : p.W;
+  const uint16_t* wsrc = (SW && wave >= 4) ? p.W3 : p.W;
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(wsrc + (size_t)w.seg * wstride + (size_t)w.n0 * p.K, (uint32_t)nb_rows * rowbytes);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
   const int kt0 = w.kt0, kt1 = w.kt1;
-  if (kt0 < kt1) {  // prologue: step kt0 into stage kt0 & 1 (a K-part can be empty)
+  if (kt0 < kt1) {
     uint16_t* st = lds + (kt0 & 1) * (2 * kStageElems);
     const int so = kt0 * kBK2 * 2;
 #pragma unroll
-    for (int uu = 0; uu < 8; ++uu) {
-      dma16(ra, st + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
-      dma16(rb, st + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
+    for (int uu = 0; uu < 4; ++uu) {
+      dma16(ra, st + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
+      dma16(rb, st + kStageElems + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
     }
   }
-  for (int kt = kt0; kt < kt1; ++kt) {
-    MOE_WAIT_VM0();                      // this wavefront's loads of step kt have landed
-    __builtin_amdgcn_s_barrier();        // ... and everyone's; stage kt+1 is free again
-    const uint16_t* st = lds + (kt & 1) * (2 * kStageElems);
-    uint16_t* nx = lds + ((kt + 1) & 1) * (2 * kStageElems);
+  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {
+    MOE_WAIT_VM0();
+    __builtin_amdgcn_s_barrier();
     const bool more = kt + 1 < kt1;
     const int so = (kt + 1) * kBK2 * 2;
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int sw = (h ^ (4 * (x & 1))) << 3;
-      fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + sw);
-      fb[0][x] = *reinterpret_cast<const bf16x8*>(
-          st + bbase + (MODE == MODE_SWIGLU_UP ? (x >> 1) * 8192 + (x & 1) * 2048 : 2048 * x) + sw);
-    }
+    for (int x = 0; x < 4; ++x)
+      fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      fb[0][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + ((x ? hb1 : hb0) << 3));
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
       const int c = kk & 1;
-      if (more && kk < 3) {
-        // slices 3 / 3 / 2 over the first three sub-steps: the last slice still has a
-        // quarter step of MFMAs to land before the wait at the top of the next step
+      if (more && kk < 2) {
 #pragma unroll
-        for (int uu = 3 * kk; uu < 3 * kk + 3; ++uu) {
-          if (uu < 8) {
-            dma16(ra, nx + (64 * wave + 8 * uu) * kBK2, voff[uu], so);
-            dma16(rb, nx + kStageElems + (64 * wave + 8 * uu) * kBK2, voffb[uu], so);
-          }
+        for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
+          dma16(ra, nx + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
+          dma16(rb, nx + kStageElems + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
         }
       }
       if (kk + 1 < kBK2 / 16) {
+        const int k2 = 2 * (kk + 1);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int sw = (h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3;
-          fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + sw);
-          fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(
-              st + bbase + (MODE == MODE_SWIGLU_UP ? (x >> 1) * 8192 + (x & 1) * 2048 : 2048 * x) + sw);
-        }
+        for (int x = 0; x < 4; ++x)
+          fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1)) ^ k2) << 3));
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + (((x ? hb1 : hb0) ^ k2) << 3));
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+  for (int kt = kt0; kt < kt1; ++kt)
+    step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
+  __syncthreads();
+
+  if (w.slot < 0) {
+    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
+    store_block64<MODE, HAS_BIAS, 4>(acc, ep, lane, kh, l32, wn, w.r0 + wm * 128, w.r1, w.n0, p.Nn, w.seg, p.bias,
+                                     p.out, p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
+  } else {
+    // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]; SwiGLU
+    // holds W1 and W3 columns in blocks of 64 (the K-part fix-up reads that layout)
+    float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      int col;
+      if (SW) {
+        const int j = 32 * wn + l32;                      // W1 / W3 output column of this lane
+        col = (j >> 6) * 128 + (j & 63) + 64 * ni;
+      } else {
+        col = 64 * wn + 32 * ni + l32;
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // 4 MFMA
-      }
+        for (int r = 0; r < 16; ++r) dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + col] = acc[mi][ni][r];
     }
   }
-  __syncthreads();   // every wavefront is done with the stages before the epilogue reuses them
+  __syncthreads();
+}
 
-  if (w.slot < 0) {
-    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-    store_block<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
-                                p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
-  } else {
-    // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]
-    float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2 + wn * 128 + l32;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
+// Persistent over the 256-row tile list: the grid holds one workgroup per CU,
+// XCD-major (workgroup b runs on XCD b % 8), and each XCD takes a contiguous
+// span of (tile, column tile, K-part) units so that the units sharing an
+// expert's weights meet in one L2.
+template <int MODE, bool HAS_BIAS, bool GATHER>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
+  constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
+  const int G = gridDim.x;
+  const int KT = p.K / kBK2;
+  const UnitPlan pb = plan_units(p.tiles[0] * p.n_ntiles, G, KT);
+  const int ub = pb.units();
+  const int per_xcd = G / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  const int span_b = (ub + kXcds - 1) / kXcds;
+  const int b0 = min(ub, xcd * span_b), cb = min(ub, b0 + span_b) - b0;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  for (int i = q; i < cb; i += per_xcd) {
+    const Unit w = decode_unit(p.tiles, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
+    big_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
   }
-  __syncthreads();   // the next unit's first loads must not overtake this epilogue
 }
 
 // ---------------------------------------------------------------------------
@@ -624,41 +664,31 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
   __syncthreads();   // the next unit's first loads must not overtake this epilogue
 }
 
-// The persistent kernel: grid = CUs rounded up to a multiple of 8, one
-// workgroup per CU.  Workgroup q of XCD x walks items q, q + G/8, ... of its
-// XCD's sequence: first the cb 256-row units of its range, then its 64-row
-// units, so a workgroup that runs out of long tiles moves on to short ones
-// while the others finish.  (Interleaving the two kinds finely measured
-// slower: the weight streams of the short tiles evict the long tiles'
-// operands from L2.)
+// Persistent over the 64-row tile list, same XCD-major unit spans as the
+// 256-row kernel.  It runs after the 256-row kernel on the same stream.
+// (One kernel that ran both lists, 256-row units first and then 64-row units
+// in every workgroup, measured slower than the two launches once the 256-row
+// tile moved to 8 wavefronts: the 64-row tile streams weights with 4.)
 template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  const UnitPlan pb = plan_units(p.tiles[0] * p.n_ntiles, G, KT);
   const UnitPlan ps = plan_units(p.tiles_small[0] * p.n_ntiles, G, KT);
-  const int ub = pb.units(), us = ps.units();
+  const int us = ps.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  const int span_b = (ub + kXcds - 1) / kXcds, span_s = (us + kXcds - 1) / kXcds;
-  const int b0 = min(ub, xcd * span_b), cb = min(ub, b0 + span_b) - b0;
+  const int span_s = (us + kXcds - 1) / kXcds;
   const int s0 = min(us, xcd * span_s), cs = min(us, s0 + span_s) - s0;
-  const int n = cb + cs;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
   const int lane = tid & 63;
-  for (int i = q; i < n; i += per_xcd) {
-    if (!FP8 && i < cb) {   // fp8 weights use 64-row tiles only
-      const Unit w = decode_unit(p.tiles, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
-      big_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
-    } else {
-      const Unit w = decode_unit(p.tiles_small, ps, s0 + (i - cb), p.n_ntiles, KT, cols_per_tile);
-      if (FP8) small_unit_fp8<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
-      else small_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
-    }
+  for (int i = q; i < cs; i += per_xcd) {
+    const Unit w = decode_unit(p.tiles_small, ps, s0 + i, p.n_ntiles, KT, cols_per_tile);
+    if (FP8) small_unit_fp8<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
+    else small_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
   }
 }
 
@@ -848,7 +878,10 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.Nn = g.Nn;
   p.n_ntiles = (g.Nn + cols - 1) / cols;
   const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
+  // fp8 weights use 64-row tiles only; with fewer than kBigTailMin rows no segment has a 256-row tile
+  if (!FP8 && g.max_rows >= kBigTailMin)
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<MODE, HAS_BIAS, GATHER>), dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((grouped_gemm_small_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
   hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(2 * grid), dim3(256), 0, s, p, grid);
 }
 
