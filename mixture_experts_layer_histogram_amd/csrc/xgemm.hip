@@ -210,9 +210,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// TN: one workgroup per (segment, M tile, N tile); workgroup b of XCD b % 8
-// takes item (b % 8) * span + b / 8 of the segment-major, M-tile-major order,
-// so an XCD's concurrent tiles share their P and Q column blocks in its L2.
+// TN: items (segment, M tile, N tile) in segment-major, M-tile-major order;
+// segments longer than kTnShortRows rows run 256 x 256 tiles in
+// gemm_tn_kernel, the others 128 x 128 tiles in gemm_tn_short_kernel.
 struct TnParams {
   const uint16_t* P;        // [rows, ldp], columns pc0 .. pc0 + M
   const uint16_t* Q;        // [rows, ldq], columns 0 .. N
@@ -222,20 +222,13 @@ struct TnParams {
   int M, N;
   float* C;                 // C_s = C + s * strideC, [M, N] row-major
   long long strideC;
-  int tiles_m, tiles_n, units, span;
+  int tiles_m, tiles_n, units;
 };
 
-__global__ __launch_bounds__(256, 1) void gemm_tn_kernel(TnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
-  const int item = (blockIdx.x % kXcds) * p.span + blockIdx.x / kXcds;
-  if (item >= p.units) return;
-  const int per_seg = p.tiles_m * p.tiles_n;
-  const int s = item / per_seg;
-  const int m0 = ((item % per_seg) / p.tiles_n) * 256;
-  const int n0 = (item % p.tiles_n) * 256;
-  const int lo = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s] : 0);
-  const int hi = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s + 1] : p.dense_rows);
+// Segments of at most this many rows go to gemm_tn_short_kernel.
+constexpr int kTnShortRows = 256;
 
+__device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s, int m0, int n0, int lo, int hi) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -298,6 +291,139 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(TnParams p) {
                                   p.C + (size_t)s * p.strideC);
 }
 
+// Persistent: grid = CUs rounded to a multiple of 8, a grid-stride loop over
+// the items (segment-major, M-tile-major), skipping those of short segments.
+// An item's work grows with its segment's length, so consecutive items are
+// dealt round-robin over the XCDs (item % 8 = the workgroup's XCD): with
+// contiguous XCD ranges a skewed routing left one XCD with three times the
+// mean work.
+__global__ __launch_bounds__(256, 1) void gemm_tn_kernel(TnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
+  for (int item = blockIdx.x; item < p.units; item += gridDim.x) {
+    const int per_seg = p.tiles_m * p.tiles_n;
+    const int s = item / per_seg;
+    const int lo = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s] : 0);
+    const int hi = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s + 1] : p.dense_rows);
+    if (hi - lo <= kTnShortRows) continue;
+    tn_tile(p, lds, s, ((item % per_seg) / p.tiles_n) * 256, (item % p.tiles_n) * 256, lo, hi);
+    __syncthreads();   // the next tile's loads must not overtake this epilogue's LDS reads
+  }
+}
+
+// ---------------------------------------------------------------------------
+// TN for short segments (at most kTnShortRows rows: most experts of a skewed
+// routing, and unused experts, whose gradient is zero).  There the product is
+// bound by writing the fp32 gradient, so the tile is small and cheap to keep
+// many of in flight: 128 x 128, 4 wavefronts of 64 x 64 (2 x 2 MFMA blocks),
+// one 32 KB K-major stage per operand pair (64 K rows x 128 columns, 256 bytes
+// per row, chunk c of row r in slot c ^ 4 (r & 3), the same swizzle as the
+// 256-column stage: it only touches the low four bits of the chunk index), and
+// the accumulators stored straight from registers (half a wavefront writes
+// 128 contiguous bytes of one row).  Several workgroups share a CU, so one's
+// stores overlap another's loads; each K step is load, barrier, 16 MFMAs.
+__device__ __forceinline__ void tr_dma_offsets128(int wave, int lane, int rowbytes, int col0, int (&voff)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int lr = 16 * wave + 4 * u + (lane >> 4);
+    const int chunk = (lane & 15) ^ (4 * (lr & 3));
+    voff[u] = lr * rowbytes + col0 * 2 + chunk * 16;
+  }
+}
+
+// As tr_lane for a 128-column stage; the wavefront's 64-column block starts
+// at column cblk, and the swizzle is applied to the chunk index within the row.
+__device__ __forceinline__ TrLane tr_lane128(int lane, int cblk) {
+  const int G = lane >> 4, i = lane & 15;
+  const int row = 8 * (G >> 1) + (i >> 2);
+  const int chunk = 2 * (G & 1) + ((i & 3) >> 1);
+  const int sw = 4 * (i >> 2);
+  TrLane t;
+  t.base = row * 128 + 4 * (i & 1);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) t.xo[x] = ((cblk / 8 + 4 * x + chunk) ^ sw) * 8;
+  t.xo[2] = t.xo[3] = 0;
+  return t;
+}
+
+__device__ __forceinline__ bf16x8 frag_tr128(const uint16_t* st, const TrLane& t, int kk, int x) {
+  const uint16_t* q = st + kk * 16 * 128 + t.base + t.xo[x];
+  const bf16x4t lo = read_tr(q);
+  const bf16x4t hi = read_tr(q + 4 * 128);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Persistent like gemm_tn_kernel over 128 x 128 items (p.tiles_m, p.tiles_n,
+// p.units count those), skipping the items of long segments.
+__global__ __launch_bounds__(256) void gemm_tn_short_kernel(TnParams p) {
+  constexpr int kOp = 64 * 128;   // elements of one operand's stage
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kOp];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int pbytes = p.ldp * 2, qbytes = p.ldq * 2;
+  const TrLane ta = tr_lane128(lane, wm * 64), tb = tr_lane128(lane, wn * 64);
+  const int per_seg = p.tiles_m * p.tiles_n;
+  for (int item = blockIdx.x; item < p.units; item += gridDim.x) {
+    const int s = item / per_seg;
+    const int lo = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s] : 0);
+    const int hi = __builtin_amdgcn_readfirstlane(p.offsets ? p.offsets[s + 1] : p.dense_rows);
+    const int rows = hi - lo;
+    if (rows > kTnShortRows) continue;
+    const int m0 = ((item % per_seg) / p.tiles_n) * 128, n0 = (item % p.tiles_n) * 128;
+    int voffp[4], voffq[4];
+    tr_dma_offsets128(wave, lane, pbytes, p.pc0 + m0, voffp);
+    tr_dma_offsets128(wave, lane, qbytes, n0, voffq);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.P + (size_t)lo * p.ldp, (uint32_t)rows * pbytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (size_t)lo * p.ldq, (uint32_t)rows * qbytes);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    for (int k0 = 0; k0 < rows; k0 += 64) {
+      __syncthreads();   // every wavefront is done with the stage (and with the previous item)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        dma16(rp, lds + (16 * wave + 4 * u) * 128, voffp[u] + k0 * pbytes, 0);
+        dma16(rq, lds + kOp + (16 * wave + 4 * u) * 128, voffq[u] + k0 * qbytes, 0);
+      }
+      MOE_WAIT_VM0();
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 fa[2], fb[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          fa[x] = frag_tr128(lds, ta, kk, x);
+          fb[x] = frag_tr128(lds + kOp, tb, kk, x);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+    float* C = p.C + (size_t)s * p.strideC;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int n = n0 + wn * 64 + ni * 32 + l32;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+          if (m < p.M) C[(size_t)m * p.N + n] = acc[mi][ni][r];
+        }
+    }
+  }
+}
+
 static int cus_rounded() {
   int dev = 0, v = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -352,11 +478,23 @@ hipError_t launch_gemm_tn(const void* P, int ldp, int pc0, const void* Q, int ld
   p.N = N;
   p.C = C;
   p.strideC = strideC;
-  p.tiles_m = (M + 255) / 256;
-  p.tiles_n = (N + 255) / 256;
-  p.units = n_seg * p.tiles_m * p.tiles_n;
-  p.span = (p.units + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)(p.span * kXcds)), dim3(256), 0, s, p);
+  // dense: the one segment's length is known here; ragged: short segments can always occur
+  const bool any_short = offsets != nullptr || dense_rows <= kTnShortRows;
+  const bool any_long = offsets != nullptr ? max_seg_rows > kTnShortRows : dense_rows > kTnShortRows;
+  const int grid = cus_rounded();
+  if (any_short) {
+    TnParams q = p;
+    q.tiles_m = (M + 127) / 128;
+    q.tiles_n = (N + 127) / 128;
+    q.units = n_seg * q.tiles_m * q.tiles_n;
+    hipLaunchKernelGGL(gemm_tn_short_kernel, dim3((unsigned)(4 * grid)), dim3(256), 0, s, q);
+  }
+  if (any_long) {
+    p.tiles_m = (M + 255) / 256;
+    p.tiles_n = (N + 255) / 256;
+    p.units = n_seg * p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
