@@ -24,6 +24,10 @@ CASES = {
     # E not a multiple of 64 (padded router width), k = 3, a ragged token count
     "e100_k3": SMALL["mixtral_prefill_small"].scaled(name="bw_e100_k3", n_tokens=333, n_experts=100, top_k=3),
     "one_token": SMALL["deepseek_v3_small"].scaled(name="bw_one_token", n_tokens=1),
+    # one hot expert (~1350 rows: 256x256 weight-gradient tiles over a long K), the others with a
+    # handful of rows or none (128x128 tiles, zero gradients); d and F not multiples of 128
+    "skewed_long_short": SMALL["switch_skewed_small"].scaled(name="bw_skewed_long_short", n_tokens=1500,
+                                                             d_model=320, d_ff=448, capacity_factor=0.0),
 }
 
 
