@@ -27,6 +27,8 @@
 // reads: group G = l / 16 takes c0 = 16 (G & 1), kb = 8 (G >> 1) and kb + 4.
 // Per half-wave the 16 (row, chunk) pairs of one read fall on 16 distinct
 // 4-bank groups under the slot swizzle above.
+#include <type_traits>
+
 #include "gemm_tile.h"
 
 namespace moe {
@@ -165,14 +167,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
     // The restrict-qualified stage pointers tell the compiler that the reads
     // of one stage never alias the direct-to-LDS loads into the other, so it
     // does not wait for those loads before each transposing read.
-    auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {
+    // Row blocks of 32 past the segment's end hold zero rows that are never
+    // stored: a wavefront runs only its NV live blocks (a compile-time count,
+    // one loop instance per count), skipping the others' fragment reads and
+    // MFMAs, so a short expert's tile costs its weight stream rather than a
+    // full tile of MFMAs.
+    const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (w.r1 - w.r0 - wm * 128 + 31) / 32)));
+    auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto nv_t) {
+      constexpr int NV = decltype(nv_t)::value;
       MOE_WAIT_VM0();
       __builtin_amdgcn_s_barrier();
       const bool more = kt + 1 < KT;
       bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
+        if (x < NV)
+          fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
         fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
       }
 #pragma unroll
@@ -186,12 +196,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
         if (kk + 1 < kBK2 / 16) {
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x +
-                                                             ((h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3));
+            if (x < NV)
+              fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x +
+                                                               ((h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3));
             fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
           }
         }
-        mfma_block(acc, fa[c], fb[c]);
+#pragma unroll
+        for (int mi = 0; mi < NV; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
       }
     };
 
@@ -199,8 +214,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) issue(lds, 0, u);
     }
-    for (int kt = 0; kt < KT; ++kt)
-      step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
+    auto loop = [&](auto nv_t) {
+      for (int kt = 0; kt < KT; ++kt)
+        step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt, nv_t);
+    };
+    switch (nv) {
+      case 4: loop(std::integral_constant<int, 4>{}); break;
+      case 3: loop(std::integral_constant<int, 3>{}); break;
+      case 2: loop(std::integral_constant<int, 2>{}); break;
+      case 1: loop(std::integral_constant<int, 1>{}); break;
+      default: loop(std::integral_constant<int, 0>{}); break;   // loads only: the barriers stay in step
+    }
     __syncthreads();
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
     store_block<MODE_DOWN, false>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.N, w.seg, nullptr, p.out,
