@@ -165,88 +165,4 @@ __device__ __forceinline__ void combine_store8(const CombineOut& cmb, int row, i
   *reinterpret_cast<uint4*>(cmb.out + o) = ov.u;
 }
 
-// Epilogue of one 128 x 128 wavefront block (rows r0 + wm*128 .., columns of
-// the output n0 ..): activation, bias, bf16 rounding, 16-byte stores.
-// `ep` is this wavefront's 16 KB of LDS; `src_acc` the accumulators.
-template <int MODE, bool HAS_BIAS>
-__device__ __forceinline__ void store_block(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
-                                            int wn, int r0, int r1, int n0, int Nn, int seg,
-                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                            const float* __restrict__ bias_f, float* __restrict__ out_f,
-                                            uint16_t* __restrict__ pre = nullptr, long long pre_plane = 0,
-                                            const CombineOut* cmb = nullptr) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
-    __builtin_amdgcn_wave_barrier();
-    const int rbase = r0 + wm * 128 + mi * 32;
-    if (MODE == MODE_LOGITS) {
-#pragma unroll 1
-      for (int pass = 0; pass < 16; ++pass) {
-        const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-        const int row = rbase + rr, col = n0 + wn * 128 + c4;
-        if (row < r1 && col < Nn) {
-          float4 v = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
-          if (HAS_BIAS) {
-            const float4 b = *reinterpret_cast<const float4*>(bias_f + col);
-            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-          }
-          *reinterpret_cast<float4*>(out_f + (size_t)row * Nn + col) = v;
-        }
-      }
-    } else if (MODE == MODE_SWIGLU_UP) {
-      // cols 0..63 hold x W1^T, cols 64..127 the matching x W3^T
-#pragma unroll 1
-      for (int pass = 0; pass < 4; ++pass) {
-        const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-        const int row = rbase + rr, col = n0 + wn * 64 + c8;
-        if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 128 + c8;
-          Vec8 o;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[64 + v]);
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-          if (pre != nullptr) {   // pre-activations x W1^T, x W3^T for the backward
-            Vec8 a1, a3;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              a1.e[v] = f32_to_bf16(src[v]);
-              a3.e[v] = f32_to_bf16(src[64 + v]);
-            }
-            *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a1.u;
-            *reinterpret_cast<uint4*>(pre + pre_plane + (size_t)row * Nn + col) = a3.u;
-          }
-        }
-      }
-    } else {
-#pragma unroll 1
-      for (int pass = 0; pass < 8; ++pass) {
-        const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
-        const int row = rbase + rr, col = n0 + wn * 128 + c8;
-        if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 128 + c8;
-          Vec8 b;
-          if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-          Vec8 o, a;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            float x = src[v];
-            if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
-            a.e[v] = f32_to_bf16(x);
-            if (MODE == MODE_GELU_UP) x = gelu_f(x);
-            o.e[v] = f32_to_bf16(x);
-          }
-          if (MODE == MODE_DOWN && cmb != nullptr && cmb->out != nullptr) combine_store8(*cmb, row, col, Nn, o);
-          else *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
-          if (MODE == MODE_GELU_UP && pre != nullptr) *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a.u;
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
 }  // namespace moe

@@ -9,10 +9,11 @@
 //       P[r, m] Q[r, n] in fp32: the weight gradients dW2_e = dY^T H,
 //       dW1_e = dA1^T X, dW_router = dZ^T X.
 //
-// Both run the 256 x 256 x 64 tile of the forward's grouped GEMM (4
-// wavefronts of 128 x 128, MFMA 32x32x16 bf16, two 64 KB LDS stages filled by
-// direct-to-LDS buffer loads, one barrier per K step).  What changes is how a
-// K-major operand sits in LDS and reaches the MFMA:
+// Both run a 256 x 256 x 64 tile like the forward's grouped GEMM, here on 4
+// wavefronts of 128 x 128 (MFMA 32x32x16 bf16, two 64 KB LDS stages filled by
+// direct-to-LDS buffer loads, one barrier per K step); TN also has a 128 x 128
+// tile for short segments.  What changes is how a K-major operand sits in LDS
+// and reaches the MFMA:
 //
 // K-major stage: 64 K rows x 256 columns, 512 bytes per row; the 16-byte
 // chunk c of row r sits in slot c ^ (4 (r & 3)).  A direct-to-LDS load moves
@@ -78,6 +79,48 @@ __device__ __forceinline__ void tr_dma_offsets(int wave, int lane, int rowbytes,
     const int lr = 16 * wave + 2 * u + (lane >> 5);
     const int chunk = (lane & 31) ^ (4 * (lr & 3));
     voff[u] = lr * rowbytes + col0 * 2 + chunk * 16;
+  }
+}
+
+// Epilogue of one wavefront's 128 x 128 block (rows r0 + wm * 128 ..,
+// columns n0 + wn * 128 ..) through its 16 KB of LDS `ep`, 32 rows at a time:
+// bf16 (F32 = false) or fp32 rows with 16-byte stores; rows >= r1 and columns
+// >= N are not written.
+template <bool F32>
+__device__ __forceinline__ void store_tile128(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
+                                              int wn, int r0, int r1, int n0, int N, uint16_t* __restrict__ out,
+                                              float* __restrict__ out_f) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
+    __builtin_amdgcn_wave_barrier();
+    const int rbase = r0 + wm * 128 + mi * 32;
+    if (F32) {
+#pragma unroll 1
+      for (int pass = 0; pass < 16; ++pass) {
+        const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+        const int row = rbase + rr, col = n0 + wn * 128 + c4;
+        if (row < r1 && col < N)
+          *reinterpret_cast<float4*>(out_f + (size_t)row * N + col) = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
+      }
+    } else {
+#pragma unroll 1
+      for (int pass = 0; pass < 8; ++pass) {
+        const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
+        const int row = rbase + rr, col = n0 + wn * 128 + c8;
+        if (row < r1 && col < N) {
+          const float* src = ep + rr * 128 + c8;
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(src[v]);
+          *reinterpret_cast<uint4*>(out + (size_t)row * N + col) = o.u;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -227,8 +270,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
     }
     __syncthreads();
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-    store_block<MODE_DOWN, false>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.N, w.seg, nullptr, p.out,
-                                  nullptr, nullptr);
+    store_tile128<false>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.N, p.out, nullptr);
     __syncthreads();
   }
 }
@@ -311,8 +353,7 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
     step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
   __syncthreads();
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-  store_block<MODE_LOGITS, false>(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, s, nullptr, nullptr, nullptr,
-                                  p.C + (size_t)s * p.strideC);
+  store_tile128<true>(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, nullptr, p.C + (size_t)s * p.strideC);
 }
 
 // Persistent: grid = CUs rounded to a multiple of 8, a grid-stride loop over
