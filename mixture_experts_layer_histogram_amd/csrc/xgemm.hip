@@ -9,11 +9,11 @@
 //       P[r, m] Q[r, n] in fp32: the weight gradients dW2_e = dY^T H,
 //       dW1_e = dA1^T X, dW_router = dZ^T X.
 //
-// Both run a 256 x 256 x 64 tile like the forward's grouped GEMM, here on 4
-// wavefronts of 128 x 128 (MFMA 32x32x16 bf16, two 64 KB LDS stages filled by
-// direct-to-LDS buffer loads, one barrier per K step); TN also has a 128 x 128
-// tile for short segments.  What changes is how a K-major operand sits in LDS
-// and reaches the MFMA:
+// Both run a 256 x 256 x 64 tile like the forward's grouped GEMM (MFMA
+// 32x32x16 bf16, two 64 KB LDS stages filled by direct-to-LDS buffer loads,
+// one barrier per K step): NN on 8 wavefronts of 128 x 64, TN on 4 of
+// 128 x 128, plus a 128 x 128 TN tile for short segments.  What changes is how
+// a K-major operand sits in LDS and reaches the MFMA:
 //
 // K-major stage: 64 K rows x 256 columns, 512 bytes per row; the 16-byte
 // chunk c of row r sits in slot c ^ (4 (r & 3)).  A direct-to-LDS load moves
@@ -82,14 +82,11 @@ __device__ __forceinline__ void tr_dma_offsets(int wave, int lane, int rowbytes,
   }
 }
 
-// Epilogue of one wavefront's 128 x 128 block (rows r0 + wm * 128 ..,
-// columns n0 + wn * 128 ..) through its 16 KB of LDS `ep`, 32 rows at a time:
-// bf16 (F32 = false) or fp32 rows with 16-byte stores; rows >= r1 and columns
-// >= N are not written.
-template <bool F32>
-__device__ __forceinline__ void store_tile128(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
-                                              int wn, int r0, int r1, int n0, int N, uint16_t* __restrict__ out,
-                                              float* __restrict__ out_f) {
+// Epilogue of one wavefront's 128 x 128 block of fp32 results (rows
+// r0 + wm * 128 .., columns n0 + wn * 128 ..) through its 16 KB of LDS `ep`,
+// 32 rows at a time, 16-byte stores; rows >= r1 and columns >= N are not written.
+__device__ __forceinline__ void store_tile128_f32(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
+                                                  int wn, int r0, int r1, int n0, int N, float* __restrict__ out_f) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -98,27 +95,12 @@ __device__ __forceinline__ void store_tile128(f32x16 (&acc)[4][4], float* ep, in
       for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
     __builtin_amdgcn_wave_barrier();
     const int rbase = r0 + wm * 128 + mi * 32;
-    if (F32) {
 #pragma unroll 1
-      for (int pass = 0; pass < 16; ++pass) {
-        const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-        const int row = rbase + rr, col = n0 + wn * 128 + c4;
-        if (row < r1 && col < N)
-          *reinterpret_cast<float4*>(out_f + (size_t)row * N + col) = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
-      }
-    } else {
-#pragma unroll 1
-      for (int pass = 0; pass < 8; ++pass) {
-        const int rr = pass * 4 + (lane >> 4), c8 = (lane & 15) * 8;
-        const int row = rbase + rr, col = n0 + wn * 128 + c8;
-        if (row < r1 && col < N) {
-          const float* src = ep + rr * 128 + c8;
-          Vec8 o;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(src[v]);
-          *reinterpret_cast<uint4*>(out + (size_t)row * N + col) = o.u;
-        }
-      }
+    for (int pass = 0; pass < 16; ++pass) {
+      const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+      const int row = rbase + rr, col = n0 + wn * 128 + c4;
+      if (row < r1 && col < N)
+        *reinterpret_cast<float4*>(out_f + (size_t)row * N + col) = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -142,8 +124,7 @@ __device__ __forceinline__ void mfma_block(f32x16 (&acc)[4][4], const bf16x8 (&f
 }
 
 // ---------------------------------------------------------------------------
-// NN: persistent over the units of a 256-row tile list (expert-major, N-tile
-// by N-tile over the expert's row tiles; each XCD a contiguous range).
+// Arguments of the NN product.
 struct NnParams {
   const uint16_t* A;        // [rows, K] in segment order
   const int32_t* tiles;     // 256-row tiles covering every row (kind 2)
@@ -156,7 +137,39 @@ struct NnParams {
   int n_ntiles;
 };
 
-__global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
+// ---------------------------------------------------------------------------
+// NN: persistent over the units of a 256-row tile list (expert-major, N-tile
+// by N-tile over the expert's row tiles; each XCD a contiguous range), on 8
+// wavefronts (two per SIMD) like the forward's 256-row tile: a 2 x 4 layout of
+// 128 x 64 blocks (4 x 2 MFMA blocks, 128 accumulators per lane), so one
+// wavefront of a SIMD issues MFMAs while the other waits.  Each wavefront
+// loads 32 A rows and 8 K rows of B per step.
+__device__ __forceinline__ void tr_dma_offsets8(int wave, int lane, int rowbytes, int col0, int (&voff)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int lr = 8 * wave + 2 * u + (lane >> 5);
+    const int chunk = (lane & 31) ^ (4 * (lr & 3));
+    voff[u] = lr * rowbytes + col0 * 2 + chunk * 16;
+  }
+}
+
+// As tr_lane for a 64-column block at column cblk of the 256-column stage;
+// the swizzle acts on the chunk index within the whole row (a 64-column block
+// starts at chunk 8 wn, so it cannot be applied to the block's own index).
+__device__ __forceinline__ TrLane tr_lane64(int lane, int cblk) {
+  const int G = lane >> 4, i = lane & 15;
+  const int row = 8 * (G >> 1) + (i >> 2);
+  const int chunk = 2 * (G & 1) + ((i & 3) >> 1);
+  const int sw = 4 * (i >> 2);
+  TrLane t;
+  t.base = row * 256 + 4 * (i & 1);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) t.xo[x] = ((cblk / 8 + 4 * x + chunk) ^ sw) * 8;
+  t.xo[2] = t.xo[3] = 0;
+  return t;
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_nn_kernel(NnParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
@@ -173,22 +186,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, kh = lane >> 5;
   const int rowbytes = p.K * 2, browbytes = p.N * 2;
   const int h = kh ^ swz8(l32);
   const int abase = (wm * 128 + l32) * kBK2;
-  const TrLane tb = tr_lane(lane, wn * 128);
+  const TrLane tb = tr_lane64(lane, wn * 64);
 
   for (int it = q; it < cnt; it += per_xcd) {
     const Unit w = decode_unit(p.tiles, plan, u0 + it, p.n_ntiles, KT, kBN2);
-    int voff[8], voffb[8];
+    int voff[4], voffb[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = 64 * wave + 8 * u + (lane >> 3);
+    for (int u = 0; u < 4; ++u) {
+      const int row = 32 * wave + 8 * u + (lane >> 3);
       voff[u] = row * rowbytes + (((lane & 7) ^ swz8(row)) * 16);
     }
-    tr_dma_offsets(wave, lane, browbytes, w.n0, voffb);
+    tr_dma_offsets8(wave, lane, browbytes, w.n0, voffb);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
     const __amdgpu_buffer_rsrc_t rb1 =
@@ -197,65 +210,61 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
         make_rsrc(p.B2 ? p.B2 + (size_t)w.seg * p.strideB : p.B1, p.B2 ? (uint32_t)p.b_rows2 * browbytes : 0u);
 
     auto issue = [&](uint16_t* st, int kt, int u) {
-      dma16(ra, st + (64 * wave + 8 * u) * kBK2, voff[u], kt * kBK2 * 2);
+      dma16(ra, st + (32 * wave + 8 * u) * kBK2, voff[u], kt * kBK2 * 2);
       const int k0 = kt * kBK2;
       const bool second = k0 >= p.K1;
       const int kb = second ? k0 - p.K1 : k0;
-      dma16(second ? rb2 : rb1, st + kStageElems + (16 * wave + 2 * u) * 256, voffb[u] + kb * browbytes, 0);
+      dma16(second ? rb2 : rb1, st + kStageElems + (8 * wave + 2 * u) * 256, voffb[u] + kb * browbytes, 0);
     };
 
-    f32x16 acc[4][4];
-    zero_acc(acc);
-    // One K step: fragments from stage `st`, the next step's loads into `nx`.
-    // The restrict-qualified stage pointers tell the compiler that the reads
-    // of one stage never alias the direct-to-LDS loads into the other, so it
-    // does not wait for those loads before each transposing read.
-    // Row blocks of 32 past the segment's end hold zero rows that are never
-    // stored: a wavefront runs only its NV live blocks (a compile-time count,
-    // one loop instance per count), skipping the others' fragment reads and
-    // MFMAs, so a short expert's tile costs its weight stream rather than a
-    // full tile of MFMAs.
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    // live 32-row blocks of this wavefront (rows past the segment are zero and never stored)
     const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (w.r1 - w.r0 - wm * 128 + 31) / 32)));
     auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto nv_t) {
       constexpr int NV = decltype(nv_t)::value;
       MOE_WAIT_VM0();
       __builtin_amdgcn_s_barrier();
       const bool more = kt + 1 < KT;
-      bf16x8 fa[2][4], fb[2][4];
+      bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        if (x < NV)
-          fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
-        fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
-      }
+      for (int x = 0; x < 4; ++x)
+        if (x < NV) fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
 #pragma unroll
       for (int kk = 0; kk < kBK2 / 16; ++kk) {
         const int c = kk & 1;
-        if (more && kk < 3) {
+        if (more && kk < 2) {
 #pragma unroll
-          for (int u = 3 * kk; u < 3 * kk + 3; ++u)
-            if (u < 8) issue(nx, kt + 1, u);
+          for (int u = 2 * kk; u < 2 * kk + 2; ++u) issue(nx, kt + 1, u);
         }
         if (kk + 1 < kBK2 / 16) {
+          const int k2 = 2 * (kk + 1);
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
+          for (int x = 0; x < 4; ++x)
             if (x < NV)
-              fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x +
-                                                               ((h ^ (4 * (x & 1)) ^ (2 * (kk + 1))) << 3));
-            fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
-          }
+              fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1)) ^ k2) << 3));
+#pragma unroll
+          for (int x = 0; x < 2; ++x) fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mi = 0; mi < NV; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
       }
     };
-
     if (KT > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) issue(lds, 0, u);
+      for (int u = 0; u < 4; ++u) issue(lds, 0, u);
     }
     auto loop = [&](auto nv_t) {
       for (int kt = 0; kt < KT; ++kt)
@@ -266,11 +275,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nn_kernel(NnParams p) {
       case 3: loop(std::integral_constant<int, 3>{}); break;
       case 2: loop(std::integral_constant<int, 2>{}); break;
       case 1: loop(std::integral_constant<int, 1>{}); break;
-      default: loop(std::integral_constant<int, 0>{}); break;   // loads only: the barriers stay in step
+      default: loop(std::integral_constant<int, 0>{}); break;
     }
     __syncthreads();
-    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-    store_tile128<false>(acc, ep, lane, kh, l32, wm, wn, w.r0, w.r1, w.n0, p.N, p.out, nullptr);
+    // epilogue: this wavefront's 128 x 64 block through its 8 KB of LDS, 32 rows at a time
+    float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+      __builtin_amdgcn_wave_barrier();
+      const int rbase = w.r0 + wm * 128 + mi * 32;
+#pragma unroll 1
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const int row = rbase + rr, col = w.n0 + wn * 64 + c8;
+        if (row < w.r1 && col < p.N) {
+          const float* src = ep + rr * 64 + c8;
+          Vec8 o;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(src[v]);
+          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.N + col) = o.u;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
     __syncthreads();
   }
 }
@@ -353,7 +384,7 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
     step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
   __syncthreads();
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-  store_tile128<true>(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, nullptr, p.C + (size_t)s * p.strideC);
+  store_tile128_f32(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, p.C + (size_t)s * p.strideC);
 }
 
 // Persistent: grid = CUs rounded to a multiple of 8, a grid-stride loop over
@@ -520,7 +551,7 @@ hipError_t launch_gemm_nn(const void* A, const int32_t* offsets, int n_seg, int 
   p.b_rows2 = b_rows2;
   p.out = (uint16_t*)out;
   p.n_ntiles = (N + kBN2 - 1) / kBN2;
-  hipLaunchKernelGGL(gemm_nn_kernel, dim3(cus_rounded()), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(gemm_nn_kernel, dim3(cus_rounded()), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
