@@ -9,11 +9,10 @@
 //       P[r, m] Q[r, n] in fp32: the weight gradients dW2_e = dY^T H,
 //       dW1_e = dA1^T X, dW_router = dZ^T X.
 //
-// Both run a 256 x 256 x 64 tile like the forward's grouped GEMM (MFMA
+// Both run the forward's 256 x 256 x 64 tile (8 wavefronts of 128 x 64, MFMA
 // 32x32x16 bf16, two 64 KB LDS stages filled by direct-to-LDS buffer loads,
-// one barrier per K step): NN on 8 wavefronts of 128 x 64, TN on 4 of
-// 128 x 128, plus a 128 x 128 TN tile for short segments.  What changes is how
-// a K-major operand sits in LDS and reaches the MFMA:
+// one barrier per K step), plus a 128 x 128 TN tile for short segments.  What
+// changes is how a K-major operand sits in LDS and reaches the MFMA:
 //
 // K-major stage: 64 K rows x 256 columns, 512 bytes per row; the 16-byte
 // chunk c of row r sits in slot c ^ (4 (r & 3)).  A direct-to-LDS load moves
@@ -42,7 +41,8 @@ __device__ __forceinline__ bf16x4t read_tr(const uint16_t* p) {
 }
 
 // Lane constants of the transposing fragment reads of a K-major stage whose
-// 128-column block for this wavefront starts at column `cblk`:
+// 128-column block for this wavefront starts at column `cblk` (a multiple of
+// 128, so the swizzle can act on the chunk index within the block):
 // element offset of fragment x (32 columns each) in sub-step kk, half h =
 //   (16 kk + 4 h) * 256 + base + xo[x].
 struct TrLane {
@@ -69,60 +69,6 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* st, const TrLane& t, i
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Direct-to-LDS loads of a K-major operand: wavefront w fills K rows
-// 16 w .. 16 w + 15 of the stage, two rows per instruction.  voff[u] is the
-// byte offset of this lane's source chunk for instruction u at K row 0 of the
-// operand (rows advance by `rowbytes`).
-__device__ __forceinline__ void tr_dma_offsets(int wave, int lane, int rowbytes, int col0, int (&voff)[8]) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int lr = 16 * wave + 2 * u + (lane >> 5);
-    const int chunk = (lane & 31) ^ (4 * (lr & 3));
-    voff[u] = lr * rowbytes + col0 * 2 + chunk * 16;
-  }
-}
-
-// Epilogue of one wavefront's 128 x 128 block of fp32 results (rows
-// r0 + wm * 128 .., columns n0 + wn * 128 ..) through its 16 KB of LDS `ep`,
-// 32 rows at a time, 16-byte stores; rows >= r1 and columns >= N are not written.
-__device__ __forceinline__ void store_tile128_f32(f32x16 (&acc)[4][4], float* ep, int lane, int kh, int l32, int wm,
-                                                  int wn, int r0, int r1, int n0, int N, float* __restrict__ out_f) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 128 + ni * 32 + l32] = acc[mi][ni][r];
-    __builtin_amdgcn_wave_barrier();
-    const int rbase = r0 + wm * 128 + mi * 32;
-#pragma unroll 1
-    for (int pass = 0; pass < 16; ++pass) {
-      const int rr = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-      const int row = rbase + rr, col = n0 + wn * 128 + c4;
-      if (row < r1 && col < N)
-        *reinterpret_cast<float4*>(out_f + (size_t)row * N + col) = *reinterpret_cast<const float4*>(ep + rr * 128 + c4);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-}
-
-__device__ __forceinline__ void mfma_block(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // Arguments of the NN product.
 struct NnParams {
@@ -144,6 +90,11 @@ struct NnParams {
 // 128 x 64 blocks (4 x 2 MFMA blocks, 128 accumulators per lane), so one
 // wavefront of a SIMD issues MFMAs while the other waits.  Each wavefront
 // loads 32 A rows and 8 K rows of B per step.
+//
+// Direct-to-LDS loads of a K-major operand: wavefront w fills K rows
+// 8 w .. 8 w + 7 of the stage, two rows per instruction.  voff[u] is the byte
+// offset of this lane's source chunk for instruction u at K row 0 of the
+// operand (rows advance by `rowbytes`).
 __device__ __forceinline__ void tr_dma_offsets8(int wave, int lane, int rowbytes, int col0, int (&voff)[4]) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -325,66 +276,95 @@ struct TnParams {
 // Segments of at most this many rows go to gemm_tn_short_kernel.
 constexpr int kTnShortRows = 256;
 
+// One 256 x 256 TN tile on 8 wavefronts (2 x 4 layout of 128 x 64 blocks, as
+// the NN kernel): P fragments through the 128-column lane map, Q fragments
+// through the 64-column one; each wavefront loads 8 K rows of both operands.
 __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s, int m0, int n0, int lo, int hi) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, kh = lane >> 5;
   const int pbytes = p.ldp * 2, qbytes = p.ldq * 2;
-  int voffp[8], voffq[8];
-  tr_dma_offsets(wave, lane, pbytes, p.pc0 + m0, voffp);
-  tr_dma_offsets(wave, lane, qbytes, n0, voffq);
-  const TrLane ta = tr_lane(lane, wm * 128), tb = tr_lane(lane, wn * 128);
+  int voffp[4], voffq[4];
+  tr_dma_offsets8(wave, lane, pbytes, p.pc0 + m0, voffp);
+  tr_dma_offsets8(wave, lane, qbytes, n0, voffq);
+  const TrLane ta = tr_lane(lane, wm * 128), tb = tr_lane64(lane, wn * 64);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.P + (size_t)lo * p.ldp, (uint32_t)(hi - lo) * pbytes);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (size_t)lo * p.ldq, (uint32_t)(hi - lo) * qbytes);
 
   auto issue = [&](uint16_t* st, int kt, int u) {
     const int r = kt * kBK2;
-    dma16(rp, st + (16 * wave + 2 * u) * 256, voffp[u] + r * pbytes, 0);
-    dma16(rq, st + kStageElems + (16 * wave + 2 * u) * 256, voffq[u] + r * qbytes, 0);
+    dma16(rp, st + (8 * wave + 2 * u) * 256, voffp[u] + r * pbytes, 0);
+    dma16(rq, st + kStageElems + (8 * wave + 2 * u) * 256, voffq[u] + r * qbytes, 0);
   };
 
-  f32x16 acc[4][4];
-  zero_acc(acc);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
   const int KT = (hi - lo + kBK2 - 1) / kBK2;
-  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {   // as in NN
+  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {
     MOE_WAIT_VM0();
     __builtin_amdgcn_s_barrier();
     const bool more = kt + 1 < KT;
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      fa[0][x] = frag_tr(st, ta, 0, x);
-      fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
-    }
+    for (int x = 0; x < 4; ++x) fa[0][x] = frag_tr(st, ta, 0, x);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) fb[0][x] = frag_tr(st + kStageElems, tb, 0, x);
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
       const int c = kk & 1;
-      if (more && kk < 3) {
+      if (more && kk < 2) {
 #pragma unroll
-        for (int u = 3 * kk; u < 3 * kk + 3; ++u)
-          if (u < 8) issue(nx, kt + 1, u);
+        for (int u = 2 * kk; u < 2 * kk + 2; ++u) issue(nx, kt + 1, u);
       }
       if (kk + 1 < kBK2 / 16) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          fa[c ^ 1][x] = frag_tr(st, ta, kk + 1, x);
-          fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
-        }
+        for (int x = 0; x < 4; ++x) fa[c ^ 1][x] = frag_tr(st, ta, kk + 1, x);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) fb[c ^ 1][x] = frag_tr(st + kStageElems, tb, kk + 1, x);
       }
-      mfma_block(acc, fa[c], fb[c]);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
   if (KT > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) issue(lds, 0, u);
+    for (int u = 0; u < 4; ++u) issue(lds, 0, u);
   }
   for (int kt = 0; kt < KT; ++kt)
     step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
   __syncthreads();
-  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 128);
-  store_tile128_f32(acc, ep, lane, kh, l32, wm, wn, m0, p.M, n0, p.N, p.C + (size_t)s * p.strideC);
+  // epilogue: the wavefront's 128 x 64 fp32 block through its 8 KB of LDS, 32 rows at a time
+  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
+  float* C = p.C + (size_t)s * p.strideC;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+    __builtin_amdgcn_wave_barrier();
+    const int rbase = m0 + wm * 128 + mi * 32;
+#pragma unroll 1
+    for (int pass = 0; pass < 8; ++pass) {
+      const int rr = pass * 4 + (lane >> 4), c4 = (lane & 15) * 4;
+      const int row = rbase + rr, col = n0 + wn * 64 + c4;
+      if (row < p.M && col < p.N)
+        *reinterpret_cast<float4*>(C + (size_t)row * p.N + col) = *reinterpret_cast<const float4*>(ep + rr * 64 + c4);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // Persistent: grid = CUs rounded to a multiple of 8, a grid-stride loop over
@@ -393,7 +373,7 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
 // dealt round-robin over the XCDs (item % 8 = the workgroup's XCD): with
 // contiguous XCD ranges a skewed routing left one XCD with three times the
 // mean work.
-__global__ __launch_bounds__(256, 1) void gemm_tn_kernel(TnParams p) {
+__global__ __launch_bounds__(512, 1) void gemm_tn_kernel(TnParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
   for (int item = blockIdx.x; item < p.units; item += gridDim.x) {
     const int per_seg = p.tiles_m * p.tiles_n;
@@ -589,7 +569,7 @@ hipError_t launch_gemm_tn(const void* P, int ldp, int pc0, const void* Q, int ld
     p.tiles_m = (M + 255) / 256;
     p.tiles_n = (N + 255) / 256;
     p.units = n_seg * p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)grid), dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }
