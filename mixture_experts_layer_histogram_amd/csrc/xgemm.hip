@@ -361,7 +361,8 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
       const int rr = pass * 4 + (lane >> 4), c4 = (lane & 15) * 4;
       const int row = rbase + rr, col = n0 + wn * 64 + c4;
       if (row < p.M && col < p.N)
-        *reinterpret_cast<float4*>(C + (size_t)row * p.N + col) = *reinterpret_cast<const float4*>(ep + rr * 64 + c4);
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ep + rr * 64 + c4),
+                                    reinterpret_cast<f32x4*>(C + (size_t)row * p.N + col));
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -395,7 +396,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_kernel(TnParams p) {
 // per row, chunk c of row r in slot c ^ 4 (r & 3), the same swizzle as the
 // 256-column stage: it only touches the low four bits of the chunk index), and
 // the accumulators stored straight from registers (half a wavefront writes
-// 128 contiguous bytes of one row).  Several workgroups share a CU, so one's
+// 128 contiguous bytes of one row) as nontemporal stores: the fp32 gradients
+// are not read again here, and streaming them past the caches measured 1.5%
+// faster.  Several workgroups share a CU, so one's
 // stores overlap another's loads; each K step is load, barrier, 16 MFMAs.
 __device__ __forceinline__ void tr_dma_offsets128(int wave, int lane, int rowbytes, int col0, int (&voff)[4]) {
 #pragma unroll
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(256) void gemm_tn_short_kernel(TnParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          if (m < p.M) C[(size_t)m * p.N + n] = acc[mi][ni][r];
+          if (m < p.M) __builtin_nontemporal_store(acc[mi][ni][r], C + (size_t)m * p.N + n);
         }
     }
   }
