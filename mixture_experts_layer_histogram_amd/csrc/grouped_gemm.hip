@@ -435,7 +435,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) dma16(ra, st + (16 * wn + 8 * uu) * kBK2, voffa[uu], so);
 #pragma unroll
-      for (int uu = 0; uu < 8; ++uu) dma16(rb, st + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+      for (int uu = 0; uu < 8; ++uu) dma16_stream(rb, st + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
     }
   }
   for (int kt = kt0; kt < kt1; ++kt) {
@@ -462,11 +462,11 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 #pragma unroll
           for (int uu = 0; uu < 2; ++uu) dma16(ra, nx + (16 * wn + 8 * uu) * kBK2, voffa[uu], so);
 #pragma unroll
-          for (int uu = 0; uu < 2; ++uu) dma16(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+          for (int uu = 0; uu < 2; ++uu) dma16_stream(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
         } else {
 #pragma unroll
           for (int uu = 3 * kk - 1; uu < 3 * kk + 2; ++uu)
-            dma16(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
+            dma16_stream(rb, nx + (kBM3 + 64 * wn + 8 * uu) * kBK2, voffb[uu], so);
         }
       }
       if (kk + 1 < kBK2 / 16) {
