@@ -374,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
 // flight per CU rather than MFMA reuse: 4 wavefronts in a 1 x 4 layout, each
 // 64 x 64 (2 x 2 MFMA 32x32x16 blocks), and a 3-stage LDS ring of 40 KB stages
 // (A: 64 rows, B: 256 rows, 128 bytes each) keeps two K steps of loads in
-// flight.
+// flight.  The weights, read once per call, arrive as nontemporal loads.
 template <int MODE, bool HAS_BIAS, bool GATHER>
 __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, uint16_t* lds, int wn, int lane) {
   const int l32 = lane & 31, kh = lane >> 5;
@@ -665,10 +665,10 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 }
 
 // Persistent over the 64-row tile list, same XCD-major unit spans as the
-// 256-row kernel.  It runs after the 256-row kernel on the same stream.
-// (One kernel that ran both lists, 256-row units first and then 64-row units
-// in every workgroup, measured slower than the two launches once the 256-row
-// tile moved to 8 wavefronts: the 64-row tile streams weights with 4.)
+// 256-row kernel.  It runs after the 256-row kernel on the same stream: the
+// two tiles want different workgroup shapes (8 and 4 wavefronts).  The pair
+// of launches measured faster than the earlier single kernel that ran both
+// lists, 256-row units first, with a 4-wavefront 256-row tile.
 template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
