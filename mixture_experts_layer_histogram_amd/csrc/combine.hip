@@ -8,7 +8,12 @@
 // the residual connection.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr size_t kLastLevelCacheBytes = 256ull << 20;   // MI355X Infinity Cache (MALL)
 
 template <typename T>
 union Vec16 {
@@ -18,7 +23,13 @@ union Vec16 {
 
 // One wavefront per token.  out = (residual + shared) + sum_j g_j * y[slot_pos_j],
 // j ascending, fp32 accumulation, one rounding to the storage type at the end.
-template <typename T>
+// STREAM: the expert rows are loaded and the output stored with nontemporal
+// hints, for calls whose expert rows exceed the 256 MB last-level cache
+// (DeepSeek-V3 shapes: 0.94 GB, 277 -> 229 us).  Below that size the rows
+// the down projection just wrote still hit in that cache, and the hints cost
+// (Mixtral prefill: 21 -> 25 us); a hint on only the loads or only the stores
+// gains 2-3%.
+template <typename T, bool STREAM>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ gates, const T* __restrict__ res,
                                                       const T* __restrict__ sh, T* __restrict__ out, int N,
@@ -54,14 +65,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
         if (pos[j] < 0) continue;
         const size_t yr = (size_t)pos[j] * d + c;
         Vec16<T> buf;
-        buf.u = *reinterpret_cast<const uint4*>(y + yr);
+        if (STREAM) {
+          const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + yr));
+          buf.u = uint4{raw.x, raw.y, raw.z, raw.w};
+        } else {
+          buf.u = *reinterpret_cast<const uint4*>(y + yr);
+        }
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g[j], Store<T>::load(buf.e, v), acc[v]);
       }
       Vec16<T> ob;
 #pragma unroll
       for (int v = 0; v < VEC; ++v) Store<T>::store(ob.e, v, acc[v]);
-      *reinterpret_cast<uint4*>(out + trow + c) = ob.u;
+      if (STREAM)
+        __builtin_nontemporal_store(u32x4{ob.u.x, ob.u.y, ob.u.z, ob.u.w}, reinterpret_cast<u32x4*>(out + trow + c));
+      else
+        *reinterpret_cast<uint4*>(out + trow + c) = ob.u;
     }
   } else {
     for (int c = lane; c < d; c += 64) {
@@ -125,13 +144,20 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
   const int N = (int)c.n_tokens;
   if (N == 0) return hipSuccess;
   const dim3 grid((N + 3) / 4);
-  if (c.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)y_perm, slot_pos,
-                       gates, (const uint16_t*)residual, (const uint16_t*)shared_y, (uint16_t*)out, N,
-                       c.d_model, c.top_k);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float*)y_perm, slot_pos, gates,
-                       (const float*)residual, (const float*)shared_y, (float*)out, N, c.d_model, c.top_k);
+  const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  const bool stream = (size_t)N * c.top_k * c.d_model * esz > kLastLevelCacheBytes;
+  auto go = [&](auto kern, auto* tp) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const T*)y_perm, slot_pos, gates, (const T*)residual,
+                       (const T*)shared_y, (T*)out, N, c.d_model, c.top_k);
+  };
+  if (c.dtype == MOE_BF16) {
+    if (stream) go(combine_kernel<uint16_t, true>, (uint16_t*)nullptr);
+    else go(combine_kernel<uint16_t, false>, (uint16_t*)nullptr);
+  } else {
+    if (stream) go(combine_kernel<float, true>, (float*)nullptr);
+    else go(combine_kernel<float, false>, (float*)nullptr);
+  }
   return hipGetLastError();
 }
 

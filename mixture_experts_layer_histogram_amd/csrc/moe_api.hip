@@ -28,7 +28,7 @@ Workspace workspace_layout(const moe_config& c) {
   // top-k blocking: L lanes per token, 4 waves, iters rounds per block
   const int L = topk_lanes(c.n_experts);
   const int per_iter = 4 * (64 / L);
-  long long iters = ((long long)N + (long long)per_iter * 256 - 1) / ((long long)per_iter * 256);
+  long long iters = ((long long)N + (long long)per_iter * 1024 - 1) / ((long long)per_iter * 1024);
   if (iters < 1) iters = 1;
   if (iters > 64) iters = 64;
   W.topk_iters = (int)iters;

@@ -18,7 +18,7 @@
 // Three passes, no atomics on values that decide positions:
 //   1. hist_rank   : per block of 1024 slots, the stable rank of every slot
 //                    among the block's slots of the same expert, and the
-//                    block's per-expert counts [E][blocks].
+//                    block's per-expert counts [blocks][E].
 //   2. scan        : per expert, the exclusive prefix of the block counts (the
 //                    rank base of each block), the total count, the kept
 //                    count min(count, C), offsets (exclusive scan over
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restric
       cnt[w][e] = a;
       a += c;
     }
-    block_counts[(size_t)e * nblk + blockIdx.x] = a;
+    block_counts[(size_t)blockIdx.x * E + e] = a;
   }
   __syncthreads();
 #pragma unroll
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(256) void hist_rank_kernel(const int32_t* __restric
 }
 
 // Pass 2 (one workgroup).  Thread e walks expert e's block counts in block
-// order; then a workgroup scan over experts gives the offsets.
+// order (the threads of a wave read one block's counts side by side); then a
+// workgroup scan over experts gives the offsets.
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ block_counts,
                                                             int nblk, int E, int capacity, int padded,
                                                             int32_t* __restrict__ counts,
@@ -110,14 +111,14 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
   long long drop = 0;
   if (tid < E) {
     int a = 0;
-    int32_t* row = block_counts + (size_t)tid * nblk;
+    int32_t* col = block_counts + tid;
     for (int b0 = 0; b0 < nblk; b0 += 16) {   // 16 loads in flight, then the running sum in order
       int c[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblk ? row[b0 + j] : 0;
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblk ? col[(size_t)(b0 + j) * E] : 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (b0 + j < nblk) row[b0 + j] = a;
+        if (b0 + j < nblk) col[(size_t)(b0 + j) * E] = a;
         a += c[j];
       }
     }
@@ -155,14 +156,14 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
 __global__ __launch_bounds__(256) void scatter_gather_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
     const int32_t* __restrict__ rank_base, const int32_t* __restrict__ offsets, int n_slots, int k,
-    int nblk, int capacity, const char* __restrict__ x, size_t row_bytes, int32_t* __restrict__ perm,
+    int nblk, int E, int capacity, const char* __restrict__ x, size_t row_bytes, int32_t* __restrict__ perm,
     int32_t* __restrict__ slot_pos, char* __restrict__ x_perm, int N, int choice) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + wave;
   if (s >= n_slots) return;
   const int e = topk_idx[s];
   const int blk = index_of(s, N, k, choice) / kHistSlotsPerBlock;
-  const int r = rank_base[(size_t)e * nblk + blk] + local_rank[s];
+  const int r = rank_base[(size_t)blk * E + e] + local_rank[s];
   if (r >= capacity) {
     if (lane == 0) slot_pos[s] = -1;
     return;
@@ -188,13 +189,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ local_rank,
                                                       const int32_t* __restrict__ rank_base,
                                                       const int32_t* __restrict__ offsets, int n_slots,
-                                                      int nblk, int capacity, int32_t* __restrict__ perm,
+                                                      int nblk, int E, int capacity, int32_t* __restrict__ perm,
                                                       int32_t* __restrict__ slot_pos, int N, int k, int choice) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= n_slots) return;
   const int e = topk_idx[s];
   const int blk = index_of(s, N, k, choice) / kHistSlotsPerBlock;
-  const int r = rank_base[(size_t)e * nblk + blk] + local_rank[s];
+  const int r = rank_base[(size_t)blk * E + e] + local_rank[s];
   if (r >= capacity) {
     slot_pos[s] = -1;
     return;
@@ -260,11 +261,11 @@ hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t
   }
   if (x_perm == nullptr) {
     hipLaunchKernelGGL(scatter_kernel, dim3((n_slots + 255) / 256), dim3(256), 0, s, topk_idx, hist_rank,
-                       hist_blocks, offsets, n_slots, nblk, capacity, perm, slot_pos, N, k, choice);
+                       hist_blocks, offsets, n_slots, nblk, E, capacity, perm, slot_pos, N, k, choice);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(scatter_gather_kernel, dim3((n_slots + 3) / 4), dim3(256), 0, s, topk_idx,
-                     hist_rank, hist_blocks, offsets, n_slots, c.top_k, nblk, capacity,
+                     hist_rank, hist_blocks, offsets, n_slots, c.top_k, nblk, E, capacity,
                      (const char*)x, row_bytes, perm, slot_pos, (char*)x_perm, N, choice);
   return hipGetLastError();
 }
