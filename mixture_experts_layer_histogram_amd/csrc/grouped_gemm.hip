@@ -508,16 +508,24 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 // ---------------------------------------------------------------------------
 // 64 x 256 tile with fp8 (E4M3) weights ([S]: quantised expert weights halve
 // the bytes a weight-streaming GEMM moves).  The B tile arrives as codes
-// (256 rows x 64 bytes per K step) through the same direct-to-LDS loads, so a
-// stage is 24 KB and a 5-stage ring keeps four K steps of loads in flight.
-// Fragments are expanded to bf16 exactly (every E4M3 value is a bf16 value)
-// with v_cvt_scalef32_pk_bf16_fp8 at scale 1 and fed to the bf16 MFMA; each
-// output column is multiplied by its weight row's scale before the epilogue.
-// B LDS layout: row r holds four 16-byte chunks, chunk c in slot
-// c ^ ((r >> 2) & 3), which spreads the 8-byte fragment reads of 16
-// consecutive rows over all banks.
-constexpr int kStages8 = 5;
-constexpr int kStage8Elems = kBM3 * kBK2 + (kBN2 * kBK2) / 2;   // bf16 A rows + fp8 B rows, in bf16 units
+// through the same direct-to-LDS loads, 128 K per step: every weight row
+// contributes one whole 128-byte line per step, so the weight stream moves
+// the same line-sized pieces as the bf16 tile (64-K steps, half lines, kept
+// the fp8 stream at 4.5 TB/s).  A stage holds the A rows as two 64-K halves
+// in the bf16 tile's layout plus 256 B rows of 128 bytes (48 KB); a 3-stage
+// ring keeps two steps of loads in flight.  Units keep their K ranges in
+// 64-K steps: a unit with an odd count ends with a half step, whose second
+// half is loaded (inside the row or its buffer) but not used.  Fragments are
+// expanded to bf16 exactly (every E4M3 value is a bf16 value) with
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1 and fed to the bf16 MFMA; each output
+// column is multiplied by its weight row's scale before the epilogue.
+// B LDS layout: row r holds eight 16-byte chunks, chunk c in slot c ^ g(r),
+// as for the bf16 operands.
+constexpr int kStages8 = 3;
+constexpr int kBK8 = 2 * kBK2;                                   // K per fp8 step
+constexpr int kStage8A = 2 * kBM3 * kBK2;                        // two 64-K halves of 64 bf16 rows
+constexpr int kStage8Elems = kStage8A + (kBN2 * kBK8) / 2;      // + 256 fp8 rows of 128 bytes, in bf16 units
+static_assert(kStages8 * kStage8Elems * 2 <= 160 * 1024, "fp8 ring exceeds the CU's LDS");
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -534,16 +542,17 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 v) {
   return u.o;
 }
 
-template <int MODE, bool HAS_BIAS, bool GATHER>
+// NMI: 32-row MFMA blocks computed (1 when the unit has at most 32 rows, as
+// at decode batch sizes; the second block's accumulators then stay zero).
+template <int MODE, bool HAS_BIAS, bool GATHER, int NMI>
 __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& w, uint16_t* lds, int wn,
                                                int lane) {
-  constexpr int P = kStages8 - 1;            // K steps in flight ahead of the one computed
-  constexpr int kLoads = 6;                  // per wavefront and K step: 2 A + 4 B
+  constexpr int kLoads = 12;                 // per wavefront and step: 4 A (2 per half) + 8 B
   const int l32 = lane & 31, kh = lane >> 5;
   const int rowbytes = p.K * 2;
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
 
-  int voffa[2], voffb[4];
+  int voffa[2], voffb[8];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = 16 * wn + 8 * u + (lane >> 3);
@@ -556,17 +565,19 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
       voffa[u] = row * rowbytes + chunk * 16;
     }
   }
-  // B: instruction u of wavefront wn fills rows 64 wn + 16 u + (lane >> 2), slot lane & 3
+  // B: instruction u of wavefront wn fills rows 64 wn + 8 u + (lane >> 3), slot lane & 7
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 64 * wn + 16 * u + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+  for (int u = 0; u < 8; ++u) {
+    const int row = 64 * wn + 8 * u + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(row);
     voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * p.K + chunk * 16;
   }
   const int h = kh ^ swz8(l32);
   const int brow0 = MODE == MODE_SWIGLU_UP ? (32 * wn + l32) : (64 * wn + l32);
   const int bstep = MODE == MODE_SWIGLU_UP ? 128 : 32;
-  const int bsw = (l32 >> 2) & 3;            // (row >> 2) & 3 of both fragment rows (bases are multiples of 32)
+  // g(row) of the two fragment rows: g(32 m + l32) = g(l32) ^ 4 (m & 1), m = wn + 4 x (SwiGLU) or 2 wn + x
+  const int bsw0 = swz8(l32) ^ (MODE == MODE_SWIGLU_UP ? 4 * (wn & 1) : 0);
+  const int bsw1 = MODE == MODE_SWIGLU_UP ? bsw0 : (bsw0 ^ 4);
 
   const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(p.A, p.a_bytes)
                                            : make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
@@ -583,49 +594,57 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  const int kt0 = w.kt0, kt1 = w.kt1;
-#define FP8_LOAD_A(u, st, kt) dma16(ra, (st) + (16 * wn + 8 * (u)) * kBK2, voffa[u], (kt) * kBK2 * 2)
-#define FP8_LOAD_B(u, st, kt) dma16(rb, (st) + kBM3 * kBK2 + (64 * wn + 16 * (u)) * (kBK2 / 2), voffb[u], (kt) * kBK2)
+  // step j covers the 64-K steps kt0 + 2j and kt0 + 2j + 1 (the second only if < kt1)
+  const int kt0 = w.kt0, n64 = w.kt1 - w.kt0, nst = (n64 + 1) >> 1;
+#define FP8_LOAD_A(hf, u, st, k64) \
+  dma16(ra, (st) + (hf) * (kBM3 * kBK2) + (16 * wn + 8 * (u)) * kBK2, voffa[u], ((k64) + (hf)) * kBK2 * 2)
+#define FP8_LOAD_B(u, st, k64) dma16(rb, (st) + kStage8A + (64 * wn + 8 * (u)) * (kBK8 / 2), voffb[u], (k64) * kBK2)
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp) {           // prologue: steps kt0 .. kt0 + P - 1
-    const int kt = kt0 + pp;
-    if (kt < kt1) {
-      uint16_t* st = lds + (kt % kStages8) * kStage8Elems;
-      FP8_LOAD_A(0, st, kt); FP8_LOAD_A(1, st, kt);
+  for (int pp = 0; pp < kStages8 - 1; ++pp) {   // prologue: steps 0 and 1
+    if (pp < nst) {
+      uint16_t* st = lds + pp * kStage8Elems;
+      const int k64 = kt0 + 2 * pp;
+      FP8_LOAD_A(0, 0, st, k64); FP8_LOAD_A(0, 1, st, k64); FP8_LOAD_A(1, 0, st, k64); FP8_LOAD_A(1, 1, st, k64);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) FP8_LOAD_B(u, st, kt);
+      for (int u = 0; u < 8; ++u) FP8_LOAD_B(u, st, k64);
     }
   }
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // outstanding in issue order: steps kt .. kt + r, r = min(P - 1, kt1 - 1 - kt)
-    const int r = min(P - 1, kt1 - 1 - kt);
-    if (r >= 3) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(3 * kLoads));
-    else if (r == 2) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(2 * kLoads));
-    else if (r == 1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(kLoads));
+  for (int j = 0; j < nst; ++j) {
+    // outstanding loads in issue order: step j, then step j + 1 (kLoads) if it exists
+    if (j + 1 < nst) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(kLoads));
     else MOE_WAIT_VM0();
-    __builtin_amdgcn_s_barrier();            // step kt landed everywhere; the slot of kt - 1 is free
-    const uint16_t* st = lds + (kt % kStages8) * kStage8Elems;
-    uint16_t* nx = lds + ((kt + P) % kStages8) * kStage8Elems;
-    const bool more = kt + P < kt1;
+    __builtin_amdgcn_s_barrier();            // step j landed everywhere; the slot of j - 1 is free
+    const uint16_t* st = lds + (j % kStages8) * kStage8Elems;
+    uint16_t* nx = lds + ((j + 2) % kStages8) * kStage8Elems;
+    const bool more = j + 2 < nst;
+    const int knx = kt0 + 2 * (j + 2);
+    const int nsub = 2 * j + 1 < n64 ? 8 : 4;   // a half step computes its first 64 K only
     bf16x8 fa[2], fb[2];
 #pragma unroll
-    for (int kk = 0; kk < kBK2 / 16; ++kk) {
-      if (more && kk < 3) {                   // next loads: 2 / 2 / 2 over the first three sub-steps
-        if (kk == 0) { FP8_LOAD_A(0, nx, kt + P); FP8_LOAD_A(1, nx, kt + P); }
-        else { FP8_LOAD_B(2 * kk - 2, nx, kt + P); FP8_LOAD_B(2 * kk - 1, nx, kt + P); }
+    for (int kk = 0; kk < kBK8 / 16; ++kk) {
+      if (more && kk < 5) {                   // next loads: 4 A, then 2 B in each of the next four sub-steps
+        if (kk == 0) {
+          FP8_LOAD_A(0, 0, nx, knx); FP8_LOAD_A(0, 1, nx, knx); FP8_LOAD_A(1, 0, nx, knx); FP8_LOAD_A(1, 1, nx, knx);
+        } else {
+          FP8_LOAD_B(2 * kk - 2, nx, knx); FP8_LOAD_B(2 * kk - 1, nx, knx);
+        }
       }
+      if (kk >= nsub) continue;
+      const int hf = kk >> 2, kq = kk & 3;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        fa[x] = *reinterpret_cast<const bf16x8*>(st + (32 * x + l32) * kBK2 + ((h ^ (4 * x) ^ (2 * kk)) << 3));
+        if (x < NMI)
+          fa[x] = *reinterpret_cast<const bf16x8*>(st + hf * (kBM3 * kBK2) + (32 * x + l32) * kBK2 +
+                                                   ((h ^ (4 * x) ^ (2 * kq)) << 3));
         const int brow = brow0 + bstep * x;
         // 8 code bytes read with the same element type as the A fragments (the compiler then
         // keeps them apart from the in-flight LDS loads as it does for A)
         const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(
-            st + kBM3 * kBK2 + ((brow * kBK2 + ((kk ^ bsw) << 4) + kh * 8) >> 1));
+            st + kStage8A + ((brow * kBK8 + ((kk ^ (x ? bsw1 : bsw0)) << 4) + kh * 8) >> 1));
         fb[x] = fp8x8_to_bf16(__builtin_bit_cast(uint2, b4));
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < NMI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
@@ -671,7 +690,7 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 // lists, 256-row units first, with a 4-wavefront 256-row tile.
 template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[FP8 ? kStages8 * kStage8Elems : kLdsElems];
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
@@ -687,7 +706,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
   const int lane = tid & 63;
   for (int i = q; i < cs; i += per_xcd) {
     const Unit w = decode_unit(p.tiles_small, ps, s0 + i, p.n_ntiles, KT, cols_per_tile);
-    if (FP8) small_unit_fp8<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
+    if (FP8) {
+      if (w.r1 - w.r0 <= 32) small_unit_fp8<MODE, HAS_BIAS, GATHER, 1>(p, w, lds, wave, lane);
+      else small_unit_fp8<MODE, HAS_BIAS, GATHER, 2>(p, w, lds, wave, lane);
+    }
     else small_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
   }
 }
