@@ -244,3 +244,37 @@ def test_down_combine_matches_unfused(variant):
     dropped = int((host(sp) < 0).sum())
     say(f"down_combine {variant}: N={N} E={E} dropped={dropped}")
     assert np.array_equal(host(out), host(ref))
+
+
+def test_combine_streaming_matches_cached():
+    """moe_combine switches to nontemporal loads and stores once the expert
+    rows exceed the 256 MB last-level cache; the arithmetic is the same, so
+    the first tokens of a large call must give the bits of a small call over
+    the same rows (the large call's parity against the oracle is covered at
+    the DeepSeek-V3 full size)."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import DEEPSEEK_V3
+    N, k, d, T = 8192, 8, 2112, 512                       # 8192 * 8 * 2112 * 2 B = 277 MB of expert rows
+    big = DEEPSEEK_V3.scaled(name="combine_stream", n_tokens=N, d_model=d, d_ff=64, d_ff_shared=0)
+    small = big.scaled(name="combine_cached", n_tokens=T)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    y = (torch.randn((N * k, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    slot_pos = torch.randperm(N * k, device="cuda", generator=gen).to(torch.int32)
+    slot_pos[3 * k + 1] = -1                                # a dropped slot
+    gates = torch.rand((N, k), device="cuda", generator=gen)
+    res = (torch.randn((N, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    out = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
+    M.combine(M.config_from(big), y, slot_pos, gates, out, residual=res)
+    # the small call reads the same rows, renumbered 0 .. T k - 1
+    sp = slot_pos[: T * k].long()
+    kept = sp >= 0
+    y_small = torch.zeros((T * k, d), dtype=torch.bfloat16, device="cuda")
+    y_small[kept.nonzero().squeeze(1)] = y[sp[kept]]
+    sp_small = torch.where(kept, torch.arange(T * k, device="cuda"), torch.full_like(sp, -1)).to(torch.int32)
+    out_small = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    M.combine(M.config_from(small), y_small, sp_small, gates[:T].contiguous(), out_small,
+              residual=res[:T].contiguous())
+    torch.cuda.synchronize()
+    say(f"combine streaming: {N * k * d * 2 / 2**20:.0f} MiB of expert rows against {T * k * d * 2 / 2**20:.0f} MiB")
+    assert torch.equal(out[:T], out_small)
