@@ -148,8 +148,10 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w,
 // expert indices.  Each of the k rounds takes the group maximum of the
 // per-lane best key (xor shuffles), ballots the lanes holding it and lets the
 // lowest such lane win: exact ties go to the lower expert index.  Keys are
-// fp64, formed from the fp32 logits and bias.
-template <int L, int V>
+// fp64, formed from the fp32 logits and bias.  KM >= k bounds the unrolled
+// selection rounds and the per-token arrays (kMaxTopK for every k kept the
+// E = 256 kernel at 189 VGPRs, two wavefronts per SIMD).
+template <int L, int V, int KM>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ zin, float* __restrict__ zout, const float* __restrict__ sel_bias,
     int N, int E, int k, int rule, int iters, int32_t* __restrict__ idx_out,
@@ -216,11 +218,11 @@ __global__ __launch_bounds__(256) void topk_kernel(
     bool taken[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) taken[v] = false;
-    int sel[kMaxTopK];
-    float zsel[kMaxTopK];
-    double psel[kMaxTopK];
+    int sel[KM];
+    float zsel[KM];
+    double psel[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       sel[j] = 0; zsel[j] = 0.f; psel[j] = 0.0;
       if (j < k) {
         double bk = -INFINITY;
@@ -253,32 +255,32 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 
     if (tv) {
-      double gate[kMaxTopK];
+      double gate[KM];
       if (rule == MOE_GATE_TOPK_SOFTMAX) {
         double m = zsel[0];
 #pragma unroll
-        for (int j = 1; j < kMaxTopK; ++j)
+        for (int j = 1; j < KM; ++j)
           if (j < k) m = fmax(m, (double)zsel[j]);
         double den = 0.0;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
+        for (int j = 0; j < KM; ++j) {
           gate[j] = j < k ? exp((double)zsel[j] - m) : 0.0;
           den += gate[j];
         }
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) gate[j] /= den;
+        for (int j = 0; j < KM; ++j) gate[j] /= den;
       } else if (rule == MOE_GATE_SOFTMAX_RENORM) {
         double den = 0.0;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) den += j < k ? psel[j] : 0.0;
+        for (int j = 0; j < KM; ++j) den += j < k ? psel[j] : 0.0;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) gate[j] = psel[j] / den;
+        for (int j = 0; j < KM; ++j) gate[j] = psel[j] / den;
       } else {
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) gate[j] = psel[j];
+        for (int j = 0; j < KM; ++j) gate[j] = psel[j];
       }
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
+      for (int j = 0; j < KM; ++j) {
         if (j < k && (j % L) == gl) {   // k may exceed L
           idx_out[(size_t)t * k + j] = sel[j];
           gates_out[(size_t)t * k + j] = (float)gate[j];
@@ -315,12 +317,23 @@ __global__ __launch_bounds__(64) void probsum_reduce_kernel(const double* __rest
   if (lane == 0) probsum[e] = (float)s;
 }
 
+template <int L, int V, int KM>
+static void launch_topk_lvk(const moe_config& c, const Workspace& W, const float* zin, float* zout,
+                            const float* sel_bias, int32_t* idx, float* gates, double* part,
+                            hipStream_t s) {
+  hipLaunchKernelGGL((topk_kernel<L, V, KM>), dim3(W.topk_blocks), dim3(256), 0, s, zin, zout, sel_bias,
+                     (int)c.n_tokens, c.n_experts, c.top_k, c.gate_rule, W.topk_iters, idx, gates, part);
+}
+
 template <int L, int V>
 static void launch_topk_lv(const moe_config& c, const Workspace& W, const float* zin, float* zout,
                            const float* sel_bias, int32_t* idx, float* gates, double* part,
                            hipStream_t s) {
-  hipLaunchKernelGGL((topk_kernel<L, V>), dim3(W.topk_blocks), dim3(256), 0, s, zin, zout, sel_bias,
-                     (int)c.n_tokens, c.n_experts, c.top_k, c.gate_rule, W.topk_iters, idx, gates, part);
+  const int k = c.top_k;
+  if (k <= 2) launch_topk_lvk<L, V, 2>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+  else if (k <= 4) launch_topk_lvk<L, V, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+  else if (k <= 8) launch_topk_lvk<L, V, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+  else launch_topk_lvk<L, V, kMaxTopK>(c, W, zin, zout, sel_bias, idx, gates, part, s);
 }
 
 hipError_t launch_topk(const moe_config& c, const Workspace& W, const float* zin, float* zout,
