@@ -54,7 +54,7 @@ __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 
 
 // Top-k blocking: L lanes per token (each owning E / L consecutive experts, at
 // most 8), so a wavefront routes 64 / L tokens at once.
-inline int topk_lanes(int E) { return E <= 64 ? 8 : (E <= 128 ? 16 : 32); }
+inline int topk_lanes(int E) { return E <= 64 ? 8 : (E <= 128 ? 16 : 64); }
 
 // Per-expert capacity C = floor(cf * N / E) in double (0x7fffffff when unlimited).
 inline int capacity_of(const moe_config& c) {

@@ -348,7 +348,7 @@ hipError_t launch_topk(const moe_config& c, const Workspace& W, const float* zin
     else if (E <= 32) launch_topk_lv<8, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
     else if (E <= 64) launch_topk_lv<8, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
     else if (E <= 128) launch_topk_lv<16, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
-    else launch_topk_lv<32, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+    else launch_topk_lv<64, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
