@@ -365,6 +365,107 @@ def check_dropped_tokens_pass_residual():
     assert not np.array_equal(out[kept], x64[kept])
 
 
+def _torch_layer_independent(cfg, inp):
+    """The whole forward in torch float64, routing included, written without
+    the oracle: logits by torch.linear; rule B keys softmax(z) + bias, ranked by
+    a stable descending torch.sort; capacity by walking the slots t*k + j in
+    ascending order with a per-expert counter; the shared SwiGLU added to every
+    token with weight 1 ([L] "Shared experts": every token passes through it)."""
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    bits = lambda a: torch.from_numpy(np.asarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).double()
+    cv = (bits if cfg.dtype == "bf16" else lambda a: torch.from_numpy(np.asarray(a, np.float32)).double())
+    x = cv(inp.x)
+    z = TF.linear(x, cv(inp.w_router))
+    if inp.logit_bias is not None:
+        z = z + torch.from_numpy(np.asarray(inp.logit_bias, np.float32)).double()
+    b = torch.zeros(E, dtype=torch.float64) if inp.sel_bias is None else \
+        torch.from_numpy(np.asarray(inp.sel_bias, np.float32)).double()
+    p = torch.softmax(z, dim=1)
+    assert cfg.gate_rule == GATE_SOFTMAX_RENORM
+    idx = torch.sort(p + b, dim=1, descending=True, stable=True).indices[:, :k]
+    ps = p.gather(1, idx)
+    g = ps / ps.sum(dim=1, keepdim=True)
+    C = cfg.capacity if cfg.capacity is not None else N * k
+    taken = [0] * E
+    kept = np.zeros((N, k), dtype=bool)
+    for s in range(N * k):
+        e = int(idx[s // k, s % k])
+        if taken[e] < C:
+            kept[s // k, s % k] = True
+            taken[e] += 1
+    out = x.clone() if cfg.residual else torch.zeros_like(x)
+    if cfg.d_ff_shared:
+        out = out + TF.linear(TF.silu(TF.linear(x, cv(inp.sh_w1))) * TF.linear(x, cv(inp.sh_w3)), cv(inp.sh_w2))
+    for e in range(E):
+        w = {n: cv(v) for n, v in inp.expert(e).items()}
+        for t in range(N):
+            for j in range(k):
+                if kept[t, j] and int(idx[t, j]) == e:
+                    xt = x[t:t + 1]
+                    y = TF.linear(TF.silu(TF.linear(xt, w["w1"])) * TF.linear(xt, w["w3"]), w["w2"])
+                    out[t] += g[t, j] * y[0]
+    return out.numpy(), idx.numpy(), kept
+
+
+def check_shared_expert_term():
+    """The forward with a shared expert, rule B, a selection bias and capacity
+    drops (so some tokens lose some or all of their slots) against the layer
+    computed independently in torch: every token, dropped or not, gets the
+    shared SwiGLU with weight 1 on top of its residual."""
+    cfg = MoEConfig(name="shared_cap", n_tokens=48, d_model=32, n_experts=6, top_k=2, d_ff=24, d_ff_shared=40,
+                    act="swiglu", gate_rule=GATE_SOFTMAX_RENORM, capacity_factor=1.0, dtype="bf16",
+                    residual=True, sel_bias_range=0.2, seed=41)
+    inp = make_inputs(cfg)
+    inp.sel_bias = inp.sel_bias.copy()
+    inp.sel_bias[2] += np.float32(0.5)                          # expert 2 over-full: drops
+    r, out = mo.oracle_layer(cfg, inp)
+    ref, idx, kept = _torch_layer_independent(cfg, inp)
+    assert np.array_equal(r.topk_idx, idx)
+    assert np.array_equal(r.disp.slot_pos.reshape(cfg.n_tokens, cfg.top_k) >= 0, kept)
+    all_dropped = np.nonzero(~kept.any(axis=1))[0]
+    part_dropped = np.nonzero(kept.any(axis=1) & ~kept.all(axis=1))[0]
+    assert all_dropped.size > 0 and part_dropped.size > 0, (all_dropped.size, part_dropped.size)
+    assert np.abs(out - ref).max() <= 1e-12 * np.abs(ref).max(), np.abs(out - ref).max()
+
+
+def check_rows_path():
+    """``oracle_layer(rows=S)`` (the sampled form the full-size tests use) gives
+    the rows S of the whole-batch output and the same routing, on shapes with a
+    shared expert, capacity drops and the padded layout.  Equal up to the
+    rounding of the matrix products only: BLAS picks its kernel by shape, so a
+    product over fewer rows may round differently (measured: one ulp)."""
+    cases = [
+        MoEConfig(name="rows_b", n_tokens=40, d_model=16, n_experts=6, top_k=3, d_ff=20, d_ff_shared=12,
+                  gate_rule=GATE_SOFTMAX_RENORM, capacity_factor=1.2, sel_bias_range=0.1, dtype="bf16", seed=42),
+        MoEConfig(name="rows_c", n_tokens=33, d_model=12, n_experts=4, top_k=1, d_ff=8, act="gelu", ffn_bias=True,
+                  gate_rule=GATE_SWITCH_TOP1, capacity_factor=0.75, capacity_layout="padded",
+                  logit_offset=(1, 1.0), init="uniform_experts", dtype="f32", seed=43),
+    ]
+    for cfg in cases:
+        inp = make_inputs(cfg)
+        r_all, out_all = mo.oracle_layer(cfg, inp)
+        assert r_all.disp.drop_count > 0, cfg.name
+        for S in (np.array([0]), np.array([cfg.n_tokens - 1, 3, 17]), np.arange(1, cfg.n_tokens, 2),
+                  np.nonzero(r_all.disp.slot_pos.reshape(cfg.n_tokens, cfg.top_k).min(axis=1) < 0)[0]):
+            r_s, out_s = mo.oracle_layer(cfg, inp, rows=S)
+            assert np.array_equal(r_s.topk_idx, r_all.topk_idx) and np.array_equal(r_s.disp.perm, r_all.disp.perm)
+            assert out_s.shape == (S.size, cfg.d_model)
+            assert np.abs(out_s - out_all[S]).max() <= 1e-14 * np.abs(out_all).max(), (cfg.name, S)
+
+
+def check_bf16_decode_library():
+    """Every one of the 65536 bfloat16 bit patterns decodes to torch's own
+    bfloat16 value (NaN patterns to NaN, both zeros with their sign)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):                         # signalling-NaN patterns
+        got = mo.to_f64(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
 # ----------------------------------------------------------------- balancing
 
 def check_aux_uniform_is_one():

@@ -12,7 +12,7 @@ import oracle.moe_oracle as mo
 import pin_checks as pc
 
 _orig = {n: getattr(mo, n) for n in ("aux_loss_backward", "e4m3_round", "quantize_fp8_rows", "gate_backward", "silu_grad", "top_k_desc", "route", "ffn_swiglu", "ffn_gelu", "gelu", "dispatch",
-                                       "aux_loss", "bias_step", "softmax_rows", "oracle_layer")}
+                                       "aux_loss", "bias_step", "softmax_rows", "oracle_layer", "to_f64")}
 
 
 def _ties_to_higher(key, k):
@@ -128,7 +128,38 @@ def _quantize_fnuz_max(w):
     return q, (sc * np.float32(448.0 / 240.0)).astype(np.float32)
 
 
+def _bf16_shift15(a, dtype):
+    if dtype != "bf16":
+        return _orig["to_f64"](a, dtype)
+    bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    with np.errstate(invalid="ignore"):
+        return bits.view(np.float32).astype(np.float64)
+
+
+def _rows_off_by_one(cfg, inputs, logits_override=None, rows=None, **kw):
+    if rows is not None:
+        rows = np.minimum(np.asarray(rows, dtype=np.int64) + 1, cfg.n_tokens - 1)
+    return _orig["oracle_layer"](cfg, inputs, logits_override, rows=rows, **kw)
+
+
+def _shared_gated(cfg, inputs, logits_override=None, rows=None, **kw):
+    """The shared expert scaled by the token's kept gate mass (1 unless slots were dropped)."""
+    r, out = _orig["oracle_layer"](cfg, inputs, logits_override, rows=rows, **kw)
+    if cfg.d_ff_shared:
+        sel = np.arange(cfg.n_tokens) if rows is None else np.asarray(rows)
+        x = mo.to_f64(inputs.x, cfg.dtype)[sel]
+        sh = mo.ffn_swiglu(x, mo.to_f64(inputs.sh_w1, cfg.dtype), mo.to_f64(inputs.sh_w3, cfg.dtype),
+                           mo.to_f64(inputs.sh_w2, cfg.dtype))
+        kept = (r.disp.slot_pos.reshape(cfg.n_tokens, cfg.top_k) >= 0)[sel]
+        mass = (r.gates[sel] * kept).sum(axis=1, keepdims=True)
+        out = out - sh + mass * sh
+    return r, out
+
+
 MUTATIONS = [
+    ("to_f64", _bf16_shift15, [pc.check_bf16_decode_library]),
+    ("oracle_layer", _rows_off_by_one, [pc.check_rows_path]),
+    ("oracle_layer", _shared_gated, [pc.check_shared_expert_term]),
     ("gate_backward", _gate_backward_no_centering, [pc.check_backward_autograd]),
     ("aux_loss_backward", _aux_backward_subset_n, [pc.check_sampled_backward_autograd]),
     ("silu_grad", _silu_grad_sigmoid_only, [pc.check_activation_grads_library, pc.check_backward_autograd]),
