@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--also", default="deepseek_v3,mixtral_decode",
+                    help="comma-separated workloads measured after the main one and reported as sub-objects "
+                         "of the same JSON line (the metric's other shapes); '' for none")
+    ap.add_argument("--also-steps", type=int, default=20, help="timed steps of each --also workload")
     ap.add_argument("--oracle-tokens", type=int, default=None,
                     help="tokens in the CPU-baseline sample (default: whole batch for prefill shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,8 +104,7 @@ def main():
         sys.exit(2)
 
     import torch
-    import mixture_experts_layer_histogram_amd as M
-    from workloads import BY_NAME, make_inputs
+    from workloads import BY_NAME
 
     cfg = BY_NAME[args.config]
     if args.capacity_layout or args.capacity_priority:
@@ -110,16 +113,38 @@ def main():
             sys.exit(2)
         cfg = cfg.scaled(capacity_layout=args.capacity_layout or cfg.capacity_layout,
                          capacity_priority=args.capacity_priority or cfg.capacity_priority)
-    dev_name = "cuda:0"
     torch.cuda.set_device(0)
+    result, inp = measure(cfg, args, args.steps, args.warmup, fp8_experts=args.fp8_experts,
+                          backward=args.backward, calib_copy_mib=args.calib_copy_mib)
+    also = [a for a in args.also.split(",") if a and a != cfg.name] if not (args.backward or args.fp8_experts) else []
+    if also:
+        result["other_shapes"] = {}
+    for name in also:
+        print(f"bench: also measuring {name}", file=sys.stderr, flush=True)
+        sub, _ = measure(BY_NAME[name], args, args.also_steps, args.warmup)
+        result["other_shapes"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                                            "expert_gemms", "breakdown_ms")}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens, args.fp8_experts)
+    print(json.dumps(result), flush=True)
+
+
+def measure(cfg, args, steps, warmup, fp8_experts=False, backward=False, calib_copy_mib=0):
+    """Time `steps` whole-layer steps of workload `cfg` (after `warmup` untimed ones) and return
+    (the JSON fields of the measurement, the host inputs)."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import make_inputs
+
+    dev_name = "cuda:0"
     t0 = time.perf_counter()
     inp = make_inputs(cfg)
     dev = M.upload_inputs(inp, dev_name)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
+    if calib_copy_mib > 0:
+        n = calib_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev_name)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -150,7 +175,7 @@ def main():
     aux = torch.empty(1, dtype=f32, device=dev_name) if cfg.aux_loss else None
     signs = torch.empty(E, dtype=torch.int8, device=dev_name)
     fp8 = None
-    if args.fp8_experts:
+    if fp8_experts:
         if cfg.dtype != "bf16":
             print("--fp8-experts needs a bf16 workload", file=sys.stderr)
             sys.exit(2)
@@ -171,7 +196,7 @@ def main():
 
     names = ["route", "permute", "expert_up", "shared", "expert_down", "combine", "aux_bias"]
     bw = None
-    if args.backward:
+    if backward:
         if fp8 is not None or cfg.dtype != "bf16":
             print("--backward runs on bf16 weights", file=sys.stderr)
             sys.exit(2)
@@ -242,11 +267,11 @@ def main():
             M.backward(c, dev, dev["x"], bw[0], bw[3], bw[1], d_aux=1.0 if cfg.aux_loss else 0.0, ws=bw[2])
             mark(8)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -271,11 +296,27 @@ def main():
     up_tflops = up_flop / t_up / 1e12
     expert_tflops = (up_flop + down_flop) / ((parts["expert_up"] + parts["expert_down"]) * 1e-3) / 1e12
     # algorithmic bytes of the up call: each used expert's weights once (+ fp8 row scales), the
-    # token rows once, h written once, b1 rows of used experts
+    # token rows once, b1 rows of used experts; the h rows it writes are an intermediate of the
+    # layer (read back by the down projection), reported apart as overhead
     esz = 2 if cfg.dtype == "bf16" else 4
     wsz = 1 if fp8 is not None else esz
-    up_bytes = (used * n_up * F * (d * wsz + (4 if fp8 is not None else 0)) + N * d * esz + kept * F * esz
+    up_bytes = (used * n_up * F * (d * wsz + (4 if fp8 is not None else 0)) + N * d * esz
                 + (used * F * esz if cfg.ffn_bias else 0))
+    h_bytes = kept * F * esz
+    # the expert GEMMs of the layer (up + down [+ shared]) against their own roofline: routed
+    # weights of used experts, shared weights, x read and out written once; FLOPs of kept rows
+    sh_flop = 6.0 * d * Fs * N
+    gemm_flop = up_flop + down_flop + sh_flop
+    gemm_bytes = (used * (n_up + 1) * F * (d * wsz + (4 if fp8 is not None else 0)) + 3 * Fs * d * esz
+                  + 2 * N * d * esz + (used * (F + d) * esz if cfg.ffn_bias else 0))
+    gemm_ms = parts["expert_up"] + parts["expert_down"] + parts["shared"]
+    t_roof_ms = max(gemm_flop / (PEAK_BF16_TFLOPS * 1e12), gemm_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    expert_gemms = {"ms": gemm_ms, "up_ms": parts["expert_up"], "down_ms": parts["expert_down"],
+                    "shared_ms": parts["shared"], "algorithmic_flop": gemm_flop, "algorithmic_bytes": gemm_bytes,
+                    "tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12, "roofline_ms": t_roof_ms,
+                    "frac": t_roof_ms / gemm_ms,
+                    "bound": "mfma" if gemm_flop / (PEAK_BF16_TFLOPS * 1e12) >= gemm_bytes / (PEAK_HBM_GBS * 1e9)
+                    else "hbm"}
     if cfg.dtype == "bf16":
         t_mfma, t_hbm = up_flop / (PEAK_BF16_TFLOPS * 1e12), up_bytes / (PEAK_HBM_GBS * 1e9)
         if t_mfma >= t_hbm:
@@ -295,7 +336,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -312,8 +353,10 @@ def main():
                                "(build_tiles_kernel, grouped_gemm_big_kernel, grouped_gemm_small_kernel, "
                                "split_fixup_kernel; one "
                                f"{'moe_expert_up_fp8' if fp8 is not None else ('moe_expert_up_save' if bw is not None else 'moe_expert_up_gather')} call)",
-                     **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop},
+                     **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop,
+                     "overhead_bytes_h": h_bytes},
         "expert_gemm_tflops": expert_tflops,
+        "expert_gemms": expert_gemms,
         **({"backward": {"ms": parts["backward"],
                          "algorithmic_tflop": bw_flop / 1e12,
                          "tflops": bw_flop / (parts["backward"] * 1e-3) / 1e12,
@@ -326,9 +369,7 @@ def main():
         "input_gen_s": gen_s,
     }
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens, fp8 is not None)
-    print(json.dumps(result), flush=True)
+    return result, inp
 
 
 def cpu_baseline(cfg, inp, n_tok, fp8=False):

@@ -112,8 +112,14 @@ typedef struct moe_config {
   int32_t capacity_priority; /* moe_capacity_priority */
 } moe_config;
 
-/* Rows R of the expert-ordered buffers (perm, x_perm, h_tmp, y_perm):
- * N k for MOE_CAPACITY_PACKED, E C for MOE_CAPACITY_PADDED. */
+/* Rows R of the expert-ordered buffers (perm, x_perm, h_tmp, y_perm, and
+ * pre_act's planes): N k for MOE_CAPACITY_PACKED, E C for MOE_CAPACITY_PADDED
+ * with C = floor(cf * N / E) ([N] item 2), the capacity evaluated as the
+ * library evaluates it (the factor's fp32 value times N over E in double,
+ * truncated).  `capacity` (may be NULL) receives C, or INT32_MAX when the
+ * capacity is unlimited.  Host only, launches nothing.  Errors: MOE_ERR_ARG
+ * for an invalid config or a NULL `rows`. */
+moe_status moe_expert_rows(const moe_config* cfg, int64_t* rows, int32_t* capacity);
 
 /* Bytes of scratch that moe_forward needs for `cfg` (the step entry points
  * need at most this much too).  Host only, launches nothing. */
@@ -380,8 +386,11 @@ typedef struct moe_grads {      /* device outputs; fp32 unless noted */
   float* dgates;                /* [N, k] | NULL: dL/dgates */
 } moe_grads;
 
-/* Workspace bytes moe_backward needs (transposed weight copies, recomputed
- * pre-activations and intermediate gradients).  Host only. */
+/* Workspace bytes moe_backward needs: the forward's scratch (tile lists,
+ * K-split partials), the pre-activations when the forward did not save them,
+ * the expert-ordered token rows, the intermediate gradients (dY, dH, dA, dX,
+ * dz) and the shared expert's intermediates.  No weight copies: every product
+ * reads the weights in their stored layout.  Host only. */
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* x [N, d], dout [N, d] (storage dtype), weights as for moe_forward; `saved`

@@ -60,6 +60,7 @@ _LIB = None
 _P = c_void_p
 _SIGS = {
     "moe_workspace_size": [ctypes.POINTER(MoeConfig), ctypes.POINTER(c_size_t)],
+    "moe_expert_rows": [ctypes.POINTER(MoeConfig), ctypes.POINTER(c_int64), ctypes.POINTER(c_int32)],
     "moe_route": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_permute": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
@@ -141,12 +142,17 @@ def make_config(n_tokens, d_model, n_experts, top_k, d_ff, d_ff_shared=0, act="s
 
 
 def expert_rows(cfg: MoeConfig) -> int:
-    """Rows of the expert-ordered buffers (perm, x_perm, h, y) for this config."""
-    if cfg.capacity_layout == LAYOUTS["padded"]:
-        # same arithmetic as the library: double(cf) * N / E, truncated
-        cap = int(float(cfg.capacity_factor) * cfg.n_tokens / cfg.n_experts) if cfg.capacity_factor > 0 else 0
-        return cfg.n_experts * cap
-    return cfg.n_tokens * cfg.top_k
+    """moe_expert_rows: rows of the expert-ordered buffers (perm, x_perm, h, y) for this config."""
+    n = c_int64(0)
+    _call("moe_expert_rows", ctypes.byref(cfg), ctypes.byref(n), None)
+    return n.value
+
+
+def capacity(cfg: MoeConfig) -> int:
+    """moe_expert_rows' capacity C = floor(cf * N / E) (INT32_MAX when unlimited)."""
+    n, c = c_int64(0), c_int32(0)
+    _call("moe_expert_rows", ctypes.byref(cfg), ctypes.byref(n), ctypes.byref(c))
+    return c.value
 
 
 def workspace_size(cfg: MoeConfig) -> int:

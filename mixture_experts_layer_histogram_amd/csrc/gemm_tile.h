@@ -50,7 +50,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __host__ inline int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 // 16 bytes per lane from `voff + soff` of the buffer straight into LDS at lds + 16 * lane.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
@@ -77,7 +77,7 @@ struct UnitPlan {
   __device__ __host__ int units() const { return full + rem * s; }
 };
 
-__device__ __forceinline__ UnitPlan plan_units(int T, int G, int KT) {
+__device__ __host__ inline UnitPlan plan_units(int T, int G, int KT) {
   UnitPlan p;
   const int rounds = T / G;
   p.rem = T - rounds * G;
@@ -99,8 +99,9 @@ struct Unit {
   int seg, r0, r1, n0, kt0, kt1, slot;
 };
 
-__device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, const UnitPlan& plan, int u,
-                                            int n_ntiles, int KT, int cols_per_tile) {
+// Plain form of decode_unit (host-callable: the CPU tests enumerate units with it).
+__device__ __host__ inline Unit decode_unit_plain(const int32_t* tiles, const UnitPlan& plan, int u, int n_ntiles,
+                                                  int KT, int cols_per_tile) {
   Unit w;
   int tile_lin;
   w.kt0 = 0;
@@ -123,16 +124,40 @@ __device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, c
   const int j = o / cnt;
   const int i = first + o % cnt;
   const int* td = tiles + 4 + kTileInts * i;
+  w.seg = td[0];
+  w.r0 = td[1];
+  w.r1 = td[2];
+  w.n0 = j * cols_per_tile;
+  return w;
+}
+
+__device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, const UnitPlan& plan, int u,
+                                            int n_ntiles, int KT, int cols_per_tile) {
+  Unit w = decode_unit_plain(tiles, plan, u, n_ntiles, KT, cols_per_tile);
   // readfirstlane: the tile entry is the same for every lane; saying so keeps
   // the buffer descriptors built from it in scalar registers
-  w.seg = __builtin_amdgcn_readfirstlane(td[0]);
-  w.r0 = __builtin_amdgcn_readfirstlane(td[1]);
-  w.r1 = __builtin_amdgcn_readfirstlane(td[2]);
-  w.n0 = __builtin_amdgcn_readfirstlane(j * cols_per_tile);
+  w.seg = __builtin_amdgcn_readfirstlane(w.seg);
+  w.r0 = __builtin_amdgcn_readfirstlane(w.r0);
+  w.r1 = __builtin_amdgcn_readfirstlane(w.r1);
+  w.n0 = __builtin_amdgcn_readfirstlane(w.n0);
   w.kt0 = __builtin_amdgcn_readfirstlane(w.kt0);
   w.kt1 = __builtin_amdgcn_readfirstlane(w.kt1);
   w.slot = __builtin_amdgcn_readfirstlane(w.slot);
   return w;
+}
+
+// fp8 64-row tile: a step loads 128 K (two 64-K halves).  A unit with an odd
+// number of 64-K steps ends with a half step, whose second half lies past the
+// unit's K range and, for the unit that ends at K, past the end of the row
+// (the next row, or past the buffer for the last row).  The buffer range
+// check covers the voffset only (the K offset travels in soffset), so those
+// loads get a voffset beyond every buffer instead and read zero; the number of
+// loads, which the vmcnt waits count, stays the same.
+//   A (bf16 rows, one load per half hf): the half step's hf = 1 loads.
+//   B (fp8 rows, 16-byte chunk `chunk` of the 128-byte step): chunks 4..7.
+__device__ __host__ inline int fp8_a_voff(int voff, int hf, bool half) { return (half && hf) ? kOobOffset : voff; }
+__device__ __host__ inline int fp8_b_voff(int voff, int chunk, bool half) {
+  return (half && chunk >= 4) ? kOobOffset : voff;
 }
 
 // Gate-weighted combine in the down projection's epilogue (top-1 routing: a

@@ -526,7 +526,7 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 // in the bf16 tile's layout plus 256 B rows of 128 bytes (48 KB); a 3-stage
 // ring keeps two steps of loads in flight.  Units keep their K ranges in
 // 64-K steps: a unit with an odd count ends with a half step, whose second
-// half is loaded (inside the row or its buffer) but not used.  Fragments are
+// half is loaded as zeros (fp8_a_voff / fp8_b_voff) and not used.  Fragments are
 // expanded to bf16 exactly (every E4M3 value is a bf16 value) with
 // v_cvt_scalef32_pk_bf16_fp8 at scale 1 and fed to the bf16 MFMA; each output
 // column is multiplied by its weight row's scale before the epilogue.
@@ -577,11 +577,14 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
     }
   }
   // B: instruction u of wavefront wn fills rows 64 wn + 8 u + (lane >> 3), slot lane & 7
+  // with the row's 16-byte chunk (lane & 7) ^ g(row); voffh[u]: the same on a half step
+  int voffh[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = 64 * wn + 8 * u + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(row);
     voffb[u] = (MODE == MODE_SWIGLU_UP ? (row & 127) : row) * p.K + chunk * 16;
+    voffh[u] = fp8_b_voff(voffb[u], chunk, true);
   }
   const int h = kh ^ swz8(l32);
   const int brow0 = MODE == MODE_SWIGLU_UP ? (32 * wn + l32) : (64 * wn + l32);
@@ -607,17 +610,22 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 
   // step j covers the 64-K steps kt0 + 2j and kt0 + 2j + 1 (the second only if < kt1)
   const int kt0 = w.kt0, n64 = w.kt1 - w.kt0, nst = (n64 + 1) >> 1;
-#define FP8_LOAD_A(hf, u, st, k64) \
-  dma16(ra, (st) + (hf) * (kBM3 * kBK2) + (16 * wn + 8 * (u)) * kBK2, voffa[u], ((k64) + (hf)) * kBK2 * 2)
-#define FP8_LOAD_B(u, st, k64) dma16(rb, (st) + kStage8A + (64 * wn + 8 * (u)) * (kBK8 / 2), voffb[u], (k64) * kBK2)
+  // loads of step j (k64 = kt0 + 2 j); `half`: step j is a half step (its second 64 K read as zero)
+#define FP8_LOAD_A(hf, u, st, k64, half)                                                           \
+  dma16(ra, (st) + (hf) * (kBM3 * kBK2) + (16 * wn + 8 * (u)) * kBK2, fp8_a_voff(voffa[u], hf, half), \
+        ((k64) + (hf)) * kBK2 * 2)
+#define FP8_LOAD_B(u, st, k64, half) \
+  dma16(rb, (st) + kStage8A + (64 * wn + 8 * (u)) * (kBK8 / 2), (half) ? voffh[u] : voffb[u], (k64) * kBK2)
 #pragma unroll
   for (int pp = 0; pp < kStages8 - 1; ++pp) {   // prologue: steps 0 and 1
     if (pp < nst) {
       uint16_t* st = lds + pp * kStage8Elems;
       const int k64 = kt0 + 2 * pp;
-      FP8_LOAD_A(0, 0, st, k64); FP8_LOAD_A(0, 1, st, k64); FP8_LOAD_A(1, 0, st, k64); FP8_LOAD_A(1, 1, st, k64);
+      const bool half = 2 * pp + 1 >= n64;
+      FP8_LOAD_A(0, 0, st, k64, half); FP8_LOAD_A(0, 1, st, k64, half);
+      FP8_LOAD_A(1, 0, st, k64, half); FP8_LOAD_A(1, 1, st, k64, half);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) FP8_LOAD_B(u, st, k64);
+      for (int u = 0; u < 8; ++u) FP8_LOAD_B(u, st, k64, half);
     }
   }
   for (int j = 0; j < nst; ++j) {
@@ -629,15 +637,17 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
     uint16_t* nx = lds + ((j + 2) % kStages8) * kStage8Elems;
     const bool more = j + 2 < nst;
     const int knx = kt0 + 2 * (j + 2);
+    const bool nhalf = 2 * (j + 2) + 1 >= n64;
     const int nsub = 2 * j + 1 < n64 ? 8 : 4;   // a half step computes its first 64 K only
     bf16x8 fa[2], fb[2];
 #pragma unroll
     for (int kk = 0; kk < kBK8 / 16; ++kk) {
       if (more && kk < 5) {                   // next loads: 4 A, then 2 B in each of the next four sub-steps
         if (kk == 0) {
-          FP8_LOAD_A(0, 0, nx, knx); FP8_LOAD_A(0, 1, nx, knx); FP8_LOAD_A(1, 0, nx, knx); FP8_LOAD_A(1, 1, nx, knx);
+          FP8_LOAD_A(0, 0, nx, knx, nhalf); FP8_LOAD_A(0, 1, nx, knx, nhalf);
+          FP8_LOAD_A(1, 0, nx, knx, nhalf); FP8_LOAD_A(1, 1, nx, knx, nhalf);
         } else {
-          FP8_LOAD_B(2 * kk - 2, nx, knx); FP8_LOAD_B(2 * kk - 1, nx, knx);
+          FP8_LOAD_B(2 * kk - 2, nx, knx, nhalf); FP8_LOAD_B(2 * kk - 1, nx, knx, nhalf);
         }
       }
       if (kk >= nsub) continue;

@@ -326,6 +326,18 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   }
 }
 
+moe_status moe_expert_rows(const moe_config* cfg, int64_t* rows, int32_t* capacity) {
+  try {
+    MOE_TRY(check_config(cfg));
+    if (!rows) return MOE_ERR_ARG;
+    *rows = expert_rows(*cfg);
+    if (capacity) *capacity = capacity_of(*cfg);
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* logit_bias,
                      const float* sel_bias, const float* logits_in, float* logits, int32_t* topk_idx,
                      float* gates, float* probsum, void* ws, size_t ws_bytes, hipStream_t stream) {

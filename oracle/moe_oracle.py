@@ -322,7 +322,8 @@ def oracle_route(cfg, logits: np.ndarray, sel_bias=None) -> RouteResult:
                        signs=signs, new_bias=new_bias, min_gap=float(gap.min()) if gap.size else math.inf)
 
 
-def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs", expert_weights="stored"):
+def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs", expert_weights="stored",
+                 progress=None):
     """The whole forward pass in fp64.
 
     ``inputs`` is a :class:`workloads.LayerInputs`.  ``logits_override`` replaces
@@ -331,7 +332,8 @@ def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"
     tokens (routing, counts and capacity still cover all N).
     ``expert_weights="fp8"`` runs the routed experts on their fp8 round trip
     (``fp8_expert_weights``); the router and the shared expert keep the stored
-    weights.
+    weights.  ``progress(e)``, if given, is called after each expert's rows are
+    done (long full-size runs report with it; it takes no part in the result).
 
     [L] "Concept / FFN swap": h + sum over the chosen experts of gate * expert(h);
     [G] example: out[tokens of e] += weight * expert_e(tokens of e) for each e;
@@ -367,6 +369,8 @@ def oracle_layer(cfg, inputs, logits_override=None, rows=None, sel_bias="inputs"
         Y = expert_apply(cfg.act, x[slots // k], w)
         for s, yrow in zip(slots, Y):
             y_slot[int(s)] = yrow
+        if progress is not None:
+            progress(e)
 
     out = np.zeros((rows.size, d_model))
     if cfg.residual:

@@ -1,0 +1,111 @@
+// Host-side model of the fp8 64-row tile's operand loads (CPU only; no GPU
+// call is made).  For every unit of a tile list — planned and decoded with the
+// kernel's own plan_units / decode_unit_plain — and every 128-K step, it forms
+// each lane's voffset and soffset the way small_unit_fp8 does (with the
+// kernel's fp8_a_voff / fp8_b_voff half-step rule) and checks that every load
+// the buffer range check lets through stays inside its allocation.
+//
+// Usage: fp8_offsets <mode: up|down> <K> <Nn> <E> <rows per expert...>
+// Prints "units=U checked=C oob=O" (O loads past their allocation) with the
+// half-step rule, then the same count without it ("nohalf_oob=").
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../../mixture_experts_layer_histogram_amd/csrc/gemm_tile.h"
+
+using namespace moe;
+
+struct Count {
+  long long units = 0, checked = 0, oob = 0;
+};
+
+static Count run(bool up, int K, int Nn, const std::vector<int>& seg_rows, bool half_rule) {
+  const int E = (int)seg_rows.size();
+  const int G = 256;                                // one workgroup per CU, a multiple of 8
+  const int KT = K / 64;
+  const int cols_per_tile = up ? 128 : 256;         // SwiGLU up: 128 W1 + 128 W3 columns per tile
+  const int n_ntiles = (Nn + cols_per_tile - 1) / cols_per_tile;
+  // 64-row tile list (kind 1): ceil(rows / 64) tiles per segment
+  std::vector<int> offs(E + 1, 0);
+  for (int e = 0; e < E; ++e) offs[e + 1] = offs[e] + seg_rows[e];
+  std::vector<int32_t> tiles(4);
+  int nt = 0;
+  for (int e = 0; e < E; ++e) {
+    const int n = (seg_rows[e] + 63) / 64;
+    for (int i = 0; i < n; ++i) {
+      const int r0 = offs[e] + 64 * i, r1 = std::min(offs[e + 1], r0 + 64);
+      const int32_t ent[8] = {e, r0, r1, nt - i, n, 0, 0, 0};
+      tiles.insert(tiles.end(), ent, ent + 8);
+      ++nt;
+    }
+  }
+  tiles[0] = nt;
+  const long long kept = offs[E];
+  const long long N = up ? kept : 0;                // gather: one token row per kept slot (k = 1 model)
+  const long long rowbytes = 2LL * K;
+  const long long a_alloc = (up ? N : kept) * rowbytes;   // x (up) or h (down) rows written / held
+  const long long b_alloc = (long long)E * Nn * K;        // fp8 weights
+  const UnitPlan plan = plan_units(nt * n_ntiles, G, KT);
+  Count c;
+  for (int u = 0; u < plan.units(); ++u) {
+    const Unit w = decode_unit_plain(tiles.data(), plan, u, n_ntiles, KT, cols_per_tile);
+    ++c.units;
+    const int n64 = w.kt1 - w.kt0, nst = (n64 + 1) / 2;
+    const long long a_base = up ? 0 : (long long)w.r0 * rowbytes;
+    const long long a_recs = up ? N * rowbytes : (long long)(w.r1 - w.r0) * rowbytes;
+    const int nb_rows = std::min(cols_per_tile, Nn - w.n0);
+    const long long b_base = (long long)w.seg * Nn * K + (long long)w.n0 * K;
+    const long long b_recs = (long long)nb_rows * K;
+    for (int j = 0; j < nst; ++j) {
+      const int k64 = w.kt0 + 2 * j;
+      const bool half = half_rule && (2 * j + 1 >= n64);
+      for (int wn = 0; wn < 4; ++wn)
+        for (int lane = 0; lane < 64; ++lane) {
+          for (int ua = 0; ua < 2; ++ua) {
+            const int row = 16 * wn + 8 * ua + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz8(row);
+            int voff;
+            if (up) {   // gather: row r of the expert order is token r (k = 1)
+              const int r = w.r0 + row;
+              voff = (r < w.r1 ? r * (int)rowbytes : kOobOffset) + chunk * 16;
+            } else {
+              voff = row * (int)rowbytes + chunk * 16;
+            }
+            for (int hf = 0; hf < 2; ++hf) {
+              const long long v = fp8_a_voff(voff, hf, half);
+              const long long so = (long long)(k64 + hf) * 128;
+              if (v >= a_recs) continue;          // range check: reads zero, no access
+              ++c.checked;
+              if (a_base + v + so + 16 > a_alloc) ++c.oob;
+            }
+          }
+          for (int ub = 0; ub < 8; ++ub) {
+            const int row = 64 * wn + 8 * ub + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz8(row);
+            const int voff = (up ? (row & 127) : row) * K + chunk * 16;
+            const long long v = fp8_b_voff(voff, chunk, half);
+            const long long so = (long long)k64 * 64;
+            if (v >= b_recs) continue;
+            ++c.checked;
+            if (b_base + v + so + 16 > b_alloc) ++c.oob;
+          }
+        }
+    }
+  }
+  return c;
+}
+
+int main(int argc, char** argv) {
+  if (argc < 5) {
+    std::fprintf(stderr, "usage: %s up|down K Nn rows...\n", argv[0]);
+    return 2;
+  }
+  const bool up = argv[1][0] == 'u';
+  const int K = std::atoi(argv[2]), Nn = std::atoi(argv[3]);
+  std::vector<int> rows;
+  for (int i = 4; i < argc; ++i) rows.push_back(std::atoi(argv[i]));
+  const Count a = run(up, K, Nn, rows, true), b = run(up, K, Nn, rows, false);
+  std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld\n", a.units, a.checked, a.oob, b.oob);
+  return 0;
+}

@@ -158,3 +158,22 @@ def test_down_combine_errors_before_launch():
     assert L.moe_expert_down_combine(ctypes.byref(c1), *bad) == _lib.MOE_ERR_ARG
     mis = (P, P, P, P, P, P, None, None, None, P + 2, P, 1 << 40, None)  # misaligned out
     assert L.moe_expert_down_combine(ctypes.byref(c1), *mis) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_expert_rows_export():
+    """moe_expert_rows: N k rows packed, E C padded, C = floor(cf N / E) with the
+    factor as fp32 (the workloads compute C the same way on their own)."""
+    from workloads import SWITCH_SKEWED
+    c = _cfg()
+    assert _lib.expert_rows(c) == 64 * 2
+    assert _lib.capacity(c) == 2**31 - 1                                   # unlimited
+    for cf, N, E in ((1.25, 16384, 64), (0.1, 1000, 7), (1.1, 333, 5)):
+        w = SWITCH_SKEWED.scaled(capacity_factor=cf, n_tokens=N, n_experts=E)
+        cp = M.make_config(N, 128, E, 1, 128, capacity_factor=cf, capacity_layout="padded")
+        assert _lib.capacity(cp) == w.capacity
+        assert _lib.expert_rows(cp) == E * w.capacity
+    assert _lib.capacity(M.make_config(16384, 2048, 64, 1, 8192, capacity_factor=1.25)) == 320
+    bad = _cfg(top_k=0)
+    n = ctypes.c_int64(0)
+    assert M.lib().moe_expert_rows(ctypes.byref(bad), ctypes.byref(n), None) == _lib.MOE_ERR_ARG
+    assert M.lib().moe_expert_rows(ctypes.byref(c), None, None) == _lib.MOE_ERR_ARG

@@ -149,10 +149,12 @@ def _sample_rows(cfg, slot_pos, n=12):
 def test_backward_full_size(name):
     """Full sizes: dx and dgates on sampled tokens, the weight gradients of
     sampled hidden units of the busiest, the least busy and the first expert
-    (and of the shared expert), each computed by the oracle one by one; the
-    router gradients through a property of every softmax-based gate rule
-    (each token's logit gradient sums to zero over the experts, so the expert
-    sums of dlogit_bias and of dw_router vanish)."""
+    (and of the shared expert), each computed by the oracle one by one.  The
+    router gradients element by element from the oracle's logit gradients of
+    every token (and dx of every token) at the Mixtral and Switch shapes; at
+    every shape also through a property of each softmax-based gate rule (a
+    token's logit gradient sums to zero over the experts, so the expert sums
+    of dlogit_bias and of dw_router vanish)."""
     import torch
     cfg = FULL[name]
     say(f"backward full {name}: generating inputs")
@@ -202,6 +204,21 @@ def test_backward_full_size(name):
             err = rel_err(host(t), gs[n])
             say(f"  shared dsh_{n} cols: rel err {err:.3e}")
             assert err <= tol, (name, "sh", n, err)
+
+    if name in ("mixtral_prefill", "mixtral_decode", "switch_skewed"):
+        # router gradients element by element: the oracle's dL/dlogits of every token, then
+        # dW_r = dz^T x and dlogit_bias = sum_t dz
+        say(f"backward full {name}: oracle dlogits of all {N} tokens")
+        ra = oracle.oracle_backward_rows(cfg, inp, dout_h, np.arange(N), d_aux=d_aux, logits_override=host(z))
+        dz = ra["logits"]
+        x64 = oracle.to_f64(inp.x, cfg.dtype)
+        for gk, ref in (("dw_router", dz.T @ x64), ("dlogit_bias", dz.sum(axis=0))):
+            err = rel_err(host(grads[gk]), ref)
+            say(f"  {gk}: rel err {err:.3e} (every element)")
+            assert err <= tol, (name, gk, err)
+        err = rel_err(host(grads["dx"]), ra["x"])
+        say(f"  dx: rel err {err:.3e} (every token)")
+        assert err <= tol, (name, "dx all", err)
 
     # router: sum over experts of each token's dlogits is zero
     db = host(grads["dlogit_bias"])

@@ -155,7 +155,8 @@ def test_expert_ffn_parity_per_segment():
         M.expert_ffn(layer.cfg, xpad, offs, dev["w1"], dev["w3"], dev["w2"], h, yp, b1=dev["b1"], b2=dev["b2"],
                      ws=layer.ws)
         torch.cuda.synchronize()
-        yp_h = host(yp)
+        with np.errstate(invalid="raise"):                 # a NaN in the written rows fails here
+            yp_h = host(yp[:kept])                         # rows past `kept` are never written
         x64 = oracle.to_f64(inp.x, cfg.dtype)
         for e in range(cfg.n_experts):
             lo, hi = int(o["offsets"][e]), int(o["offsets"][e + 1])

@@ -1,0 +1,57 @@
+"""Host-side (CPU) models of GPU index arithmetic, built from the kernels' own
+host-callable helpers (no GPU call is made).
+
+fp8 64-row tile: every operand load of every unit, for reduction lengths with
+odd 64-K step counts (K = 320) and the decode shapes' K-split parts (K = 4096,
+14336), must stay inside its allocation once the buffer range check has let
+it through.  The same model without the half-step rule finds loads past the
+end (the hazard the rule removes), which shows the model can see it."""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "host_model", "fp8_offsets.hip")
+
+
+@pytest.fixture(scope="module")
+def fp8_model(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("host_model") / "fp8_offsets")
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    r = subprocess.run([hipcc, "-x", "hip", "--cuda-host-only", "-O1", "-std=c++17", "-I",
+                        os.path.join(ROOT, "include"), SRC, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def _run(exe, mode, K, Nn, rows):
+    out = subprocess.run([exe, mode, str(K), str(Nn), *map(str, rows)], capture_output=True, text=True,
+                         check=True).stdout
+    return dict(kv.split("=") for kv in out.split())
+
+
+CASES = [
+    ("down", 320, 256, [3, 7, 0, 64, 65, 1, 2]),          # K/64 odd: every unit ends on a half step
+    ("up", 320, 384, [70, 3, 130, 1]),
+    ("up", 4096, 14336, [5] * 5),                         # decode up: K-parts of odd length at the end
+    ("up", 4096, 14336, [2, 3, 1, 4, 8, 5, 7]),
+    ("down", 14336, 4096, [40] * 3),                      # decode down: s = 5 parts, the last one odd
+    ("down", 14336, 4096, [40] * 5),
+    ("down", 14336, 4096, [2, 3, 1, 4, 8, 5, 7]),
+    ("down", 2048, 7168, [9, 26, 31, 0, 64, 1]),
+]
+
+
+@pytest.mark.parametrize("mode,K,Nn,rows", CASES)
+def test_fp8_loads_in_bounds(fp8_model, mode, K, Nn, rows):
+    r = _run(fp8_model, mode, K, Nn, rows)
+    assert int(r["units"]) > 0 and int(r["checked"]) > 0
+    assert int(r["oob"]) == 0, r
+
+
+def test_fp8_model_sees_the_half_step_hazard(fp8_model):
+    hits = [int(_run(fp8_model, *c)["nohalf_oob"]) for c in CASES]
+    assert hits[0] > 0 and hits[4] > 0, hits
