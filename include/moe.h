@@ -171,6 +171,21 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const voi
                        int64_t* drop_count, void* x_perm, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moe_permute for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same arguments
+ * and results (bit-identical), but no workspace.  Its scratch (per-slot ranks
+ * and per-block expert counts, 5 MiB) is a static device array inside the
+ * library, one copy per GPU, held until the process ends; the call allocates
+ * and frees nothing.  Limit: N k <= 2^20 slots (E <= 256 as everywhere);
+ * larger batches return MOE_ERR_WORKSPACE before any launch.  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller.
+ * Errors as moe_permute, plus MOE_ERR_HIP if the scratch address cannot be
+ * obtained on the current device. */
+moe_status moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                               int64_t* drop_count, void* x_perm, hipStream_t stream);
+
 /* Grouped expert FFN over the ragged expert segments of x_perm ([L] "FFN swap";
  * [X] "Future of expert parallelism": grouped GEMMs that batch many experts).  Rows
  * [offsets[e], offsets[e+1]) of x_perm go through expert e.

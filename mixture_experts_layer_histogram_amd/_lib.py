@@ -63,6 +63,7 @@ _SIGS = {
     "moe_expert_rows": [ctypes.POINTER(MoeConfig), ctypes.POINTER(c_int64), ctypes.POINTER(c_int32)],
     "moe_route": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_permute": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
+    "moe_permute_noalloc": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_up_gather": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
@@ -177,6 +178,12 @@ def permute(cfg, topk_idx, x, counts, offsets, perm, slot_pos, x_perm=None, drop
     wp, wb = _ws(ws)
     _call("moe_permute", ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(perm),
           _ptr(slot_pos), _ptr(drop_count), _ptr(x_perm), wp, wb, _stream(stream))
+
+
+def permute_noalloc(cfg, topk_idx, x, counts, offsets, perm, slot_pos, x_perm=None, drop_count=None, stream=None):
+    """moe_permute_noalloc: moe_permute on the library's static per-GPU scratch (no workspace)."""
+    _call("moe_permute_noalloc", ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+          _ptr(perm), _ptr(slot_pos), _ptr(drop_count), _ptr(x_perm), _stream(stream))
 
 
 def expert_ffn(cfg, x_perm, offsets, w1, w3, w2, h_tmp, y_perm, b1=None, b2=None, ws=None, stream=None):

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace moe {
 
@@ -299,6 +300,40 @@ bool gather_ok(const moe_config& c) {
   return (size_t)c.n_tokens * (size_t)c.d_model * 2 <= grouped_gemm_gather_max_bytes();
 }
 
+// ------------------------------------------------ scratch of the allocation-free dispatch
+// moe_permute_noalloc keeps its scratch in this array instead of a caller's
+// workspace: the per-slot ranks (kNoAllocMaxSlots int32), then the per-block
+// expert counts ([kNoAllocMaxSlots / kHistSlotsPerBlock][kMaxExperts] int32).
+// Every GPU the library runs on holds its own copy until the process ends; the
+// host reaches it only through the address hipGetSymbolAddress returns on that
+// device (the array's name is a host-side stand-in, not a device address).
+constexpr long long kNoAllocMaxSlots = 1ll << 20;
+constexpr size_t kNoAllocRankBytes = (size_t)kNoAllocMaxSlots * 4;
+constexpr size_t kNoAllocScratchBytes =
+    kNoAllocRankBytes + (size_t)(kNoAllocMaxSlots / kHistSlotsPerBlock) * kMaxExperts * 4;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+moe_status scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,6 +407,30 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const voi
     const Workspace W = workspace_layout(c);
     MOE_TRY(check_ws(ws, ws_bytes, scratch_end(W)));
     return do_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm, ws, stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* slot_pos, int64_t* drop_count,
+                               void* x_perm, hipStream_t stream) {
+  try {
+    MOE_TRY(check_config(cfg));
+    const moe_config& c = *cfg;
+    const bool any = c.n_tokens > 0;
+    if (!counts || !offsets) return MOE_ERR_ARG;
+    if (any && (!topk_idx || !perm || !slot_pos || (x_perm && !x))) return MOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+    if (c.n_tokens * (long long)c.top_k > kNoAllocMaxSlots) return MOE_ERR_WORKSPACE;
+    const Workspace W = workspace_layout(c);   // host arithmetic only (the block count)
+    void* base = nullptr;
+    MOE_TRY(scratch_on_device(&base));
+    int32_t* ranks = static_cast<int32_t*>(base);
+    int32_t* blocks = reinterpret_cast<int32_t*>(static_cast<char*>(base) + kNoAllocRankBytes);
+    MOE_HIP(launch_permute(c, W, topk_idx, x, counts, offsets, perm, slot_pos, drop_count, x_perm, ranks, blocks,
+                           stream));
+    return MOE_OK;
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

@@ -177,3 +177,15 @@ def test_expert_rows_export():
     n = ctypes.c_int64(0)
     assert M.lib().moe_expert_rows(ctypes.byref(bad), ctypes.byref(n), None) == _lib.MOE_ERR_ARG
     assert M.lib().moe_expert_rows(ctypes.byref(c), None, None) == _lib.MOE_ERR_ARG
+
+
+def test_permute_noalloc_rejects_before_launch():
+    """moe_permute_noalloc: more than 2^20 slots exceeds its static scratch (MOE_ERR_WORKSPACE),
+    a NULL required pointer is MOE_ERR_ARG; both before anything touches a device."""
+    L = M.lib()
+    P = 4096
+    big = _cfg(n_tokens=(1 << 19) + 1)                    # (2^19 + 1) * 2 slots
+    assert L.moe_permute_noalloc(ctypes.byref(big), P, None, P, P, P, P, None, None, None) == _lib.MOE_ERR_WORKSPACE
+    c = _cfg()
+    assert L.moe_permute_noalloc(ctypes.byref(c), P, None, None, P, P, P, None, None, None) == _lib.MOE_ERR_ARG
+    assert L.moe_permute_noalloc(ctypes.byref(c), P, None, P, P, P, P, None, P, None) == _lib.MOE_ERR_ARG
