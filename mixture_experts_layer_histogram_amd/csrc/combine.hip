@@ -29,15 +29,20 @@ union Vec16 {
 // the down projection just wrote still hit in that cache, and the hints cost
 // (Mixtral prefill: 21 -> 25 us); a hint on only the loads or only the stores
 // gains 2-3%.
+// `parts` wavefronts share a token's row (each its own contiguous 1 / parts of
+// the columns; same per-element arithmetic), so that a small batch (decode)
+// still keeps every column's loads in flight at once.
 template <typename T, bool STREAM>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ gates, const T* __restrict__ res,
                                                       const T* __restrict__ sh, T* __restrict__ out, int N,
-                                                      int d, int k) {
+                                                      int d, int k, int parts) {
   constexpr int VEC = 16 / sizeof(T);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int gw = blockIdx.x * 4 + wave;
+  const int t = gw / parts, part = gw % parts;
   if (t >= N) return;
+  const int span = d / parts, c_beg = part * span, c_end = c_beg + span;
   int pos[kMaxTopK];
   float g[kMaxTopK];
 #pragma unroll
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   const size_t trow = (size_t)t * d;
   if (d % VEC == 0) {
 #pragma unroll 2
-    for (int c = lane * VEC; c < d; c += 64 * VEC) {   // two chunks in flight per lane
+    for (int c = c_beg + lane * VEC; c < c_end; c += 64 * VEC) {   // two chunks in flight per lane
       float acc[VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
         *reinterpret_cast<uint4*>(out + trow + c) = ob.u;
     }
   } else {
-    for (int c = lane; c < d; c += 64) {
+    for (int c = c_beg + lane; c < c_end; c += 64) {
       float acc = res ? Store<T>::load(res, trow + c) : 0.f;
       if (sh) acc += Store<T>::load(sh, trow + c);
 #pragma unroll
@@ -143,13 +148,18 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
                           void* out, hipStream_t s) {
   const int N = (int)c.n_tokens;
   if (N == 0) return hipSuccess;
-  const dim3 grid((N + 3) / 4);
   const size_t esz = c.dtype == MOE_BF16 ? 2 : 4;
+  // wavefronts per token: up to 8, while the batch has fewer than 1024 tokens, each keeping whole
+  // 16-byte chunks of 64 lanes (a column count that does not split that way keeps one wavefront)
+  const int chunk = 64 * (int)(16 / esz);
+  int parts = 1;
+  while (parts < 8 && (long long)N * parts < 1024 && c.d_model % (2 * parts * chunk) == 0) parts *= 2;
+  const dim3 grid((unsigned)(((long long)N * parts + 3) / 4));
   const bool stream = (size_t)N * c.top_k * c.d_model * esz > kLastLevelCacheBytes;
   auto go = [&](auto kern, auto* tp) {
     using T = std::remove_pointer_t<decltype(tp)>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const T*)y_perm, slot_pos, gates, (const T*)residual,
-                       (const T*)shared_y, (T*)out, N, c.d_model, c.top_k);
+                       (const T*)shared_y, (T*)out, N, c.d_model, c.top_k, parts);
   };
   if (c.dtype == MOE_BF16) {
     if (stream) go(combine_kernel<uint16_t, true>, (uint16_t*)nullptr);

@@ -226,6 +226,107 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict
   }
 }
 
+// All three passes in one workgroup, for at most kHistSlotsPerBlock slots with
+// the packed layout and no row copy (decode batches: three launches become
+// one).  Pass 1 is hist_rank_kernel's for the single block; its counts are the
+// expert totals, so pass 2 is the scan over experts and every block base is 0;
+// pass 3 places each slot from the rank it still holds in registers.  Ranks,
+// offsets and positions are the ones the three-kernel path computes.
+__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ topk_idx, int n_slots,
+                                                             int E, int capacity, int N, int k, int choice,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ slot_pos,
+                                                             int64_t* __restrict__ drop_count) {
+  __shared__ int cnt[kHistWaves][kMaxExperts];
+  __shared__ int off[kMaxExperts];
+  __shared__ int wave_tot[kHistWaves];
+  __shared__ long long wave_drop[kHistWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kHistWaves * kMaxExperts; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  // pass 1: stable rank of each slot among the slots of its expert (ballot match per 64-slot chunk)
+  const int base = wave * 64 * kHistChunks;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank[kHistChunks], eid[kHistChunks];
+#pragma unroll
+  for (int ch = 0; ch < kHistChunks; ++ch) {
+    const int i = base + ch * 64 + lane;
+    const int e = i < n_slots ? topk_idx[slot_of(i, N, k, choice)] : -1;
+    uint64_t match = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const int on = (e >> bit) & 1;
+      const uint64_t bb = __ballot(on);
+      match &= on ? bb : ~bb;
+    }
+    const int r = __popcll(match & lower);
+    const int before = e >= 0 ? cnt[wave][e] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && r == 0) cnt[wave][e] = before + __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+    rank[ch] = before + r;
+    eid[ch] = e;
+  }
+  __syncthreads();
+  // pass 2: per expert, the exclusive prefix over waves and the total; then the scan over experts
+  int kept = 0;
+  long long drop = 0;
+  if (tid < E) {
+    int a = 0;
+#pragma unroll
+    for (int w = 0; w < kHistWaves; ++w) {
+      const int c = cnt[w][tid];
+      cnt[w][tid] = a;
+      a += c;
+    }
+    counts[tid] = a;
+    kept = a < capacity ? a : capacity;
+    drop = (long long)(a - kept);
+  }
+  int incl = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  long long dsum = drop;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dsum += __shfl_xor(dsum, o);
+  if (lane == 63) wave_tot[wave] = incl;
+  if (lane == 0) wave_drop[wave] = dsum;
+  __syncthreads();
+  int prefix = 0;
+  for (int w = 0; w < wave; ++w) prefix += wave_tot[w];
+  if (tid < E) {
+    off[tid] = prefix + incl - kept;
+    offsets[tid] = prefix + incl - kept;
+  }
+  if (tid == 0) {
+    int tot = 0;
+    long long dt = 0;
+    for (int w = 0; w < kHistWaves; ++w) { tot += wave_tot[w]; dt += wave_drop[w]; }
+    offsets[E] = tot;
+    if (drop_count) *drop_count = dt;
+  }
+  __syncthreads();
+  // pass 3: positions
+#pragma unroll
+  for (int ch = 0; ch < kHistChunks; ++ch) {
+    const int i = base + ch * 64 + lane;
+    if (i >= n_slots) continue;
+    const int s = slot_of(i, N, k, choice), e = eid[ch];
+    const int r = cnt[wave][e] + rank[ch];
+    if (r >= capacity) {
+      slot_pos[s] = -1;
+    } else {
+      const int pos = off[e] + r;
+      perm[pos] = s;
+      slot_pos[s] = pos;
+    }
+  }
+}
+
 hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t* topk_idx,
                           const void* x, int32_t* counts, int32_t* offsets, int32_t* perm,
                           int32_t* slot_pos, int64_t* drop_count, void* x_perm,
@@ -238,6 +339,11 @@ hipError_t launch_permute(const moe_config& c, const Workspace& W, const int32_t
   const int N = (int)c.n_tokens, k = c.top_k;
   const int choice = c.capacity_priority == MOE_PRIORITY_CHOICE ? 1 : 0;
   const int padded = c.capacity_layout == MOE_CAPACITY_PADDED ? 1 : 0;
+  if (n_slots > 0 && n_slots <= kHistSlotsPerBlock && !padded && x_perm == nullptr) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), 0, s, topk_idx, n_slots, E, capacity, N, k, choice,
+                       counts, offsets, perm, slot_pos, drop_count);
+    return hipGetLastError();
+  }
   if (n_slots > 0) {
     hipLaunchKernelGGL(hist_rank_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, n_slots, E, nblk,
                        hist_rank, hist_blocks, N, k, choice);

@@ -279,3 +279,70 @@ def test_combine_streaming_matches_cached():
     torch.cuda.synchronize()
     say(f"combine streaming: {N * k * d * 2 / 2**20:.0f} MiB of expert rows against {T * k * d * 2 / 2**20:.0f} MiB")
     assert torch.equal(out[:T], out_small)
+
+
+@pytest.mark.parametrize("d,T", [(4096, 16), (4096, 100), (2048, 3), (7168, 8)])
+def test_combine_small_batch_split_matches(d, T):
+    """A batch of fewer than 1024 tokens spreads each token's row over up to 8
+    wavefronts (contiguous column ranges, the same per-element arithmetic): its
+    output must be bit-identical to one wavefront per token, which a batch of
+    1024 or more tokens uses, over the same expert rows and shared-expert rows."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import MIXTRAL_PREFILL
+    N, k = 1100, 2
+    big = MIXTRAL_PREFILL.scaled(name="combine_big", n_tokens=N, d_model=d, d_ff=64)
+    small = big.scaled(name="combine_small", n_tokens=T)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    y = (torch.randn((N * k, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    slot_pos = torch.randperm(N * k, device="cuda", generator=gen).to(torch.int32)
+    slot_pos[1] = -1                                        # a dropped slot
+    gates = torch.rand((N, k), device="cuda", generator=gen)
+    res = (torch.randn((N, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    sh = (torch.randn((N, d), device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    out = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
+    M.combine(M.config_from(big), y, slot_pos, gates, out, residual=res, shared_y=sh)
+    out_small = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    M.combine(M.config_from(small), y, slot_pos[: T * k].contiguous(), gates[:T].contiguous(), out_small,
+              residual=res[:T].contiguous(), shared_y=sh[:T].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(out[:T], out_small)
+
+
+@pytest.mark.parametrize("priority", ["slot", "choice"])
+def test_small_dispatch_matches_three_pass(priority):
+    """At most 1024 slots, packed, no row copy: the single-workgroup dispatch
+    kernel.  Its counts, offsets, permutation, slot positions and drop count
+    must equal the three-kernel path's (taken when x_perm is requested) and the
+    oracle's dispatch of the same routing, with capacity drops."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import SWITCH_SKEWED
+    cfg = SWITCH_SKEWED.scaled(name="small_dispatch", n_tokens=500, n_experts=64, top_k=2, d_model=128, d_ff=128,
+                               gate_rule="topk_softmax", capacity_factor=1.5, capacity_priority=priority)
+    c = M.config_from(cfg)
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    # skewed routing: expert 3 in most tokens' first choice, second choices spread
+    idx = torch.randint(0, E, (N, k), device="cuda", generator=gen, dtype=torch.int32)
+    idx[: 2 * N // 3, 0] = 3
+    idx[:, 1] = torch.where(idx[:, 1] == idx[:, 0], (idx[:, 1] + 1) % E, idx[:, 1])
+    x = torch.zeros((N, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device="cuda")
+    outs = []
+    for xp in (None, torch.empty((N * k, cfg.d_model), dtype=torch.bfloat16, device="cuda")):
+        o = [torch.full((E,), -7, dtype=torch.int32, device="cuda"), torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+             torch.full((N * k,), -7, dtype=torch.int32, device="cuda"), torch.full((N * k,), -7, dtype=torch.int32, device="cuda"),
+             torch.full((1,), -7, dtype=torch.int64, device="cuda")]
+        M.permute(c, idx, x, o[0], o[1], o[2], o[3], xp, drop_count=o[4], ws=ws)
+        torch.cuda.synchronize()
+        outs.append([host(t) for t in o])
+    kept = int(outs[0][1][-1])
+    ref = oracle.dispatch(host(idx).astype(np.int64), E, cfg.capacity, "packed", priority)
+    assert ref.drop_count > 0
+    (cf, of, pf, sf, df), (ct, ot, pt, st, dt) = outs               # fused, three-pass
+    assert np.array_equal(cf, ct) and np.array_equal(of, ot) and np.array_equal(sf, st) and np.array_equal(df, dt)
+    assert np.array_equal(pf[:kept], pt[:kept])
+    assert np.array_equal(outs[0][0], ref.counts) and np.array_equal(outs[0][1], ref.offsets)
+    assert np.array_equal(outs[0][2][:kept], ref.perm) and np.array_equal(outs[0][3], ref.slot_pos)
+    assert int(outs[0][4][0]) == ref.drop_count
