@@ -36,12 +36,15 @@ Workspace workspace_layout(const moe_config& c) {
   W.topk_tokens_per_block = per_iter * W.topk_iters;
   W.topk_blocks = (int)((N + W.topk_tokens_per_block - 1) / W.topk_tokens_per_block);
   W.hist_blocks_n = (int)((slots + kHistSlotsPerBlock - 1) / kHistSlotsPerBlock);
+  // fused router: groups of 16 tokens (E <= 16) or 64, at most 1024 workgroups
+  const long long rtm = c.n_experts <= 16 ? 16 : 64;
+  W.route_blocks = (int)std::min<long long>(std::max<long long>(((long long)N + rtm - 1) / rtm, 1), 1024);
   W.max_tiles = grouped_gemm_max_tiles((int)(rows > slots ? rows : slots), (int)E);
   W.max_tiles_small = grouped_gemm_max_small_tiles((int)(rows > slots ? rows : slots), (int)E);
   W.max_tiles_sh = Fs ? grouped_gemm_max_tiles((int)N, 1) : 0;
   W.max_tiles_sh_small = Fs ? grouped_gemm_max_small_tiles((int)N, 1) : 0;
 
-  W.probsum_part = take((size_t)W.topk_blocks * E * sizeof(double));
+  W.probsum_part = take((size_t)std::max(W.topk_blocks, W.route_blocks) * E * sizeof(double));
   W.hist_rank = take(slots * 4);
   W.hist_blocks = take(E * (size_t)(W.hist_blocks_n > 0 ? W.hist_blocks_n : 1) * 4);
   W.tiles = take((4 + 8 * (size_t)W.max_tiles) * 4);
@@ -145,6 +148,12 @@ moe_status do_route(const moe_config& c, const Workspace& W, const void* x, cons
                     int32_t* topk_idx, float* gates, float* probsum, void* ws, hipStream_t s) {
   const float* zin = logits_in;
   float* zout = nullptr;
+  if (!zin && route_fused_supported(c) && (ws != nullptr || probsum == nullptr)) {
+    // router GEMM, softmax, top-k and gates in one launch
+    MOE_HIP(launch_route_fused(c, W, x, w_router, logit_bias, sel_bias, logits, topk_idx, gates,
+                               ws ? reinterpret_cast<float*>(wsp(ws, W.probsum_part)) : nullptr, probsum, s));
+    return MOE_OK;
+  }
   if (!zin) {
     // Wide routers (E a multiple of 64) run on the grouped GEMM with fp32 output; it needs the
     // scratch part of the workspace.  Narrow ones use the router kernel, which needs none.

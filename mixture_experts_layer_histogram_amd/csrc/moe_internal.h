@@ -79,7 +79,7 @@ struct Workspace {
          aux, signs, x_perm, h, y, h_sh, y_sh;
   size_t total;
   int topk_blocks, topk_tokens_per_block, topk_iters, hist_blocks_n, max_tiles, max_tiles_small, max_tiles_sh,
-      max_tiles_sh_small;
+      max_tiles_sh_small, route_blocks;
 };
 
 // Layout of the workspace for one config (host).
@@ -89,6 +89,11 @@ Workspace workspace_layout(const moe_config& c);
 
 hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w,
                               const float* logit_bias, float* logits, hipStream_t s);
+// Router GEMM + softmax + top-k + gates in one kernel (bf16 storage, E <= 64).
+bool route_fused_supported(const moe_config& c);
+hipError_t launch_route_fused(const moe_config& c, const Workspace& W, const void* x, const void* w,
+                              const float* logit_bias, const float* sel_bias, float* logits, int32_t* idx,
+                              float* gates, float* probsum_part, float* probsum, hipStream_t s);
 hipError_t launch_topk(const moe_config& c, const Workspace& L, const float* z_in, float* z_out,
                        const float* sel_bias, int32_t* idx, float* gates, float* probsum_part,
                        float* probsum, hipStream_t s);

@@ -151,6 +151,137 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w,
 // fp64, formed from the fp32 logits and bias.  KM >= k bounds the unrolled
 // selection rounds and the per-token arrays (kMaxTopK for every k kept the
 // E = 256 kernel at 189 VGPRs, two wavefronts per SIMD).
+// One token's selection and gates from its logits z (lane gl of the token's
+// L-lane group holds experts gl*V .. gl*V+V-1).  Writes idx/gates when `tv`;
+// returns the full-softmax probabilities in p (zero unless `want_p`).
+template <int L, int V, int KM>
+__device__ __forceinline__ void select_token(const float (&z)[V], const int (&ex)[V], const bool (&valid)[V],
+                                             const double (&b)[V], int k, int rule, bool want_p, bool tv, int t,
+                                             int lane, int gl, int gbase, uint64_t gmask,
+                                             int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
+                                             double (&p)[V]) {
+  if (want_p) {
+    float m = z[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) m = fmaxf(m, z[v]);
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+    double sum = 0.0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      p[v] = valid[v] ? exp((double)z[v] - (double)m) : 0.0;
+      sum += p[v];
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, L);
+#pragma unroll
+    for (int v = 0; v < V; ++v) p[v] = p[v] / sum;
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) p[v] = 0.0;
+  }
+  double key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const double kv = rule == MOE_GATE_SOFTMAX_RENORM ? p[v] + b[v] : (double)z[v] + b[v];
+    key[v] = valid[v] ? kv : -INFINITY;
+  }
+
+  bool taken[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) taken[v] = false;
+  int sel[KM];
+  float zsel[KM];
+  double psel[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    sel[j] = 0; zsel[j] = 0.f; psel[j] = 0.0;
+    if (j < k) {
+      double bk = -INFINITY;
+      int bi = 0x7fffffff;
+      float bz = 0.f;
+      double bp = 0.0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (valid[v] && !taken[v] && (bi == 0x7fffffff || key[v] > bk)) {
+          bk = key[v]; bi = ex[v]; bz = z[v]; bp = p[v];
+        }
+      }
+      double gm = bk;
+#pragma unroll
+      for (int off = L / 2; off >= 1; off >>= 1) gm = fmax(gm, __shfl_xor(gm, off, L));
+      const bool cand = (bi != 0x7fffffff) && (bk == gm);
+      uint64_t mine = __ballot(cand) & gmask;
+      if (mine == 0) mine = __ballot(bi != 0x7fffffff) & gmask;   // only with NaN keys
+      const int wl = mine ? __builtin_ctzll(mine) : gbase;
+      const int ew = __shfl(bi, wl);
+      const float zw = __shfl(bz, wl);
+      const double pw = __shfl(bp, wl);
+      if (lane == wl) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          if (ex[v] == ew) taken[v] = true;
+      }
+      sel[j] = ew; zsel[j] = zw; psel[j] = pw;
+    }
+  }
+
+  if (tv) {
+    double gate[KM];
+    if (rule == MOE_GATE_TOPK_SOFTMAX) {
+      double m = zsel[0];
+#pragma unroll
+      for (int j = 1; j < KM; ++j)
+        if (j < k) m = fmax(m, (double)zsel[j]);
+      double den = 0.0;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        gate[j] = j < k ? exp((double)zsel[j] - m) : 0.0;
+        den += gate[j];
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) gate[j] /= den;
+    } else if (rule == MOE_GATE_SOFTMAX_RENORM) {
+      double den = 0.0;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) den += j < k ? psel[j] : 0.0;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) gate[j] = psel[j] / den;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) gate[j] = psel[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k && (j % L) == gl) {   // k may exceed L
+        idx_out[(size_t)t * k + j] = sel[j];
+        gates_out[(size_t)t * k + j] = (float)gate[j];
+      }
+    }
+  }
+}
+
+// Per-expert probability sums of one workgroup: in each wave the groups in
+// order, then the waves in order (`nw` waves hold tokens).
+template <int L, int V>
+__device__ __forceinline__ void probsum_block(const double (&pacc)[V], const int (&ex)[V], const bool (&valid)[V],
+                                              int wave, int nw, int lane, int gl, int E,
+                                              double (*psum_lds)[kMaxExperts], double* __restrict__ out) {
+  constexpr int G = 64 / L;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    double tot = pacc[v];
+    for (int gg = 1; gg < G; ++gg) tot += __shfl(pacc[v], gg * L + gl);
+    if (wave < nw && lane < L && valid[v]) psum_lds[wave][ex[v]] = tot;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    double s = psum_lds[0][e];
+    for (int w = 1; w < nw; ++w) s += psum_lds[w][e];
+    out[(size_t)blockIdx.x * E + e] = s;
+  }
+}
+
 template <int L, int V, int KM>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ zin, float* __restrict__ zout, const float* __restrict__ sel_bias,
@@ -185,123 +316,147 @@ __global__ __launch_bounds__(256) void topk_kernel(
       if (zout != nullptr && tv && valid[v]) zout[(size_t)t * E + ex[v]] = z[v];
     }
     double p[V];
-    if (want_p) {
-      float m = z[0];
-#pragma unroll
-      for (int v = 1; v < V; ++v) m = fmaxf(m, z[v]);
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
-      double sum = 0.0;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        p[v] = valid[v] ? exp((double)z[v] - (double)m) : 0.0;
-        sum += p[v];
-      }
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, L);
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        p[v] = p[v] / sum;
-        if (tv) pacc[v] += p[v];
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v) p[v] = 0.0;
-    }
-    double key[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const double kv = rule == MOE_GATE_SOFTMAX_RENORM ? p[v] + b[v] : (double)z[v] + b[v];
-      key[v] = valid[v] ? kv : -INFINITY;
-    }
-
-    bool taken[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) taken[v] = false;
-    int sel[KM];
-    float zsel[KM];
-    double psel[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      sel[j] = 0; zsel[j] = 0.f; psel[j] = 0.0;
-      if (j < k) {
-        double bk = -INFINITY;
-        int bi = 0x7fffffff;
-        float bz = 0.f;
-        double bp = 0.0;
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          if (valid[v] && !taken[v] && (bi == 0x7fffffff || key[v] > bk)) {
-            bk = key[v]; bi = ex[v]; bz = z[v]; bp = p[v];
-          }
-        }
-        double gm = bk;
-#pragma unroll
-        for (int off = L / 2; off >= 1; off >>= 1) gm = fmax(gm, __shfl_xor(gm, off, L));
-        const bool cand = (bi != 0x7fffffff) && (bk == gm);
-        uint64_t mine = __ballot(cand) & gmask;
-        if (mine == 0) mine = __ballot(bi != 0x7fffffff) & gmask;   // only with NaN keys
-        const int wl = mine ? __builtin_ctzll(mine) : gbase;
-        const int ew = __shfl(bi, wl);
-        const float zw = __shfl(bz, wl);
-        const double pw = __shfl(bp, wl);
-        if (lane == wl) {
-#pragma unroll
-          for (int v = 0; v < V; ++v)
-            if (ex[v] == ew) taken[v] = true;
-        }
-        sel[j] = ew; zsel[j] = zw; psel[j] = pw;
-      }
-    }
-
+    select_token<L, V, KM>(z, ex, valid, b, k, rule, want_p, tv, t, lane, gl, gbase, gmask, idx_out, gates_out, p);
     if (tv) {
-      double gate[KM];
-      if (rule == MOE_GATE_TOPK_SOFTMAX) {
-        double m = zsel[0];
 #pragma unroll
-        for (int j = 1; j < KM; ++j)
-          if (j < k) m = fmax(m, (double)zsel[j]);
-        double den = 0.0;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-          gate[j] = j < k ? exp((double)zsel[j] - m) : 0.0;
-          den += gate[j];
-        }
-#pragma unroll
-        for (int j = 0; j < KM; ++j) gate[j] /= den;
-      } else if (rule == MOE_GATE_SOFTMAX_RENORM) {
-        double den = 0.0;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) den += j < k ? psel[j] : 0.0;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) gate[j] = psel[j] / den;
-      } else {
-#pragma unroll
-        for (int j = 0; j < KM; ++j) gate[j] = psel[j];
-      }
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        if (j < k && (j % L) == gl) {   // k may exceed L
-          idx_out[(size_t)t * k + j] = sel[j];
-          gates_out[(size_t)t * k + j] = (float)gate[j];
-        }
-      }
+      for (int v = 0; v < V; ++v) pacc[v] += p[v];
     }
   }
 
   if (probsum_part == nullptr) return;
   // Per-expert sums: groups of this wave in order, then the four waves in order.
+  probsum_block<L, V>(pacc, ex, valid, wave, 4, lane, gl, E, psum_lds, probsum_part);
+}
+
+// --------------------------------------------------------------------------- fused router
+//
+// Router GEMM, softmax, top-k and gates in one kernel for E <= 64 ([L] Step 1:
+// one linear layer, then top-k and softmax; [G] "How an MoE layer works").  A
+// workgroup of 8 wavefronts takes TM = 16 MB tokens at a time (16 for E <= 16,
+// else 64, which halves the router weight's L2 traffic per token): each wavefront
+// multiplies the tokens' rows by all E router rows (MFMA 16x16x32, NB blocks
+// of 16 experts) over its eighth of d; the eight partial tiles are added in
+// LDS in wavefront order (+ logit bias), so the logits do not depend on
+// timing; then 8-lane groups select from the logits in LDS exactly as
+// topk_kernel does (fp64 keys, ties to the lower index), and the workgroup
+// keeps its per-expert probability sums for probsum_reduce_kernel.  x streams
+// from HBM once; the router weight (E d bf16) is read from L2 once per TM
+// tokens.  The logits are still written (the parity hook compares them).
+constexpr int kRouteWaves = 8;
+
+template <int NB, int MB, int KM>
+__global__ __launch_bounds__(512) void route_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ logit_bias,
+    const float* __restrict__ sel_bias, float* __restrict__ logits, int N, int d, int E, int k, int rule,
+    int32_t* __restrict__ idx_out, float* __restrict__ gates_out, double* __restrict__ probsum_part) {
+  constexpr int TM = 16 * MB, EP = 16 * NB, L = 8, V = EP / L;
+  __shared__ float red[kRouteWaves][TM][EP];
+  __shared__ double psum_lds[kRouteWaves][kMaxExperts];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int g = lane / L, gl = lane % L, gbase = g * L;
+  const uint64_t gmask = ((1ull << L) - 1ull) << gbase;
+  const bool want_p = (rule != MOE_GATE_TOPK_SOFTMAX) || (probsum_part != nullptr);
+  const int ksteps = d / 32;
+  const int per = (ksteps + kRouteWaves - 1) / kRouteWaves;
+  const int ks0 = wave * per, ks1 = min(ksteps, ks0 + per);
+
+  const uint16_t* wb[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wb[nb] = w + (size_t)min(nb * 16 + r16, E - 1) * d + kq * 8;
+  int ex[V];
+  bool valid[V];
+  double b[V], pacc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    double tot = pacc[v];
-    for (int gg = 1; gg < G; ++gg) tot += __shfl(pacc[v], gg * L + gl);
-    if (g == 0 && valid[v]) psum_lds[wave][ex[v]] = tot;
+    ex[v] = gl * V + v;
+    valid[v] = ex[v] < E;
+    b[v] = (sel_bias != nullptr && valid[v] && rule != MOE_GATE_SWITCH_TOP1) ? (double)sel_bias[ex[v]] : 0.0;
+    pacc[v] = 0.0;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const double s = ((psum_lds[0][e] + psum_lds[1][e]) + psum_lds[2][e]) + psum_lds[3][e];
-    probsum_part[(size_t)blockIdx.x * E + e] = s;
+
+  const int groups = (N + TM - 1) / TM;
+  for (int grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int t0 = grp * TM;
+    // 1. this wavefront's share of d for all TM tokens and all experts
+    const uint16_t* xa[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xa[mb] = x + (size_t)min(t0 + mb * 16 + r16, N - 1) * d + kq * 8;
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // UNR K steps of loads in flight (as many as the registers allow), then the remainder one by one
+    constexpr int UNR = MB + NB <= 2 ? 16 : (MB + NB <= 4 ? 8 : 4);
+    auto kstep = [&](const bf16x8 (&a)[MB], const bf16x8 (&bb)[NB]) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bb[nb], acc[mb][nb], 0, 0, 0);
+    };
+    int ks = ks0;
+    for (; ks + UNR <= ks1; ks += UNR) {
+      bf16x8 a[UNR][MB], bb[UNR][NB];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) a[u][mb] = *reinterpret_cast<const bf16x8*>(xa[mb] + (ks + u) * 32);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bb[u][nb] = *reinterpret_cast<const bf16x8*>(wb[nb] + (ks + u) * 32);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) kstep(a[u], bb[u]);
+    }
+    for (; ks < ks1; ++ks) {
+      bf16x8 a[MB], bb[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const bf16x8*>(xa[mb] + ks * 32);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bb[nb] = *reinterpret_cast<const bf16x8*>(wb[nb] + ks * 32);
+      kstep(a, bb);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][mb * 16 + kq * 4 + i][nb * 16 + r16] = acc[mb][nb][i];
+    __syncthreads();
+    // 2. partial tiles added in wavefront order, + logit bias; logits out
+    for (int i = threadIdx.x; i < TM * EP; i += blockDim.x) {
+      const int row = i / EP, col = i % EP;
+      float z = red[0][row][col];
+#pragma unroll
+      for (int ww = 1; ww < kRouteWaves; ++ww) z += red[ww][row][col];
+      if (col < E) {
+        if (logit_bias) z += logit_bias[col];
+        if (t0 + row < N) logits[(size_t)(t0 + row) * E + col] = z;
+      }
+      red[0][row][col] = z;
+    }
+    __syncthreads();
+    // 3. selection: token t0 + 8 wave + g of the group
+    const int tk = wave * (64 / L) + g;
+    if (wave < TM / (64 / L)) {
+      const int t = t0 + tk;
+      const bool tv = t < N;
+      float z[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) z[v] = valid[v] ? (tv ? red[0][tk][ex[v]] : 0.f) : -INFINITY;
+      double p[V];
+      select_token<L, V, KM>(z, ex, valid, b, k, rule, want_p, tv, t, lane, gl, gbase, gmask, idx_out, gates_out,
+                             p);
+      if (tv) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) pacc[v] += p[v];
+      }
+    }
+    __syncthreads();   // red is rewritten by the next group
   }
+  if (probsum_part == nullptr) return;
+  probsum_block<L, V>(pacc, ex, valid, wave, TM / (64 / L), lane, gl, E, psum_lds, probsum_part);
 }
 
 // Sum the per-block partials of expert e = blockIdx.x: lane l adds blocks
@@ -334,6 +489,51 @@ static void launch_topk_lv(const moe_config& c, const Workspace& W, const float*
   else if (k <= 4) launch_topk_lvk<L, V, 4>(c, W, zin, zout, sel_bias, idx, gates, part, s);
   else if (k <= 8) launch_topk_lvk<L, V, 8>(c, W, zin, zout, sel_bias, idx, gates, part, s);
   else launch_topk_lvk<L, V, kMaxTopK>(c, W, zin, zout, sel_bias, idx, gates, part, s);
+}
+
+template <int NB, int MB>
+static void launch_route_fused_nm(const moe_config& c, const Workspace& W, const void* x, const void* w,
+                                  const float* lb, const float* sel_bias, float* logits, int32_t* idx, float* gates,
+                                  double* part, hipStream_t s) {
+  const int k = c.top_k;
+  const dim3 grid(W.route_blocks), block(64 * kRouteWaves);
+  const uint16_t *xx = (const uint16_t*)x, *ww = (const uint16_t*)w;
+  const int N = (int)c.n_tokens;
+  if (k <= 2)
+    hipLaunchKernelGGL((route_fused_kernel<NB, MB, 2>), grid, block, 0, s, xx, ww, lb, sel_bias, logits, N,
+                       c.d_model, c.n_experts, k, c.gate_rule, idx, gates, part);
+  else if (k <= 4)
+    hipLaunchKernelGGL((route_fused_kernel<NB, MB, 4>), grid, block, 0, s, xx, ww, lb, sel_bias, logits, N,
+                       c.d_model, c.n_experts, k, c.gate_rule, idx, gates, part);
+  else if (k <= 8)
+    hipLaunchKernelGGL((route_fused_kernel<NB, MB, 8>), grid, block, 0, s, xx, ww, lb, sel_bias, logits, N,
+                       c.d_model, c.n_experts, k, c.gate_rule, idx, gates, part);
+  else
+    hipLaunchKernelGGL((route_fused_kernel<NB, MB, kMaxTopK>), grid, block, 0, s, xx, ww, lb, sel_bias, logits, N,
+                       c.d_model, c.n_experts, k, c.gate_rule, idx, gates, part);
+}
+
+bool route_fused_supported(const moe_config& c) { return c.dtype == MOE_BF16 && c.n_experts <= 64; }
+
+hipError_t launch_route_fused(const moe_config& c, const Workspace& W, const void* x, const void* w,
+                              const float* logit_bias, const float* sel_bias, float* logits, int32_t* idx,
+                              float* gates, float* probsum_part_f, float* probsum, hipStream_t s) {
+  if (!route_fused_supported(c)) return hipErrorInvalidValue;
+  double* part = probsum ? reinterpret_cast<double*>(probsum_part_f) : nullptr;
+  if (c.n_tokens > 0) {
+    const int nb = (c.n_experts + 15) / 16;
+    if (nb <= 1) launch_route_fused_nm<1, 1>(c, W, x, w, logit_bias, sel_bias, logits, idx, gates, part, s);
+    else if (nb <= 2) launch_route_fused_nm<2, 4>(c, W, x, w, logit_bias, sel_bias, logits, idx, gates, part, s);
+    else launch_route_fused_nm<4, 4>(c, W, x, w, logit_bias, sel_bias, logits, idx, gates, part, s);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (probsum) {
+    const int nblk = c.n_tokens > 0 ? W.route_blocks : 0;
+    hipLaunchKernelGGL(probsum_reduce_kernel, dim3(c.n_experts), dim3(64), 0, s, part, nblk, c.n_experts, probsum);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const moe_config& c, const Workspace& W, const float* zin, float* zout,

@@ -169,9 +169,11 @@ def test_expert_ffn_parity_per_segment():
 
 
 def test_router_paths_agree():
-    """Wide routers (E a multiple of 64, bf16) run on the grouped GEMM when a workspace is
-    given, otherwise on the router kernel: both match the oracle's logits, and each routing
-    is bit-exact against the oracle run on its own logits."""
+    """bf16 routers with E <= 64 run the fused router kernel (GEMM, softmax, top-k in one
+    launch) with or without a workspace; wider ones with E a multiple of 64 run on the
+    grouped GEMM when a workspace is given, otherwise on the router kernel.  Every path
+    matches the oracle's logits, and each routing is bit-exact against the oracle run on
+    its own logits."""
     import torch
     import mixture_experts_layer_histogram_amd as M
     for name in ("deepseek_v3_small", "switch_skewed_small"):
