@@ -160,6 +160,140 @@ __device__ __host__ inline int fp8_b_voff(int voff, int chunk, bool half) {
   return (half && chunk >= 4) ? kOobOffset : voff;
 }
 
+// ---------------------------------------------------------------------------
+// Per-segment tile table of the forward grouped GEMM.  Segment e (rows
+// [off[e], off[e+1])) is cut into 256-row tiles (kind 0: floor(rows / 256),
+// plus one more when at least kBigTailMin rows remain; kind 1: none) and
+// 64-row tiles for the rest; pb / ps are the exclusive prefix counts of the two
+// kinds over the segments.  Every workgroup builds the table in LDS from the
+// offsets (E <= 256, one wavefront) and decodes its units from it, so no
+// separate launch has to write a tile list first.  Unit order as for the tile
+// lists: segment by segment, column tile by column tile over the segment's
+// row tiles.
+constexpr int kBigTailMin = 128;
+
+struct SegTable {
+  int off[kMaxExperts + 1];
+  int pb[kMaxExperts + 1];
+  int ps[kMaxExperts + 1];
+};
+constexpr int kSegTableElems = (int)((sizeof(SegTable) + 15) / 16) * 8;   // in 16-bit LDS elements
+
+__device__ __host__ inline void seg_tiles(int rows, int kind, int& nb, int& ns) {
+  nb = kind == 1 ? 0 : rows / 256;
+  int rest = rows - nb * 256;
+  if (kind == 0 && rest >= kBigTailMin) {
+    nb += 1;
+    rest = 0;
+  }
+  ns = rest > 0 ? (rest + 63) / 64 : 0;
+}
+
+// Called by every thread of the workgroup; wavefront 0 fills the table (lane l
+// takes segments 4l .. 4l + 3), then a barrier.
+__device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __restrict__ offsets, int n_seg,
+                                                int dense_rows, int kind) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int o[4], nb[4], ns[4], sb = 0, ss = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      int lo = 0, hi = 0;
+      if (e < n_seg) {
+        lo = offsets ? offsets[e] : 0;
+        hi = offsets ? offsets[e + 1] : dense_rows;
+      }
+      o[i] = lo;
+      seg_tiles(hi - lo, kind, nb[i], ns[i]);
+      if (e >= n_seg) nb[i] = ns[i] = 0;
+      sb += nb[i];
+      ss += ns[i];
+    }
+    int ib = sb, is = ss;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int vb = __shfl_up(ib, d), vs = __shfl_up(is, d);
+      if (lane >= d) { ib += vb; is += vs; }
+    }
+    int eb = ib - sb, es = is - ss;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < n_seg) {
+        t.off[e] = o[i];
+        t.pb[e] = eb;
+        t.ps[e] = es;
+      }
+      eb += nb[i];
+      es += ns[i];
+    }
+    if (lane == 63) {
+      t.off[n_seg] = n_seg > 0 ? (offsets ? offsets[n_seg] : dense_rows) : 0;
+      t.pb[n_seg] = ib;
+      t.ps[n_seg] = is;
+    }
+  }
+  __syncthreads();
+}
+
+// Unit u of the 256-row (big) or 64-row list: the segment is the last one whose
+// prefix count is at most the unit's tile index (binary search).
+__device__ __host__ inline Unit decode_unit_seg(const SegTable& t, int n_seg, bool big, const UnitPlan& plan, int u,
+                                                int n_ntiles, int KT, int cols_per_tile) {
+  Unit w;
+  int tile_lin;
+  w.kt0 = 0;
+  w.kt1 = KT;
+  w.slot = -1;
+  if (u < plan.full) {
+    tile_lin = u;
+  } else {
+    const int v = u - plan.full;
+    tile_lin = plan.full + v / plan.s;
+    const int part = v % plan.s;
+    w.kt0 = (int)((long long)KT * part / plan.s);
+    w.kt1 = (int)((long long)KT * (part + 1) / plan.s);
+    w.slot = v;
+  }
+  const int* pre = big ? t.pb : t.ps;
+  const int ti = tile_lin / n_ntiles;
+  int lo = 0, hi = n_seg - 1;           // largest e with pre[e] <= ti
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= ti) lo = mid; else hi = mid - 1;
+  }
+  const int seg = lo, first = pre[seg], cnt = pre[seg + 1] - first;
+  const int o = tile_lin - first * n_ntiles;
+  const int j = o / cnt, m = o % cnt;
+  const int seg_lo = t.off[seg], seg_hi = t.off[seg + 1];
+  w.seg = seg;
+  if (big) {
+    w.r0 = seg_lo + m * 256;
+    w.r1 = seg_hi < w.r0 + 256 ? seg_hi : w.r0 + 256;
+  } else {
+    const int nbig = t.pb[seg + 1] - t.pb[seg];
+    const int split = seg_hi < seg_lo + nbig * 256 ? seg_hi : seg_lo + nbig * 256;
+    w.r0 = split + m * 64;
+    w.r1 = seg_hi < w.r0 + 64 ? seg_hi : w.r0 + 64;
+  }
+  w.n0 = j * cols_per_tile;
+  return w;
+}
+
+__device__ __forceinline__ Unit decode_unit_lds(const SegTable& t, int n_seg, bool big, const UnitPlan& plan, int u,
+                                                int n_ntiles, int KT, int cols_per_tile) {
+  Unit w = decode_unit_seg(t, n_seg, big, plan, u, n_ntiles, KT, cols_per_tile);
+  w.seg = __builtin_amdgcn_readfirstlane(w.seg);
+  w.r0 = __builtin_amdgcn_readfirstlane(w.r0);
+  w.r1 = __builtin_amdgcn_readfirstlane(w.r1);
+  w.n0 = __builtin_amdgcn_readfirstlane(w.n0);
+  w.kt0 = __builtin_amdgcn_readfirstlane(w.kt0);
+  w.kt1 = __builtin_amdgcn_readfirstlane(w.kt1);
+  w.slot = __builtin_amdgcn_readfirstlane(w.slot);
+  return w;
+}
+
 // Gate-weighted combine in the down projection's epilogue (top-1 routing: a
 // token has at most one slot, so the row holding it is the token's only
 // writer).  Same arithmetic as the separate combine: Y rounded to bf16, then

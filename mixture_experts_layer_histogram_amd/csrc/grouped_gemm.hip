@@ -9,13 +9,14 @@
 // up-projection reads those rows straight from the token matrix instead of a
 // gathered copy.
 //
-// Work decomposition.  A one-workgroup kernel turns `offsets` into two tile
-// lists on the device (256-row tiles for long segments, 64-row tiles for
-// short segments and short tails), so the host never waits for the routing
-// result.  Two persistent kernels follow it on the stream, one per list: the
-// 256-row tiles are bound by the matrix cores and run on 8 wavefronts per CU,
-// the 64-row tiles are bound by streaming the expert's weights and run on 4.
-// A K-split fix-up kernel closes the call.
+// Work decomposition.  Every workgroup turns `offsets` into a per-segment
+// tile table in LDS (256-row tiles for long segments, 64-row tiles for short
+// segments and short tails; SegTable in gemm_tile.h), so the host never waits
+// for the routing result and no launch has to write a tile list first.  Two
+// persistent kernels run, one per tile kind: the 256-row tiles are bound by
+// the matrix cores and run on 8 wavefronts per CU, the 64-row tiles are bound
+// by streaming the expert's weights and run on 4.  A K-split fix-up kernel
+// closes the call.
 //
 // MFMA 32x32x16 layout (lane l): A row l%32, k = 8*(l/32)..+7; B column l%32,
 // same k; D column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
@@ -26,14 +27,11 @@ namespace moe {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 
-// Splits every segment into 256-row tiles and 64-row tiles: floor(rows / 256)
-// full tiles, one more 256-row tile when at least kBigTailMin rows remain,
-// otherwise ceil(rest / 64) 64-row tiles.  kind 1: 64-row tiles only; kind 2:
-// 256-row tiles only (ceil(rows / 256)).  Each list: [0] = tile count; tile i
+// Tile lists for the backward's NN product (xgemm.hip): every segment split
+// into 256-row and 64-row tiles as SegTable does (kind 0, 1), or into 256-row
+// tiles only (kind 2: ceil(rows / 256)).  Each list: [0] = tile count; tile i
 // at [4 + 8 i] = (segment, row_begin, row_end, first tile of the segment in
 // this list, tiles of the segment in this list, 0, 0, 0).
-constexpr int kBigTailMin = 128;
-
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int n_seg,
                                                           int dense_rows, int32_t* __restrict__ big,
                                                           int max_big, int32_t* __restrict__ small,
@@ -87,8 +85,6 @@ struct GemmParams {
   const int32_t* perm;        // gather: expert-order row -> slot id; token = slot / gk
   int gk;                     // gather: slots per token
   uint32_t a_bytes;           // gather: bytes of the token matrix
-  const int32_t* tiles;       // 256-row tile list
-  const int32_t* tiles_small; // 64-row tile list
   const uint16_t* W;          // [n_seg, Nn, K]
   const uint16_t* W3;         // SwiGLU: [n_seg, Nn, K]
   const uint16_t* bias;       // [n_seg, Nn] or null
@@ -105,6 +101,8 @@ struct GemmParams {
   float* partials;            // K-part tiles of the 256-row list
   float* partials_small;      // K-part tiles of the 64-row list
   int K, Nn, n_ntiles;
+  const int32_t* offsets;     // segment row offsets [n_seg + 1], or null: one dense segment of dense_rows
+  int n_seg, dense_rows, kind;   // kind: tile table kind (0: 256- and 64-row tiles, 1: 64-row only)
 };
 
 template <int MODE, bool HAS_BIAS, int NMI = 2>
@@ -359,11 +357,16 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 // expert's weights meet in one L2.
 template <int MODE, bool HAS_BIAS, bool GATHER>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems];
+  // one LDS object: the operand stages, then the tile table (a second __shared__ object
+  // would keep the compiler from telling the fragment reads apart from the in-flight
+  // direct-to-LDS loads, and it would then wait for those loads before every read)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems + kSegTableElems];
+  SegTable& segt = *reinterpret_cast<SegTable*>(lds + 2 * 2 * kStageElems);
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  const UnitPlan pb = plan_units(p.tiles[0] * p.n_ntiles, G, KT);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
   const int ub = pb.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   for (int i = q; i < cb; i += per_xcd) {
-    const Unit w = decode_unit(p.tiles, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_lds(segt, p.n_seg, true, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
     big_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
   }
 }
@@ -711,11 +714,14 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 // lists, 256-row units first, with a 4-wavefront 256-row tile.
 template <int MODE, bool HAS_BIAS, bool GATHER, bool FP8>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[FP8 ? kStages8 * kStage8Elems : kLdsElems];
+  constexpr int kRing = FP8 ? kStages8 * kStage8Elems : kStages3 * kStage3Elems;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kRing + kSegTableElems];   // one LDS object, as above
+  SegTable& segt = *reinterpret_cast<SegTable*>(lds + kRing);
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  const UnitPlan ps = plan_units(p.tiles_small[0] * p.n_ntiles, G, KT);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
   const int us = ps.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
   const int lane = tid & 63;
   for (int i = q; i < cs; i += per_xcd) {
-    const Unit w = decode_unit(p.tiles_small, ps, s0 + i, p.n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_lds(segt, p.n_seg, false, ps, s0 + i, p.n_ntiles, KT, cols_per_tile);
     if (FP8) {
       if (w.r1 - w.r0 <= 32) small_unit_fp8<MODE, HAS_BIAS, GATHER, 1>(p, w, lds, wave, lane);
       else small_unit_fp8<MODE, HAS_BIAS, GATHER, 2>(p, w, lds, wave, lane);
@@ -743,11 +749,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
 // 64-row tiles): a1 = oc + (oc / half) * half, a3 = a1 + half.
 template <int MODE, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
+  __shared__ SegTable segt;
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   constexpr int groups = cols_per_tile / 8;
   const int KT = p.K / kBK2;
-  const UnitPlan pb = plan_units(p.tiles[0] * p.n_ntiles, G, KT);
-  const UnitPlan ps = plan_units(p.tiles_small[0] * p.n_ntiles, G, KT);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
+  const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
   const long long nb = (long long)pb.rem * kBM2 * groups;
   const long long n = nb + (long long)ps.rem * kBM3 * groups;
   for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < n;
@@ -759,8 +767,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
     const int rem_it = (int)(jt - (long long)t * bm * groups);
     const int row_in = rem_it / groups, oc = (rem_it % groups) * 8;
     const UnitPlan& pl = big ? pb : ps;
-    const int32_t* tiles = big ? p.tiles : p.tiles_small;
-    const Unit w = decode_unit(tiles, pl, pl.full + t * pl.s, p.n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_seg(segt, p.n_seg, big, pl, pl.full + t * pl.s, p.n_ntiles, KT, cols_per_tile);
     const int row = w.r0 + row_in, col = w.n0 + oc;
     if (row >= w.r1 || col >= p.Nn) continue;
     const float* part = (big ? p.partials : p.partials_small) + (size_t)t * pl.s * bm * kBN2 +
@@ -896,8 +903,10 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.perm = g.perm;
   p.gk = g.gather_k > 0 ? g.gather_k : 1;
   p.a_bytes = GATHER ? (uint32_t)((size_t)g.a_rows * g.K * 2) : 0u;
-  p.tiles = g.tiles;
-  p.tiles_small = g.tiles_small;
+  p.offsets = g.offsets;
+  p.n_seg = g.n_seg;
+  p.dense_rows = g.max_rows;
+  p.kind = FP8 ? 1 : 0;
   p.W = (const uint16_t*)g.w;
   p.W3 = (const uint16_t*)g.w3;
   p.bias = (const uint16_t*)g.bias;
@@ -955,10 +964,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   if (g.fp8 && (g.mode == MODE_LOGITS || (g.mode != MODE_DOWN && !gather) || !g.w8 || !g.scale1 ||
                 (g.mode == MODE_SWIGLU_UP && (!g.w8_3 || !g.scale3))))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, g.offsets, g.n_seg, g.max_rows, g.tiles,
-                     g.max_tiles, g.tiles_small, g.max_tiles_small, g.fp8 ? 1 : 0);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (g.n_seg < 1 || g.n_seg > kMaxExperts) return hipErrorInvalidValue;
   if (g.fp8) {   // fp8 weights: up with the row gather, or down
     if (g.mode == MODE_SWIGLU_UP) launch_bf16<MODE_SWIGLU_UP, false, true, true>(g, s);
     else if (g.mode == MODE_GELU_UP)

@@ -1,13 +1,16 @@
 // Host-side model of the fp8 64-row tile's operand loads (CPU only; no GPU
-// call is made).  For every unit of a tile list — planned and decoded with the
-// kernel's own plan_units / decode_unit_plain — and every 128-K step, it forms
-// each lane's voffset and soffset the way small_unit_fp8 does (with the
-// kernel's fp8_a_voff / fp8_b_voff half-step rule) and checks that every load
-// the buffer range check lets through stays inside its allocation.
+// call is made).  For every unit — planned and decoded with the kernels' own
+// plan_units / decode_unit_seg from the per-segment tile table — and every
+// 128-K step, it forms each lane's voffset and soffset the way small_unit_fp8
+// does (with the kernel's fp8_a_voff / fp8_b_voff half-step rule) and checks
+// that every load the buffer range check lets through stays inside its
+// allocation.  It also decodes every unit through the tile-list form
+// (decode_unit_plain over the list build_tiles_kernel writes for the same
+// segments) and counts the units on which the two decoders disagree.
 //
-// Usage: fp8_offsets <mode: up|down> <K> <Nn> <E> <rows per expert...>
-// Prints "units=U checked=C oob=O" (O loads past their allocation) with the
-// half-step rule, then the same count without it ("nohalf_oob=").
+// Usage: fp8_offsets <mode: up|down> <K> <Nn> <rows per expert...>
+// Prints "units=U checked=C oob=O nohalf_oob=H list_mismatch=M": O loads past
+// their allocation with the half-step rule, H without it.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -17,8 +20,23 @@
 using namespace moe;
 
 struct Count {
-  long long units = 0, checked = 0, oob = 0;
+  long long units = 0, checked = 0, oob = 0, mismatch = 0;
 };
+
+// The table build_seg_table writes (exclusive prefix counts of seg_tiles).
+static SegTable seg_table(const std::vector<int>& offs, int kind) {
+  SegTable t{};
+  const int E = (int)offs.size() - 1;
+  int b = 0, sm = 0;
+  for (int e = 0; e < E; ++e) {
+    int nb, ns;
+    seg_tiles(offs[e + 1] - offs[e], kind, nb, ns);
+    t.off[e] = offs[e]; t.pb[e] = b; t.ps[e] = sm;
+    b += nb; sm += ns;
+  }
+  t.off[E] = offs[E]; t.pb[E] = b; t.ps[E] = sm;
+  return t;
+}
 
 static Count run(bool up, int K, int Nn, const std::vector<int>& seg_rows, bool half_rule) {
   const int E = (int)seg_rows.size();
@@ -46,10 +64,15 @@ static Count run(bool up, int K, int Nn, const std::vector<int>& seg_rows, bool 
   const long long rowbytes = 2LL * K;
   const long long a_alloc = (up ? N : kept) * rowbytes;   // x (up) or h (down) rows written / held
   const long long b_alloc = (long long)E * Nn * K;        // fp8 weights
-  const UnitPlan plan = plan_units(nt * n_ntiles, G, KT);
+  const SegTable table = seg_table(offs, 1);
+  const UnitPlan plan = plan_units(table.ps[E] * n_ntiles, G, KT);
   Count c;
   for (int u = 0; u < plan.units(); ++u) {
-    const Unit w = decode_unit_plain(tiles.data(), plan, u, n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_seg(table, E, false, plan, u, n_ntiles, KT, cols_per_tile);
+    const Unit wl = decode_unit_plain(tiles.data(), plan, u, n_ntiles, KT, cols_per_tile);
+    if (w.seg != wl.seg || w.r0 != wl.r0 || w.r1 != wl.r1 || w.n0 != wl.n0 || w.kt0 != wl.kt0 || w.kt1 != wl.kt1 ||
+        w.slot != wl.slot)
+      ++c.mismatch;
     ++c.units;
     const int n64 = w.kt1 - w.kt0, nst = (n64 + 1) / 2;
     const long long a_base = up ? 0 : (long long)w.r0 * rowbytes;
@@ -96,6 +119,49 @@ static Count run(bool up, int K, int Nn, const std::vector<int>& seg_rows, bool 
   return c;
 }
 
+// Kind 0 (the bf16 path: 256-row tiles, a 256-row tile for tails of at least
+// kBigTailMin rows, 64-row tiles for the rest): both lists in build_tiles_kernel's
+// layout, and the units of each decoded both ways; returns the disagreements.
+static long long kind0_mismatch(int K, int Nn, int cols_per_tile, const std::vector<int>& seg_rows) {
+  const int E = (int)seg_rows.size(), KT = K / 64, G = 256;
+  const int n_ntiles = (Nn + cols_per_tile - 1) / cols_per_tile;
+  std::vector<int> offs(E + 1, 0);
+  for (int e = 0; e < E; ++e) offs[e + 1] = offs[e] + seg_rows[e];
+  std::vector<int32_t> big(4), small(4);
+  int nbt = 0, nst = 0;
+  for (int e = 0; e < E; ++e) {
+    int nb, ns;
+    seg_tiles(seg_rows[e], 0, nb, ns);
+    const int split = std::min(offs[e + 1], offs[e] + nb * 256);
+    for (int i = 0; i < nb; ++i) {
+      const int32_t ent[8] = {e, offs[e] + 256 * i, std::min(offs[e + 1], offs[e] + 256 * (i + 1)), nbt - i, nb,
+                              0, 0, 0};
+      big.insert(big.end(), ent, ent + 8);
+      ++nbt;
+    }
+    for (int i = 0; i < ns; ++i) {
+      const int32_t ent[8] = {e, split + 64 * i, std::min(offs[e + 1], split + 64 * (i + 1)), nst - i, ns, 0, 0, 0};
+      small.insert(small.end(), ent, ent + 8);
+      ++nst;
+    }
+  }
+  big[0] = nbt;
+  small[0] = nst;
+  const SegTable t = seg_table(offs, 0);
+  long long bad = 0;
+  for (int kind = 0; kind < 2; ++kind) {
+    const bool isbig = kind == 0;
+    const UnitPlan plan = plan_units((isbig ? nbt : nst) * n_ntiles, G, KT);
+    for (int u = 0; u < plan.units(); ++u) {
+      const Unit a = decode_unit_seg(t, E, isbig, plan, u, n_ntiles, KT, cols_per_tile);
+      const Unit b = decode_unit_plain((isbig ? big : small).data(), plan, u, n_ntiles, KT, cols_per_tile);
+      bad += a.seg != b.seg || a.r0 != b.r0 || a.r1 != b.r1 || a.n0 != b.n0 || a.kt0 != b.kt0 || a.kt1 != b.kt1 ||
+             a.slot != b.slot;
+    }
+  }
+  return bad;
+}
+
 int main(int argc, char** argv) {
   if (argc < 5) {
     std::fprintf(stderr, "usage: %s up|down K Nn rows...\n", argv[0]);
@@ -106,6 +172,8 @@ int main(int argc, char** argv) {
   std::vector<int> rows;
   for (int i = 4; i < argc; ++i) rows.push_back(std::atoi(argv[i]));
   const Count a = run(up, K, Nn, rows, true), b = run(up, K, Nn, rows, false);
-  std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld\n", a.units, a.checked, a.oob, b.oob);
+  const long long m0 = kind0_mismatch(K, Nn, up ? 128 : 256, rows);
+  std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld list_mismatch=%lld kind0_mismatch=%lld\n", a.units,
+              a.checked, a.oob, b.oob, a.mismatch, m0);
   return 0;
 }

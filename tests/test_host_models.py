@@ -1,6 +1,11 @@
 """Host-side (CPU) models of GPU index arithmetic, built from the kernels' own
 host-callable helpers (no GPU call is made).
 
+Unit decoding: the per-segment tile table each workgroup builds (SegTable,
+decode_unit_seg) gives, for every unit, the segment, rows, columns and K range
+that the earlier tile list (decode_unit_plain over build_tiles_kernel's list)
+gave; so the split of the work, and the results, are unchanged.
+
 fp8 64-row tile: every operand load of every unit, for reduction lengths with
 odd 64-K step counts (K = 320) and the decode shapes' K-split parts (K = 4096,
 14336), must stay inside its allocation once the buffer range check has let
@@ -42,6 +47,8 @@ CASES = [
     ("down", 14336, 4096, [40] * 5),
     ("down", 14336, 4096, [2, 3, 1, 4, 8, 5, 7]),
     ("down", 2048, 7168, [9, 26, 31, 0, 64, 1]),
+    ("up", 4096, 14336, [1003, 1073, 1024, 1017, 1040, 1029, 1000, 1006]),   # Mixtral prefill: 256-row tiles + tails
+    ("down", 14336, 4096, [4926, 0, 7, 130, 127, 128, 255, 256, 257, 383, 384, 1]),
 ]
 
 
@@ -50,6 +57,8 @@ def test_fp8_loads_in_bounds(fp8_model, mode, K, Nn, rows):
     r = _run(fp8_model, mode, K, Nn, rows)
     assert int(r["units"]) > 0 and int(r["checked"]) > 0
     assert int(r["oob"]) == 0, r
+    assert int(r["list_mismatch"]) == 0, r      # the LDS table decodes the units the tile list did
+    assert int(r["kind0_mismatch"]) == 0, r     # also for 256-row + 64-row tiles (bf16)
 
 
 def test_fp8_model_sees_the_half_step_hazard(fp8_model):
