@@ -63,6 +63,9 @@ def parse():
                     help="a training step: the forward (its up-projection keeping the pre-activations) plus "
                          "moe_backward (dout = seeded noise, d_aux = 1 with an aux loss); reports the backward's "
                          "time and algorithmic TFLOP/s")
+    ap.add_argument("--no-library-reference", action="store_true",
+                    help="skip timing the vendor library (torch.matmul, hipBLASLt) on the dense equivalent of the "
+                         "up projection (a comparison point for the roofline, reported as library_reference)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -124,9 +127,38 @@ def main():
         sub, _ = measure(BY_NAME[name], args, args.also_steps, args.warmup)
         result["other_shapes"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
                                                             "expert_gemms", "up_call_ms_timed", "breakdown_ms")}
+    if not args.no_library_reference and cfg.dtype == "bf16" and not args.fp8_experts:
+        result["library_reference"] = library_reference(cfg, result["config"]["kept_slots"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens, args.fp8_experts)
     print(json.dumps(result), flush=True)
+
+
+def library_reference(cfg, kept, reps=10):
+    """The vendor library (torch.matmul -> hipBLASLt) on the dense equivalent of the up
+    projection: [kept, d] x [d, n_up F] bf16, N(0, 1) data (the MFMA rate depends on the
+    data through the clock, so zeros or small integers would overstate it).  A comparison
+    point for the up projection's roofline figure, not part of the layer."""
+    import torch
+    n_up = 2 if cfg.act == "swiglu" else 1
+    M, K, Nc = max(int(kept), 1), cfg.d_model, n_up * cfg.d_ff
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+    b = torch.randn((K, Nc), device="cuda", generator=gen).to(torch.bfloat16)
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record()
+    for i in range(reps):
+        c = torch.matmul(a, b)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+    del a, b, c
+    flop = 2.0 * M * K * Nc
+    return {"op": f"torch.matmul bf16 [{M},{K}] x [{K},{Nc}]", "ms": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+            "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
 def measure(cfg, args, steps, warmup, fp8_experts=False, backward=False, calib_copy_mib=0):
@@ -361,8 +393,7 @@ def measure(cfg, args, steps, warmup, fp8_experts=False, backward=False, calib_c
                    "used_experts": used,
                    "expert_weights": "fp8_e4m3_row_scaled" if fp8 is not None else cfg.dtype},
         "roofline": {"kernel": "expert up-projection grouped GEMM with fused row gather and activation "
-                               "(build_tiles_kernel, grouped_gemm_big_kernel, grouped_gemm_small_kernel, "
-                               "split_fixup_kernel; one "
+                               "(grouped_gemm_big_kernel, grouped_gemm_small_kernel, split_fixup_kernel; one "
                                f"{'moe_expert_up_fp8' if fp8 is not None else ('moe_expert_up_save' if bw is not None else 'moe_expert_up_gather')} call)",
                      **roof, "traffic": traffic, "algorithmic_bytes": up_bytes, "algorithmic_flop": up_flop,
                      "overhead_bytes_h": h_bytes},
