@@ -52,6 +52,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __host__ inline int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
+// Epilogue staging layout: a wavefront's 32 x 64 fp32 block, 16 chunks of 4
+// floats per row, chunk c of row r stored in slot c ^ ep_swz(r).  With rows
+// of 64 floats every row starts on bank 0; the XOR spreads the accumulator
+// writes (rows r and r + 4 in one instruction) and the 16-byte reads of
+// every mode (4, 2 or 1 rows per 16 lanes) over all 64 banks (the up
+// projection's 256-row kernel 1.4% faster at the Mixtral shape, the
+// DeepSeek-V3 down projection 2.9%; identical results).
+__device__ __forceinline__ int ep_swz(int r) { return (r & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 3); }
+__device__ __forceinline__ int ep_at(int r, int c) { return r * 64 + (((c >> 2) ^ ep_swz(r)) << 2) + (c & 3); }
+
 // 16 bytes per lane from `voff + soff` of the buffer straight into LDS at lds + 16 * lane.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
@@ -163,7 +173,9 @@ __device__ __host__ inline int fp8_b_voff(int voff, int chunk, bool half) {
 // ---------------------------------------------------------------------------
 // Per-segment tile table of the forward grouped GEMM.  Segment e (rows
 // [off[e], off[e+1])) is cut into 256-row tiles (kind 0: floor(rows / 256),
-// plus one more when at least kBigTailMin rows remain; kind 1: none) and
+// plus one more when at least kBigTailMin rows remain; kind 1: none; kind 2:
+// as kind 0, but a segment of at least 256 rows puts its whole tail in one
+// more 256-row tile; kinds 3, 4: kind 0 or 2 by choose_tail_kind) and
 // 64-row tiles for the rest; pb / ps are the exclusive prefix counts of the two
 // kinds over the segments.  Every workgroup builds the table in LDS from the
 // offsets (E <= 256, one wavefront) and decodes its units from it, so no
@@ -182,20 +194,37 @@ constexpr int kSegTableElems = (int)((sizeof(SegTable) + 15) / 16) * 8;   // in 
 __device__ __host__ inline void seg_tiles(int rows, int kind, int& nb, int& ns) {
   nb = kind == 1 ? 0 : rows / 256;
   int rest = rows - nb * 256;
-  if (kind == 0 && rest >= kBigTailMin) {
+  if ((kind == 0 && rest >= kBigTailMin) || (kind == 2 && rest > 0 && (nb > 0 || rest >= kBigTailMin))) {
     nb += 1;
     rest = 0;
   }
   ns = rest > 0 ? (rest + 63) / 64 : 0;
 }
 
+// Kinds 3 (up projection) and 4 (down projection) choose between kind 0 and
+// kind 2 from the segment sizes, the same way in every workgroup.  Kind 2
+// moves the short tails of long segments from the 64-row kernel, which
+// streams the expert's weights again for them, into 256-row units that find
+// those weights in L2, at the price of more 256-row units, all of which a
+// workgroup runs in turn.  Taken when that adds no round of 256-row units
+// (ceil(T2 / G) = ceil(T0 / G)), or, for a down projection, when the 256-row
+// units already take 8 or more rounds.  (Measured: DeepSeek-V3 down projection
+// 2.76 -> 2.68 ms, the Switch shape's up and down 3% faster each; Mixtral's
+// down projection 0.89 -> 1.21 ms and the DeepSeek-V3 and Mixtral up
+// projections 2-3% slower with kind 2, and the rule keeps kind 0 for them.)
+__device__ __host__ inline int choose_tail_kind(long long t0, long long t2, int G, bool down) {
+  const long long r0 = (t0 + G - 1) / G, r2 = (t2 + G - 1) / G;
+  return (r2 == r0 || (down && t0 >= 8LL * G)) ? 2 : 0;
+}
+
 // Called by every thread of the workgroup; wavefront 0 fills the table (lane l
-// takes segments 4l .. 4l + 3), then a barrier.
+// takes segments 4l .. 4l + 3), then a barrier.  n_ntiles and G (the grid)
+// serve kinds 3 and 4 only.
 __device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __restrict__ offsets, int n_seg,
-                                                int dense_rows, int kind) {
+                                                int dense_rows, int kind, int n_ntiles = 0, int G = 1) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int o[4], nb[4], ns[4], sb = 0, ss = 0;
+    int o[4], rows[4], nb[4], ns[4], sb = 0, ss = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
@@ -205,8 +234,29 @@ __device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __re
         hi = offsets ? offsets[e + 1] : dense_rows;
       }
       o[i] = lo;
-      seg_tiles(hi - lo, kind, nb[i], ns[i]);
-      if (e >= n_seg) nb[i] = ns[i] = 0;
+      rows[i] = hi - lo;
+    }
+    if (kind >= 3) {
+      int c0 = 0, c2 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int b0, b2, s_;
+        seg_tiles(rows[i], 0, b0, s_);
+        seg_tiles(rows[i], 2, b2, s_);
+        c0 += b0;
+        c2 += b2;
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        c0 += __shfl_xor(c0, d);
+        c2 += __shfl_xor(c2, d);
+      }
+      kind = choose_tail_kind((long long)c0 * n_ntiles, (long long)c2 * n_ntiles, G, kind == 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      seg_tiles(rows[i], kind, nb[i], ns[i]);
+      if (4 * lane + i >= n_seg) nb[i] = ns[i] = 0;
       sb += nb[i];
       ss += ns[i];
     }

@@ -20,6 +20,8 @@
 //
 // MFMA 32x32x16 layout (lane l): A row l%32, k = 8*(l/32)..+7; B column l%32,
 // same k; D column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+#include <type_traits>
+
 #include "gemm_tile.h"
 
 namespace moe {
@@ -117,7 +119,7 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+      for (int r = 0; r < 16; ++r) ep[ep_at((r >> 2) * 8 + kh * 4 + (r & 3), ni * 32 + l32)] = acc[mi][ni][r];
     __builtin_amdgcn_wave_barrier();
     const int rbase = r0 + mi * 32;
     if (MODE == MODE_LOGITS) {
@@ -126,7 +128,7 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
         const int rr = pass * 4 + (lane >> 4), c4 = (lane & 15) * 4;
         const int row = rbase + rr, col = n0 + wn * 64 + c4;
         if (row < r1 && col < Nn) {
-          float4 v = *reinterpret_cast<const float4*>(ep + rr * 64 + c4);
+          float4 v = *reinterpret_cast<const float4*>(ep + ep_at(rr, c4));
           if (HAS_BIAS) {
             const float4 b = *reinterpret_cast<const float4*>(bias_f + col);
             v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
@@ -141,7 +143,13 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
         const int rr = pass * 16 + (lane >> 2), c8 = (lane & 3) * 8;
         const int row = rbase + rr, col = n0 + wn * 32 + c8;
         if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 64 + c8;
+          float src[40];   // columns c8 .. c8 + 7 and c8 + 32 .. c8 + 39 of the row (only those are read)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = c8 + (q & 1) * 4 + (q >> 1) * 32;
+            *reinterpret_cast<float4*>(src + (q & 1) * 4 + (q >> 1) * 32) =
+                *reinterpret_cast<const float4*>(ep + ep_at(rr, c));
+          }
           Vec8 o;
 #pragma unroll
           for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[32 + v]);
@@ -164,7 +172,10 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
         const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
         const int row = rbase + rr, col = n0 + wn * 64 + c8;
         if (row < r1 && col < Nn) {
-          const float* src = ep + rr * 64 + c8;
+          float src[8];
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<float4*>(src + q * 4) = *reinterpret_cast<const float4*>(ep + ep_at(rr, c8 + q * 4));
           Vec8 b;
           if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
           Vec8 o, a;
@@ -274,7 +285,11 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
       dma16(rb, st + kStageElems + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
     }
   }
-  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt) {
+  // live 32-row blocks of this wavefront: a tile that ends inside the wavefront's 128 rows
+  // (the tail of a long segment) skips the MFMAs and fragment reads of the empty blocks
+  const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (w.r1 - w.r0 - wm * 128 + 31) / 32)));
+  auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto nv_t) {
+    constexpr int NV = decltype(nv_t)::value;
     MOE_WAIT_VM0();
     __builtin_amdgcn_s_barrier();
     const bool more = kt + 1 < kt1;
@@ -282,10 +297,10 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
     bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
-      fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
+      if (x < NV) fa[0][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1))) << 3));
 #pragma unroll
     for (int x = 0; x < 2; ++x)
-      fb[0][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + ((x ? hb1 : hb0) << 3));
+      if (NV > 0) fb[0][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + ((x ? hb1 : hb0) << 3));
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
       const int c = kk & 1;
@@ -300,29 +315,42 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
         const int k2 = 2 * (kk + 1);
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1)) ^ k2) << 3));
+          if (x < NV)
+            fa[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1)) ^ k2) << 3));
 #pragma unroll
         for (int x = 0; x < 2; ++x)
-          fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + (((x ? hb1 : hb0) ^ k2) << 3));
+          if (NV > 0)
+            fb[c ^ 1][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + (((x ? hb1 : hb0) ^ k2) << 3));
       }
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < NV; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
+      if (NV == 4) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMA
+        for (int r = 0; r < 2; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
-  for (int kt = kt0; kt < kt1; ++kt)
-    step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt);
+  auto loop = [&](auto nv_t) {
+    for (int kt = kt0; kt < kt1; ++kt)
+      step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt, nv_t);
+  };
+  switch (nv) {
+    case 4: loop(std::integral_constant<int, 4>{}); break;
+    case 3: loop(std::integral_constant<int, 3>{}); break;
+    case 2: loop(std::integral_constant<int, 2>{}); break;
+    case 1: loop(std::integral_constant<int, 1>{}); break;
+    default: loop(std::integral_constant<int, 0>{}); break;
+  }
   __syncthreads();
 
   if (w.slot < 0) {
@@ -365,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
   const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
   const int ub = pb.units();
   const int per_xcd = G / kXcds;
@@ -720,7 +748,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
   const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
   const int us = ps.units();
   const int per_xcd = G / kXcds;
@@ -753,7 +781,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   constexpr int groups = cols_per_tile / 8;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
   const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
   const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
   const long long nb = (long long)pb.rem * kBM2 * groups;
@@ -906,7 +934,8 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.offsets = g.offsets;
   p.n_seg = g.n_seg;
   p.dense_rows = g.max_rows;
-  p.kind = FP8 ? 1 : 0;
+  // routed segments: the 256-row / 64-row split of each expert's tail is chosen on the device
+  p.kind = FP8 ? 1 : (g.offsets == nullptr || MODE == MODE_LOGITS ? 0 : (MODE == MODE_DOWN ? 4 : 3));
   p.W = (const uint16_t*)g.w;
   p.W3 = (const uint16_t*)g.w3;
   p.bias = (const uint16_t*)g.bias;
@@ -931,10 +960,21 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.n_ntiles = (g.Nn + cols - 1) / cols;
   const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
   // fp8 weights use 64-row tiles only; with fewer than kBigTailMin rows no segment has a 256-row tile
-  if (!FP8 && g.max_rows >= kBigTailMin)
+  bool run_big = !FP8 && g.max_rows >= kBigTailMin, run_small = true, run_fixup = true;
+  if (g.offsets == nullptr) {   // one dense segment of max_rows rows: the host knows both tile counts and plans
+    int nb = 0, ns = 0;
+    seg_tiles(g.max_rows, p.kind, nb, ns);
+    const int KT = g.K / kBK2;
+    run_big = nb > 0;
+    run_small = ns > 0;
+    run_fixup = plan_units(nb * p.n_ntiles, grid, KT).rem > 0 || plan_units(ns * p.n_ntiles, grid, KT).rem > 0;
+  }
+  if (run_big)
     hipLaunchKernelGGL((grouped_gemm_big_kernel<MODE, HAS_BIAS, GATHER>), dim3(grid), dim3(512), 0, s, p);
-  hipLaunchKernelGGL((grouped_gemm_small_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(2 * grid), dim3(256), 0, s, p, grid);
+  if (run_small)
+    hipLaunchKernelGGL((grouped_gemm_small_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
+  if (run_fixup)
+    hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(2 * grid), dim3(256), 0, s, p, grid);
 }
 
 template <int MODE, bool HAS_BIAS>

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nn_kernel(NnParams p) {
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+        for (int r = 0; r < 16; ++r) ep[ep_at((r >> 2) * 8 + kh * 4 + (r & 3), ni * 32 + l32)] = acc[mi][ni][r];
       __builtin_amdgcn_wave_barrier();
       const int rbase = w.r0 + wm * 128 + mi * 32;
 #pragma unroll 1
@@ -244,7 +244,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nn_kernel(NnParams p) {
         const int rr = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
         const int row = rbase + rr, col = w.n0 + wn * 64 + c8;
         if (row < w.r1 && col < p.N) {
-          const float* src = ep + rr * 64 + c8;
+          float src[8];
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<float4*>(src + q * 4) = *reinterpret_cast<const float4*>(ep + ep_at(rr, c8 + q * 4));
           Vec8 o;
 #pragma unroll
           for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(src[v]);
@@ -353,7 +356,7 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + kh * 4 + (r & 3)) * 64 + ni * 32 + l32] = acc[mi][ni][r];
+      for (int r = 0; r < 16; ++r) ep[ep_at((r >> 2) * 8 + kh * 4 + (r & 3), ni * 32 + l32)] = acc[mi][ni][r];
     __builtin_amdgcn_wave_barrier();
     const int rbase = m0 + wm * 128 + mi * 32;
 #pragma unroll 1
@@ -361,7 +364,7 @@ __device__ __forceinline__ void tn_tile(const TnParams& p, uint16_t* lds, int s,
       const int rr = pass * 4 + (lane >> 4), c4 = (lane & 15) * 4;
       const int row = rbase + rr, col = n0 + wn * 64 + c4;
       if (row < p.M && col < p.N)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ep + rr * 64 + c4),
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ep + ep_at(rr, c4)),
                                     reinterpret_cast<f32x4*>(C + (size_t)row * p.N + col));
     }
     __builtin_amdgcn_wave_barrier();

@@ -9,8 +9,10 @@
 // segments) and counts the units on which the two decoders disagree.
 //
 // Usage: fp8_offsets <mode: up|down> <K> <Nn> <rows per expert...>
-// Prints "units=U checked=C oob=O nohalf_oob=H list_mismatch=M": O loads past
-// their allocation with the half-step rule, H without it.
+// Prints "units=U checked=C oob=O nohalf_oob=H list_mismatch=M kind0_mismatch=M0
+// cover_bad=B": O loads past their allocation with the half-step rule, H without
+// it; B cells of (row, column tile, K step) that the bf16 units of tile kinds 0,
+// 2, 3 and 4 cover other than once.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -23,10 +25,22 @@ struct Count {
   long long units = 0, checked = 0, oob = 0, mismatch = 0;
 };
 
-// The table build_seg_table writes (exclusive prefix counts of seg_tiles).
-static SegTable seg_table(const std::vector<int>& offs, int kind) {
+// The table build_seg_table writes (exclusive prefix counts of seg_tiles; kinds 3
+// and 4 resolved to 0 or 2 with the kernels' choose_tail_kind).
+static SegTable seg_table(const std::vector<int>& offs, int kind, int n_ntiles = 0, int G = 256) {
   SegTable t{};
   const int E = (int)offs.size() - 1;
+  if (kind >= 3) {
+    long long c0 = 0, c2 = 0;
+    for (int e = 0; e < E; ++e) {
+      int b0, b2, s_;
+      seg_tiles(offs[e + 1] - offs[e], 0, b0, s_);
+      seg_tiles(offs[e + 1] - offs[e], 2, b2, s_);
+      c0 += b0;
+      c2 += b2;
+    }
+    kind = choose_tail_kind(c0 * n_ntiles, c2 * n_ntiles, G, kind == 4);
+  }
   int b = 0, sm = 0;
   for (int e = 0; e < E; ++e) {
     int nb, ns;
@@ -162,6 +176,36 @@ static long long kind0_mismatch(int K, int Nn, int cols_per_tile, const std::vec
   return bad;
 }
 
+// Every kind of the bf16 path (0, 2, and the chosen one for 3 and 4): the
+// 256-row and 64-row units, decoded from the table, cover every (row, output
+// column tile, K step) of every segment exactly once and nothing outside the
+// segments; returns the number of cells covered other than once.
+static long long cover_bad(int K, int Nn, int cols_per_tile, const std::vector<int>& seg_rows, int kind) {
+  const int E = (int)seg_rows.size(), KT = K / 64, G = 256;
+  const int n_ntiles = (Nn + cols_per_tile - 1) / cols_per_tile;
+  std::vector<int> offs(E + 1, 0);
+  for (int e = 0; e < E; ++e) offs[e + 1] = offs[e] + seg_rows[e];
+  const SegTable t = seg_table(offs, kind, n_ntiles, G);
+  const int R = offs[E];
+  std::vector<unsigned char> hits((size_t)R * n_ntiles * KT, 0);
+  long long bad = 0;
+  for (int big = 0; big < 2; ++big) {
+    const UnitPlan plan = plan_units((big ? t.pb[E] : t.ps[E]) * n_ntiles, G, KT);
+    for (int u = 0; u < plan.units(); ++u) {
+      const Unit w = decode_unit_seg(t, E, big != 0, plan, u, n_ntiles, KT, cols_per_tile);
+      if (w.r1 - w.r0 > (big ? 256 : 64) || w.r0 < offs[w.seg] || w.r1 > offs[w.seg + 1] || w.r0 >= w.r1) {
+        ++bad;
+        continue;
+      }
+      const int j = w.n0 / cols_per_tile;
+      for (int r = w.r0; r < w.r1; ++r)
+        for (int kt = w.kt0; kt < w.kt1; ++kt) ++hits[((size_t)r * n_ntiles + j) * KT + kt];
+    }
+  }
+  for (unsigned char h : hits) bad += h != 1;
+  return bad;
+}
+
 int main(int argc, char** argv) {
   if (argc < 5) {
     std::fprintf(stderr, "usage: %s up|down K Nn rows...\n", argv[0]);
@@ -172,8 +216,11 @@ int main(int argc, char** argv) {
   std::vector<int> rows;
   for (int i = 4; i < argc; ++i) rows.push_back(std::atoi(argv[i]));
   const Count a = run(up, K, Nn, rows, true), b = run(up, K, Nn, rows, false);
-  const long long m0 = kind0_mismatch(K, Nn, up ? 128 : 256, rows);
-  std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld list_mismatch=%lld kind0_mismatch=%lld\n", a.units,
-              a.checked, a.oob, b.oob, a.mismatch, m0);
+  const int cpt = up ? 128 : 256;
+  const long long m0 = kind0_mismatch(K, Nn, cpt, rows);
+  long long cov = 0;
+  for (int kind : {0, 2, 3, 4}) cov += cover_bad(K, Nn, cpt, rows, kind);
+  std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld list_mismatch=%lld kind0_mismatch=%lld "
+              "cover_bad=%lld\n", a.units, a.checked, a.oob, b.oob, a.mismatch, m0, cov);
   return 0;
 }

@@ -59,6 +59,7 @@ def test_fp8_loads_in_bounds(fp8_model, mode, K, Nn, rows):
     assert int(r["oob"]) == 0, r
     assert int(r["list_mismatch"]) == 0, r      # the LDS table decodes the units the tile list did
     assert int(r["kind0_mismatch"]) == 0, r     # also for 256-row + 64-row tiles (bf16)
+    assert int(r["cover_bad"]) == 0, r          # every tile kind covers each row, column tile, K step once
 
 
 def test_fp8_model_sees_the_half_step_hazard(fp8_model):
