@@ -973,7 +973,7 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((grouped_gemm_big_kernel<MODE, HAS_BIAS, GATHER>), dim3(grid), dim3(512), 0, s, p);
   if (run_small)
     hipLaunchKernelGGL((grouped_gemm_small_kernel<MODE, HAS_BIAS, GATHER, FP8>), dim3(grid), dim3(256), 0, s, p);
-  if (run_fixup)
+  if (run_fixup && !(MODE == MODE_LOGITS && g.no_fixup))
     hipLaunchKernelGGL((split_fixup_kernel<MODE, HAS_BIAS>), dim3(2 * grid), dim3(256), 0, s, p, grid);
 }
 
@@ -984,6 +984,25 @@ static void launch_f32(const GroupedGemmArgs& g, hipStream_t s) {
                      0, s, (const float*)g.a, g.perm, g.gather_k > 0 ? g.gather_k : 1, g.offsets, g.n_seg,
                      g.max_rows, (const float*)g.w, (const float*)g.w3, (const float*)g.bias, (float*)g.out, g.K,
                      g.Nn);
+}
+
+LogitParts logits_parts(const GroupedGemmArgs& g) {
+  // the plans launch_bf16 gives the two kernels for one dense segment (tile kind 0)
+  LogitParts z{};
+  const int grid = ((device_cus() + kXcds - 1) / kXcds) * kXcds;
+  const int KT = g.K / kBK2, n_ntiles = (g.Nn + kBN2 - 1) / kBN2;
+  seg_tiles(g.max_rows, 0, z.nb, z.ns);
+  const UnitPlan pb = plan_units(z.nb * n_ntiles, grid, KT), ps = plan_units(z.ns * n_ntiles, grid, KT);
+  z.logits = g.out_f32;
+  z.part_big = g.partials;
+  z.part_small = g.partials + (size_t)kMaxSplitUnits * kBM2 * kBN2;
+  z.bias = g.bias_f32;
+  z.full_b = pb.full;
+  z.s_b = pb.s;
+  z.full_s = ps.full;
+  z.s_s = ps.s;
+  z.ld = kBN2;
+  return z;
 }
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
@@ -1001,6 +1020,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s) {
   if (gather && (g.mode == MODE_LOGITS || (size_t)g.a_rows * g.K * 2 > grouped_gemm_gather_max_bytes()))
     return hipErrorInvalidValue;
   if (g.mode == MODE_LOGITS && (g.Nn % 8 != 0 || g.n_seg != 1)) return hipErrorInvalidValue;
+  if (g.no_fixup && (g.mode != MODE_LOGITS || g.offsets != nullptr || g.Nn > kBN2)) return hipErrorInvalidValue;
   if (g.fp8 && (g.mode == MODE_LOGITS || (g.mode != MODE_DOWN && !gather) || !g.w8 || !g.scale1 ||
                 (g.mode == MODE_SWIGLU_UP && (!g.w8_3 || !g.scale3))))
     return hipErrorInvalidValue;

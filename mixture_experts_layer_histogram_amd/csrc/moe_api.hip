@@ -171,6 +171,15 @@ moe_status do_route(const moe_config& c, const Workspace& W, const void* x, cons
       g.w = w_router;
       g.out_f32 = logits;
       g.bias_f32 = logit_bias;
+      if (topk_from_parts_supported(c)) {
+        // the selection completes the logits from the GEMM's K-part partials (its fix-up
+        // pass folded into the top-k kernel: one launch and one pass over the logits fewer)
+        g.no_fixup = true;
+        MOE_HIP(launch_grouped_gemm(g, s));
+        MOE_HIP(launch_topk_from_parts(c, W, logits_parts(g), sel_bias, topk_idx, gates,
+                                       reinterpret_cast<float*>(wsp(ws, W.probsum_part)), probsum, s));
+        return MOE_OK;
+      }
       MOE_HIP(launch_grouped_gemm(g, s));
     } else {
       MOE_HIP(launch_router_gemm(c, x, w_router, logit_bias, logits, s));

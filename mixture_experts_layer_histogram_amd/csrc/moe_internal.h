@@ -97,6 +97,24 @@ hipError_t launch_route_fused(const moe_config& c, const Workspace& W, const voi
 hipError_t launch_topk(const moe_config& c, const Workspace& L, const float* z_in, float* z_out,
                        const float* sel_bias, int32_t* idx, float* gates, float* probsum_part,
                        float* probsum, hipStream_t s);
+// Logits left by the grouped GEMM in its fp32-logits mode without its fix-up (one dense
+// segment of N rows, E <= 256 columns): rows of unsplit tiles are final in `logits`; the
+// rows of split tiles are the sum, in part order, of their K-part partial tiles, + bias.
+struct LogitParts {
+  float* logits;                 // [N, E]: read for unsplit rows, written for split rows
+  const float* part_big;         // [slot][256 rows][256 columns] fp32
+  const float* part_small;       // [slot][64 rows][256 columns] fp32
+  const float* bias;             // logit bias [E] or null
+  int nb, full_b, s_b;           // 256-row tiles; the first full_b unsplit; s_b K-parts each after them
+  int ns, full_s, s_s;           // 64-row tiles after row 256 nb, likewise
+  int ld;                        // columns of a partial-tile row
+};
+// Selection (top-k, gates, probability sums) that first completes the logits from the
+// K-part partials of the logits GEMM (E in (128, 256]: 64 lanes of 4 experts per token).
+bool topk_from_parts_supported(const moe_config& c);
+hipError_t launch_topk_from_parts(const moe_config& c, const Workspace& L, const LogitParts& z,
+                                  const float* sel_bias, int32_t* idx, float* gates, float* probsum_part,
+                                  float* probsum, hipStream_t s);
 
 hipError_t launch_permute(const moe_config& c, const Workspace& L, const int32_t* topk_idx,
                           const void* x, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -138,6 +156,7 @@ struct GroupedGemmArgs {
   const void* comb_shared;
   void* comb_out;
   bool fp8;              // weights are E4M3 codes (w8, w8_3) with row scales (64-row tiles only)
+  bool no_fixup;         // MODE_LOGITS: leave the K-part partials for launch_topk_from_parts
   const uint8_t* w8;     // fp8 W1 (up) or W2 (down): [n_seg, Nn, K]
   const uint8_t* w8_3;   // fp8 W3 (SwiGLU up)
   const float* scale1;   // row scales of w8 [n_seg, Nn]
@@ -151,6 +170,8 @@ struct GroupedGemmArgs {
   float* partials;       // scratch for K-split partial tiles (grouped_gemm_partials_bytes())
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& g, hipStream_t s);
+// The K-part plan of a dense MODE_LOGITS call (what its no_fixup launch leaves in g.partials).
+LogitParts logits_parts(const GroupedGemmArgs& g);
 int grouped_gemm_max_tiles(int max_rows, int n_seg);
 int grouped_gemm_max_small_tiles(int max_rows, int n_seg);
 size_t grouped_gemm_partials_bytes();

@@ -282,11 +282,49 @@ __device__ __forceinline__ void probsum_block(const double (&pacc)[V], const int
   }
 }
 
-template <int L, int V, int KM>
+// Logit of token t, experts 4 gl .. 4 gl + 3, from the logits GEMM's K-part
+// partials: the tile's parts summed in part order, then the bias (the order of
+// the GEMM's fix-up, so the values are the ones it would have written); rows of
+// unsplit tiles are final already.  Writes the completed logits.
+__device__ __forceinline__ float4 logits_from_parts(const LogitParts zp, int t, int gl, int E) {
+  const int col = 4 * gl;
+  const float* base = nullptr;
+  int parts = 0, stride = 0;
+  if (t < zp.nb * 256) {
+    const int i = t >> 8;
+    if (i >= zp.full_b) {
+      base = zp.part_big + ((size_t)(i - zp.full_b) * zp.s_b * 256 + (t & 255)) * zp.ld;
+      parts = zp.s_b;
+      stride = 256 * zp.ld;
+    }
+  } else {
+    const int j = (t - zp.nb * 256) >> 6;
+    if (j >= zp.full_s) {
+      base = zp.part_small + ((size_t)(j - zp.full_s) * zp.s_s * 64 + ((t - zp.nb * 256) & 63)) * zp.ld;
+      parts = zp.s_s;
+      stride = 64 * zp.ld;
+    }
+  }
+  float4 z;
+  if (base == nullptr) return *reinterpret_cast<const float4*>(zp.logits + (size_t)t * E + col);
+  z = *reinterpret_cast<const float4*>(base + col);
+  for (int q = 1; q < parts; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(base + (size_t)q * stride + col);
+    z.x += x.x; z.y += x.y; z.z += x.z; z.w += x.w;
+  }
+  if (zp.bias) {
+    const float4 b = *reinterpret_cast<const float4*>(zp.bias + col);
+    z.x += b.x; z.y += b.y; z.z += b.z; z.w += b.w;
+  }
+  *reinterpret_cast<float4*>(zp.logits + (size_t)t * E + col) = z;
+  return z;
+}
+
+template <int L, int V, int KM, bool PARTS = false>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ zin, float* __restrict__ zout, const float* __restrict__ sel_bias,
     int N, int E, int k, int rule, int iters, int32_t* __restrict__ idx_out,
-    float* __restrict__ gates_out, double* __restrict__ probsum_part) {
+    float* __restrict__ gates_out, double* __restrict__ probsum_part, LogitParts zp = {}) {
   constexpr int G = 64 / L;
   __shared__ double psum_lds[4][kMaxExperts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -310,10 +348,20 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const int t = blockIdx.x * tokens_per_block + (it * 4 + wave) * G + g;
     const bool tv = t < N;
     float z[V];
+    if (PARTS) {   // L = 64, V = 4, E a multiple of 4: the lane's experts are one float4
+      static_assert(!PARTS || V == 4, "one float4 of logits per lane");
+      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tv && valid[0]) q = logits_from_parts(zp, t, gl, E);
+      z[0] = valid[0] ? q.x : -INFINITY;
+      z[1 % V] = valid[1 % V] ? q.y : -INFINITY;
+      z[2 % V] = valid[2 % V] ? q.z : -INFINITY;
+      z[3 % V] = valid[3 % V] ? q.w : -INFINITY;
+    } else {
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      z[v] = valid[v] ? (tv ? zin[(size_t)t * E + ex[v]] : 0.f) : -INFINITY;
-      if (zout != nullptr && tv && valid[v]) zout[(size_t)t * E + ex[v]] = z[v];
+      for (int v = 0; v < V; ++v) {
+        z[v] = valid[v] ? (tv ? zin[(size_t)t * E + ex[v]] : 0.f) : -INFINITY;
+        if (zout != nullptr && tv && valid[v]) zout[(size_t)t * E + ex[v]] = z[v];
+      }
     }
     double p[V];
     select_token<L, V, KM>(z, ex, valid, b, k, rule, want_p, tv, t, lane, gl, gbase, gmask, idx_out, gates_out, p);
@@ -530,6 +578,38 @@ hipError_t launch_route_fused(const moe_config& c, const Workspace& W, const voi
   }
   if (probsum) {
     const int nblk = c.n_tokens > 0 ? W.route_blocks : 0;
+    hipLaunchKernelGGL(probsum_reduce_kernel, dim3(c.n_experts), dim3(64), 0, s, part, nblk, c.n_experts, probsum);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+bool topk_from_parts_supported(const moe_config& c) {
+  return c.n_experts > 128 && c.n_experts <= 256 && c.n_experts % 4 == 0;
+}
+
+hipError_t launch_topk_from_parts(const moe_config& c, const Workspace& W, const LogitParts& zp,
+                                  const float* sel_bias, int32_t* idx, float* gates, float* probsum_part_f,
+                                  float* probsum, hipStream_t s) {
+  if (!topk_from_parts_supported(c) || topk_lanes(c.n_experts) != 64) return hipErrorInvalidValue;
+  double* part = probsum ? reinterpret_cast<double*>(probsum_part_f) : nullptr;
+  if (c.n_tokens > 0) {
+    const int k = c.top_k;
+    const dim3 grid(W.topk_blocks), block(256);
+    const int N = (int)c.n_tokens, E = c.n_experts;
+#define MOE_TOPK_PARTS(KMV)                                                                                  \
+  hipLaunchKernelGGL((topk_kernel<64, 4, KMV, true>), grid, block, 0, s, nullptr, nullptr, sel_bias, N, E, k, \
+                     c.gate_rule, W.topk_iters, idx, gates, part, zp)
+    if (k <= 2) MOE_TOPK_PARTS(2);
+    else if (k <= 4) MOE_TOPK_PARTS(4);
+    else if (k <= 8) MOE_TOPK_PARTS(8);
+    else MOE_TOPK_PARTS(kMaxTopK);
+#undef MOE_TOPK_PARTS
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (probsum) {
+    const int nblk = c.n_tokens > 0 ? W.topk_blocks : 0;
     hipLaunchKernelGGL(probsum_reduce_kernel, dim3(c.n_experts), dim3(64), 0, s, part, nblk, c.n_experts, probsum);
     return hipGetLastError();
   }
