@@ -12,6 +12,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace moe {
 
 // --------------------------------------------------------------------------- router GEMM
@@ -143,17 +145,68 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w,
 
 // --------------------------------------------------------------------------- top-k and gates
 //
-// A group of L lanes handles one token; lane gl of the group owns the V
-// consecutive experts gl*V .. gl*V+V-1, so a lower lane always holds lower
-// expert indices.  Each of the k rounds takes the group maximum of the
-// per-lane best key (xor shuffles), ballots the lanes holding it and lets the
-// lowest such lane win: exact ties go to the lower expert index.  Keys are
-// fp64, formed from the fp32 logits and bias.  KM >= k bounds the unrolled
-// selection rounds and the per-token arrays (kMaxTopK for every k kept the
-// E = 256 kernel at 189 VGPRs, two wavefronts per SIMD).
-// One token's selection and gates from its logits z (lane gl of the token's
-// L-lane group holds experts gl*V .. gl*V+V-1).  Writes idx/gates when `tv`;
-// returns the full-softmax probabilities in p (zero unless `want_p`).
+// A group of L lanes (8, 16 or 64, aligned) handles one token; lane gl of the
+// group owns the V consecutive experts gl*V .. gl*V+V-1, so a lower lane always
+// holds lower expert indices.  Each of the k rounds takes the group maximum of
+// the per-lane best key; among the lanes holding it the lowest expert index
+// wins (a group minimum), so exact ties go to the lower expert index, and the
+// winner's logit and probability reach the group by an OR of the one lane's
+// bits.  Keys are fp64, formed from the fp32 logits and bias.  KM >= k bounds
+// the unrolled selection rounds and the per-token arrays (kMaxTopK for every k
+// kept the E = 256 kernel at 189 VGPRs, two wavefronts per SIMD).
+//
+// The group reductions move data between lanes with DPP within each row of 16
+// lanes (quad permutations, then the half-row and row mirrors: after each step
+// a lane and its partner hold the same pair, so every lane ends with the same
+// bits) and, for 64-lane groups, read the four row results with v_readlane.
+// (Through ds_bpermute, each of the 6 steps of a 64-lane reduction waited on an
+// LDS round trip.)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = dpp_i32<CTRL>((int)(unsigned)(b & 0xffffffffll)), hi = dpp_i32<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)(unsigned)(b & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+// op over the L-lane group; T is int, float or double
+template <int L, class T, class Op>
+__device__ __forceinline__ T group_reduce(T x, Op op) {
+  static_assert(L == 8 || L == 16 || L == 64, "group of 8, 16 or 64 lanes");
+  auto mv = [](T v, auto ctrl) -> T {
+    constexpr int C = decltype(ctrl)::value;
+    if constexpr (sizeof(T) == 8) return dpp_f64<C>(v);
+    else if constexpr (std::is_same<T, float>::value) return __int_as_float(dpp_i32<C>(__float_as_int(v)));
+    else return dpp_i32<C>(v);
+  };
+  x = op(x, mv(x, std::integral_constant<int, kDppQuadXor1>{}));
+  x = op(x, mv(x, std::integral_constant<int, kDppQuadXor2>{}));
+  x = op(x, mv(x, std::integral_constant<int, kDppRowHalfMirror>{}));
+  if (L >= 16) x = op(x, mv(x, std::integral_constant<int, kDppRowMirror>{}));
+  if (L == 64) {
+    T r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(T) == 8) r[i] = readlane_f64(x, 16 * i);
+      else if constexpr (std::is_same<T, float>::value)
+        r[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * i));
+      else r[i] = __builtin_amdgcn_readlane(x, 16 * i);
+    }
+    x = op(op(r[0], r[1]), op(r[2], r[3]));
+  }
+  return x;
+}
+
 template <int L, int V, int KM>
 __device__ __forceinline__ void select_token(const float (&z)[V], const int (&ex)[V], const bool (&valid)[V],
                                              const double (&b)[V], int k, int rule, bool want_p, bool tv, int t,
@@ -164,16 +217,14 @@ __device__ __forceinline__ void select_token(const float (&z)[V], const int (&ex
     float m = z[0];
 #pragma unroll
     for (int v = 1; v < V; ++v) m = fmaxf(m, z[v]);
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+    m = group_reduce<L>(m, [](float a, float c) { return fmaxf(a, c); });
     double sum = 0.0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       p[v] = valid[v] ? exp((double)z[v] - (double)m) : 0.0;
       sum += p[v];
     }
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, L);
+    sum = group_reduce<L>(sum, [](double a, double c) { return a + c; });
 #pragma unroll
     for (int v = 0; v < V; ++v) p[v] = p[v] / sum;
   } else {
@@ -207,17 +258,19 @@ __device__ __forceinline__ void select_token(const float (&z)[V], const int (&ex
           bk = key[v]; bi = ex[v]; bz = z[v]; bp = p[v];
         }
       }
-      double gm = bk;
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) gm = fmax(gm, __shfl_xor(gm, off, L));
+      const double gm = group_reduce<L>(bk, [](double a, double c) { return fmax(a, c); });
       const bool cand = (bi != 0x7fffffff) && (bk == gm);
-      uint64_t mine = __ballot(cand) & gmask;
-      if (mine == 0) mine = __ballot(bi != 0x7fffffff) & gmask;   // only with NaN keys
-      const int wl = mine ? __builtin_ctzll(mine) : gbase;
-      const int ew = __shfl(bi, wl);
-      const float zw = __shfl(bz, wl);
-      const double pw = __shfl(bp, wl);
-      if (lane == wl) {
+      auto imin = [](int a, int c) { return a < c ? a : c; };
+      int ew = group_reduce<L>(cand ? bi : 0x7fffffff, imin);
+      if (ew == 0x7fffffff) ew = group_reduce<L>(bi, imin);   // only with NaN keys: the lowest open expert
+      const bool win = bi == ew && bi != 0x7fffffff;          // one lane of the group
+      auto ior = [](int a, int c) { return a | c; };
+      const long long pb = __double_as_longlong(bp);
+      const float zw = __int_as_float(group_reduce<L>(win ? __float_as_int(bz) : 0, ior));
+      const int plo = group_reduce<L>(win ? (int)(unsigned)(pb & 0xffffffffll) : 0, ior);
+      const int phi = group_reduce<L>(win ? (int)(pb >> 32) : 0, ior);
+      const double pw = __longlong_as_double(((long long)phi << 32) | (unsigned)plo);
+      if (win) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
           if (ex[v] == ew) taken[v] = true;
