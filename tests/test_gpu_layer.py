@@ -348,3 +348,46 @@ def test_small_dispatch_matches_three_pass(priority):
     assert np.array_equal(outs[0][0], ref.counts) and np.array_equal(outs[0][1], ref.offsets)
     assert np.array_equal(outs[0][2][:kept], ref.perm) and np.array_equal(outs[0][3], ref.slot_pos)
     assert int(outs[0][4][0]) == ref.drop_count
+
+
+@pytest.mark.parametrize("n_tokens,d_model", [(1100, 512), (66000, 512)])
+def test_wide_router_split_logits(n_tokens, d_model):
+    """E = 256 on the logits GEMM: the top-k kernel completes the logits from the
+    GEMM's K-part partials.  1100 tokens: four 256-row tiles and two 64-row
+    tiles, all split along K; 66000 tokens: more 256-row tiles than workgroups,
+    so the first ones are final in the GEMM's own epilogue and only the
+    remainder is split.  Logits against the oracle's and the router kernel's
+    (no workspace), routing and probability sums oracle-exact on the GPU's
+    logits."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import DEEPSEEK_V3
+    cfg = DEEPSEEK_V3.scaled(name=f"wide_router_{n_tokens}", n_tokens=n_tokens, d_model=d_model, d_ff=64,
+                             d_ff_shared=0)
+    say(f"wide router: N={n_tokens} d={d_model} E={cfg.n_experts}")
+    inp = make_inputs(cfg)
+    c = M.config_from(cfg)
+    N, E, k = cfg.n_tokens, cfg.n_experts, cfg.top_k
+    x = M.to_device(inp.x, "cuda", cfg.dtype)
+    wr = M.to_device(inp.w_router, "cuda", cfg.dtype)
+    sb = M.to_device(inp.sel_bias, "cuda", "f32")
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device="cuda")
+    z_ref = oracle.router_logits(oracle.to_f64(inp.x, cfg.dtype), oracle.to_f64(inp.w_router, cfg.dtype),
+                                 inp.logit_bias)
+    zs = []
+    for w in (ws, None):
+        z = torch.empty((N, E), dtype=torch.float32, device="cuda")
+        idx = torch.empty((N, k), dtype=torch.int32, device="cuda")
+        g = torch.empty((N, k), dtype=torch.float32, device="cuda")
+        ps = torch.empty(E, dtype=torch.float32, device="cuda")
+        M.route(c, x, wr, idx, g, sel_bias=sb, logits=z, probsum=ps if w is not None else None, ws=w)
+        torch.cuda.synchronize()
+        zh = host(z)
+        assert rel_err(zh, z_ref) <= TOL[cfg.dtype], (w is None, rel_err(zh, z_ref))
+        r = oracle.oracle_route(cfg, zh, inp.sel_bias)
+        assert np.array_equal(host(idx), r.topk_idx), w is None
+        assert rel_err(host(g), r.gates) <= TOL[cfg.dtype]
+        if w is not None:
+            assert rel_err(host(ps), r.probs.sum(axis=0)) <= 1e-5
+        zs.append(zh)
+    assert rel_err(zs[0], zs[1]) <= 1e-5, rel_err(zs[0], zs[1])
