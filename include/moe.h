@@ -137,10 +137,13 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *   gates      [N, k] fp32   out: gate weights by `gate_rule`
  *   probsum    [E] fp32 | NULL   out: sum over tokens of softmax(z)[t, e] (for moe_aux_loss)
  *   ws/ws_bytes workspace of moe_workspace_size(cfg) bytes; required when probsum is
- *              requested.  When given (and large enough), routers with bf16 storage
- *              and E a multiple of 64 compute the logits on the grouped-GEMM kernel
- *              with its K-split scratch; otherwise a dedicated router kernel runs.
- *              Both accumulate in fp32; their rounding orders differ.
+ *              requested.  bf16 routers with E <= 64 run one fused kernel (router GEMM,
+ *              softmax, top-k and gates; the logits are still written).  Wider bf16
+ *              routers with E a multiple of 64 compute the logits on the grouped-GEMM
+ *              kernel with its K-split scratch when the workspace is given (for E in
+ *              (128, 256] the top-k kernel completes the K-split logits); otherwise a
+ *              dedicated router kernel runs.  All accumulate in fp32; their rounding
+ *              orders differ.
  * Selection keys are formed and compared in fp64 from the fp32 logits and bias. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* logit_bias, const float* sel_bias, const float* logits_in,
@@ -401,8 +404,8 @@ typedef struct moe_grads {      /* device outputs; fp32 unless noted */
   float* dgates;                /* [N, k] | NULL: dL/dgates */
 } moe_grads;
 
-/* Workspace bytes moe_backward needs: the forward's scratch (tile lists,
- * K-split partials), the pre-activations when the forward did not save them,
+/* Workspace bytes moe_backward needs: the forward's scratch (the backward's
+ * tile lists, K-split partials), the pre-activations when the forward did not save them,
  * the expert-ordered token rows, the intermediate gradients (dY, dH, dA, dX,
  * dz) and the shared expert's intermediates.  No weight copies: every product
  * reads the weights in their stored layout.  Host only. */
