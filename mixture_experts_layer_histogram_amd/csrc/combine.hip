@@ -32,7 +32,10 @@ union Vec16 {
 // `parts` wavefronts share a token's row (each its own contiguous 1 / parts of
 // the columns; same per-element arithmetic), so that a small batch (decode)
 // still keeps every column's loads in flight at once.
-template <typename T, bool STREAM>
+// KM >= k bounds the unrolled slot loop.  All KM expert rows of a chunk are loaded before the
+// first is used (a dropped slot, or one past k, loads row 0 and is not added), so a lane has
+// KM + 2 loads in flight per chunk instead of waiting on each row in turn.
+template <typename T, bool STREAM, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ gates, const T* __restrict__ res,
                                                       const T* __restrict__ sh, T* __restrict__ out, int N,
@@ -43,10 +46,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   const int t = gw / parts, part = gw % parts;
   if (t >= N) return;
   const int span = d / parts, c_beg = part * span, c_end = c_beg + span;
-  int pos[kMaxTopK];
-  float g[kMaxTopK];
+  int pos[KM];
+  float g[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
     g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
   }
@@ -54,6 +57,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   if (d % VEC == 0) {
 #pragma unroll 2
     for (int c = c_beg + lane * VEC; c < c_end; c += 64 * VEC) {   // two chunks in flight per lane
+      Vec16<T> yb[KM];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {   // no branch around the loads: slots past k and dropped slots read row 0
+        const size_t yr = (size_t)(pos[j] >= 0 ? pos[j] : 0) * d + c;
+        if (STREAM) {
+          const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + yr));
+          yb[j].u = uint4{raw.x, raw.y, raw.z, raw.w};
+        } else {
+          yb[j].u = *reinterpret_cast<const uint4*>(y + yr);
+        }
+      }
       float acc[VEC];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -66,18 +80,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
         for (int v = 0; v < VEC; ++v) acc[v] += Store<T>::load(sh, trow + c + v);
       }
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (pos[j] < 0) continue;
-        const size_t yr = (size_t)pos[j] * d + c;
-        Vec16<T> buf;
-        if (STREAM) {
-          const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + yr));
-          buf.u = uint4{raw.x, raw.y, raw.z, raw.w};
-        } else {
-          buf.u = *reinterpret_cast<const uint4*>(y + yr);
-        }
+      for (int j = 0; j < KM; ++j) {
+        if (j >= k || pos[j] < 0) continue;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g[j], Store<T>::load(buf.e, v), acc[v]);
+        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g[j], Store<T>::load(yb[j].e, v), acc[v]);
       }
       Vec16<T> ob;
 #pragma unroll
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
       float acc = res ? Store<T>::load(res, trow + c) : 0.f;
       if (sh) acc += Store<T>::load(sh, trow + c);
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
+      for (int j = 0; j < KM; ++j)
         if (pos[j] >= 0) acc = fmaf(g[j], Store<T>::load(y, (size_t)pos[j] * d + c), acc);
       Store<T>::store(out, trow + c, acc);
     }
@@ -161,12 +167,21 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const T*)y_perm, slot_pos, gates, (const T*)residual,
                        (const T*)shared_y, (T*)out, N, c.d_model, c.top_k, parts);
   };
+  auto by_k = [&](auto t_s, auto s_s) {
+    using T = decltype(t_s);
+    constexpr bool S = decltype(s_s)::value;
+    const int k = c.top_k;
+    if (k <= 2) go(combine_kernel<T, S, 2>, (T*)nullptr);
+    else if (k <= 4) go(combine_kernel<T, S, 4>, (T*)nullptr);
+    else if (k <= 8) go(combine_kernel<T, S, 8>, (T*)nullptr);
+    else go(combine_kernel<T, S, kMaxTopK>, (T*)nullptr);
+  };
   if (c.dtype == MOE_BF16) {
-    if (stream) go(combine_kernel<uint16_t, true>, (uint16_t*)nullptr);
-    else go(combine_kernel<uint16_t, false>, (uint16_t*)nullptr);
+    if (stream) by_k(uint16_t{}, std::true_type{});
+    else by_k(uint16_t{}, std::false_type{});
   } else {
-    if (stream) go(combine_kernel<float, true>, (float*)nullptr);
-    else go(combine_kernel<float, false>, (float*)nullptr);
+    if (stream) by_k(float{}, std::true_type{});
+    else by_k(float{}, std::false_type{});
   }
   return hipGetLastError();
 }
