@@ -311,6 +311,7 @@ __device__ __forceinline__ void add8(float (&a)[8], const uint4& v) {
   for (int e = 0; e < 8; ++e) a[e] += bf16_to_f32(x.e[e]);
 }
 
+template <int KM>
 __global__ __launch_bounds__(256) void dx_gather_kernel(const uint16_t* __restrict__ dout,
                                                         const uint16_t* __restrict__ dX,
                                                         const int32_t* __restrict__ slot_pos,
@@ -321,13 +322,20 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const uint16_t* __restri
   const int t = blockIdx.x * 4 + wave;
   if (t >= N) return;
   const size_t row = (size_t)t * d;
+  int pos[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
   for (int c = lane; c < d / 8; c += 64) {
+    // every slot's row loaded before the first is added (no branch around the loads:
+    // dropped slots and slots past k read row 0 and are not added)
+    uint4 r[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) r[j] = reinterpret_cast<const uint4*>(dX + (size_t)(pos[j] >= 0 ? pos[j] : 0) * d)[c];
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (dout) add8(a, reinterpret_cast<const uint4*>(dout + row)[c]);
-    for (int j = 0; j < k; ++j) {
-      const int pos = slot_pos[(size_t)t * k + j];
-      if (pos >= 0) add8(a, reinterpret_cast<const uint4*>(dX + (size_t)pos * d)[c]);
-    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (pos[j] >= 0) add8(a, r[j]);
     if (dxs) add8(a, reinterpret_cast<const uint4*>(dxs + row)[c]);
     if (dxr) add8(a, reinterpret_cast<const uint4*>(dxr + row)[c]);
     Vec8 o;
@@ -429,9 +437,14 @@ hipError_t launch_dx_gather(const moe_config& c, const void* dout, const void* d
   const int N = (int)c.n_tokens;
   if (N == 0) return hipSuccess;
   if (c.d_model % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dx_gather_kernel, dim3((N + 3) / 4), dim3(256), 0, s, (const uint16_t*)dout,
-                     (const uint16_t*)dX, slot_pos, (const uint16_t*)dxs, (const uint16_t*)dxr, N, c.top_k,
-                     c.d_model, (uint16_t*)dx);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((N + 3) / 4), dim3(256), 0, s, (const uint16_t*)dout, (const uint16_t*)dX,
+                       slot_pos, (const uint16_t*)dxs, (const uint16_t*)dxr, N, c.top_k, c.d_model, (uint16_t*)dx);
+  };
+  if (c.top_k <= 2) go(dx_gather_kernel<2>);
+  else if (c.top_k <= 4) go(dx_gather_kernel<4>);
+  else if (c.top_k <= 8) go(dx_gather_kernel<8>);
+  else go(dx_gather_kernel<kMaxTopK>);
   return hipGetLastError();
 }
 
