@@ -391,3 +391,40 @@ def test_wide_router_split_logits(n_tokens, d_model):
             assert rel_err(host(ps), r.probs.sum(axis=0)) <= 1e-5
         zs.append(zh)
     assert rel_err(zs[0], zs[1]) <= 1e-5, rel_err(zs[0], zs[1])
+
+
+@pytest.mark.parametrize("n_tokens,d_model,d_ff_shared", [
+    (100, 256, 192),     # under 128 rows: 64-row tiles only
+    (200, 256, 192),     # one 256-row tile (at least 128 rows), no 64-row tile
+    (512, 2048, 256),    # two whole 256-row tiles, few units: K-split, fix-up
+    (600, 256, 192),     # 256-row tiles and a 64-row tail
+    (1300, 512, 2048),   # 256-row tiles (a tail of 20 rows in 64-row tiles), many units
+])
+def test_shared_ffn_dense_plans(n_tokens, d_model, d_ff_shared):
+    """The shared expert is one dense segment whose tile counts and K-split plan the host
+    knows, so only the kernels that have work are launched.  Every row of y_sh against
+    the oracle's SwiGLU, over row counts that need 64-row tiles only, 256-row tiles only,
+    both, and with and without K-parts."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import DEEPSEEK_V3
+    cfg = DEEPSEEK_V3.scaled(name=f"shared_{n_tokens}_{d_model}_{d_ff_shared}", n_tokens=n_tokens,
+                             d_model=d_model, n_experts=8, top_k=2, d_ff=64, d_ff_shared=d_ff_shared)
+    inp = make_inputs(cfg)
+    c = M.config_from(cfg)
+    N, d, Fs = cfg.n_tokens, cfg.d_model, cfg.d_ff_shared
+    dt = cfg.dtype
+    x = M.to_device(inp.x, "cuda", dt)
+    w1, w3, w2 = (M.to_device(a, "cuda", dt) for a in (inp.sh_w1, inp.sh_w3, inp.sh_w2))
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device="cuda")
+    h = torch.empty((N, Fs), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.shared_ffn(c, x, w1, w3, w2, h, y, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.ffn_swiglu(oracle.to_f64(inp.x, dt), oracle.to_f64(inp.sh_w1, dt), oracle.to_f64(inp.sh_w3, dt),
+                            oracle.to_f64(inp.sh_w2, dt))
+    yh = host(y)
+    assert np.isfinite(yh).all(), "rows left unwritten"
+    err = rel_err(yh, ref)
+    say(f"shared N={N} d={d} Fs={Fs}: rel err {err:.3e}")
+    assert err <= TOL[dt], err
