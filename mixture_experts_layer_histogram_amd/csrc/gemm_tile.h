@@ -105,8 +105,11 @@ __device__ __host__ inline UnitPlan plan_units(int T, int G, int KT) {
 
 // One unit of work: rows [r0, r1) of segment `seg`, output columns from n0,
 // K steps [kt0, kt1); slot >= 0 marks a K-part that writes partial tile `slot`.
+// Rows [x0, x1) (x0 == x1: none) are a segment's short tail attached to a
+// whole 256-row tile (tile kind 5): the unit computes them too, with the
+// same weight tile.
 struct Unit {
-  int seg, r0, r1, n0, kt0, kt1, slot;
+  int seg, r0, r1, n0, kt0, kt1, slot, x0, x1;
 };
 
 // Plain form of decode_unit (host-callable: the CPU tests enumerate units with it).
@@ -117,6 +120,7 @@ __device__ __host__ inline Unit decode_unit_plain(const int32_t* tiles, const Un
   w.kt0 = 0;
   w.kt1 = KT;
   w.slot = -1;
+  w.x0 = w.x1 = 0;
   if (u < plan.full) {
     tile_lin = u;
   } else {
@@ -153,6 +157,8 @@ __device__ __forceinline__ Unit decode_unit(const int32_t* __restrict__ tiles, c
   w.kt0 = __builtin_amdgcn_readfirstlane(w.kt0);
   w.kt1 = __builtin_amdgcn_readfirstlane(w.kt1);
   w.slot = __builtin_amdgcn_readfirstlane(w.slot);
+  w.x0 = __builtin_amdgcn_readfirstlane(w.x0);
+  w.x1 = __builtin_amdgcn_readfirstlane(w.x1);
   return w;
 }
 
@@ -188,16 +194,35 @@ struct SegTable {
   int off[kMaxExperts + 1];
   int pb[kMaxExperts + 1];
   int ps[kMaxExperts + 1];
+  int kind;   // the tile kind the table was built for (kinds 3 and 4 resolved)
 };
+
+// Kind 5: kind 0, except that a segment of at least 256 rows whose tail is
+// shorter than kBigTailMin attaches up to 32 tail rows to each of its whole
+// 256-row tiles (attach_rows of them in all, 32 to each of the first tiles);
+// only the rest of the tail goes to 64-row tiles.
+constexpr int kAttachRows = 32;
+// The forward 256-row kernel's stage: A rows 0..255 of the tile and 256..287 for attached rows, then the
+// 256 B rows; its K-part partial tiles have kBM2P rows (the attached ones at 256..287).
+constexpr int kARows = 256 + kAttachRows;
+constexpr int kStageA = kARows * 64;
+constexpr int kStage2 = (kARows + 256) * 64;
+constexpr int kBM2P = kARows;
+__device__ __host__ inline int attach_rows(int rows) {
+  const int nb = rows / 256, rest = rows - 256 * nb;
+  return rest < kBigTailMin ? (rest < kAttachRows * nb ? rest : kAttachRows * nb) : 0;
+}
 constexpr int kSegTableElems = (int)((sizeof(SegTable) + 15) / 16) * 8;   // in 16-bit LDS elements
 
 __device__ __host__ inline void seg_tiles(int rows, int kind, int& nb, int& ns) {
   nb = kind == 1 ? 0 : rows / 256;
   int rest = rows - nb * 256;
-  if ((kind == 0 && rest >= kBigTailMin) || (kind == 2 && rest > 0 && (nb > 0 || rest >= kBigTailMin))) {
+  if (((kind == 0 || kind == 5) && rest >= kBigTailMin) ||
+      (kind == 2 && rest > 0 && (nb > 0 || rest >= kBigTailMin))) {
     nb += 1;
     rest = 0;
   }
+  if (kind == 5) rest -= attach_rows(rows);
   ns = rest > 0 ? (rest + 63) / 64 : 0;
 }
 
@@ -219,9 +244,10 @@ __device__ __host__ inline int choose_tail_kind(long long t0, long long t2, int 
 
 // Called by every thread of the workgroup; wavefront 0 fills the table (lane l
 // takes segments 4l .. 4l + 3), then a barrier.  n_ntiles and G (the grid)
-// serve kinds 3 and 4 only.
+// serve kinds 3 and 4 only; with `attach`, kind 0 (given or chosen) becomes 5.
 __device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __restrict__ offsets, int n_seg,
-                                                int dense_rows, int kind, int n_ntiles = 0, int G = 1) {
+                                                int dense_rows, int kind, int n_ntiles = 0, int G = 1,
+                                                bool attach = false) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int o[4], rows[4], nb[4], ns[4], sb = 0, ss = 0;
@@ -253,6 +279,7 @@ __device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __re
       }
       kind = choose_tail_kind((long long)c0 * n_ntiles, (long long)c2 * n_ntiles, G, kind == 4);
     }
+    if (attach && kind == 0) kind = 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       seg_tiles(rows[i], kind, nb[i], ns[i]);
@@ -282,6 +309,7 @@ __device__ __forceinline__ void build_seg_table(SegTable& t, const int32_t* __re
       t.off[n_seg] = n_seg > 0 ? (offsets ? offsets[n_seg] : dense_rows) : 0;
       t.pb[n_seg] = ib;
       t.ps[n_seg] = is;
+      t.kind = kind;
     }
   }
   __syncthreads();
@@ -296,6 +324,7 @@ __device__ __host__ inline Unit decode_unit_seg(const SegTable& t, int n_seg, bo
   w.kt0 = 0;
   w.kt1 = KT;
   w.slot = -1;
+  w.x0 = w.x1 = 0;
   if (u < plan.full) {
     tile_lin = u;
   } else {
@@ -315,15 +344,25 @@ __device__ __host__ inline Unit decode_unit_seg(const SegTable& t, int n_seg, bo
   }
   const int seg = lo, first = pre[seg], cnt = pre[seg + 1] - first;
   const int o = tile_lin - first * n_ntiles;
-  const int j = o / cnt, m = o % cnt;
+  const int j = o / cnt;
+  // kind 5: the M tiles of column tile j start at tile j mod cnt, so that the
+  // tiles carrying attached rows (the first ones) are spread over the
+  // workgroups, which take every 32nd unit of their span
+  const int m = t.kind == 5 ? (o % cnt + j) % cnt : o % cnt;
   const int seg_lo = t.off[seg], seg_hi = t.off[seg + 1];
   w.seg = seg;
+  const int xa = t.kind == 5 ? attach_rows(seg_hi - seg_lo) : 0;
   if (big) {
     w.r0 = seg_lo + m * 256;
     w.r1 = seg_hi < w.r0 + 256 ? seg_hi : w.r0 + 256;
+    if (m * kAttachRows < xa) {
+      const int nbig = t.pb[seg + 1] - t.pb[seg];
+      w.x0 = seg_lo + nbig * 256 + m * kAttachRows;
+      w.x1 = w.x0 + (xa - m * kAttachRows < kAttachRows ? xa - m * kAttachRows : kAttachRows);
+    }
   } else {
     const int nbig = t.pb[seg + 1] - t.pb[seg];
-    const int split = seg_hi < seg_lo + nbig * 256 ? seg_hi : seg_lo + nbig * 256;
+    const int split = seg_hi < seg_lo + nbig * 256 + xa ? seg_hi : seg_lo + nbig * 256 + xa;
     w.r0 = split + m * 64;
     w.r1 = seg_hi < w.r0 + 64 ? seg_hi : w.r0 + 64;
   }
@@ -341,6 +380,8 @@ __device__ __forceinline__ Unit decode_unit_lds(const SegTable& t, int n_seg, bo
   w.kt0 = __builtin_amdgcn_readfirstlane(w.kt0);
   w.kt1 = __builtin_amdgcn_readfirstlane(w.kt1);
   w.slot = __builtin_amdgcn_readfirstlane(w.slot);
+  w.x0 = __builtin_amdgcn_readfirstlane(w.x0);
+  w.x1 = __builtin_amdgcn_readfirstlane(w.x1);
   return w;
 }
 

@@ -105,6 +105,7 @@ struct GemmParams {
   int K, Nn, n_ntiles;
   const int32_t* offsets;     // segment row offsets [n_seg + 1], or null: one dense segment of dense_rows
   int n_seg, dense_rows, kind;   // kind: tile table kind (0: 256- and 64-row tiles, 1: 64-row only)
+  int attach;                    // short tails attach to whole 256-row tiles (tile kind 0 becomes 5)
 };
 
 template <int MODE, bool HAS_BIAS, int NMI = 2>
@@ -206,6 +207,71 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
   }
 }
 
+// Epilogue of the attached rows of a 256-row unit: each wavefront stages its
+// 32 x 32 fp32 block (rows x0.., the 32 columns of its B block ni = wm) in
+// LDS, then the outputs are formed and stored 8 columns per lane.  SwiGLU: the
+// W1 block of wavefront wn and the W3 block of wavefront wn + 4 meet there.
+template <int MODE, bool HAS_BIAS>
+__device__ __forceinline__ void store_attached(const GemmParams& p, const Unit& w, const f32x16& accx, float* xs,
+                                               int wave, int lane) {
+  const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, kh = lane >> 5;
+  float* mine = xs + wave * 1024;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mine[(8 * (r >> 2) + 4 * kh + (r & 3)) * 32 + l32] = accx[r];
+  __syncthreads();
+  const int nxr = w.x1 - w.x0;
+  if (MODE == MODE_SWIGLU_UP) {
+    if (wave < 4) {
+      const float* a = xs + wn * 1024;
+      const float* b = xs + (wn + 4) * 1024;
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) {
+        const int rr = pass * 16 + (lane >> 2), c8 = (lane & 3) * 8;
+        const int row = w.x0 + rr, col = w.n0 + 32 * wn + c8;
+        if (rr < nxr && col < p.Nn) {
+          Vec8 o, a1, a3;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const float av = a[rr * 32 + c8 + v], bv = b[rr * 32 + c8 + v];
+            o.e[v] = f32_to_bf16(silu_f(av) * bv);
+            a1.e[v] = f32_to_bf16(av);
+            a3.e[v] = f32_to_bf16(bv);
+          }
+          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
+          if (p.pre != nullptr) {
+            *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = a1.u;
+            *reinterpret_cast<uint4*>(p.pre + p.pre_plane + (size_t)row * p.Nn + col) = a3.u;
+          }
+        }
+      }
+    }
+  } else if (MODE == MODE_GELU_UP || MODE == MODE_DOWN) {
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int rr = pass * 16 + (lane >> 2), c8 = (lane & 3) * 8;
+      const int row = w.x0 + rr, col = w.n0 + 64 * wn + 32 * wm + c8;
+      if (rr < nxr && col < p.Nn) {
+        Vec8 b, o, a;
+        if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(p.bias + (size_t)w.seg * p.Nn + col);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          float x = mine[rr * 32 + c8 + v];
+          if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
+          a.e[v] = f32_to_bf16(x);
+          if (MODE == MODE_GELU_UP) x = gelu_f(x);
+          o.e[v] = f32_to_bf16(x);
+        }
+        if (MODE == MODE_DOWN)
+          __builtin_nontemporal_store(u32x4{o.u.x, o.u.y, o.u.z, o.u.w},
+                                      reinterpret_cast<u32x4*>(p.out + (size_t)row * p.Nn + col));
+        else
+          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
+        if (MODE == MODE_GELU_UP && p.pre != nullptr) *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = a.u;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 256 x 256 tile (long segments: the routed experts of prefill batches, the
 // shared expert, the router logits).
@@ -255,7 +321,7 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   // B rows (SwiGLU) 128 ni + 32 wn + l32 -> ^ 4 (wn & 1), else 64 wn + 32 ni + l32 -> ^ 4 (ni & 1).
   const int h = kh ^ swz8(l32);
   const int abase = (wm * 128 + l32) * kBK2;
-  const int bb0 = kStageElems + (SW ? (32 * wn + l32) : (64 * wn + l32)) * kBK2;
+  const int bb0 = kStageA + (SW ? (32 * wn + l32) : (64 * wn + l32)) * kBK2;
   const int bstep = (SW ? 128 : 32) * kBK2;
   const int hb0 = SW ? (h ^ (4 * (wn & 1))) : h;
   const int hb1 = SW ? hb0 : (h ^ 4);
@@ -267,23 +333,44 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(wsrc + (size_t)w.seg * wstride + (size_t)w.n0 * p.K, (uint32_t)nb_rows * rowbytes);
 
-  f32x16 acc[4][2];
+  // attached tail rows [x0, x1): A rows 256 .. 287 of the stage, loaded by wavefronts 0-3 (8 rows each);
+  // wavefront (wm, wn) multiplies them by its B block ni = wm (32 columns)
+  const int nxr = w.x1 - w.x0;
+  int voffx = kOobOffset;
+  __amdgpu_buffer_rsrc_t rax = ra;
+  if (nxr > 0) {
+    const int row = 8 * (wave & 3) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(row);   // swz8(256 + row) = swz8(row)
+    if (GATHER) {
+      const int r = w.x0 + row;
+      const int pr = r < w.x1 ? p.perm[r] : -1;
+      voffx = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
+    } else {
+      rax = make_rsrc(p.A + (size_t)w.x0 * p.K, (uint32_t)nxr * rowbytes);
+      voffx = row * rowbytes + chunk * 16;
+    }
+  }
+  const bool xload = nxr > 0 && wave < 4;
+  f32x16 acc[4][2], accx;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accx[r] = 0.f;
 
   const int kt0 = w.kt0, kt1 = w.kt1;
   if (kt0 < kt1) {
-    uint16_t* st = lds + (kt0 & 1) * (2 * kStageElems);
+    uint16_t* st = lds + (kt0 & 1) * kStage2;
     const int so = kt0 * kBK2 * 2;
 #pragma unroll
     for (int uu = 0; uu < 4; ++uu) {
       dma16(ra, st + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
-      dma16(rb, st + kStageElems + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+      dma16(rb, st + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
     }
+    if (xload) dma16(rax, st + (256 + 8 * wave) * kBK2, voffx, so);
   }
   // live 32-row blocks of this wavefront: a tile that ends inside the wavefront's 128 rows
   // (the tail of a long segment) skips the MFMAs and fragment reads of the empty blocks
@@ -308,7 +395,7 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 #pragma unroll
         for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
           dma16(ra, nx + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
-          dma16(rb, nx + kStageElems + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+          dma16(rb, nx + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
         }
       }
       if (kk + 1 < kBK2 / 16) {
@@ -340,10 +427,62 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
       }
     }
   };
+  // A whole tile with attached rows: the A fragments are read at the start of each sub-step
+  // instead of one ahead (the registers go to the attached rows' accumulators), and every
+  // wavefront adds one MFMA for the attached rows against its B block ni = wm.
+  auto step_x = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto wm_t) {
+    constexpr int WM = decltype(wm_t)::value;   // = wm: the B block the attached rows use
+    MOE_WAIT_VM0();
+    __builtin_amdgcn_s_barrier();
+    const bool more = kt + 1 < kt1;
+    const int so = (kt + 1) * kBK2 * 2;
+    bf16x8 fb[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      fb[0][x] = *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + ((x ? hb1 : hb0) << 3));
+#pragma unroll
+    for (int kk = 0; kk < kBK2 / 16; ++kk) {
+      const int c = kk & 1, k2 = 2 * kk;
+      if (more && kk < 2) {
+#pragma unroll
+        for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
+          dma16(ra, nx + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
+          dma16(rb, nx + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+        }
+        if (kk == 1 && xload) dma16(rax, nx + (256 + 8 * wave) * kBK2, voffx, so);
+      }
+      bf16x8 fa[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        fa[x] = *reinterpret_cast<const bf16x8*>(st + abase + 2048 * x + ((h ^ (4 * (x & 1)) ^ k2) << 3));
+      const bf16x8 fx = *reinterpret_cast<const bf16x8*>(st + (256 + l32) * kBK2 + ((h ^ k2) << 3));
+      if (kk + 1 < kBK2 / 16) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          fb[c ^ 1][x] =
+              *reinterpret_cast<const bf16x8*>(st + bb0 + bstep * x + (((x ? hb1 : hb0) ^ (k2 + 2)) << 3));
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fb[c][WM], accx, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  };
   auto loop = [&](auto nv_t) {
     for (int kt = kt0; kt < kt1; ++kt)
-      step(lds + (kt & 1) * (2 * kStageElems), lds + ((kt + 1) & 1) * (2 * kStageElems), kt, nv_t);
+      step(lds + (kt & 1) * kStage2, lds + ((kt + 1) & 1) * kStage2, kt, nv_t);
   };
+  if (nxr > 0) {   // attached rows come only with whole 256-row tiles
+    auto loop_x = [&](auto wm_t) {
+      for (int kt = kt0; kt < kt1; ++kt) step_x(lds + (kt & 1) * kStage2, lds + ((kt + 1) & 1) * kStage2, kt, wm_t);
+    };
+    if (wm) loop_x(std::integral_constant<int, 1>{});
+    else loop_x(std::integral_constant<int, 0>{});
+  } else
   switch (nv) {
     case 4: loop(std::integral_constant<int, 4>{}); break;
     case 3: loop(std::integral_constant<int, 3>{}); break;
@@ -357,10 +496,11 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
     store_block64<MODE, HAS_BIAS, 4>(acc, ep, lane, kh, l32, wn, w.r0 + wm * 128, w.r1, w.n0, p.Nn, w.seg, p.bias,
                                      p.out, p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
+    if (nxr > 0) store_attached<MODE, HAS_BIAS>(p, w, accx, reinterpret_cast<float*>(lds) + 16384, wave, lane);
   } else {
-    // fp32 partial tile, row-major [slot][256 rows][256 accumulator columns]; SwiGLU
-    // holds W1 and W3 columns in blocks of 64 (the K-part fix-up reads that layout)
-    float* dst = p.partials + (size_t)w.slot * (kBM2 * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2;
+    // fp32 partial tile, row-major [slot][kBM2P rows][256 accumulator columns] (rows 256 .. 287: the
+    // attached rows); SwiGLU holds W1 and W3 columns in blocks of 64 (the K-part fix-up reads that layout)
+    float* dst = p.partials + (size_t)w.slot * (kBM2P * kBN2) + (size_t)(wm * 128 + 4 * kh) * kBN2;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
       int col;
@@ -375,6 +515,18 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 #pragma unroll
         for (int r = 0; r < 16; ++r) dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + col] = acc[mi][ni][r];
     }
+    if (nxr > 0) {
+      int col;
+      if (SW) {
+        const int j = 32 * wn + l32;
+        col = (j >> 6) * 128 + (j & 63) + 64 * wm;
+      } else {
+        col = 64 * wn + 32 * wm + l32;
+      }
+      float* dx = p.partials + (size_t)w.slot * (kBM2P * kBN2) + (size_t)(256 + 4 * kh) * kBN2 + col;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dx[(8 * (r >> 2) + (r & 3)) * kBN2] = accx[r];
+    }
   }
   __syncthreads();
 }
@@ -388,12 +540,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
   // one LDS object: the operand stages, then the tile table (a second __shared__ object
   // would keep the compiler from telling the fragment reads apart from the in-flight
   // direct-to-LDS loads, and it would then wait for those loads before every read)
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * kStageElems + kSegTableElems];
-  SegTable& segt = *reinterpret_cast<SegTable*>(lds + 2 * 2 * kStageElems);
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStage2 + kSegTableElems];
+  SegTable& segt = *reinterpret_cast<SegTable*>(lds + 2 * kStage2);
+  static_assert(2 * kStage2 * 2 >= 96 * 1024, "the epilogue staging (64 KB + 32 KB of attached rows) fits the ring");
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G, p.attach != 0);
   const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
   const int ub = pb.units();
   const int per_xcd = G / kXcds;
@@ -748,7 +901,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G, p.attach != 0);
   const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
   const int us = ps.units();
   const int per_xcd = G / kXcds;
@@ -781,23 +934,25 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   constexpr int groups = cols_per_tile / 8;
   const int KT = p.K / kBK2;
-  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G);
+  build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G, p.attach != 0);
   const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
   const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
-  const long long nb = (long long)pb.rem * kBM2 * groups;
+  const long long nb = (long long)pb.rem * kBM2P * groups;
   const long long n = nb + (long long)ps.rem * kBM3 * groups;
   for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < n;
        it += (long long)gridDim.x * blockDim.x) {
     const bool big = it < nb;
     const long long jt = big ? it : it - nb;
-    const int bm = big ? kBM2 : kBM3;
+    const int bm = big ? kBM2P : kBM3;
     const int t = (int)(jt / ((long long)bm * groups));
     const int rem_it = (int)(jt - (long long)t * bm * groups);
     const int row_in = rem_it / groups, oc = (rem_it % groups) * 8;
     const UnitPlan& pl = big ? pb : ps;
     const Unit w = decode_unit_seg(segt, p.n_seg, big, pl, pl.full + t * pl.s, p.n_ntiles, KT, cols_per_tile);
-    const int row = w.r0 + row_in, col = w.n0 + oc;
-    if (row >= w.r1 || col >= p.Nn) continue;
+    // partial rows 0 .. 255: the tile's rows; 256 .. 287 (256-row tiles): its attached rows
+    const int row = row_in < 256 ? w.r0 + row_in : w.x0 + (row_in - 256);
+    const int col = w.n0 + oc;
+    if (row >= (row_in < 256 ? w.r1 : w.x1) || col >= p.Nn) continue;
     const float* part = (big ? p.partials : p.partials_small) + (size_t)t * pl.s * bm * kBN2 +
                         (size_t)row_in * kBN2;
     const int half = big ? 64 : 32;
@@ -907,7 +1062,7 @@ hipError_t launch_build_tiles(const int32_t* offsets, int n_seg, int dense_rows,
 int grouped_gemm_max_tiles(int max_rows, int n_seg) { return max_rows / 256 + n_seg; }
 int grouped_gemm_max_small_tiles(int max_rows, int n_seg) { return max_rows / 64 + n_seg; }
 size_t grouped_gemm_partials_bytes() {
-  return (size_t)kMaxSplitUnits * (kBM2 + kBM3) * kBN2 * sizeof(float);
+  return (size_t)kMaxSplitUnits * (kBM2P + kBM3) * kBN2 * sizeof(float);
 }
 size_t grouped_gemm_gather_max_bytes() { return (size_t)kOobOffset - (1u << 20); }
 
@@ -936,6 +1091,8 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.dense_rows = g.max_rows;
   // routed segments: the 256-row / 64-row split of each expert's tail is chosen on the device
   p.kind = FP8 ? 1 : (g.offsets == nullptr || MODE == MODE_LOGITS ? 0 : (MODE == MODE_DOWN ? 4 : 3));
+  // short tails ride on whole 256-row tiles (the attached-row epilogue covers these modes)
+  p.attach = !FP8 && (MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP || (MODE == MODE_DOWN && g.comb_out == nullptr));
   p.W = (const uint16_t*)g.w;
   p.W3 = (const uint16_t*)g.w3;
   p.bias = (const uint16_t*)g.bias;
@@ -954,7 +1111,7 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   p.scale1 = g.scale1;
   p.scale3 = g.scale3;
   p.partials = g.partials;
-  p.partials_small = g.partials + (size_t)kMaxSplitUnits * kBM2 * kBN2;
+  p.partials_small = g.partials + (size_t)kMaxSplitUnits * kBM2P * kBN2;
   p.K = g.K;
   p.Nn = g.Nn;
   p.n_ntiles = (g.Nn + cols - 1) / cols;
@@ -963,7 +1120,7 @@ static void launch_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   bool run_big = !FP8 && g.max_rows >= kBigTailMin, run_small = true, run_fixup = true;
   if (g.offsets == nullptr) {   // one dense segment of max_rows rows: the host knows both tile counts and plans
     int nb = 0, ns = 0;
-    seg_tiles(g.max_rows, p.kind, nb, ns);
+    seg_tiles(g.max_rows, p.attach && p.kind == 0 ? 5 : p.kind, nb, ns);
     const int KT = g.K / kBK2;
     run_big = nb > 0;
     run_small = ns > 0;
@@ -995,7 +1152,8 @@ LogitParts logits_parts(const GroupedGemmArgs& g) {
   const UnitPlan pb = plan_units(z.nb * n_ntiles, grid, KT), ps = plan_units(z.ns * n_ntiles, grid, KT);
   z.logits = g.out_f32;
   z.part_big = g.partials;
-  z.part_small = g.partials + (size_t)kMaxSplitUnits * kBM2 * kBN2;
+  z.part_small = g.partials + (size_t)kMaxSplitUnits * kBM2P * kBN2;
+  z.rows_big = kBM2P;
   z.bias = g.bias_f32;
   z.full_b = pb.full;
   z.s_b = pb.s;

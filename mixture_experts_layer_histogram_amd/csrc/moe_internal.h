@@ -108,6 +108,7 @@ struct LogitParts {
   int nb, full_b, s_b;           // 256-row tiles; the first full_b unsplit; s_b K-parts each after them
   int ns, full_s, s_s;           // 64-row tiles after row 256 nb, likewise
   int ld;                        // columns of a partial-tile row
+  int rows_big;                  // rows of a 256-row tile's partial slot
 };
 // Selection (top-k, gates, probability sums) that first completes the logits from the
 // K-part partials of the logits GEMM (E in (128, 256]: 64 lanes of 4 experts per token).

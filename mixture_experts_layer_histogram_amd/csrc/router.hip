@@ -346,9 +346,9 @@ __device__ __forceinline__ float4 logits_from_parts(const LogitParts zp, int t, 
   if (t < zp.nb * 256) {
     const int i = t >> 8;
     if (i >= zp.full_b) {
-      base = zp.part_big + ((size_t)(i - zp.full_b) * zp.s_b * 256 + (t & 255)) * zp.ld;
+      base = zp.part_big + ((size_t)(i - zp.full_b) * zp.s_b * zp.rows_big + (t & 255)) * zp.ld;
       parts = zp.s_b;
-      stride = 256 * zp.ld;
+      stride = zp.rows_big * zp.ld;
     }
   } else {
     const int j = (t - zp.nb * 256) >> 6;

@@ -27,7 +27,8 @@ struct Count {
 
 // The table build_seg_table writes (exclusive prefix counts of seg_tiles; kinds 3
 // and 4 resolved to 0 or 2 with the kernels' choose_tail_kind).
-static SegTable seg_table(const std::vector<int>& offs, int kind, int n_ntiles = 0, int G = 256) {
+static SegTable seg_table(const std::vector<int>& offs, int kind, int n_ntiles = 0, int G = 256,
+                          bool attach = false) {
   SegTable t{};
   const int E = (int)offs.size() - 1;
   if (kind >= 3) {
@@ -41,6 +42,8 @@ static SegTable seg_table(const std::vector<int>& offs, int kind, int n_ntiles =
     }
     kind = choose_tail_kind(c0 * n_ntiles, c2 * n_ntiles, G, kind == 4);
   }
+  if (attach && kind == 0) kind = 5;
+  t.kind = kind;
   int b = 0, sm = 0;
   for (int e = 0; e < E; ++e) {
     int nb, ns;
@@ -180,12 +183,13 @@ static long long kind0_mismatch(int K, int Nn, int cols_per_tile, const std::vec
 // 256-row and 64-row units, decoded from the table, cover every (row, output
 // column tile, K step) of every segment exactly once and nothing outside the
 // segments; returns the number of cells covered other than once.
-static long long cover_bad(int K, int Nn, int cols_per_tile, const std::vector<int>& seg_rows, int kind) {
+static long long cover_bad(int K, int Nn, int cols_per_tile, const std::vector<int>& seg_rows, int kind,
+                           bool attach = false) {
   const int E = (int)seg_rows.size(), KT = K / 64, G = 256;
   const int n_ntiles = (Nn + cols_per_tile - 1) / cols_per_tile;
   std::vector<int> offs(E + 1, 0);
   for (int e = 0; e < E; ++e) offs[e + 1] = offs[e] + seg_rows[e];
-  const SegTable t = seg_table(offs, kind, n_ntiles, G);
+  const SegTable t = seg_table(offs, kind, n_ntiles, G, attach);
   const int R = offs[E];
   std::vector<unsigned char> hits((size_t)R * n_ntiles * KT, 0);
   long long bad = 0;
@@ -200,6 +204,15 @@ static long long cover_bad(int K, int Nn, int cols_per_tile, const std::vector<i
       const int j = w.n0 / cols_per_tile;
       for (int r = w.r0; r < w.r1; ++r)
         for (int kt = w.kt0; kt < w.kt1; ++kt) ++hits[((size_t)r * n_ntiles + j) * KT + kt];
+      if (w.x1 > w.x0) {   // attached tail rows: only on whole 256-row tiles, at most 32, in the same segment
+        if (!big || w.r1 - w.r0 != 256 || w.x1 - w.x0 > kAttachRows || w.x0 < offs[w.seg] ||
+            w.x1 > offs[w.seg + 1]) {
+          ++bad;
+          continue;
+        }
+        for (int r = w.x0; r < w.x1; ++r)
+          for (int kt = w.kt0; kt < w.kt1; ++kt) ++hits[((size_t)r * n_ntiles + j) * KT + kt];
+      }
     }
   }
   for (unsigned char h : hits) bad += h != 1;
@@ -219,8 +232,15 @@ int main(int argc, char** argv) {
   const int cpt = up ? 128 : 256;
   const long long m0 = kind0_mismatch(K, Nn, cpt, rows);
   long long cov = 0;
-  for (int kind : {0, 2, 3, 4}) cov += cover_bad(K, Nn, cpt, rows, kind);
+  for (int kind : {0, 2, 3, 4}) cov += cover_bad(K, Nn, cpt, rows, kind) + cover_bad(K, Nn, cpt, rows, kind, true);
+  long long attached = 0;   // rows the attaching table hands to 256-row units (the cases must exercise it)
+  {
+    std::vector<int> offs(rows.size() + 1, 0);
+    for (size_t e = 0; e < rows.size(); ++e) offs[e + 1] = offs[e] + rows[e];
+    const SegTable t = seg_table(offs, 0, 1, 256, true);
+    for (size_t e = 0; e < rows.size(); ++e) attached += t.kind == 5 ? attach_rows(rows[e]) : 0;
+  }
   std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld list_mismatch=%lld kind0_mismatch=%lld "
-              "cover_bad=%lld\n", a.units, a.checked, a.oob, b.oob, a.mismatch, m0, cov);
+              "cover_bad=%lld attached=%lld\n", a.units, a.checked, a.oob, b.oob, a.mismatch, m0, cov, attached);
   return 0;
 }

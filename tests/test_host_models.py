@@ -6,6 +6,10 @@ decode_unit_seg) gives, for every unit, the segment, rows, columns and K range
 that the earlier tile list (decode_unit_plain over build_tiles_kernel's list)
 gave; so the split of the work, and the results, are unchanged.
 
+Tile kinds 0, 2, 3, 4 and 5 (short tails attached to whole 256-row tiles):
+the units decoded from the table cover every (row, column tile, K step) of
+every segment exactly once.
+
 fp8 64-row tile: every operand load of every unit, for reduction lengths with
 odd 64-K step counts (K = 320) and the decode shapes' K-split parts (K = 4096,
 14336), must stay inside its allocation once the buffer range check has let
@@ -60,6 +64,15 @@ def test_fp8_loads_in_bounds(fp8_model, mode, K, Nn, rows):
     assert int(r["list_mismatch"]) == 0, r      # the LDS table decodes the units the tile list did
     assert int(r["kind0_mismatch"]) == 0, r     # also for 256-row + 64-row tiles (bf16)
     assert int(r["cover_bad"]) == 0, r          # every tile kind covers each row, column tile, K step once
+
+
+def test_attached_tails_are_exercised(fp8_model):
+    """The coverage check of tile kind 5 (short tails attached to whole 256-row tiles)
+    must see attached rows in the cases that have such tails."""
+    r = _run(fp8_model, "up", 4096, 14336, [1003, 1073, 1024, 1017, 1040, 1029, 1000, 1006])
+    assert int(r["attached"]) == 49 + 16 + 5, r      # the tails of 1073, 1040 and 1029 rows
+    r = _run(fp8_model, "down", 14336, 4096, [4926, 0, 7, 130, 127, 128, 255, 256, 257, 383, 384, 1])
+    assert int(r["attached"]) == 62 + 1 + 32, r      # 4926 and 257 whole; 32 of 383's 127 (one 256-row tile)
 
 
 def test_fp8_model_sees_the_half_step_hazard(fp8_model):
