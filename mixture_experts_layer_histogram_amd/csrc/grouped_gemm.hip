@@ -11,8 +11,10 @@
 //
 // Work decomposition.  Every workgroup turns `offsets` into a per-segment
 // tile table in LDS (256-row tiles for long segments, 64-row tiles for short
-// segments and short tails; SegTable in gemm_tile.h), so the host never waits
-// for the routing result and no launch has to write a tile list first.  Two
+// segments; a long segment's short tail rides on its whole 256-row tiles as
+// up to 32 attached rows each, or goes to 64-row tiles; SegTable in
+// gemm_tile.h), so the host never waits for the routing result and no launch
+// has to write a tile list first.  Two
 // persistent kernels run, one per tile kind: the 256-row tiles are bound by
 // the matrix cores and run on 8 wavefronts per CU, the 64-row tiles are bound
 // by streaming the expert's weights and run on 4.  A K-split fix-up kernel
