@@ -345,10 +345,12 @@ __device__ __host__ inline Unit decode_unit_seg(const SegTable& t, int n_seg, bo
   const int seg = lo, first = pre[seg], cnt = pre[seg + 1] - first;
   const int o = tile_lin - first * n_ntiles;
   const int j = o / cnt;
-  // kind 5: the M tiles of column tile j start at tile j mod cnt, so that the
-  // tiles carrying attached rows (the first ones) are spread over the
-  // workgroups, which take every 32nd unit of their span
-  const int m = t.kind == 5 ? (o % cnt + j) % cnt : o % cnt;
+  // kind 5: the M tiles of column tile j are rotated by j + j cnt / 32, so that
+  // the tiles carrying attached rows (the first ones) are spread over the
+  // workgroups: those of an XCD take every 32nd unit of its span, which with
+  // cnt dividing 32 is the same M position at every column tile, and the
+  // j cnt / 32 term moves that position by one from one of them to the next
+  const int m = t.kind == 5 ? (o % cnt + j + j * cnt / 32) % cnt : o % cnt;
   const int seg_lo = t.off[seg], seg_hi = t.off[seg + 1];
   w.seg = seg;
   const int xa = t.kind == 5 ? attach_rows(seg_hi - seg_lo) : 0;
