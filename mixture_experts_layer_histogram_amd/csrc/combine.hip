@@ -132,10 +132,7 @@ __global__ __launch_bounds__(256) void combine_dropped_kernel(const int32_t* __r
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] += bf16_to_f32(y.e[v]);
     }
-    Vec8 o;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(acc[v]);
-    *reinterpret_cast<uint4*>(out + trow + c) = o.u;
+    *reinterpret_cast<uint4*>(out + trow + c) = pack_bf16x8(acc);
   }
 }
 

@@ -419,10 +419,9 @@ __device__ __forceinline__ void combine_store8(const CombineOut& cmb, int row, i
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[v] += bf16_to_f32(sy.e[v]);
   }
-  Vec8 ov;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) ov.e[v] = f32_to_bf16(fmaf(g, bf16_to_f32(y.e[v]), acc[v]));
-  *reinterpret_cast<uint4*>(cmb.out + o) = ov.u;
+  for (int v = 0; v < 8; ++v) acc[v] = fmaf(g, bf16_to_f32(y.e[v]), acc[v]);
+  *reinterpret_cast<uint4*>(cmb.out + o) = pack_bf16x8(acc);
 }
 
 }  // namespace moe

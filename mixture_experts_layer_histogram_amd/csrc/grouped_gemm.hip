@@ -153,19 +153,14 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
             *reinterpret_cast<float4*>(src + (q & 1) * 4 + (q >> 1) * 32) =
                 *reinterpret_cast<const float4*>(ep + ep_at(rr, c));
           }
-          Vec8 o;
+          float hv[8];
 #pragma unroll
-          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(silu_f(src[v]) * src[32 + v]);
-          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = o.u;
+          for (int v = 0; v < 8; ++v) hv[v] = silu_f(src[v]) * src[32 + v];
+          *reinterpret_cast<uint4*>(out + (size_t)row * Nn + col) = pack_bf16x8(hv);
           if (pre != nullptr) {
-            Vec8 a1, a3;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              a1.e[v] = f32_to_bf16(src[v]);
-              a3.e[v] = f32_to_bf16(src[32 + v]);
-            }
-            *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = a1.u;
-            *reinterpret_cast<uint4*>(pre + pre_plane + (size_t)row * Nn + col) = a3.u;
+            *reinterpret_cast<uint4*>(pre + (size_t)row * Nn + col) = pack_bf16x8(*reinterpret_cast<float(*)[8]>(src));
+            *reinterpret_cast<uint4*>(pre + pre_plane + (size_t)row * Nn + col) =
+                pack_bf16x8(*reinterpret_cast<float(*)[8]>(src + 32));
           }
         }
       }
@@ -179,17 +174,16 @@ __device__ __forceinline__ void store_block64(f32x16 (&acc)[NMI][2], float* ep, 
 #pragma unroll
           for (int q = 0; q < 2; ++q)
             *reinterpret_cast<float4*>(src + q * 4) = *reinterpret_cast<const float4*>(ep + ep_at(rr, c8 + q * 4));
-          Vec8 b;
+          Vec8 b, o, a;
           if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(bias + (size_t)seg * Nn + col);
-          Vec8 o, a;
+          float xa[8], xo[8];
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            float x = src[v];
-            if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
-            a.e[v] = f32_to_bf16(x);
-            if (MODE == MODE_GELU_UP) x = gelu_f(x);
-            o.e[v] = f32_to_bf16(x);
+            xa[v] = HAS_BIAS ? src[v] + bf16_to_f32(b.e[v]) : src[v];
+            xo[v] = MODE == MODE_GELU_UP ? gelu_f(xa[v]) : xa[v];
           }
+          o.u = pack_bf16x8(xo);
+          if (MODE == MODE_GELU_UP && pre != nullptr) a.u = pack_bf16x8(xa);
           if (MODE == MODE_DOWN && cmb->out != nullptr) {
             combine_store8(*cmb, row, col, Nn, o);
           } else if (MODE == MODE_DOWN) {
@@ -231,18 +225,17 @@ __device__ __forceinline__ void store_attached(const GemmParams& p, const Unit& 
         const int rr = pass * 16 + (lane >> 2), c8 = (lane & 3) * 8;
         const int row = w.x0 + rr, col = w.n0 + 32 * wn + c8;
         if (rr < nxr && col < p.Nn) {
-          Vec8 o, a1, a3;
+          float av[8], bv[8], hv[8];
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            const float av = a[rr * 32 + c8 + v], bv = b[rr * 32 + c8 + v];
-            o.e[v] = f32_to_bf16(silu_f(av) * bv);
-            a1.e[v] = f32_to_bf16(av);
-            a3.e[v] = f32_to_bf16(bv);
+            av[v] = a[rr * 32 + c8 + v];
+            bv[v] = b[rr * 32 + c8 + v];
+            hv[v] = silu_f(av[v]) * bv[v];
           }
-          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
+          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = pack_bf16x8(hv);
           if (p.pre != nullptr) {
-            *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = a1.u;
-            *reinterpret_cast<uint4*>(p.pre + p.pre_plane + (size_t)row * p.Nn + col) = a3.u;
+            *reinterpret_cast<uint4*>(p.pre + (size_t)row * p.Nn + col) = pack_bf16x8(av);
+            *reinterpret_cast<uint4*>(p.pre + p.pre_plane + (size_t)row * p.Nn + col) = pack_bf16x8(bv);
           }
         }
       }
@@ -255,14 +248,14 @@ __device__ __forceinline__ void store_attached(const GemmParams& p, const Unit& 
       if (rr < nxr && col < p.Nn) {
         Vec8 b, o, a;
         if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(p.bias + (size_t)w.seg * p.Nn + col);
+        float xa[8], xo[8];
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
-          float x = mine[rr * 32 + c8 + v];
-          if (HAS_BIAS) x += bf16_to_f32(b.e[v]);
-          a.e[v] = f32_to_bf16(x);
-          if (MODE == MODE_GELU_UP) x = gelu_f(x);
-          o.e[v] = f32_to_bf16(x);
+          xa[v] = HAS_BIAS ? mine[rr * 32 + c8 + v] + bf16_to_f32(b.e[v]) : mine[rr * 32 + c8 + v];
+          xo[v] = MODE == MODE_GELU_UP ? gelu_f(xa[v]) : xa[v];
         }
+        o.u = pack_bf16x8(xo);
+        if (MODE == MODE_GELU_UP && p.pre != nullptr) a.u = pack_bf16x8(xa);
         if (MODE == MODE_DOWN)
           __builtin_nontemporal_store(u32x4{o.u.x, o.u.y, o.u.z, o.u.w},
                                       reinterpret_cast<u32x4*>(p.out + (size_t)row * p.Nn + col));
@@ -989,20 +982,20 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int G) {
     }
     Vec8 b, o, s1, s3;
     if (HAS_BIAS) b.u = *reinterpret_cast<const uint4*>(p.bias + (size_t)w.seg * p.Nn + col);
+    float xa[8], xo[8];   // the pre-activation (W1 part for SwiGLU) and the output
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = v1[e];
       if (MODE == MODE_SWIGLU_UP) {
-        s1.e[e] = f32_to_bf16(x);
-        s3.e[e] = f32_to_bf16(v3[e]);
-        x = silu_f(x) * v3[e];
+        xa[e] = v1[e];
+        xo[e] = silu_f(v1[e]) * v3[e];
       } else {
-        if (HAS_BIAS) x += bf16_to_f32(b.e[e]);
-        s1.e[e] = f32_to_bf16(x);
-        if (MODE == MODE_GELU_UP) x = gelu_f(x);
+        xa[e] = HAS_BIAS ? v1[e] + bf16_to_f32(b.e[e]) : v1[e];
+        xo[e] = MODE == MODE_GELU_UP ? gelu_f(xa[e]) : xa[e];
       }
-      o.e[e] = f32_to_bf16(x);
     }
+    o.u = pack_bf16x8(xo);
+    s1.u = pack_bf16x8(xa);
+    if (MODE == MODE_SWIGLU_UP) s3.u = pack_bf16x8(v3);
     if (MODE == MODE_DOWN && p.cmb.out != nullptr) combine_store8(p.cmb, row, col, p.Nn, o);
     else *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = o.u;
     if ((MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP) && p.pre != nullptr) {

@@ -25,12 +25,21 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 in one word (lo in the low half), round to nearest even, NaN
+// stays NaN: gfx950's packed conversion, one instruction for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pack_bf16x2(f, f)); }
+
+// Eight fp32 values -> eight bf16, one 16-byte vector.
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
 }
 
 // Eight bf16 values as one 16-byte load or store.
@@ -49,7 +58,11 @@ template <> struct Store<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-__device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+// u sigmoid(u), the sigmoid as the hardware reciprocal of 1 + 2^(-u log2 e) (each step within
+// about an fp32 ulp, far below the bf16 rounding that follows; a divide costs 11 instructions)
+__device__ __forceinline__ float silu_f(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.44269504088896341f));
+}
 __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 0.70710678118654752f); }
 
 // Top-k blocking: L lanes per token (each owning E / L consecutive experts, at

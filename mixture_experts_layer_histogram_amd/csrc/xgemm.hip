@@ -248,10 +248,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nn_kernel(NnParams p) {
 #pragma unroll
           for (int q = 0; q < 2; ++q)
             *reinterpret_cast<float4*>(src + q * 4) = *reinterpret_cast<const float4*>(ep + ep_at(rr, c8 + q * 4));
-          Vec8 o;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) o.e[v] = f32_to_bf16(src[v]);
-          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.N + col) = o.u;
+          *reinterpret_cast<uint4*>(p.out + (size_t)row * p.N + col) = pack_bf16x8(src);
         }
       }
       __builtin_amdgcn_wave_barrier();

@@ -240,7 +240,14 @@ int main(int argc, char** argv) {
     const SegTable t = seg_table(offs, 0, 1, 256, true);
     for (size_t e = 0; e < rows.size(); ++e) attached += t.kind == 5 ? attach_rows(rows[e]) : 0;
   }
+  int auto_kind;   // the kind the forward kernels resolve for these segments (rule 3 up, 4 down, attaching)
+  {
+    std::vector<int> offs(rows.size() + 1, 0);
+    for (size_t e = 0; e < rows.size(); ++e) offs[e + 1] = offs[e] + rows[e];
+    auto_kind = seg_table(offs, up ? 3 : 4, (Nn + cpt - 1) / cpt, 256, true).kind;
+  }
   std::printf("units=%lld checked=%lld oob=%lld nohalf_oob=%lld list_mismatch=%lld kind0_mismatch=%lld "
-              "cover_bad=%lld attached=%lld\n", a.units, a.checked, a.oob, b.oob, a.mismatch, m0, cov, attached);
+              "cover_bad=%lld attached=%lld auto_kind=%d\n", a.units, a.checked, a.oob, b.oob, a.mismatch, m0, cov,
+              attached, auto_kind);
   return 0;
 }

@@ -168,6 +168,62 @@ def test_expert_ffn_parity_per_segment():
             assert err <= TOL[cfg.dtype], (name, e, err)
 
 
+# Segment sizes that make the forward kernels attach short tails to whole 256-row tiles
+# (tails of 1, 14, 31, 32, 33, 44, 84 and 127 rows on one whole tile; of 1, 38, 64, 88
+# and 127 rows on two; 384 rows with a tail of exactly 128 as a whole tile; empty and
+# tile-less segments); the last 80 of the 336 whole-tile units, among them the 639-row
+# segment's attached rows, run as K-parts with a fix-up.  The host-model test
+# test_attach_edge_sizes_select_attaching_tiles shows the kernels' tail rule picks the
+# attaching kind for these sizes.
+ATTACH_EDGE_ROWS = [257, 270, 287, 288, 289, 300, 340, 383, 513, 550, 576, 600, 639, 384, 0, 1, 64, 127, 128]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu_bias"])
+def test_attached_tail_segments(act):
+    """Every row of y_perm against the oracle's expert FFN for segments whose short tails
+    ride on whole 256-row tiles, in the up projection (SwiGLU, or GELU + bias) and the down
+    projection; the gathered up projection writes the same bits as the one on pre-gathered
+    rows."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    from workloads import MIXTRAL_PREFILL, SWITCH_SKEWED
+    rows = ATTACH_EDGE_ROWS
+    R, E = sum(rows), len(rows)
+    if act == "swiglu":
+        cfg = MIXTRAL_PREFILL.scaled(name="attach_swiglu", n_tokens=R, n_experts=E, top_k=1, d_ff=2048)
+    else:
+        cfg = SWITCH_SKEWED.scaled(name="attach_gelu", n_tokens=R, n_experts=E, top_k=1, d_model=4096, d_ff=4096,
+                                   capacity_factor=0.0, logit_offset=None)
+    say(f"attached tails {act}: R={R} E={E} d={cfg.d_model} F={cfg.d_ff}")
+    inp = make_inputs(cfg)
+    dev = M.upload_inputs(inp, "cuda")
+    c = M.config_from(cfg)
+    ws = torch.empty(M.workspace_size(c), dtype=torch.uint8, device="cuda")
+    offs_h = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    perm_h = np.random.default_rng(7).permutation(R).astype(np.int32)   # the expert order's token rows
+    offs = torch.from_numpy(offs_h).cuda()
+    perm = torch.from_numpy(perm_h).cuda()
+    xp = dev["x"][perm.long()].contiguous()
+    h = torch.empty((R, cfg.d_ff), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.empty_like(h)
+    y = torch.full((R, cfg.d_model), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.expert_ffn(c, xp, offs, dev["w1"], dev["w3"], dev["w2"], h, y, b1=dev["b1"], b2=dev["b2"], ws=ws)
+    M.expert_up_gather(c, dev["x"], perm, offs, dev["w1"], dev["w3"], h2, b1=dev["b1"], ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16)), "gathered up projection differs"
+    yh = host(y)
+    assert np.isfinite(yh).all(), "rows left unwritten"
+    x64 = oracle.to_f64(inp.x, cfg.dtype)
+    for e in range(E):
+        lo, hi = int(offs_h[e]), int(offs_h[e + 1])
+        if hi == lo:
+            continue
+        w = {n: oracle.to_f64(v, cfg.dtype) for n, v in inp.expert(e).items()}
+        ref = oracle.expert_apply(cfg.act, x64[perm_h[lo:hi]], w)
+        err = rel_err(yh[lo:hi], ref)
+        assert err <= TOL[cfg.dtype], (act, e, rows[e], err)
+
+
 def test_router_paths_agree():
     """bf16 routers with E <= 64 run the fused router kernel (GEMM, softmax, top-k in one
     launch) with or without a workspace; wider ones with E a multiple of 64 run on the

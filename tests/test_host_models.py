@@ -75,6 +75,22 @@ def test_attached_tails_are_exercised(fp8_model):
     assert int(r["attached"]) == 62 + 1 + 32, r      # 4926 and 257 whole; 32 of 383's 127 (one 256-row tile)
 
 
+# Segment sizes of the GPU test of attached tails (tails of 1 to 127 rows on one or two whole
+# tiles, a tail of exactly kBigTailMin, segments with no whole tile); 16 column tiles each way.
+ATTACH_EDGE_ROWS = [257, 270, 287, 288, 289, 300, 340, 383, 513, 550, 576, 600, 639, 384, 0, 1, 64, 127, 128]
+
+
+@pytest.mark.parametrize("mode,K,Nn", [("up", 4096, 2048), ("down", 2048, 4096)])
+def test_attach_edge_sizes_select_attaching_tiles(fp8_model, mode, K, Nn):
+    """The forward kernels' own tail rule picks the attaching tile kind for the GPU test's
+    segment sizes (21 whole tiles, 34 with every tail as a whole tile: 2 against 3 rounds
+    of 256 workgroups), which attaches 437 rows, so that test runs that kind."""
+    r = _run(fp8_model, mode, K, Nn, ATTACH_EDGE_ROWS)
+    assert int(r["auto_kind"]) == 5, r
+    assert int(r["attached"]) == 437, r
+    assert int(r["cover_bad"]) == 0, r
+
+
 def test_fp8_model_sees_the_half_step_hazard(fp8_model):
     hits = [int(_run(fp8_model, *c)["nohalf_oob"]) for c in CASES]
     assert hits[0] > 0 and hits[4] > 0, hits
