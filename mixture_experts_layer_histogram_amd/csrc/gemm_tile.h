@@ -79,6 +79,8 @@ __device__ __forceinline__ void dma16_stream(__amdgpu_buffer_rsrc_t r, uint16_t*
 // bits 3:0 in bits 3:0 and bits 5:4 in bits 15:14; expcnt 6:4; lgkmcnt 11:8).
 #define MOE_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 #define MOE_WAIT_VM0() __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0))
+// s_waitcnt lgkmcnt(0): this wavefront's LDS operations complete; vmcnt and expcnt left alone.
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 // How the units of one tile list are laid out: T tiles of KT steps; the
 // first `full` tiles run whole, the remaining `rem` tiles run in s K-parts.
@@ -213,6 +215,11 @@ __device__ __host__ inline int attach_rows(int rows) {
   return rest < kBigTailMin ? (rest < kAttachRows * nb ? rest : kAttachRows * nb) : 0;
 }
 constexpr int kSegTableElems = (int)((sizeof(SegTable) + 15) / 16) * 8;   // in 16-bit LDS elements
+// The forward 256-row kernel's LDS: two operand stages, the tile table, then a tail that stages
+// the attached rows' outputs (32 rows x (256 + 8) bf16, or 4 x 1024 fp32).
+constexpr int kTailOff = ((2 * kStage2 + kSegTableElems + 127) / 128) * 128;
+constexpr int kTailElems = 32 * (256 + 8);
+static_assert(kTailOff + kTailElems <= 80 * 1024, "the 256-row kernel's LDS fits 160 KB");
 
 __device__ __host__ inline void seg_tiles(int rows, int kind, int& nb, int& ns) {
   nb = kind == 1 ? 0 : rows / 256;

@@ -267,6 +267,155 @@ __device__ __forceinline__ void store_attached(const GemmParams& p, const Unit& 
   }
 }
 
+// Workgroup barrier for LDS hand-offs: this wavefront's LDS operations complete, then s_barrier.
+// Unlike __syncthreads() it does not wait for the wavefront's global stores.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  MOE_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Stores 32 staged rows (rows 32q.. of `src`, SC bf16 columns, row pitch RS) of a 256-row unit to
+// output rows r0 + rbase + 32q.., 16 bytes per lane.
+template <int MODE, int SC, int RS>
+__device__ __forceinline__ void store_staged(const GemmParams& p, const Unit& w, const uint16_t* src, int rbase, int q,
+                                             int lane) {
+  constexpr int LPR = SC / 8, RPI = 64 / LPR, NI = 32 / RPI;   // lanes per row, rows per instruction
+  const int c8 = (lane % LPR) * 8, col = w.n0 + c8;
+  uint4 v[NI];   // every LDS read first, then the stores (one wait, not one per row)
+#pragma unroll
+  for (int i = 0; i < NI; ++i) v[i] = *reinterpret_cast<const uint4*>(src + (32 * q + RPI * i + lane / LPR) * RS + c8);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = w.r0 + rbase + 32 * q + RPI * i + lane / LPR;
+    if (row < w.r1 && col < p.Nn) {
+      if (MODE == MODE_DOWN)   // Y is read once, by the combine: a streaming store
+        __builtin_nontemporal_store(u32x4{v[i].x, v[i].y, v[i].z, v[i].w},
+                                    reinterpret_cast<u32x4*>(p.out + (size_t)row * p.Nn + col));
+      else
+        *reinterpret_cast<uint4*>(p.out + (size_t)row * p.Nn + col) = v[i];
+    }
+  }
+}
+
+// Epilogue of a whole 256-row unit (SwiGLU, GELU or down projection; no K-part, no pre-activation
+// copy, no fused combine).  Wavefronts 0-3 issue all operand loads and wavefronts 4-7 all output
+// stores, so the stores drain while the next unit computes instead of holding up its first step:
+// every wavefront rounds its outputs to bf16 into LDS (tile rows 0..127 into the stage-1 buffer,
+// rows 128..255 into stage 0, attached rows into the tail); after a barrier wavefronts 4-7 store
+// stage 0's rows, a second barrier hands stage 0 to the next unit's first loads, and they store
+// the rest (the next unit writes stage 1 only after its first step's barrier).
+template <int MODE, bool HAS_BIAS>
+__device__ __forceinline__ void store_split(const GemmParams& p, const Unit& w, const f32x16 (&acc)[4][2],
+                                            const f32x16& accx, uint16_t* lds, int wave, int lane) {
+  constexpr bool SW = MODE == MODE_SWIGLU_UP;
+  constexpr int SC = SW ? kBN2 / 2 : kBN2;   // staged columns per row
+  constexpr int RS = SC + 8;                  // pitch: rows r and r + 4 of one write fall on other banks
+  asm volatile("" : "+v"(lane));   // the LDS and store addresses are formed here, not kept across the unit
+  const int wm = wave >> 2, wn = wave & 3, l32 = lane & 31, kh = lane >> 5;
+  const int nxr = w.x1 - w.x0;
+  uint16_t* S = lds + (wm ? 0 : kStage2);
+  uint16_t* T = lds + kTailOff;
+  // accumulator register r of a 32 x 32 block: row 8 (r >> 2) + 4 kh + (r & 3), column l32
+  if (SW) {   // W1 and W3 columns of one output sit in one lane (blocks ni = 0 and 1)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = 32 * mi + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const uint32_t v = pack_bf16x2(silu_f(acc[mi][0][r]) * acc[mi][1][r],
+                                       silu_f(acc[mi][0][r + 1]) * acc[mi][1][r + 1]);
+        S[row * RS + 32 * wn + l32] = (uint16_t)v;
+        S[(row + 1) * RS + 32 * wn + l32] = (uint16_t)(v >> 16);
+      }
+    if (nxr > 0 && wm == 0) {   // the attached rows' W1 block, for wavefront wn + 4 (which holds W3)
+      float* tw = reinterpret_cast<float*>(T) + wn * 1024;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tw[r * 64 + lane] = accx[r];
+    }
+  } else {
+    float b[2] = {0.f, 0.f}, bx = 0.f;
+    if (HAS_BIAS) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col = w.n0 + 64 * wn + 32 * ni + l32;
+        b[ni] = col < p.Nn ? bf16_to_f32(p.bias[(size_t)w.seg * p.Nn + col]) : 0.f;
+      }
+      bx = b[wm];
+    }
+    auto act = [&](float x) { return MODE == MODE_GELU_UP ? gelu_f(x) : x; };
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = 32 * mi + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const uint32_t v = pack_bf16x2(act(acc[mi][ni][r] + b[ni]), act(acc[mi][ni][r + 1] + b[ni]));
+          S[row * RS + 64 * wn + 32 * ni + l32] = (uint16_t)v;
+          S[(row + 1) * RS + 64 * wn + 32 * ni + l32] = (uint16_t)(v >> 16);
+        }
+    if (nxr > 0) {   // attached rows: columns 64 wn + 32 wm + l32
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+        const uint32_t v = pack_bf16x2(act(accx[r] + bx), act(accx[r + 1] + bx));
+        T[row * RS + 64 * wn + 32 * wm + l32] = (uint16_t)v;
+        T[(row + 1) * RS + 64 * wn + 32 * wm + l32] = (uint16_t)(v >> 16);
+      }
+    }
+  }
+  lds_barrier();   // the staged tile is complete
+  const int q = wave - 4;
+  if (wm == 1) store_staged<MODE, SC, RS>(p, w, lds, 128, q, lane);
+  lds_barrier();   // stage 0 is free for the next unit's first loads
+  if (wm == 1) {
+    store_staged<MODE, SC, RS>(p, w, lds + kStage2, 0, q, lane);
+    if (nxr > 0) {
+      if (SW) {
+        float* tw = reinterpret_cast<float*>(T) + q * 1024;
+        float hv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hv[r] = silu_f(tw[r * 64 + lane]) * accx[r];
+        asm volatile("" ::: "memory");   // the W1 values are read before this wavefront reuses their slot
+        uint16_t* tb = T + q * 2048;      // 32 x 32 bf16, pitch 40
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+          const uint32_t v = pack_bf16x2(hv[r], hv[r + 1]);
+          tb[row * 40 + l32] = (uint16_t)v;
+          tb[(row + 1) * 40 + l32] = (uint16_t)(v >> 16);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rr = 16 * i + (lane >> 2), c8 = (lane & 3) * 8;
+          const int col = w.n0 + 32 * q + c8;
+          if (rr < nxr && col < p.Nn)
+            *reinterpret_cast<uint4*>(p.out + (size_t)(w.x0 + rr) * p.Nn + col) =
+                *reinterpret_cast<const uint4*>(tb + rr * 40 + c8);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 8 * q + 2 * i + (lane >> 5), c8 = (lane & 31) * 8;
+          const int col = w.n0 + c8;
+          if (rr < nxr && col < p.Nn) {
+            const uint4 v = *reinterpret_cast<const uint4*>(T + rr * RS + c8);
+            if (MODE == MODE_DOWN)
+              __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                          reinterpret_cast<u32x4*>(p.out + (size_t)(w.x0 + rr) * p.Nn + col));
+            else
+              *reinterpret_cast<uint4*>(p.out + (size_t)(w.x0 + rr) * p.Nn + col) = v;
+          }
+        }
+      }
+    }
+    MOE_WAIT_LGKM0();   // every read of stage 1 is complete before the next unit's first barrier
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 256 x 256 tile (long segments: the routed experts of prefill batches, the
 // shared expert, the router logits).
@@ -276,10 +425,12 @@ __device__ __forceinline__ void store_attached(const GemmParams& p, const Unit& 
 // per lane), so while one wavefront of a SIMD waits on its loads or fragment
 // reads the other issues MFMAs; s_setprio favours the wavefront that is in
 // its MFMA run.  Two 64 KB LDS stages (A 256 rows, B 256 rows, 128 bytes
-// each); the loads for step k+1 are issued in slices between the MFMAs of the
-// first two sub-steps of step k, and the fragments of each 16-wide sub-step
-// are read from LDS while the previous sub-step's 8 MFMAs issue.  One
-// fence-free barrier per step.
+// each); wavefronts 0-3 issue the loads for step k+1 in slices between the
+// MFMAs of the first two sub-steps of step k, and the fragments of each
+// 16-wide sub-step are read from LDS while the previous sub-step's 8 MFMAs
+// issue.  One fence-free barrier per step.  Wavefronts 4-7 issue no loads and
+// store the whole output tile (store_split), so their stores never stall a
+// K step (a load wait counts a wavefront's stores too).
 //   SwiGLU up : the B tile holds 128 rows of W1 and the same 128 rows of W3;
 //               wavefront wn owns W1 columns 32 wn .. 32 wn + 31 (B rows
 //               32 wn + ..) and the same W3 columns (B rows 128 + 32 wn + ..),
@@ -297,20 +448,24 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   constexpr bool SW = MODE == MODE_SWIGLU_UP;
   constexpr int cols_per_tile = SW ? kBN2 / 2 : kBN2;
 
-  // DMA: wavefront w fills rows 32w..32w+31 of both operands, 8 rows per instruction.
-  int voff[4], voffb[4];
+  // DMA: wavefronts 0-3 fill the stages, wavefront w rows 64w .. 64w + 63 of both operands, 8 rows per
+  // instruction; wavefronts 4-7 issue no loads, so none of their K steps waits on their output stores
+  // (they store every output, see store_split).  Row 64w + 8u + (lane >> 3) takes 16-byte chunk c0 ^ u
+  // of its K slice (c0 = (lane & 7) ^ (lane >> 3), the swizzle of swz8), so its offset is that of u = 0
+  // with the chunk bits flipped and 8u rows added (row pitches are multiples of 128 bytes).
+  const bool dmaw = wave < 4;
+  const int l8 = lane >> 3, c0 = (lane & 7) ^ l8;
+  const int arow0 = 64 * (wave & 3) + l8;
+  int va0 = arow0 * rowbytes + (c0 << 4);
+  int vb0 = (SW ? (arow0 & 127) : arow0) * rowbytes + (c0 << 4);   // SwiGLU: W1 rows, then the W3 rows
+  int vg[8];
+  if (GATHER && dmaw) {   // the 8 token indices are loaded back to back (rows past the tile read its last one)
+    int pv[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 32 * wave + 8 * u + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz8(row);
-    if (GATHER) {
-      const int r = w.r0 + row;
-      const int pr = r < w.r1 ? p.perm[r] : -1;
-      voff[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
-    } else {
-      voff[u] = row * rowbytes + chunk * 16;
-    }
-    voffb[u] = (SW ? (row & 127) : row) * rowbytes + chunk * 16;
+    for (int u = 0; u < 8; ++u) pv[u] = p.perm[min(w.r0 + arow0 + 8 * u, w.r1 - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      vg[u] = (w.r0 + arow0 + 8 * u < w.r1 && pv[u] >= 0 ? (pv[u] / p.gk) * rowbytes : kOobOffset) + ((c0 ^ u) << 4);
   }
   // Fragment reads: A rows wm 128 + 32 mi + l32 -> slot (2 kk + kh) ^ g(l32) ^ 4 (mi & 1);
   // B rows (SwiGLU) 128 ni + 32 wn + l32 -> ^ 4 (wn & 1), else 64 wn + 32 ni + l32 -> ^ 4 (ni & 1).
@@ -324,16 +479,18 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(p.A, p.a_bytes)
                                            : make_rsrc(p.A + (size_t)w.r0 * p.K, (uint32_t)(w.r1 - w.r0) * rowbytes);
   const int nb_rows = min(cols_per_tile, p.Nn - w.n0);
-  const uint16_t* wsrc = (SW && wave >= 4) ? p.W3 : p.W;
+  const uint16_t* wsrc = (SW && wave >= 2) ? p.W3 : p.W;
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(wsrc + (size_t)w.seg * wstride + (size_t)w.n0 * p.K, (uint32_t)nb_rows * rowbytes);
+  auto aoff = [&](int u) { return GATHER ? vg[u] : (va0 ^ (u << 4)) + u * 8 * rowbytes; };
+  auto boff = [&](int u) { return (vb0 ^ (u << 4)) + u * 8 * rowbytes; };
 
   // attached tail rows [x0, x1): A rows 256 .. 287 of the stage, loaded by wavefronts 0-3 (8 rows each);
   // wavefront (wm, wn) multiplies them by its B block ni = wm (32 columns)
   const int nxr = w.x1 - w.x0;
   int voffx = kOobOffset;
   __amdgpu_buffer_rsrc_t rax = ra;
-  if (nxr > 0) {
+  if (nxr > 0 && dmaw) {
     const int row = 8 * (wave & 3) + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(row);   // swz8(256 + row) = swz8(row)
     if (GATHER) {
@@ -357,23 +514,25 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   for (int r = 0; r < 16; ++r) accx[r] = 0.f;
 
   const int kt0 = w.kt0, kt1 = w.kt1;
-  if (kt0 < kt1) {
-    uint16_t* st = lds + (kt0 & 1) * kStage2;
+  // the ring counts from the unit's first step: that step's loads go to stage 0 (store_split keeps
+  // stage 1 busy into the next unit)
+  if (kt0 < kt1 && dmaw) {
     const int so = kt0 * kBK2 * 2;
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-      dma16(ra, st + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
-      dma16(rb, st + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+    for (int u = 0; u < 8; ++u) {
+      dma16(ra, lds + (64 * wave + 8 * u) * kBK2, aoff(u), so);
+      dma16(rb, lds + kStageA + (64 * wave + 8 * u) * kBK2, boff(u), so);
     }
-    if (xload) dma16(rax, st + (256 + 8 * wave) * kBK2, voffx, so);
+    if (xload) dma16(rax, lds + (256 + 8 * wave) * kBK2, voffx, so);
   }
   // live 32-row blocks of this wavefront: a tile that ends inside the wavefront's 128 rows
   // (the tail of a long segment) skips the MFMAs and fragment reads of the empty blocks
   const int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (w.r1 - w.r0 - wm * 128 + 31) / 32)));
   auto step = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto nv_t) {
     constexpr int NV = decltype(nv_t)::value;
-    MOE_WAIT_VM0();
+    if (dmaw) MOE_WAIT_VM0();
     __builtin_amdgcn_s_barrier();
+    asm volatile("" : "+v"(va0), "+v"(vb0));   // the 16 offsets are formed per load, not kept in registers
     const bool more = kt + 1 < kt1;
     const int so = (kt + 1) * kBK2 * 2;
     bf16x8 fa[2][4], fb[2][2];
@@ -386,11 +545,11 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
       const int c = kk & 1;
-      if (more && kk < 2) {
+      if (more && kk < 2 && dmaw) {
 #pragma unroll
-        for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
-          dma16(ra, nx + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
-          dma16(rb, nx + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+        for (int u = 4 * kk; u < 4 * kk + 4; ++u) {
+          dma16(ra, nx + (64 * wave + 8 * u) * kBK2, aoff(u), so);
+          dma16(rb, nx + kStageA + (64 * wave + 8 * u) * kBK2, boff(u), so);
         }
       }
       if (kk + 1 < kBK2 / 16) {
@@ -427,8 +586,9 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   // wavefront adds one MFMA for the attached rows against its B block ni = wm.
   auto step_x = [&](const uint16_t* __restrict__ st, uint16_t* __restrict__ nx, int kt, auto wm_t) {
     constexpr int WM = decltype(wm_t)::value;   // = wm: the B block the attached rows use
-    MOE_WAIT_VM0();
+    if (dmaw) MOE_WAIT_VM0();
     __builtin_amdgcn_s_barrier();
+    asm volatile("" : "+v"(va0), "+v"(vb0));   // the 16 offsets are formed per load, not kept in registers
     const bool more = kt + 1 < kt1;
     const int so = (kt + 1) * kBK2 * 2;
     bf16x8 fb[2][2];
@@ -438,11 +598,11 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
       const int c = kk & 1, k2 = 2 * kk;
-      if (more && kk < 2) {
+      if (more && kk < 2 && dmaw) {
 #pragma unroll
-        for (int uu = 2 * kk; uu < 2 * kk + 2; ++uu) {
-          dma16(ra, nx + (32 * wave + 8 * uu) * kBK2, voff[uu], so);
-          dma16(rb, nx + kStageA + (32 * wave + 8 * uu) * kBK2, voffb[uu], so);
+        for (int u = 4 * kk; u < 4 * kk + 4; ++u) {
+          dma16(ra, nx + (64 * wave + 8 * u) * kBK2, aoff(u), so);
+          dma16(rb, nx + kStageA + (64 * wave + 8 * u) * kBK2, boff(u), so);
         }
         if (kk == 1 && xload) dma16(rax, nx + (256 + 8 * wave) * kBK2, voffx, so);
       }
@@ -469,11 +629,12 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
   };
   auto loop = [&](auto nv_t) {
     for (int kt = kt0; kt < kt1; ++kt)
-      step(lds + (kt & 1) * kStage2, lds + ((kt + 1) & 1) * kStage2, kt, nv_t);
+      step(lds + ((kt - kt0) & 1) * kStage2, lds + ((kt - kt0 + 1) & 1) * kStage2, kt, nv_t);
   };
   if (nxr > 0) {   // attached rows come only with whole 256-row tiles
     auto loop_x = [&](auto wm_t) {
-      for (int kt = kt0; kt < kt1; ++kt) step_x(lds + (kt & 1) * kStage2, lds + ((kt + 1) & 1) * kStage2, kt, wm_t);
+      for (int kt = kt0; kt < kt1; ++kt)
+        step_x(lds + ((kt - kt0) & 1) * kStage2, lds + ((kt - kt0 + 1) & 1) * kStage2, kt, wm_t);
     };
     if (wm) loop_x(std::integral_constant<int, 1>{});
     else loop_x(std::integral_constant<int, 0>{});
@@ -485,13 +646,21 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
     case 1: loop(std::integral_constant<int, 1>{}); break;
     default: loop(std::integral_constant<int, 0>{}); break;
   }
-  __syncthreads();
+  // Nothing is in flight here but the previous unit's output stores of wavefronts 4-7, long done;
+  // the wait also tells the compiler that no direct-to-LDS load is, so the epilogue's LDS reads
+  // need no wait of their own (a wait would also wait for the stores issued just before them).
+  MOE_WAIT_VM0();
+  lds_barrier();   // every wavefront is done with the ring
 
-  if (w.slot < 0) {
+  constexpr bool SPLIT = MODE == MODE_SWIGLU_UP || MODE == MODE_GELU_UP || MODE == MODE_DOWN;
+  if (SPLIT && w.slot < 0 && p.pre == nullptr && p.cmb.out == nullptr) {
+    store_split<MODE, HAS_BIAS>(p, w, acc, accx, lds, wave, lane);
+  } else if (w.slot < 0) {
     float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
     store_block64<MODE, HAS_BIAS, 4>(acc, ep, lane, kh, l32, wn, w.r0 + wm * 128, w.r1, w.n0, p.Nn, w.seg, p.bias,
                                      p.out, p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
     if (nxr > 0) store_attached<MODE, HAS_BIAS>(p, w, accx, reinterpret_cast<float*>(lds) + 16384, wave, lane);
+    __syncthreads();   // the next unit's first loads must not overtake this epilogue
   } else {
     // fp32 partial tile, row-major [slot][kBM2P rows][256 accumulator columns] (rows 256 .. 287: the
     // attached rows); SwiGLU holds W1 and W3 columns in blocks of 64 (the K-part fix-up reads that layout)
@@ -523,7 +692,6 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
       for (int r = 0; r < 16; ++r) dx[(8 * (r >> 2) + (r & 3)) * kBN2] = accx[r];
     }
   }
-  __syncthreads();
 }
 
 // Persistent over the 256-row tile list: the grid holds one workgroup per CU,
@@ -535,9 +703,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
   // one LDS object: the operand stages, then the tile table (a second __shared__ object
   // would keep the compiler from telling the fragment reads apart from the in-flight
   // direct-to-LDS loads, and it would then wait for those loads before every read)
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStage2 + kSegTableElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kTailOff + kTailElems];
   SegTable& segt = *reinterpret_cast<SegTable*>(lds + 2 * kStage2);
   static_assert(2 * kStage2 * 2 >= 96 * 1024, "the epilogue staging (64 KB + 32 KB of attached rows) fits the ring");
+  static_assert(128 * (kBN2 + 8) <= kStage2, "store_split stages 128 rows of the tile in one operand stage");
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
   const int G = gridDim.x;
   const int KT = p.K / kBK2;
