@@ -105,6 +105,27 @@ __device__ __host__ inline UnitPlan plan_units(int T, int G, int KT) {
   return p;
 }
 
+// The units the workgroups of one XCD share: a contiguous slice of the plan's whole units and a
+// contiguous slice of its K-part units (with one slice of the whole list, the parts, which come
+// last, would all fall to the last XCDs, whose workgroups then run half units while the others
+// run whole ones).  Workgroup q of the XCD takes every (G / 8)-th unit of the slices, q first.
+struct XcdSlice {
+  int f0, fc, p0, pc;
+};
+__device__ __host__ inline XcdSlice xcd_slice(const UnitPlan& pl, int xcd) {
+  const int P = pl.rem * pl.s;
+  const int fs = (pl.full + kXcds - 1) / kXcds, ps = (P + kXcds - 1) / kXcds;
+  XcdSlice x;
+  x.f0 = pl.full < xcd * fs ? pl.full : xcd * fs;
+  x.fc = (pl.full < x.f0 + fs ? pl.full : x.f0 + fs) - x.f0;
+  x.p0 = P < xcd * ps ? P : xcd * ps;
+  x.pc = (P < x.p0 + ps ? P : x.p0 + ps) - x.p0;
+  return x;
+}
+__device__ __host__ inline int xcd_unit(const UnitPlan& pl, const XcdSlice& x, int i) {
+  return i < x.fc ? x.f0 + i : pl.full + x.p0 + (i - x.fc);
+}
+
 // One unit of work: rows [r0, r1) of segment `seg`, output columns from n0,
 // K steps [kt0, kt1); slot >= 0 marks a K-part that writes partial tile `slot`.
 // Rows [x0, x1) (x0 == x1: none) are a segment's short tail attached to a

@@ -696,8 +696,8 @@ __device__ __forceinline__ void big_unit(const GemmParams& p, const Unit& w, uin
 
 // Persistent over the 256-row tile list: the grid holds one workgroup per CU,
 // XCD-major (workgroup b runs on XCD b % 8), and each XCD takes a contiguous
-// span of (tile, column tile, K-part) units so that the units sharing an
-// expert's weights meet in one L2.
+// span of the whole (tile, column tile) units, so that the units sharing an
+// expert's weights meet in one L2, and one of the K-part units (xcd_slice).
 template <int MODE, bool HAS_BIAS, bool GATHER>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) {
   // one LDS object: the operand stages, then the tile table (a second __shared__ object
@@ -712,16 +712,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(GemmParams p) 
   const int KT = p.K / kBK2;
   build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G, p.attach != 0);
   const UnitPlan pb = plan_units(segt.pb[p.n_seg] * p.n_ntiles, G, KT);
-  const int ub = pb.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  const int span_b = (ub + kXcds - 1) / kXcds;
-  const int b0 = min(ub, xcd * span_b), cb = min(ub, b0 + span_b) - b0;
+  const XcdSlice xs = xcd_slice(pb, xcd);
+  const int cb = xs.fc + xs.pc;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   for (int i = q; i < cb; i += per_xcd) {
-    const Unit w = decode_unit_lds(segt, p.n_seg, true, pb, b0 + i, p.n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_lds(segt, p.n_seg, true, pb, xcd_unit(pb, xs, i), p.n_ntiles, KT, cols_per_tile);
     big_unit<MODE, HAS_BIAS, GATHER>(p, w, lds, wave, lane);
   }
 }
@@ -1067,17 +1066,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_small_kernel(GemmParams p
   const int KT = p.K / kBK2;
   build_seg_table(segt, p.offsets, p.n_seg, p.dense_rows, p.kind, p.n_ntiles, G, p.attach != 0);
   const UnitPlan ps = plan_units(segt.ps[p.n_seg] * p.n_ntiles, G, KT);
-  const int us = ps.units();
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  const int span_s = (us + kXcds - 1) / kXcds;
-  const int s0 = min(us, xcd * span_s), cs = min(us, s0 + span_s) - s0;
+  const XcdSlice xs = xcd_slice(ps, xcd);
+  const int cs = xs.fc + xs.pc;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps buffer descriptors scalar
   const int lane = tid & 63;
   for (int i = q; i < cs; i += per_xcd) {
-    const Unit w = decode_unit_lds(segt, p.n_seg, false, ps, s0 + i, p.n_ntiles, KT, cols_per_tile);
+    const Unit w = decode_unit_lds(segt, p.n_seg, false, ps, xcd_unit(ps, xs, i), p.n_ntiles, KT, cols_per_tile);
     if (FP8) {
       if (w.r1 - w.r0 <= 32) small_unit_fp8<MODE, HAS_BIAS, GATHER, 1>(p, w, lds, wave, lane);
       else small_unit_fp8<MODE, HAS_BIAS, GATHER, 2>(p, w, lds, wave, lane);

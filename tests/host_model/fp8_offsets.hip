@@ -195,7 +195,15 @@ static long long cover_bad(int K, int Nn, int cols_per_tile, const std::vector<i
   long long bad = 0;
   for (int big = 0; big < 2; ++big) {
     const UnitPlan plan = plan_units((big ? t.pb[E] : t.ps[E]) * n_ntiles, G, KT);
-    for (int u = 0; u < plan.units(); ++u) {
+    // the units as the kernels reach them: workgroup q of XCD x walks its XCD's slices
+    std::vector<int> order;
+    for (int x = 0; x < kXcds; ++x) {
+      const XcdSlice xs = xcd_slice(plan, x);
+      for (int q = 0; q < G / kXcds; ++q)
+        for (int i = q; i < xs.fc + xs.pc; i += G / kXcds) order.push_back(xcd_unit(plan, xs, i));
+    }
+    if ((long long)order.size() != plan.units()) bad += 1000000;
+    for (int u : order) {
       const Unit w = decode_unit_seg(t, E, big != 0, plan, u, n_ntiles, KT, cols_per_tile);
       if (w.r1 - w.r0 > (big ? 256 : 64) || w.r0 < offs[w.seg] || w.r1 > offs[w.seg + 1] || w.r0 >= w.r1) {
         ++bad;

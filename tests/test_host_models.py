@@ -7,8 +7,9 @@ that the earlier tile list (decode_unit_plain over build_tiles_kernel's list)
 gave; so the split of the work, and the results, are unchanged.
 
 Tile kinds 0, 2, 3, 4 and 5 (short tails attached to whole 256-row tiles):
-the units decoded from the table cover every (row, column tile, K step) of
-every segment exactly once.
+the units decoded from the table, reached the way the kernels' workgroups
+reach them (each XCD's slices of whole and K-part units, xcd_slice), cover
+every (row, column tile, K step) of every segment exactly once.
 
 fp8 64-row tile: every operand load of every unit, for reduction lengths with
 odd 64-K step counts (K = 320) and the decode shapes' K-split parts (K = 4096,
@@ -51,6 +52,7 @@ CASES = [
     ("down", 14336, 4096, [40] * 5),
     ("down", 14336, 4096, [2, 3, 1, 4, 8, 5, 7]),
     ("down", 2048, 7168, [9, 26, 31, 0, 64, 1]),
+    ("up", 4096, 14336, [4] * 8),                         # decode: 896 tiles = 3 rounds + 128 tiles in 2 K-parts
     ("up", 4096, 14336, [1003, 1073, 1024, 1017, 1040, 1029, 1000, 1006]),   # Mixtral prefill: 256-row tiles + tails
     ("down", 14336, 4096, [4926, 0, 7, 130, 127, 128, 255, 256, 257, 383, 384, 1]),
 ]
