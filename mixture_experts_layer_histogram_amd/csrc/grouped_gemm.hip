@@ -850,15 +850,17 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
     store_block64<MODE, HAS_BIAS>(acc, ep, lane, kh, l32, wn, w.r0, w.r1, w.n0, p.Nn, w.seg, p.bias, p.out,
                                   p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
   } else {
-    // fp32 partial tile, row-major [slot][64 rows][256 accumulator columns]
+    // fp32 partial tile, row-major [slot][64 rows][256 accumulator columns]; only the tile's rows
+    // (the fix-up reads no others; a decode tile has a handful of its 64)
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
+    const int live = w.r1 - w.r0 - 4 * kh;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
+          if (mi * 32 + 8 * (r >> 2) + (r & 3) < live) dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
   }
   __syncthreads();   // the next unit's first loads must not overtake this epilogue
 }
@@ -1040,13 +1042,14 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
                                   p.bias_f, p.out_f, p.pre, p.pre_plane, &p.cmb);
   } else {
     float* dst = p.partials_small + (size_t)w.slot * (kBM3 * kBN2) + (size_t)(4 * kh) * kBN2 + wn * 64 + l32;
+    const int live = w.r1 - w.r0 - 4 * kh;   // the tile's rows only, as in small_unit
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
+          if (mi * 32 + 8 * (r >> 2) + (r & 3) < live) dst[(mi * 32 + 8 * (r >> 2) + (r & 3)) * kBN2 + ni * 32] = acc[mi][ni][r];
   }
   __syncthreads();   // the next unit's first loads must not overtake this epilogue
 }
