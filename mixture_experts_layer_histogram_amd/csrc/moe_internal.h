@@ -63,7 +63,27 @@ template <> struct Store<uint16_t> {
 __device__ __forceinline__ float silu_f(float u) {
   return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.44269504088896341f));
 }
-__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * erfcf(-u * 0.70710678118654752f); }
+// GELU u Phi(u) = (u / 2) erfc(-u / sqrt 2), erfc from the Chebyshev fit of Numerical Recipes (section
+// 6.2, "erfcc"): for z >= 0, erfc z = t exp(-z^2 + P(t)), t = 1 / (1 + z / 2), P of degree 9, with a
+// fractional error below 1.2e-7 everywhere; erfc(-z) = 2 - erfc z.  The hardware reciprocal and exp2
+// serve; evaluated in fp32 it changes one bf16 rounding in about 10^4 against the exact GELU, and
+// costs a third of the library erfc's instructions.
+__device__ __forceinline__ float gelu_f(float u) {
+  const float z = u * -0.70710678118654752f, az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, az, 1.0f));
+  float q = 0.17087277f;
+  q = fmaf(q, t, -0.82215223f);
+  q = fmaf(q, t, 1.48851587f);
+  q = fmaf(q, t, -1.13520398f);
+  q = fmaf(q, t, 0.27886807f);
+  q = fmaf(q, t, -0.18628806f);
+  q = fmaf(q, t, 0.09678418f);
+  q = fmaf(q, t, 0.37409196f);
+  q = fmaf(q, t, 1.00002368f);
+  q = fmaf(q, t, -1.26551223f);
+  const float r = t * __builtin_amdgcn_exp2f((q - az * az) * 1.44269504088896341f);
+  return 0.5f * u * (z >= 0.f ? r : 2.0f - r);
+}
 
 // Top-k blocking: L lanes per token (each owning E / L consecutive experts, at
 // most 8), so a wavefront routes 64 / L tokens at once.
