@@ -988,9 +988,29 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
     const int knx = kt0 + 2 * (j + 2);
     const bool nhalf = 2 * (j + 2) + 1 >= n64;
     const int nsub = 2 * j + 1 < n64 ? 8 : 4;   // a half step computes its first 64 K only
-    bf16x8 fa[2], fb[2];
+    // fragments of sub-step kk into buffer c: A as read, B's 8 code bytes converted to bf16; the
+    // next sub-step's are read and converted while this one's MFMAs issue (with one wavefront
+    // per SIMD nothing else would cover the LDS latency and the conversions)
+    bf16x8 fa[2][2], fb[2][2];
+    auto frag = [&](int kk, int c) {
+      const int hf = kk >> 2, kq = kk & 3;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (x < NMI)
+          fa[c][x] = *reinterpret_cast<const bf16x8*>(st + hf * (kBM3 * kBK2) + (32 * x + l32) * kBK2 +
+                                                      ((h ^ (4 * x) ^ (2 * kq)) << 3));
+        const int brow = brow0 + bstep * x;
+        // 8 code bytes read with the same element type as the A fragments (the compiler then
+        // keeps them apart from the in-flight LDS loads as it does for A)
+        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(
+            st + kStage8A + ((brow * kBK8 + ((kk ^ (x ? bsw1 : bsw0)) << 4) + kh * 8) >> 1));
+        fb[c][x] = fp8x8_to_bf16(__builtin_bit_cast(uint2, b4));
+      }
+    };
+    frag(0, 0);
 #pragma unroll
     for (int kk = 0; kk < kBK8 / 16; ++kk) {
+      const int c = kk & 1;
       if (more && kk < 5) {                   // next loads: 4 A, then 2 B in each of the next four sub-steps
         if (kk == 0) {
           FP8_LOAD_A(0, 0, nx, knx, nhalf); FP8_LOAD_A(0, 1, nx, knx, nhalf);
@@ -1000,24 +1020,12 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
         }
       }
       if (kk >= nsub) continue;
-      const int hf = kk >> 2, kq = kk & 3;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        if (x < NMI)
-          fa[x] = *reinterpret_cast<const bf16x8*>(st + hf * (kBM3 * kBK2) + (32 * x + l32) * kBK2 +
-                                                   ((h ^ (4 * x) ^ (2 * kq)) << 3));
-        const int brow = brow0 + bstep * x;
-        // 8 code bytes read with the same element type as the A fragments (the compiler then
-        // keeps them apart from the in-flight LDS loads as it does for A)
-        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(
-            st + kStage8A + ((brow * kBK8 + ((kk ^ (x ? bsw1 : bsw0)) << 4) + kh * 8) >> 1));
-        fb[x] = fp8x8_to_bf16(__builtin_bit_cast(uint2, b4));
-      }
+      if (kk + 1 < nsub) frag(kk + 1, c ^ 1);
 #pragma unroll
       for (int mi = 0; mi < NMI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
     }
   }
 #undef FP8_LOAD_A
