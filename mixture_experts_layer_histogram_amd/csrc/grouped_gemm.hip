@@ -742,13 +742,16 @@ __device__ __forceinline__ void small_unit(const GemmParams& p, const Unit& w, u
 
   // DMA: wavefront w fills A rows 16w..16w+15 (2 instructions) and B rows 64w..64w+63 (8).
   int voffa[2], voffb[8];
+  int pv[2];   // gather: the two token indices loaded back to back (rows past the tile read its last one)
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (GATHER) pv[u] = p.perm[min(w.r0 + 16 * wn + 8 * u + (lane >> 3), w.r1 - 1)];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = 16 * wn + 8 * u + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
-      const int r = w.r0 + row;
-      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      const int pr = w.r0 + row < w.r1 ? pv[u] : -1;   // -1 also: a padding row of the [E, C] layout
       voffa[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voffa[u] = row * rowbytes + chunk * 16;
@@ -913,13 +916,16 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
   constexpr int cols_per_tile = MODE == MODE_SWIGLU_UP ? kBN2 / 2 : kBN2;
 
   int voffa[2], voffb[8];
+  int pv[2];   // gather: the two token indices loaded back to back (rows past the tile read its last one)
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (GATHER) pv[u] = p.perm[min(w.r0 + 16 * wn + 8 * u + (lane >> 3), w.r1 - 1)];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = 16 * wn + 8 * u + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(row);
     if (GATHER) {
-      const int r = w.r0 + row;
-      const int pr = r < w.r1 ? p.perm[r] : -1;   // -1: a padding row of the [E, C] layout
+      const int pr = w.r0 + row < w.r1 ? pv[u] : -1;   // -1 also: a padding row of the [E, C] layout
       voffa[u] = (pr >= 0 ? (pr / p.gk) * rowbytes : kOobOffset) + chunk * 16;
     } else {
       voffa[u] = row * rowbytes + chunk * 16;
@@ -957,6 +963,17 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
+  // per-column weight scales (lane's column l32 of each 32-wide block), loaded before the first
+  // operand loads so that their latency is over by the epilogue (the waits below count them too:
+  // loads complete in issue order)
+  float sc[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int col = MODE == MODE_SWIGLU_UP ? w.n0 + 32 * wn + l32 : w.n0 + 64 * wn + 32 * ni + l32;
+    const float* sp = (MODE == MODE_SWIGLU_UP && ni == 1) ? p.scale3 : p.scale1;
+    sc[ni] = sp[(size_t)w.seg * p.Nn + min(col, p.Nn - 1)];
+    if (col >= p.Nn) sc[ni] = 0.f;
+  }
   // step j covers the 64-K steps kt0 + 2j and kt0 + 2j + 1 (the second only if < kt1)
   const int kt0 = w.kt0, n64 = w.kt1 - w.kt0, nst = (n64 + 1) >> 1;
   // loads of step j (k64 = kt0 + 2 j); `half`: step j is a half step (its second 64 K read as zero)
@@ -1030,14 +1047,6 @@ __device__ __forceinline__ void small_unit_fp8(const GemmParams& p, const Unit& 
   }
 #undef FP8_LOAD_A
 #undef FP8_LOAD_B
-  // per-column weight scales (lane's column l32 of each 32-wide block)
-  float sc[2];
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int col = MODE == MODE_SWIGLU_UP ? w.n0 + 32 * wn + l32 : w.n0 + 64 * wn + 32 * ni + l32;
-    const float* sp = (MODE == MODE_SWIGLU_UP && ni == 1) ? p.scale3 : p.scale1;
-    sc[ni] = col < p.Nn ? sp[(size_t)w.seg * p.Nn + col] : 0.f;
-  }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
