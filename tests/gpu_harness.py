@@ -6,7 +6,8 @@ import sys
 
 import numpy as np
 
-from workloads import (TINY_TOP2_FP32, MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, SWITCH_SKEWED,
+from workloads import (TINY_TOP2_FP32, MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, DEEPSEEK_V3_BALANCED,
+                       SWITCH_SKEWED,
                        make_inputs)
 
 # Tolerances of the parity bar: max|gpu - ref| / max|ref|.
@@ -25,7 +26,7 @@ SMALL = {
                                                 d_ff=512),
 }
 
-FULL = {c.name: c for c in (MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, SWITCH_SKEWED)}
+FULL = {c.name: c for c in (MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, DEEPSEEK_V3_BALANCED, SWITCH_SKEWED)}
 
 
 def say(*a):

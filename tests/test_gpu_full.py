@@ -13,7 +13,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["mixtral_prefill", "mixtral_decode", "switch_skewed", "deepseek_v3"])
+@pytest.mark.parametrize("name", ["mixtral_prefill", "mixtral_decode", "switch_skewed", "deepseek_v3",
+                                  "deepseek_v3_balanced"])
 def test_full_size_parity(name):
     cfg = FULL[name]
     say(f"full {name}: generating inputs")

@@ -93,11 +93,15 @@ DEEPSEEK_V3 = MoEConfig(
     d_ff_shared=2048, act=ACT_SWIGLU, gate_rule=GATE_SOFTMAX_RENORM, residual=True,
     sel_bias_range=0.05, gamma=1e-3, seed=1003)
 
+# The same layer at the balancing's starting point (selection biases zero): routing by the
+# scores alone, close to uniform over the experts (about 256 rows each).
+DEEPSEEK_V3_BALANCED = DEEPSEEK_V3.scaled(name="deepseek_v3_balanced", sel_bias_range=0.0)
+
 # delta = 3.7475 puts P(argmax = 3) at 0.900 for i.i.d. N(0,1) logits of 64 experts.
 SWITCH_SKEWED = MoEConfig(
     name="switch_skewed", n_tokens=16384, d_model=2048, n_experts=64, top_k=1, d_ff=8192,
     act=ACT_GELU, ffn_bias=True, gate_rule=GATE_SWITCH_TOP1, capacity_factor=1.25,
     residual=True, logit_offset=(3, 3.7475), aux_loss=True, init="uniform_experts", seed=1004)
 
-CONFIGS = [TINY_TOP2_FP32, MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, SWITCH_SKEWED]
+CONFIGS = [TINY_TOP2_FP32, MIXTRAL_PREFILL, MIXTRAL_DECODE, DEEPSEEK_V3, DEEPSEEK_V3_BALANCED, SWITCH_SKEWED]
 BY_NAME = {c.name: c for c in CONFIGS}

@@ -20,7 +20,8 @@ regenerated without the others):
   torch's CPU generator after ``manual_seed(0)``: eight experts
   Linear(d, 4d) / GELU / Linear(4d, d) first, then the bias-free router
   Linear(d, E), then ``randn(N, d)`` tokens;
-* selection bias ``~ U(-r, r)`` per expert (fp32); a fixed router logit offset
+* selection bias ``~ U(-r, r)`` per expert (fp32; zeros when ``r == 0`` and the layer has a
+  bias step); a fixed router logit offset
   ``(expert, delta)`` becomes an fp32 ``logit_bias[E]`` vector.
 """
 from __future__ import annotations
@@ -161,6 +162,8 @@ def make_inputs(cfg: MoEConfig, materialize_experts: bool = True,
     if cfg.sel_bias_range > 0:
         u = _rng(cfg, T_SEL_BIAS, 0).random(E, dtype=np.float32)
         sel_bias = ((u * np.float32(2.0) - np.float32(1.0)) * np.float32(cfg.sel_bias_range)).astype(np.float32)
+    elif cfg.gamma > 0:
+        sel_bias = np.zeros(E, np.float32)   # a bias step with no starting bias: the balancing's first step
     inp = LayerInputs(cfg=cfg, x=x, w_router=w_router, logit_bias=logit_bias, sel_bias=sel_bias)
     if Fs > 0:
         inp.sh_w1 = _normal(cfg, T_SH_W1, 0, (Fs, d), 1.0 / math.sqrt(d))
