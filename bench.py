@@ -14,6 +14,9 @@ algorithmic FLOPs over kept rows / its HIP-event time on the launch stream
 inside the timed region; `traffic` = rocprofv3 FETCH_SIZE + WRITE_SIZE bytes
 per call, scaled by a copy kernel, when taken on the current source);
 `cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+`measured_ceilings` are the chip's read-stream and bf16 MFMA rates measured in the
+same run by the library's probes; each roofline carries `frac_of_measured` (the
+same achieved rate against them) next to `frac` (against the published peaks).
 """
 from __future__ import annotations
 
@@ -66,6 +69,9 @@ def parse():
     ap.add_argument("--no-library-reference", action="store_true",
                     help="skip timing the vendor library (torch.matmul, hipBLASLt) on the dense equivalent of the "
                          "up projection (a comparison point for the roofline, reported as library_reference)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the chip's read-stream and MFMA ceilings with the library's probes "
+                         "(reported as measured_ceilings, with frac_of_measured next to each roofline frac)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -129,9 +135,66 @@ def main():
                                                             "expert_gemms", "up_call_ms_timed", "breakdown_ms")}
     if not args.no_library_reference and cfg.dtype == "bf16" and not args.fp8_experts:
         result["library_reference"] = library_reference(cfg, result["config"]["kept_slots"])
+    if not args.no_ceilings:
+        ceil = measured_ceilings()
+        result["measured_ceilings"] = ceil
+        for sub in [result] + list(result.get("other_shapes", {}).values()):
+            add_measured_fracs(sub, ceil)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.oracle_tokens, args.fp8_experts)
     print(json.dumps(result), flush=True)
+
+
+def measured_ceilings(hbm_gib=4, mfma_iters=400000, reps=5):
+    """The chip's practical ceilings, measured in the same run by the library's probes: one
+    read of a 4 GiB buffer (moe_probe_hbm_read: 16-byte nontemporal loads, one persistent
+    workgroup per CU) and a stream of independent bf16 MFMAs on random operands on every
+    wavefront (moe_probe_mfma_bf16).  Context for the roofline fractions, which stay against
+    the published peaks."""
+    import torch
+    import mixture_experts_layer_histogram_amd as M
+    buf = torch.empty(hbm_gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ops = torch.randn(4096, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record()
+        for i in range(reps):
+            f()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+    hbm_ms = timed(lambda: M.probe_hbm_read(buf, sink))
+    mfma_ms = timed(lambda: M.probe_mfma_bf16(ops, mfma_iters, sink))
+    flop = float(M.probe_mfma_flop_per_iter()) * mfma_iters
+    nbytes = buf.numel()
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read": {"kernel": "moe_probe_hbm_read", "bytes": nbytes, "ms": hbm_ms,
+                         "GBps": nbytes / (hbm_ms * 1e-3) / 1e9},
+            "mfma_bf16": {"kernel": "moe_probe_mfma_bf16", "flop": flop, "ms": mfma_ms,
+                          "TFLOPs": flop / (mfma_ms * 1e-3) / 1e12},
+            "note": "measured in this run on this GPU; roofline fractions stay against the published peaks "
+                    "(HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s); frac_of_measured divides by these"}
+
+
+def add_measured_fracs(res, ceil):
+    """frac_of_measured next to frac: the same achieved rate against the measured ceilings."""
+    roof = res.get("roofline")
+    if roof and roof.get("bound") == "hbm":
+        roof["frac_of_measured"] = roof["achieved"] / ceil["hbm_read"]["GBps"]
+    elif roof and roof.get("bound") == "mfma":
+        roof["frac_of_measured"] = roof["achieved"] / ceil["mfma_bf16"]["TFLOPs"]
+    g = res.get("expert_gemms")
+    if g:
+        t = max(g["algorithmic_flop"] / (ceil["mfma_bf16"]["TFLOPs"] * 1e12),
+                g["algorithmic_bytes"] / (ceil["hbm_read"]["GBps"] * 1e9)) * 1e3
+        g["frac_of_measured"] = t / g["ms"]
 
 
 def library_reference(cfg, kept, reps=10):

@@ -424,6 +424,32 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                         float d_aux, const moe_saved* saved, const moe_grads* grads, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Measurement probes.  They compute nothing of the layer: they measure, on
+ * the GPU at hand, the practical ceilings of the two resources its kernels are
+ * bound by, so that a benchmark can state roofline fractions against what the
+ * chip sustains as well as against its published peaks (HBM 8 TB/s, dense
+ * bf16 MFMA 2.5 PFLOP/s).  Each enqueues one kernel on `stream`; time it with
+ * events on that stream.
+ *
+ * moe_probe_hbm_read: reads `bytes` of the device buffer `buf` once (16-byte
+ *   nontemporal loads, one persistent workgroup per CU, 256 KB chunks dealt
+ *   round robin).  `sink` is a device uint32 the kernel may overwrite.
+ *   Errors: MOE_ERR_ARG for a NULL buf or sink with bytes > 0;
+ *   MOE_ERR_UNSUPPORTED when buf is not 16-byte aligned or bytes is not a
+ *   multiple of 16.
+ * moe_probe_mfma_bf16: every CU runs 8 wavefronts that each issue `iters`
+ *   rounds of two independent v_mfma_f32_32x32x16_bf16 on operands read
+ *   once from `operands` (at least 4 KB of device bf16 data, 16-byte aligned;
+ *   random values give the switching activity of real data).  `sink` is a
+ *   device float the kernel may overwrite.  Errors: MOE_ERR_ARG for iters < 0
+ *   or a NULL pointer with iters > 0; MOE_ERR_UNSUPPORTED for an unaligned
+ *   operand buffer.
+ * moe_probe_mfma_flop_per_iter: the FLOPs one iteration of
+ *   moe_probe_mfma_bf16 performs on the current device (host only). */
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+moe_status moe_probe_mfma_bf16(const void* operands, int64_t iters, float* sink, hipStream_t stream);
+moe_status moe_probe_mfma_flop_per_iter(int64_t* flop);
+
 /* Static text for a status code. */
 const char* moe_status_str(moe_status s);
 

@@ -72,6 +72,9 @@ _SIGS = {
     "moe_expert_down_combine": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t,
                                 _P],
     "moe_quantize_fp8": [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P],
+    "moe_probe_hbm_read": [_P, c_size_t, _P, _P],
+    "moe_probe_mfma_bf16": [_P, ctypes.c_int64, _P, _P],
+    "moe_probe_mfma_flop_per_iter": [ctypes.POINTER(c_int64)],
     "moe_expert_up_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_expert_down_fp8": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
     "moe_shared_ffn": [ctypes.POINTER(MoeConfig), _P, _P, _P, _P, _P, _P, _P, c_size_t, _P],
@@ -224,6 +227,22 @@ def quantize_fp8(w, q, scales, stream=None):
     cols = int(w.shape[-1])
     rows = int(w.numel() // cols) if cols else 0
     _call("moe_quantize_fp8", _ptr(w), rows, cols, _ptr(q), _ptr(scales), _stream(stream))
+
+
+def probe_hbm_read(buf, sink, stream=None):
+    """moe_probe_hbm_read: one read of every byte of `buf` (a device tensor)."""
+    _call("moe_probe_hbm_read", _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream))
+
+
+def probe_mfma_bf16(operands, iters, sink, stream=None):
+    """moe_probe_mfma_bf16: `iters` rounds of independent bf16 MFMAs on every wavefront of the chip."""
+    _call("moe_probe_mfma_bf16", _ptr(operands), int(iters), _ptr(sink), _stream(stream))
+
+
+def probe_mfma_flop_per_iter() -> int:
+    n = c_int64(0)
+    _call("moe_probe_mfma_flop_per_iter", ctypes.byref(n))
+    return n.value
 
 
 def expert_up_fp8(cfg, x, perm, offsets, w1q, w3q, s1, s3, h_tmp, b1=None, ws=None, stream=None):

@@ -598,6 +598,36 @@ moe_status moe_quantize_fp8(const void* w, int64_t rows, int32_t cols, uint8_t* 
   }
 }
 
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  try {
+    if (bytes > 0 && (!buf || !sink)) return MOE_ERR_ARG;
+    if (!aligned16(buf) || bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    MOE_HIP(launch_hbm_read_probe(buf, bytes, sink, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_probe_mfma_bf16(const void* operands, int64_t iters, float* sink, hipStream_t stream) {
+  try {
+    if (iters < 0) return MOE_ERR_ARG;
+    if (iters > 0 && (!operands || !sink)) return MOE_ERR_ARG;
+    if (!aligned16(operands)) return MOE_ERR_UNSUPPORTED;
+    MOE_HIP(launch_mfma_probe(operands, iters, sink, stream));
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_probe_mfma_flop_per_iter(int64_t* flop) {
+  if (!flop) return MOE_ERR_ARG;
+  // every wavefront of the grid (G CUs x 8) issues two 32x32x16 MFMAs per iteration
+  *flop = (int64_t)probe_grid() * 8 * 2 * (2ll * 32 * 32 * 16);
+  return MOE_OK;
+}
+
 moe_status moe_expert_up_fp8(const moe_config* cfg, const void* x, const int32_t* perm, const int32_t* offsets,
                              const uint8_t* w1q, const uint8_t* w3q, const float* s1, const float* s3,
                              const void* b1, void* h_tmp, void* ws, size_t ws_bytes, hipStream_t stream) {

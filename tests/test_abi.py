@@ -189,3 +189,21 @@ def test_permute_noalloc_rejects_before_launch():
     c = _cfg()
     assert L.moe_permute_noalloc(ctypes.byref(c), P, None, None, P, P, P, None, None, None) == _lib.MOE_ERR_ARG
     assert L.moe_permute_noalloc(ctypes.byref(c), P, None, P, P, P, P, None, P, None) == _lib.MOE_ERR_ARG
+
+
+def test_probes_reject_before_launch():
+    """The measurement probes validate before any launch: NULL buffers with work to do are
+    MOE_ERR_ARG, unaligned buffers or lengths MOE_ERR_UNSUPPORTED, a negative iteration count
+    MOE_ERR_ARG; zero work enqueues nothing and succeeds."""
+    L = M.lib()
+    P = 4096
+    assert L.moe_probe_hbm_read(None, 16, P, None) == _lib.MOE_ERR_ARG
+    assert L.moe_probe_hbm_read(P, 16, None, None) == _lib.MOE_ERR_ARG
+    assert L.moe_probe_hbm_read(P + 8, 16, P, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_probe_hbm_read(P, 24, P, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_probe_hbm_read(None, 0, None, None) == _lib.MOE_OK
+    assert L.moe_probe_mfma_bf16(P, -1, P, None) == _lib.MOE_ERR_ARG
+    assert L.moe_probe_mfma_bf16(None, 5, P, None) == _lib.MOE_ERR_ARG
+    assert L.moe_probe_mfma_bf16(P + 4, 5, P, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_probe_mfma_bf16(None, 0, None, None) == _lib.MOE_OK
+    assert L.moe_probe_mfma_flop_per_iter(None) == _lib.MOE_ERR_ARG
