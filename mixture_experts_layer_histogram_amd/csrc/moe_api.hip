@@ -72,6 +72,11 @@ Workspace workspace_layout(const moe_config& c) {
   return W;
 }
 
+// measurement probes (probe.hip)
+hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_mfma_probe(const void* operands, long long iters, float* sink, hipStream_t s);
+int probe_grid();
+
 }  // namespace moe
 
 using namespace moe;

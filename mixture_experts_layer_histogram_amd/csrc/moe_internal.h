@@ -212,10 +212,6 @@ size_t grouped_gemm_partials_bytes();
 size_t grouped_gemm_gather_max_bytes();   // largest token matrix (bytes) the bf16 gather path addresses
 
 // Per-row fp8 (E4M3) quantisation of a bf16 [rows, cols] matrix: codes and fp32 scales.
-// measurement probes (probe.hip)
-hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
-hipError_t launch_mfma_probe(const void* operands, long long iters, float* sink, hipStream_t s);
-int probe_grid();
 hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint8_t* q, float* scales,
                                hipStream_t s);
 
